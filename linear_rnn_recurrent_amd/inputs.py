@@ -1,0 +1,234 @@
+"""Seeded synthetic inputs for the selective state update.
+
+This module only draws random numbers and casts them to storage dtypes; it
+holds none of the update's arithmetic.  Both the HIP path (through the tests
+and the benchmark) and the fp64 oracle consume exactly the tensors it returns:
+the oracle sees them upcast to float64, which is exact for fp32/fp16/bf16.
+
+Value recipe (per head h, per batch row b, per token t):
+  A[h]       = -exp(U(ln 1, ln 16))                     fp32
+  dt_bias[h] = log(expm1(U(1e-3, 0.1)))                 fp32  (softplus^-1 of U)
+  dt         ~ N(0, std 0.5)                            fp32
+  D[h]       ~ N(0, 1)                                  fp32
+  x, z       ~ N(0, 1)                                  io dtype
+  B, C       ~ N(0, std bc_std)                         bc dtype
+  state      ~ N(0, 1) or zeros                         state dtype
+Replay stash (the stash a verify prefill would have written):
+  DT         = exp(U(ln 4e-4, ln 0.33))                 fp32  (range of dt' above)
+  dA         = A[h] * DT, rounded once to fp32          fp32  (log-decay)
+  u          ~ N(0, 1), replayB ~ N(0, std 1/sqrt(dstate))
+Values are drawn in float64 (float32 for the large state pools), rounded to
+fp32, then cast on the CPU by torch (round to nearest even) to bf16/fp16.
+"""
+from dataclasses import dataclass, field
+from typing import Dict, Optional
+
+import numpy as np
+import torch
+
+DTYPES = {"f32": torch.float32, "f16": torch.float16, "bf16": torch.bfloat16}
+
+
+@dataclass
+class Workload:
+    """One batch of inputs.  `kind` is 'decode', 'prefill' or 'replay'."""
+    name: str
+    kind: str
+    dims: Dict[str, int]
+    tensors: Dict[str, Optional[torch.Tensor]]
+    dt_softplus: bool = True
+    active_batch: Optional[int] = None
+    notes: Dict[str, str] = field(default_factory=dict)
+
+    def __getitem__(self, k):
+        return self.tensors[k]
+
+
+def _t(a, dtype):
+    return torch.from_numpy(np.ascontiguousarray(a, dtype=np.float32)).to(DTYPES[dtype])
+
+
+def _head_params(rng, nheads):
+    A = -np.exp(rng.uniform(np.log(1.0), np.log(16.0), nheads))
+    dt_bias = np.log(np.expm1(rng.uniform(1e-3, 0.1, nheads)))
+    D = rng.standard_normal(nheads)
+    return A, dt_bias, D
+
+
+def _pool(rng, shape, dtype, zero=False):
+    if zero:
+        return torch.zeros(shape, dtype=DTYPES[dtype])
+    a = rng.standard_normal(int(np.prod(shape)), dtype=np.float32).reshape(shape)
+    return torch.from_numpy(a).to(DTYPES[dtype])
+
+
+def decode_workload(*, batch, nheads, dim, dstate, ngroups, pool_rows, seed,
+                    state_dtype="f32", io_dtype="bf16", bc_dtype="bf16",
+                    bc_std=None, indices="perm", n_live=None, with_z=True,
+                    with_D=True, with_bias=True, dt_softplus=True,
+                    zero_state=False, name="decode"):
+    """indices: 'perm' (unique rows of the pool), 'none' (row = b), or an int list.
+    n_live: keep the first n_live indices, pad the rest with -1."""
+    rng = np.random.default_rng(seed)
+    if bc_std is None:
+        bc_std = 1.0
+    A, dt_bias, D = _head_params(rng, nheads)
+    state = _pool(rng, (pool_rows, nheads, dim, dstate), state_dtype, zero_state)
+    x = rng.standard_normal((batch, nheads, dim))
+    z = rng.standard_normal((batch, nheads, dim))
+    Bm = rng.standard_normal((batch, ngroups, dstate)) * bc_std
+    Cm = rng.standard_normal((batch, ngroups, dstate)) * bc_std
+    dt = rng.standard_normal((batch, nheads)) * 0.5
+    if isinstance(indices, str) and indices == "perm":
+        idx = rng.permutation(pool_rows)[:batch].astype(np.int32)
+    elif isinstance(indices, str) and indices == "none":
+        idx = None
+    else:
+        idx = np.asarray(indices, dtype=np.int32)
+    if idx is not None and n_live is not None:
+        idx = idx.copy()
+        idx[n_live:] = -1
+    T = {
+        "x": _t(x, io_dtype), "z": _t(z, io_dtype) if with_z else None,
+        "B": _t(Bm, bc_dtype), "C": _t(Cm, bc_dtype), "dt": _t(dt, "f32"),
+        "A": _t(A, "f32"), "dt_bias": _t(dt_bias, "f32") if with_bias else None,
+        "D": _t(D, "f32") if with_D else None, "state": state,
+        "state_indices": None if idx is None else torch.from_numpy(idx),
+    }
+    dims = dict(batch=batch, nheads=nheads, dim=dim, dstate=dstate, ngroups=ngroups,
+                pool_rows=pool_rows, seq_len=1)
+    return Workload(name, "decode", dims, T, dt_softplus)
+
+
+def prefill_workload(*, batch, seq_len, nheads, dim, dstate, ngroups, pool_rows, seed,
+                     state_dtype="f32", io_dtype="bf16", bc_dtype="bf16", bc_std=None,
+                     ctx=("uniform", 1, None), indices="perm", n_live=None,
+                     with_z=True, with_D=True, with_bias=True, dt_softplus=True,
+                     zero_state=False, name="prefill"):
+    """ctx: ('uniform', lo, hi) inclusive (hi None -> seq_len), ('none',), or a list."""
+    rng = np.random.default_rng(seed)
+    if bc_std is None:
+        bc_std = 1.0
+    A, dt_bias, D = _head_params(rng, nheads)
+    state = _pool(rng, (pool_rows, nheads, dim, dstate), state_dtype, zero_state)
+    x = rng.standard_normal((batch, seq_len, nheads, dim))
+    z = rng.standard_normal((batch, seq_len, nheads, dim))
+    Bm = rng.standard_normal((batch, seq_len, ngroups, dstate)) * bc_std
+    Cm = rng.standard_normal((batch, seq_len, ngroups, dstate)) * bc_std
+    dt = rng.standard_normal((batch, seq_len, nheads)) * 0.5
+    if ctx[0] == "uniform":
+        hi = seq_len if ctx[2] is None else ctx[2]
+        cl = rng.integers(ctx[1], hi + 1, batch).astype(np.int32)
+    elif ctx[0] == "none":
+        cl = None
+    else:
+        cl = np.asarray(ctx, dtype=np.int32)
+    if isinstance(indices, str) and indices == "perm":
+        idx = rng.permutation(pool_rows)[:batch].astype(np.int32)
+    elif isinstance(indices, str) and indices == "none":
+        idx = None
+    else:
+        idx = np.asarray(indices, dtype=np.int32)
+    if idx is not None and n_live is not None:
+        idx = idx.copy()
+        idx[n_live:] = -1
+    T = {
+        "x": _t(x, io_dtype), "z": _t(z, io_dtype) if with_z else None,
+        "B": _t(Bm, bc_dtype), "C": _t(Cm, bc_dtype), "dt": _t(dt, "f32"),
+        "A": _t(A, "f32"), "dt_bias": _t(dt_bias, "f32") if with_bias else None,
+        "D": _t(D, "f32") if with_D else None, "state": state,
+        "context_lengths": None if cl is None else torch.from_numpy(cl),
+        "state_indices": None if idx is None else torch.from_numpy(idx),
+    }
+    dims = dict(batch=batch, nheads=nheads, dim=dim, dstate=dstate, ngroups=ngroups,
+                pool_rows=pool_rows, seq_len=seq_len)
+    return Workload(name, "prefill", dims, T, dt_softplus)
+
+
+def replay_workload(*, active_batch, seq_len, nheads, dim, dstate, ngroups, pool_rows,
+                    seed, state_dtype="f32", accepted=("uniform", 0, None),
+                    indices="perm", n_live=None, stash_batch=None, name="replay"):
+    """stash_batch: leading extent of the stash and accepted arrays (>= active_batch);
+    entries at or beyond active_batch are filled with poison values."""
+    rng = np.random.default_rng(seed)
+    nb = active_batch if stash_batch is None else stash_batch
+    A, _, _ = _head_params(rng, nheads)
+    state = _pool(rng, (pool_rows, nheads, dim, dstate), state_dtype)
+    DT = np.exp(rng.uniform(np.log(4e-4), np.log(0.33), (nb, seq_len, nheads))).astype(np.float32)
+    dA = (A.astype(np.float32)[None, None, :] * DT).astype(np.float32)
+    u = rng.standard_normal((nb, seq_len, nheads, dim))
+    Bst = rng.standard_normal((nb, seq_len, ngroups, dstate)) / np.sqrt(dstate)
+    if accepted[0] == "uniform":
+        hi = seq_len if accepted[2] is None else accepted[2]
+        acc = rng.integers(accepted[1], hi + 1, nb).astype(np.int32)
+    else:
+        acc = np.asarray(accepted, dtype=np.int32)
+    if nb > active_batch:
+        acc[active_batch:] = 1 << 30   # poison: must never be read
+    if isinstance(indices, str) and indices == "perm":
+        idx = rng.permutation(pool_rows)[:nb].astype(np.int32)
+    elif isinstance(indices, str) and indices == "none":
+        idx = None
+    else:
+        idx = np.asarray(indices, dtype=np.int32)
+    if idx is not None and n_live is not None:
+        idx = idx.copy()
+        idx[n_live:] = -1
+    T = {
+        "state": state, "replay_dA": _t(dA, "f32"), "replay_u": _t(u, "f32"),
+        "replay_B": _t(Bst, "f32"), "replay_dt": _t(DT, "f32"),
+        "accepted_lengths": torch.from_numpy(acc),
+        "state_indices": None if idx is None else torch.from_numpy(idx),
+        "A": _t(A, "f32"),
+    }
+    dims = dict(batch=active_batch, nheads=nheads, dim=dim, dstate=dstate, ngroups=ngroups,
+                pool_rows=pool_rows, seq_len=seq_len)
+    return Workload(name, "replay", dims, T, False, active_batch=active_batch)
+
+
+# ---------------------------------------------------------------------------
+# The five benchmark configurations.
+# ---------------------------------------------------------------------------
+CONFIG_NAMES = {
+    0: "tiny decode B2 H4 Dm16 N16 G1, fp32 pool P4",
+    1: "Mamba2-2.7B-shaped decode B64 H80 Dm64 N128 G1, fp32 pool P256",
+    2: "prefill B8 T512 H80 Dm64 N128 G1, ctx~U[64,512], fp32 pool P64 (zeros)",
+    3: "padded decode B128 (97 live) H64 Dm64 N128 G8, fp16 pool P160",
+    4: "MTP replay active32/48 T4 H80 Dm64 N128 G1, fp32 pool P48",
+}
+
+
+def config(i: int, seed: Optional[int] = None) -> Workload:
+    s = i if seed is None else seed
+    if i == 0:
+        return decode_workload(batch=2, nheads=4, dim=16, dstate=16, ngroups=1, pool_rows=4,
+                               seed=s, state_dtype="f32", io_dtype="f32", bc_dtype="f32",
+                               bc_std=1.0, indices=[2, 0], name=CONFIG_NAMES[0])
+    if i == 1:
+        return decode_workload(batch=64, nheads=80, dim=64, dstate=128, ngroups=1,
+                               pool_rows=256, seed=s, state_dtype="f32", io_dtype="bf16",
+                               bc_dtype="bf16", bc_std=1.0 / np.sqrt(128), name=CONFIG_NAMES[1])
+    if i == 2:
+        return prefill_workload(batch=8, seq_len=512, nheads=80, dim=64, dstate=128,
+                                ngroups=1, pool_rows=64, seed=s, state_dtype="f32",
+                                io_dtype="bf16", bc_dtype="bf16", bc_std=1.0 / np.sqrt(128),
+                                ctx=("uniform", 64, 512), zero_state=True,
+                                name=CONFIG_NAMES[2])
+    if i == 3:
+        return decode_workload(batch=128, nheads=64, dim=64, dstate=128, ngroups=8,
+                               pool_rows=160, seed=s, state_dtype="f16", io_dtype="bf16",
+                               bc_dtype="bf16", bc_std=1.0 / np.sqrt(128), n_live=97,
+                               name=CONFIG_NAMES[3])
+    if i == 4:
+        return replay_workload(active_batch=32, seq_len=4, nheads=80, dim=64, dstate=128,
+                               ngroups=1, pool_rows=48, seed=s, state_dtype="f32",
+                               accepted=("uniform", 0, 4), name=CONFIG_NAMES[4])
+    raise ValueError(f"no configuration {i}")
+
+
+def rotation_index_sets(pool_rows: int, batch: int, seed: int):
+    """Disjoint index sets that together cover the whole pool (one per step)."""
+    rng = np.random.default_rng(seed)
+    perm = rng.permutation(pool_rows).astype(np.int32)
+    return [torch.from_numpy(perm[i:i + batch].copy())
+            for i in range(0, pool_rows - batch + 1, batch)]

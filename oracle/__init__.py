@@ -1,0 +1,125 @@
+"""fp64 CPU oracle for the selective state update (numpy front end over ssu_oracle.c).
+
+TEST INFRASTRUCTURE ONLY: tests/, __graft_entry__.smoke() and bench.py's
+cpu_baseline leg are the only callers.  The HIP library never imports, links
+or calls anything here, and nothing here imports the HIP library.
+
+All arrays are float64 (int32 for index arrays) in the layouts of the
+TensorRT-Edge-LLM "Selective State Update" page (invokeSelectiveStateUpdate
+shape list; invokeSelectiveStateUpdatePrefill; MambaReplayLayerInfo):
+
+  decode : x [b,h,d]  B,C [b,g,n]  dt [b,h]  z/out [b,h,d]
+  prefill: x [b,t,h,d]  B,C [b,t,g,n]  dt [b,t,h]  z/out [b,t,h,d]
+  replay : dA,DT [b,t,h]  u [b,t,h,d]  Bst [b,t,g,n]
+  state  : [rows, h, d, n], or a flat buffer with `row_stride` elements per row
+
+`state`, `out` and the stash arrays are updated in place.
+"""
+import ctypes
+import os
+
+import numpy as np
+
+from . import build as _build
+
+_LIB = None
+_F64P = ctypes.POINTER(ctypes.c_double)
+_I32P = ctypes.POINTER(ctypes.c_int32)
+
+
+def _lib():
+    global _LIB
+    if _LIB is None:
+        if not os.path.exists(_build.LIB):
+            _build.build()
+        lib = ctypes.CDLL(_build.LIB)
+        i32, i64 = ctypes.c_int32, ctypes.c_int64
+        lib.oracle_ssu_decode.argtypes = [i32] * 5 + [i64] + [_F64P] * 10 + [i32, _I32P]
+        lib.oracle_ssu_prefill.argtypes = ([i32] * 6 + [i64] + [_F64P] * 10 + [i32, _I32P, _I32P]
+                                           + [_F64P] * 5)
+        lib.oracle_ssu_replay.argtypes = [i32] * 6 + [i64] + [_F64P] * 5 + [_I32P, _I32P]
+        for f in (lib.oracle_ssu_decode, lib.oracle_ssu_prefill, lib.oracle_ssu_replay):
+            f.restype = None
+        _LIB = lib
+    return _LIB
+
+
+def _f64(a, name, writable=False):
+    if a is None:
+        return None, None
+    if not isinstance(a, np.ndarray) or a.dtype != np.float64 or not a.flags.c_contiguous:
+        if writable:
+            raise TypeError(f"{name} must be a C-contiguous float64 ndarray (updated in place)")
+        a = np.ascontiguousarray(a, dtype=np.float64)
+    return a, a.ctypes.data_as(_F64P)
+
+
+def _i32(a):
+    if a is None:
+        return None, None
+    a = np.ascontiguousarray(a, dtype=np.int32)
+    return a, a.ctypes.data_as(_I32P)
+
+
+def _row_stride(state, nheads, dim, dstate, row_stride):
+    tile = nheads * dim * dstate
+    if row_stride in (None, 0):
+        row_stride = tile
+    if row_stride < tile:
+        raise ValueError("row_stride smaller than one pool row")
+    return row_stride
+
+
+def decode(x, A, B, C, dt, state, out, *, dt_bias=None, D=None, z=None,
+           dt_softplus=True, state_indices=None, row_stride=None):
+    batch, nheads, dim = x.shape
+    ngroups, dstate = B.shape[1], B.shape[2]
+    rs = _row_stride(state, nheads, dim, dstate, row_stride)
+    keep = [_f64(v, k) for k, v in (("x", x), ("A", A), ("B", B), ("C", C), ("dt", dt),
+                                     ("dt_bias", dt_bias), ("D", D), ("z", z))]
+    st = _f64(state, "state", True)
+    ot = _f64(out, "out", True)
+    ix = _i32(state_indices)
+    _lib().oracle_ssu_decode(batch, nheads, dim, dstate, ngroups, rs,
+                             *[k[1] for k in keep[:8]], st[1], ot[1],
+                             1 if dt_softplus else 0, ix[1])
+
+
+def prefill(x, A, B, C, dt, state, out, *, dt_bias=None, D=None, z=None,
+            dt_softplus=True, context_lengths=None, state_indices=None,
+            stash=None, row_stride=None):
+    """stash: None or dict of float64 arrays 'dA', 'u', 'B', 'dt' (filled in)."""
+    batch, seq_len, nheads, dim = x.shape
+    ngroups, dstate = B.shape[2], B.shape[3]
+    rs = _row_stride(state, nheads, dim, dstate, row_stride)
+    keep = [_f64(v, k) for k, v in (("x", x), ("A", A), ("B", B), ("C", C), ("dt", dt),
+                                     ("dt_bias", dt_bias), ("D", D), ("z", z))]
+    st = _f64(state, "state", True)
+    ot = _f64(out, "out", True)
+    cl = _i32(context_lengths)
+    ix = _i32(state_indices)
+    if stash is not None:
+        sd = [_f64(stash[k], "stash " + k, True) for k in ("dA", "u", "B", "dt")]
+        scratch = np.empty(batch * nheads * dim * dstate, dtype=np.float64)
+        sp = [s[1] for s in sd] + [scratch.ctypes.data_as(_F64P)]
+    else:
+        sp = [None] * 5
+    _lib().oracle_ssu_prefill(batch, seq_len, nheads, dim, dstate, ngroups, rs,
+                              *[k[1] for k in keep[:8]], st[1], ot[1],
+                              1 if dt_softplus else 0, cl[1], ix[1], *sp)
+
+
+def replay(state, dA, u, Bst, DT, accepted_lengths, *, state_indices=None,
+           active_batch=None, row_stride=None):
+    nb, seq_len, nheads = dA.shape
+    dim = u.shape[3]
+    ngroups, dstate = Bst.shape[2], Bst.shape[3]
+    if active_batch is None:
+        active_batch = nb
+    rs = _row_stride(state, nheads, dim, dstate, row_stride)
+    keep = [_f64(v, k) for k, v in (("dA", dA), ("u", u), ("B", Bst), ("DT", DT))]
+    st = _f64(state, "state", True)
+    ac = _i32(accepted_lengths)
+    ix = _i32(state_indices)
+    _lib().oracle_ssu_replay(active_batch, seq_len, nheads, dim, dstate, ngroups, rs,
+                             st[1], *[k[1] for k in keep], ac[1], ix[1])

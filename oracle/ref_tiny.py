@@ -1,0 +1,156 @@
+"""Second, independent scalar oracle in pure Python (tiny shapes only).
+
+TEST INFRASTRUCTURE ONLY: imported by tests/ alone.  It is written apart from
+oracle/ssu_oracle.c (no shared code, different loop structure) so that the two
+can be checked against each other by brute force on small inputs.
+
+Definitions followed (TensorRT-Edge-LLM "Selective State Update" page):
+  * mamba_ssm::invokeSelectiveStateUpdate, "Computes":
+      new_state = state * exp(A * dt) + B * dt * x
+      output    = sum_i new_state_i * C_i + D * x, then * silu(z) if z is given
+  * invokeSelectiveStateUpdatePrefill: all seq_len tokens in order; with the
+    replay stash the committed state stays read-only.
+  * MambaReplayLayerInfo: replay the first acceptedLengths[b] stashed tokens.
+Padding rows (negative index) follow the FlashInfer gdn_fused_decode_step page,
+parameter state_indices.
+
+Every argument is a numpy float64/int32 array (or None) in the layouts of the
+C oracle; every loop below runs over Python scalars.
+"""
+import math
+
+
+def _sp(v):
+    # softplus(v) = log(1 + e^v) evaluated without overflow
+    if v > 0:
+        return v + math.log1p(math.exp(-v))
+    return math.log1p(math.exp(v))
+
+
+def _gate(zv):
+    return zv * (1.0 / (1.0 + math.exp(-zv)))
+
+
+def _dt_proc(raw, bias, softplus):
+    v = float(raw) + (0.0 if bias is None else float(bias))
+    return _sp(v) if softplus else v
+
+
+def _row(idx, b):
+    return b if idx is None else int(idx[b])
+
+
+def decode(x, A, B, C, dt, state, out, dt_bias=None, D=None, z=None,
+           dt_softplus=True, state_indices=None):
+    """x [b,h,d]; B,C [b,g,n]; dt [b,h]; state [rows,h,d,n]; out [b,h,d]."""
+    nb, nh, nd = x.shape
+    ng, ns = B.shape[1], B.shape[2]
+    per_group = nh // ng
+    for b in range(nb):
+        r = _row(state_indices, b)
+        for h in range(nh):
+            if r < 0:
+                for d in range(nd):
+                    out[b, h, d] = 0.0
+                continue
+            grp = h // per_group
+            dtp = _dt_proc(dt[b, h], None if dt_bias is None else dt_bias[h], dt_softplus)
+            dec = math.exp(float(A[h]) * dtp)
+            for d in range(nd):
+                xv = float(x[b, h, d])
+                total = 0.0
+                for n in range(ns):
+                    new = float(state[r, h, d, n]) * dec + float(B[b, grp, n]) * dtp * xv
+                    state[r, h, d, n] = new
+                    total += new * float(C[b, grp, n])
+                if D is not None:
+                    total += float(D[h]) * xv
+                if z is not None:
+                    total *= _gate(float(z[b, h, d]))
+                out[b, h, d] = total
+
+
+def prefill(x, A, B, C, dt, state, out, dt_bias=None, D=None, z=None,
+            dt_softplus=True, context_lengths=None, state_indices=None,
+            stash=None):
+    """x [b,t,h,d]; B,C [b,t,g,n]; dt [b,t,h]; out [b,t,h,d].
+
+    stash: None or dict with arrays 'dA' [b,t,h], 'u' [b,t,h,d], 'B' [b,t,g,n],
+    'dt' [b,t,h] that are filled in while the state is left untouched.
+    """
+    nb, nt, nh, nd = x.shape
+    ng, ns = B.shape[2], B.shape[3]
+    per_group = nh // ng
+    for b in range(nb):
+        r = _row(state_indices, b)
+        length = nt if context_lengths is None else min(max(int(context_lengths[b]), 0), nt)
+        if r < 0:
+            for t in range(nt):
+                for h in range(nh):
+                    for d in range(nd):
+                        out[b, t, h, d] = 0.0
+            continue
+        for h in range(nh):
+            grp = h // per_group
+            # a private copy of this head's state for the whole sequence
+            s = [[float(state[r, h, d, n]) for n in range(ns)] for d in range(nd)]
+            for t in range(nt):
+                if t >= length:
+                    for d in range(nd):
+                        out[b, t, h, d] = 0.0
+                    if stash is not None:
+                        stash['dA'][b, t, h] = 0.0
+                        stash['dt'][b, t, h] = 0.0
+                        for d in range(nd):
+                            stash['u'][b, t, h, d] = 0.0
+                        for n in range(ns):
+                            stash['B'][b, t, grp, n] = 0.0
+                    continue
+                dtp = _dt_proc(dt[b, t, h], None if dt_bias is None else dt_bias[h], dt_softplus)
+                dec = math.exp(float(A[h]) * dtp)
+                for d in range(nd):
+                    xv = float(x[b, t, h, d])
+                    total = 0.0
+                    for n in range(ns):
+                        s[d][n] = s[d][n] * dec + float(B[b, t, grp, n]) * dtp * xv
+                        total += s[d][n] * float(C[b, t, grp, n])
+                    if D is not None:
+                        total += float(D[h]) * xv
+                    if z is not None:
+                        total *= _gate(float(z[b, t, h, d]))
+                    out[b, t, h, d] = total
+                if stash is not None:
+                    stash['dA'][b, t, h] = float(A[h]) * dtp
+                    stash['dt'][b, t, h] = dtp
+                    for d in range(nd):
+                        stash['u'][b, t, h, d] = float(x[b, t, h, d])
+                    for n in range(ns):
+                        stash['B'][b, t, grp, n] = float(B[b, t, grp, n])
+            if stash is None:
+                for d in range(nd):
+                    for n in range(ns):
+                        state[r, h, d, n] = s[d][n]
+
+
+def replay(state, dA, u, Bst, DT, accepted_lengths, state_indices=None,
+           active_batch=None):
+    """dA, DT [b,t,h]; u [b,t,h,d]; Bst [b,t,g,n]; state [rows,h,d,n]."""
+    nb_stash, nt, nh = dA.shape
+    nd = u.shape[3]
+    ng, ns = Bst.shape[2], Bst.shape[3]
+    per_group = nh // ng
+    nb = nb_stash if active_batch is None else active_batch
+    for b in range(nb):
+        r = _row(state_indices, b)
+        steps = min(int(accepted_lengths[b]), nt)
+        if r < 0 or steps <= 0:
+            continue
+        for h in range(nh):
+            grp = h // per_group
+            for t in range(steps):
+                dec = math.exp(float(dA[b, t, h]))
+                for d in range(nd):
+                    for n in range(ns):
+                        state[r, h, d, n] = (float(state[r, h, d, n]) * dec
+                                             + float(Bst[b, t, grp, n]) * float(DT[b, t, h])
+                                             * float(u[b, t, h, d]))
