@@ -1,0 +1,300 @@
+#!/usr/bin/env python3
+"""Throughput of the selective state update on one MI355X.
+
+Default workload: decode of the Mamba2-2.7B-shaped batch (B=64, H=80, dim=64,
+dstate=128, G=1, fp32 state, bf16 x/z/B/C/out) over a 256-row fp32 pool
+(671 MB). One step is one ssu_decode launch over 64 rows; consecutive steps use
+four disjoint 64-row index sets that together cover the pool, so every step
+streams state rows the previous three steps did not touch and the 256 MB
+last-level cache cannot serve them.
+
+    python bench.py [--steps K] [--warmup W] [--config {1,2,3,4}]
+
+--config 2/3/4 time prefill / padded decode / MTP replay instead; those pools
+fit in the last-level cache, so each timed launch there is preceded by a 1 GiB
+write that evicts it, and only the kernel itself is timed.
+
+Prints one JSON line: value = algorithmic GB/s (bytes the method must move,
+each element counted once, divided by the average launch time measured with
+HIP events on the launch stream), plus token*head updates/s, the roofline
+object of the timed kernel and the fp64 oracle's throughput on the host
+(cpu_baseline, a reported baseline and not a target).
+"""
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0            # MI355X HBM3E, 8 TB/s
+VALU_PEAK_TOPS = 256 * 4 * 16 * 2.4e9 / 1e12   # fp32 VALU lane-ops/s without packed math
+
+
+def metric_name():
+    return "state-update GB/s and % of HBM peak; token·head updates/s (B=64 decode)"
+
+
+def esize(t):
+    return t.element_size()
+
+
+def decode_bytes(T, live):
+    """Algorithmic bytes of one decode launch (element counted once; B/C per group)."""
+    b, h, d = T["x"].shape
+    g, n = T["B"].shape[1], T["B"].shape[2]
+    s_s, s_x = esize(T["state"]), esize(T["x"])
+    s_z = esize(T["z"]) if T["z"] is not None else 0
+    per_live = h * d * n * 2 * s_s + h * d * (s_x + s_z) + 2 * g * n * esize(T["B"]) + 4 * h
+    return live * per_live + b * h * d * s_x + 12 * h + 4 * b
+
+
+def prefill_bytes(T, L):
+    b, t, h, d = T["x"].shape
+    g, n = T["B"].shape[2], T["B"].shape[3]
+    s_s, s_x = esize(T["state"]), esize(T["x"])
+    per_tok = h * d * (2 * s_x + (s_x if T["z"] is not None else 0)) + 2 * g * n * esize(T["B"]) + 4 * h
+    total = 0
+    for Lb in L:
+        total += h * d * n * 2 * s_s + int(Lb) * per_tok
+        total += (t - int(Lb)) * h * d * s_x
+    return total + 12 * h + 8 * b
+
+
+def replay_bytes(T, k_rows):
+    h = T["replay_dA"].shape[2]
+    d = T["replay_u"].shape[3]
+    g, n = T["replay_B"].shape[2], T["replay_B"].shape[3]
+    s_s = esize(T["state"])
+    total = 0
+    for k in k_rows:
+        if k > 0:
+            total += h * d * n * 2 * s_s + k * (4 * h * d + 4 * g * n + 8 * h)
+    return total + 8 * len(k_rows)
+
+
+def source_hash(*names):
+    hsh = hashlib.sha256()
+    for n in names:
+        with open(os.path.join(ROOT, "linear_rnn_recurrent_amd", "csrc", n), "rb") as f:
+            hsh.update(f.read())
+    return hsh.hexdigest()[:16]
+
+
+def measured_traffic(kernel_key, src_hash):
+    """HBM bytes per launch from the committed rocprofv3 counter summary, if it was
+    taken on the current kernel source; otherwise None."""
+    path = os.path.join(ROOT, "profiles", "traffic.json")
+    try:
+        with open(path) as f:
+            rec = json.load(f).get(kernel_key)
+    except (OSError, ValueError):
+        return None
+    if not rec or rec.get("source_hash") != src_hash:
+        return None
+    return rec.get("bytes_per_launch")
+
+
+def cpu_baseline(kind, w, seconds, bytes_per_call, units_per_call):
+    """The fp64 oracle, as it stands, on a bounded sample of the same workload."""
+    import numpy as np
+    import oracle
+
+    a = {k: (None if v is None else (v.double().numpy() if v.is_floating_point() else v.numpy()))
+         for k, v in w.tensors.items()}
+    if kind == "decode":
+        idx = a["state_indices"]
+        live = idx[idx >= 0]
+        st = a["state"][live].copy()                # compact pool of the addressed rows
+        remap = np.full(idx.shape, -1, dtype=np.int32)
+        remap[idx >= 0] = np.arange(live.size, dtype=np.int32)
+        out = np.zeros(a["x"].shape)
+
+        def call():
+            oracle.decode(a["x"], a["A"], a["B"], a["C"], a["dt"], st, out, dt_bias=a["dt_bias"],
+                          D=a["D"], z=a["z"], dt_softplus=w.dt_softplus, state_indices=remap)
+        sample = f"the full {a['x'].shape[0]}-row batch of this workload"
+    elif kind == "prefill":
+        st = a["state"].copy()
+        out = np.zeros(a["x"].shape)
+
+        def call():
+            oracle.prefill(a["x"], a["A"], a["B"], a["C"], a["dt"], st, out, dt_bias=a["dt_bias"],
+                           D=a["D"], z=a["z"], dt_softplus=w.dt_softplus,
+                           context_lengths=a["context_lengths"], state_indices=a["state_indices"])
+        sample = "the full prefill batch of this workload"
+    else:
+        st = a["state"].copy()
+
+        def call():
+            oracle.replay(st, a["replay_dA"], a["replay_u"], a["replay_B"], a["replay_dt"],
+                          a["accepted_lengths"], state_indices=a["state_indices"],
+                          active_batch=w.active_batch)
+        sample = "the full replay batch of this workload"
+    calls, t0 = 0, time.perf_counter()
+    while True:
+        call()
+        calls += 1
+        el = time.perf_counter() - t0
+        if el >= seconds:
+            break
+    gbs = bytes_per_call * calls / el / 1e9
+    return {"value": round(gbs, 4), "unit": "GB/s", "cores": oracle.num_threads(), "kind": "oracle",
+            "sample": f"{sample}, {calls} call(s) in {el:.1f} s (fp64, OpenMP)",
+            "token_head_updates_per_s": units_per_call * calls / el}
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__.splitlines()[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=400)
+    ap.add_argument("--warmup", type=int, default=40)
+    ap.add_argument("--config", type=int, default=1, choices=[1, 2, 3, 4])
+    ap.add_argument("--cpu-seconds", type=float, default=10.0)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print("bench.py measures one GPU: the selective state update needs no collective, "
+              "so only --gpus 1 is supported", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    from linear_rnn_recurrent_amd import inputs, load_library, ssu_decode, ssu_prefill, ssu_replay
+
+    load_library()
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    w = inputs.config(args.config)
+    T = {k: (None if v is None else v.to(dev)) for k, v in w.tensors.items()}
+    stream = torch.cuda.current_stream(dev)
+    flush = None
+
+    if args.config in (1, 3):
+        kind = "decode"
+        B = T["x"].shape[0]
+        if args.config == 1:
+            idx_sets = [s.to(dev) for s in inputs.rotation_index_sets(w.dims["pool_rows"], B, seed=1)]
+        else:
+            idx_sets = [T["state_indices"]]
+            flush = torch.empty(1 << 28, dtype=torch.float32, device=dev)
+        live = int((idx_sets[0] >= 0).sum().item())
+        nbytes = decode_bytes(T, live)
+        units = live * T["x"].shape[1]
+        out = torch.empty_like(T["x"])
+
+        def step(i):
+            ssu_decode(T["x"], T["A"], T["B"], T["C"], T["dt"], T["state"], out,
+                       dt_bias=T["dt_bias"], D=T["D"], z=T["z"], dt_softplus=w.dt_softplus,
+                       state_indices=idx_sets[i % len(idx_sets)])
+        src = source_hash("ssu_decode.hip", "ssu_device.h")
+        kkey = f"decode_config{args.config}"
+        bound, peak, unit = "hbm", HBM_PEAK_GBS, "GB/s"
+    elif args.config == 2:
+        kind = "prefill"
+        L = T["context_lengths"].clamp(0, T["x"].shape[1]).cpu().tolist()
+        nbytes = prefill_bytes(T, L)
+        units = sum(L) * T["x"].shape[2]
+        out = torch.empty_like(T["x"])
+        flush = torch.empty(1 << 28, dtype=torch.float32, device=dev)
+
+        def step(i):
+            ssu_prefill(T["x"], T["A"], T["B"], T["C"], T["dt"], T["state"], out,
+                        dt_bias=T["dt_bias"], D=T["D"], z=T["z"], dt_softplus=w.dt_softplus,
+                        context_lengths=T["context_lengths"], state_indices=T["state_indices"])
+        src = source_hash("ssu_prefill.hip", "ssu_device.h")
+        kkey = "prefill_config2"
+        elems = sum(L) * T["x"].shape[2] * T["x"].shape[3] * T["B"].shape[3]
+        bound, peak, unit = "alu", VALU_PEAK_TOPS, "TOP/s"
+    else:
+        kind = "replay"
+        acc = T["accepted_lengths"][: w.active_batch].cpu()
+        idx = T["state_indices"][: w.active_batch].cpu()
+        k_rows = [min(int(a), T["replay_dA"].shape[1]) if int(i) >= 0 else 0
+                  for a, i in zip(acc, idx)]
+        nbytes = replay_bytes(T, k_rows)
+        units = sum(k_rows) * T["replay_dA"].shape[2]
+        flush = torch.empty(1 << 28, dtype=torch.float32, device=dev)
+
+        def step(i):
+            ssu_replay(T["state"], T["replay_dA"], T["replay_u"], T["replay_B"], T["replay_dt"],
+                       T["accepted_lengths"], state_indices=T["state_indices"],
+                       active_batch=w.active_batch)
+        src = source_hash("ssu_replay.hip", "ssu_device.h")
+        kkey = "replay_config4"
+        bound, peak, unit = "hbm", HBM_PEAK_GBS, "GB/s"
+
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+    print(f"[bench] config {args.config} ({kind}) warmed up, timing {args.steps} steps",
+          file=sys.stderr, flush=True)
+
+    wall0 = time.perf_counter()
+    if flush is None:
+        # back-to-back launches on one stream; events on that same stream
+        ev0 = torch.cuda.Event(enable_timing=True)
+        ev1 = torch.cuda.Event(enable_timing=True)
+        ev0.record(stream)
+        for i in range(args.steps):
+            step(args.warmup + i)
+        ev1.record(stream)
+        torch.cuda.synchronize()
+        total_ms = ev0.elapsed_time(ev1)
+    else:
+        # evict the last-level cache before every launch; time the kernel alone
+        evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+               for _ in range(args.steps)]
+        for i, (e0, e1) in enumerate(evs):
+            flush.fill_(float(i))
+            e0.record(stream)
+            step(args.warmup + i)
+            e1.record(stream)
+        torch.cuda.synchronize()
+        total_ms = sum(e0.elapsed_time(e1) for e0, e1 in evs)
+    wall = time.perf_counter() - wall0
+    torch.cuda.synchronize()
+
+    ms = total_ms / args.steps
+    gbs = nbytes / (ms * 1e-3) / 1e9
+    if bound == "hbm":
+        achieved = gbs
+    else:
+        achieved = 3.0 * elems / (ms * 1e-3) / 1e12     # mul + fma + fma per element-token
+    traffic = measured_traffic(kkey, src)
+    rec = {
+        "metric": metric_name(),
+        "value": round(gbs, 2),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic",
+        "config": {"workload": inputs.CONFIG_NAMES[args.config]
+                   + ("; steps rotate 4 disjoint 64-row index sets over the pool"
+                      if args.config == 1 else "; LLC evicted before each timed launch"),
+                   "kernel": kind, "algorithmic_bytes_per_step": nbytes,
+                   "token_head_updates_per_step": units},
+        "hbm_frac": round(gbs / HBM_PEAK_GBS, 4),
+        "token_head_updates_per_s": round(units / (ms * 1e-3), 1),
+        "roofline": {"bound": bound, "achieved": round(achieved, 3), "peak": round(peak, 3),
+                     "unit": unit, "frac": round(achieved / peak, 4), "traffic": traffic},
+        "wall_s_timed": round(wall, 3),
+    }
+    if not args.no_cpu_baseline:
+        print(f"[bench] timing the fp64 oracle for about {args.cpu_seconds:.0f} s",
+              file=sys.stderr, flush=True)
+        rec["cpu_baseline"] = cpu_baseline(kind, w, args.cpu_seconds, nbytes, units)
+    print(json.dumps(rec), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,202 @@
+/*
+ * ssu.h -- C ABI of libssu: the Mamba-style selective state update (SSU) over a
+ * paged recurrent-state pool, for AMD Instinct MI355X (gfx950).
+ *
+ * Sources of the operations (page titles and the passage on each page):
+ *   [SSU]  TensorRT-Edge-LLM, "Selective State Update" page:
+ *          mamba_ssm::invokeSelectiveStateUpdate (decode, "Computes" paragraph
+ *          and shape list), invokeSelectiveStateUpdatePrefill (prefill loop,
+ *          replay stash), struct MambaReplayLayerInfo (replay reconstruct),
+ *          invokeMambaStateClear (slot clear, slot -1 = all).
+ *   [PAD]  FlashInfer, "flashinfer.gdn_fused_decode_step" page, parameters
+ *          ssm_state (paged pool, padded row stride) and state_indices
+ *          (negative index = padding row; index >= rows is a caller bug).
+ *   [RSM]  TensorRT-Edge-LLM, "Recurrent State Manager" page: constructor,
+ *          clear, clearSlot, capture, restore, copySlotFrom, bytesPerSlot,
+ *          stateBytesPerSlot, findState.
+ *
+ * Conventions shared by every entry point
+ *   - Every tensor pointer is a DEVICE pointer owned by the caller, dense
+ *     (C-contiguous) in the layout stated below, except that pool rows of
+ *     `state` may be padded (state_row_stride). state, B, C and replay_B are
+ *     read with 16-byte vector loads and must be 16-byte aligned; every other
+ *     pointer must be aligned to its element size.
+ *   - Every compute call is asynchronous on `stream` (0 = the null stream). It
+ *     allocates nothing, never synchronises and never reads device data on the
+ *     host, so it may be recorded under hipGraph stream capture.
+ *   - Host-side argument checks only. A failed check returns SSU_EINVAL or
+ *     SSU_ENOTSUP, launches nothing and writes nothing; ssu_last_error() then
+ *     describes it. Errors never propagate as C++ exceptions.
+ *   - Values inside device arrays are never validated: a negative state index
+ *     is a padding row [PAD]; an index >= pool rows, or the same live index
+ *     twice in one call, is undefined behaviour (a caller bug, as [PAD] states
+ *     for out-of-range indices).
+ *   - Floating-point arithmetic is fp32 whatever the storage dtype. fp16 and
+ *     bf16 stores round to nearest even.
+ */
+#ifndef SSU_H
+#define SSU_H
+
+#include <stddef.h>
+#include <stdint.h>
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef int32_t ssu_status;
+#define SSU_OK 0      /* success                                            */
+#define SSU_EINVAL 1  /* invalid argument (null pointer, bad shape, range)   */
+#define SSU_ENOTSUP 2 /* valid but unsupported (dtype, dstate)               */
+#define SSU_EHIP 3    /* a HIP runtime call or kernel launch failed          */
+#define SSU_ENOMEM 4  /* device allocation failed                            */
+
+/* Storage dtypes (ssu_dims fields and ssu_state_spec.dtype). */
+#define SSU_F32 0
+#define SSU_F16 1
+#define SSU_BF16 2
+#define SSU_U8 3 /* raw bytes: pool specs only */
+
+/* Geometry and dtypes of one call [SSU shape lists].
+ *   nheads % ngroups == 0; head h reads group h / (nheads / ngroups).
+ *   dstate in {16, 32, 64, 128, 256}; 1 <= dim <= 4096.
+ *   state_dtype: SSU_F32, SSU_F16 or SSU_BF16 ([SSU] "half or float"; bf16 extra).
+ *   io_dtype (x, z, out) and bc_dtype (B, C): SSU_F32, SSU_F16 or SSU_BF16.
+ *   A, dt, dt_bias, D and the replay stash are always fp32.
+ *   state_row_stride: elements between consecutive pool rows; 0 means dense
+ *   (nheads*dim*dstate). A larger stride is allowed [PAD ssm_state]; stride
+ *   times the element size must be a multiple of 16 bytes. */
+typedef struct ssu_dims {
+    int32_t batch;      /* rows of x / indices (decode, prefill); stash rows (replay) */
+    int32_t nheads;
+    int32_t dim;        /* head dimension */
+    int32_t dstate;
+    int32_t ngroups;
+    int32_t pool_rows;  /* leading extent of `state`; with no state_indices, batch <= pool_rows */
+    int64_t state_row_stride;
+    int32_t state_dtype;
+    int32_t io_dtype;
+    int32_t bc_dtype;
+    int32_t reserved;   /* must be 0 */
+} ssu_dims;
+
+/* ssu_decode -- one token (seq_len == 1) [SSU invokeSelectiveStateUpdate]:
+ *   dt'       = dt[b,h] + dt_bias[h];  dt' = softplus(dt') if dt_softplus
+ *   state[r,h,d,n] = state[r,h,d,n] * exp(A[h]*dt') + B[b,g,n] * dt' * x[b,h,d]
+ *   out[b,h,d]     = sum_n state[r,h,d,n]*C[b,g,n] + D[h]*x[b,h,d], then
+ *                    * silu(z[b,h,d]) if z is given
+ * with r = state_indices[b] (or b when state_indices is NULL).
+ * Layouts: x, z, out [batch, nheads, dim] (io_dtype); A, dt_bias, D [nheads];
+ * dt [batch, nheads]; B, C [batch, ngroups, dstate] (bc_dtype);
+ * state [pool_rows, nheads, dim, dstate] (state_dtype), updated in place.
+ * Padding [PAD]: r < 0 -> state not read or written, out[b] = +0.0.
+ * Optional (NULL allowed): dt_bias, D, z, state_indices. */
+ssu_status ssu_decode(const ssu_dims *dims, const void *x, const float *A, const void *B,
+                      const void *C, const float *dt, const float *dt_bias, const float *D,
+                      const void *z, void *state, void *out, int32_t dt_softplus,
+                      const int32_t *state_indices, hipStream_t stream);
+
+/* ssu_prefill -- seq_len tokens in one launch [SSU invokeSelectiveStateUpdatePrefill].
+ * Layouts: x, z, out [batch, seq_len, nheads, dim]; dt [batch, seq_len, nheads];
+ * B, C [batch, seq_len, ngroups, dstate]; other tensors as ssu_decode.
+ * context_lengths [batch] (NULL = all seq_len): row b runs tokens
+ * t < L_b = clamp(context_lengths[b], 0, seq_len) through the decode step in
+ * order and writes out[b,t] = +0.0 for t >= L_b; the state is left after L_b
+ * tokens (untouched when L_b == 0).
+ * Replay stash (all four or none) [SSU]: when given, the committed state is
+ * read-only and, for t < L_b, the kernel stores
+ *   replay_dA [batch, seq_len, nheads]          = A[h] * dt'   (log-decay)
+ *   replay_dt [batch, seq_len, nheads]          = dt'
+ *   replay_u  [batch, seq_len, nheads, dim]     = x  (unscaled, fp32)
+ *   replay_B  [batch, seq_len, ngroups, dstate] = B  (fp32)
+ * and zeros for t >= L_b; outputs are produced as without the stash.
+ * Padding rows: out[b,:] = +0.0, state and stash rows untouched. */
+ssu_status ssu_prefill(const ssu_dims *dims, int32_t seq_len, const void *x, const float *A,
+                       const void *B, const void *C, const float *dt, const float *dt_bias,
+                       const float *D, const void *z, void *state, void *out,
+                       int32_t dt_softplus, const int32_t *context_lengths,
+                       const int32_t *state_indices, float *replay_dA, float *replay_u,
+                       float *replay_B, float *replay_dt, hipStream_t stream);
+
+/* ssu_replay -- commit accepted draft tokens [SSU MambaReplayLayerInfo]:
+ * for b < active_batch with r = state_indices[b] >= 0 and
+ * k = min(accepted_lengths[b], seq_len) > 0, apply k tokens in place:
+ *   state[r,h,d,n] = state[r,h,d,n]*exp(replay_dA[b,t,h])
+ *                    + replay_B[b,t,g,n]*replay_dt[b,t,h]*replay_u[b,t,h,d]
+ * Stash layouts as ssu_prefill with dims->batch rows (the allocation);
+ * accepted_lengths and state_indices [dims->batch] int32. Entries at
+ * b >= active_batch are never read; rows with k == 0 are left untouched.
+ * Requires 0 <= active_batch <= dims->batch. state_indices may be NULL (r = b). */
+ssu_status ssu_replay(const ssu_dims *dims, int32_t seq_len, void *state,
+                      const float *replay_dA, const float *replay_u, const float *replay_B,
+                      const float *replay_dt, const int32_t *accepted_lengths,
+                      const int32_t *state_indices, int32_t active_batch, hipStream_t stream);
+
+/* ------------------------------------------------------------------------
+ * Recurrent-state pool [RSM]: one zeroed, contiguous slab per state spec,
+ * shaped [slot_count] + spec.shape, so slot s of state i starts at byte
+ * s * stateBytesPerSlot(i) of slab i. Spec order is fixed: capture and
+ * restore match buffers to states by position.
+ * ---------------------------------------------------------------------- */
+typedef struct ssu_pool ssu_pool; /* opaque; not copyable, freed once */
+
+typedef struct ssu_state_spec {
+    int32_t kind;     /* caller-defined state kind (e.g. 0 recurrent, 1 conv) */
+    int32_t layer;    /* absolute layer index, >= 0 */
+    int32_t rank;     /* entries of shape in use, 1..4 */
+    int32_t dtype;    /* SSU_F32, SSU_F16, SSU_BF16 or SSU_U8 */
+    int64_t shape[4]; /* per-slot shape; every used entry > 0 */
+} ssu_state_spec;
+
+/* Bytes one slot occupies across `specs` (static: no pool needed) [RSM bytesPerSlot].
+ * Fails with SSU_EINVAL on an invalid spec list (see ssu_pool_alloc). */
+ssu_status ssu_pool_bytes_per_slot(const ssu_state_spec *specs, int32_t n_specs, size_t *out);
+
+/* Allocate one zeroed slab per spec on the current device; the zeroing runs on
+ * `stream` [RSM constructor]. SSU_EINVAL if a spec has non-positive volume, a
+ * negative layer, a bad rank or dtype, or repeats a {kind, layer} pair.
+ * slot_count == 0 or n_specs == 0 gives a valid pool that owns no memory.
+ * The pool keeps its own copy of the specs. Free with ssu_pool_free. */
+ssu_status ssu_pool_alloc(const ssu_state_spec *specs, int32_t n_specs, int32_t slot_count,
+                          hipStream_t stream, ssu_pool **out);
+/* Release the slabs (after synchronising the device). NULL is a no-op. */
+ssu_status ssu_pool_free(ssu_pool *pool);
+/* Geometry queries [RSM slotCount, numStates, state, stateBytesPerSlot, findState]. */
+ssu_status ssu_pool_info(const ssu_pool *pool, int32_t *num_states, int32_t *slot_count);
+ssu_status ssu_pool_state_ptr(const ssu_pool *pool, int32_t state_idx, void **dev_ptr);
+ssu_status ssu_pool_state_bytes_per_slot(const ssu_pool *pool, int32_t state_idx, size_t *out);
+/* *state_idx = index of the state with this {kind, layer}, or -1 if none. */
+ssu_status ssu_pool_find_state(const ssu_pool *pool, int32_t kind, int32_t layer,
+                               int32_t *state_idx);
+/* Zero every slot of every state, in one launch [RSM clear]. */
+ssu_status ssu_pool_clear(ssu_pool *pool, hipStream_t stream);
+/* Zero one slot of every state in one launch, leaving other slots untouched;
+ * slot == -1 zeroes every slot [RSM clearSlot; SSU invokeMambaStateClear].
+ * SSU_EINVAL unless -1 <= slot < slot_count. */
+ssu_status ssu_pool_clear_slot(ssu_pool *pool, int32_t slot, hipStream_t stream);
+/* Copy slot `slot` of state i into dst[i] (a caller-owned device buffer of
+ * exactly dst_bytes[i] == stateBytesPerSlot(i) bytes), for every state, in one
+ * launch [RSM capture]. n must equal the number of states. */
+ssu_status ssu_pool_capture(const ssu_pool *pool, int32_t slot, void *const *dst,
+                            const size_t *dst_bytes, int32_t n, hipStream_t stream);
+/* Write a checkpoint back into one slot [RSM restore]: states 0..n_saved-1
+ * from src[i] (src_bytes[i] must equal stateBytesPerSlot(i)); states beyond
+ * n_saved are zeroed. Every entry is validated before anything is written. */
+ssu_status ssu_pool_restore(ssu_pool *pool, int32_t slot, const void *const *src,
+                            const size_t *src_bytes, int32_t n_saved, hipStream_t stream);
+/* Copy slot src_slot of every state of `source` into slot dst_slot of `pool`;
+ * both pools must hold identical specs in the same order [RSM copySlotFrom]. */
+ssu_status ssu_pool_copy_slot_from(ssu_pool *pool, const ssu_pool *source, int32_t dst_slot,
+                                   int32_t src_slot, hipStream_t stream);
+
+/* Message for the last non-OK status returned on this thread ("" if none). */
+const char *ssu_last_error(void);
+/* Library version as major*10000 + minor*100 + patch. */
+int32_t ssu_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* SSU_H */

@@ -1,0 +1,582 @@
+// C ABI of libssu: host-side argument checks, dispatch to the kernel
+// launchers, and the recurrent-state pool. No entry point reads device memory
+// on the host, synchronises, or allocates, except ssu_pool_alloc/ssu_pool_free.
+#include <stdarg.h>
+#include <stdio.h>
+#include <string.h>
+
+#include <new>
+#include <string>
+#include <vector>
+
+#include "ssu.h"
+#include "ssu_internal.h"
+
+namespace {
+
+thread_local std::string g_last_error;
+
+ssu_status fail(ssu_status st, const char *fmt, ...)
+{
+    char buf[512];
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(buf, sizeof(buf), fmt, ap);
+    va_end(ap);
+    g_last_error = buf;
+    return st;
+}
+
+ssu_status ok()
+{
+    g_last_error.clear();
+    return SSU_OK;
+}
+
+ssu_status hip_status(hipError_t e, const char *what)
+{
+    if (e == hipSuccess)
+        return ok();
+    return fail(SSU_EHIP, "%s: %s", what, hipGetErrorString(e));
+}
+
+size_t dtype_bytes(int32_t dt)
+{
+    switch (dt) {
+    case SSU_F32: return 4;
+    case SSU_F16: return 2;
+    case SSU_BF16: return 2;
+    case SSU_U8: return 1;
+    default: return 0;
+    }
+}
+
+bool compute_dtype(int32_t dt) { return dt == SSU_F32 || dt == SSU_F16 || dt == SSU_BF16; }
+
+bool supported_dstate(int32_t n) { return n == 16 || n == 32 || n == 64 || n == 128 || n == 256; }
+
+// Shared geometry checks; fills the common part of the launch parameters.
+ssu_status check_dims(const ssu_dims *d, const char *fn, bool need_pool_rows_for_batch,
+                      bool have_indices, ssu::DecodeParams *out)
+{
+    if (!d)
+        return fail(SSU_EINVAL, "%s: dims is NULL", fn);
+    if (d->reserved != 0)
+        return fail(SSU_EINVAL, "%s: dims.reserved must be 0", fn);
+    if (d->batch < 0)
+        return fail(SSU_EINVAL, "%s: batch %d < 0", fn, d->batch);
+    if (d->nheads <= 0 || d->dim <= 0 || d->dstate <= 0 || d->ngroups <= 0)
+        return fail(SSU_EINVAL, "%s: nheads/dim/dstate/ngroups must be > 0 (got %d/%d/%d/%d)", fn,
+                    d->nheads, d->dim, d->dstate, d->ngroups);
+    if (d->nheads % d->ngroups != 0)
+        return fail(SSU_EINVAL, "%s: nheads %d is not a multiple of ngroups %d", fn, d->nheads,
+                    d->ngroups);
+    if (d->pool_rows <= 0)
+        return fail(SSU_EINVAL, "%s: pool_rows must be > 0 (got %d)", fn, d->pool_rows);
+    if (d->dim > 4096)
+        return fail(SSU_ENOTSUP, "%s: dim %d > 4096", fn, d->dim);
+    if (!supported_dstate(d->dstate))
+        return fail(SSU_ENOTSUP, "%s: dstate %d not in {16,32,64,128,256}", fn, d->dstate);
+    if (!compute_dtype(d->state_dtype) || !compute_dtype(d->io_dtype) || !compute_dtype(d->bc_dtype))
+        return fail(SSU_ENOTSUP, "%s: unsupported dtype (state %d, io %d, bc %d)", fn,
+                    d->state_dtype, d->io_dtype, d->bc_dtype);
+    const int64_t tile = (int64_t)d->nheads * d->dim * d->dstate;
+    int64_t stride = d->state_row_stride;
+    if (stride < 0)
+        return fail(SSU_EINVAL, "%s: state_row_stride %lld < 0", fn, (long long)stride);
+    if (stride == 0)
+        stride = tile;
+    if (stride < tile)
+        return fail(SSU_EINVAL, "%s: state_row_stride %lld < nheads*dim*dstate %lld", fn,
+                    (long long)stride, (long long)tile);
+    if ((stride * (int64_t)dtype_bytes(d->state_dtype)) % 16 != 0)
+        return fail(SSU_EINVAL, "%s: state row stride of %lld bytes is not a multiple of 16", fn,
+                    (long long)(stride * (int64_t)dtype_bytes(d->state_dtype)));
+    if (need_pool_rows_for_batch && !have_indices && d->batch > d->pool_rows)
+        return fail(SSU_EINVAL, "%s: batch %d > pool_rows %d with no state_indices", fn, d->batch,
+                    d->pool_rows);
+    out->row_stride = stride;
+    out->batch = d->batch;
+    out->nheads = d->nheads;
+    out->dim = d->dim;
+    out->dstate = d->dstate;
+    out->ngroups = d->ngroups;
+    out->state_dtype = d->state_dtype;
+    out->io_dtype = d->io_dtype;
+    out->bc_dtype = d->bc_dtype;
+    return SSU_OK;
+}
+
+size_t io_bytes(int32_t dt) { return dt == SSU_F32 ? 4 : 2; }
+
+// Tensors read with 16-byte vector loads (state, B, C, replay_B) must be 16-byte
+// aligned; every other tensor only needs the alignment of its element type.
+#define SSU_REQUIRE_PTR(p, align, fn)                                                   \
+    do {                                                                                \
+        if (!(p))                                                                       \
+            return fail(SSU_EINVAL, "%s: required pointer '%s' is NULL", fn, #p);       \
+        if (((uintptr_t)(p) % (align)) != 0)                                            \
+            return fail(SSU_EINVAL, "%s: pointer '%s' is not %d-byte aligned", fn, #p,  \
+                        (int)(align));                                                  \
+    } while (0)
+
+#define SSU_OPTIONAL_PTR(p, align, fn)                                                  \
+    do {                                                                                \
+        if ((p) && ((uintptr_t)(p) % (align)) != 0)                                     \
+            return fail(SSU_EINVAL, "%s: pointer '%s' is not %d-byte aligned", fn, #p,  \
+                        (int)(align));                                                  \
+    } while (0)
+
+}  // namespace
+
+extern "C" {
+
+const char *ssu_last_error(void) { return g_last_error.c_str(); }
+
+int32_t ssu_version(void) { return 10000; }
+
+ssu_status ssu_decode(const ssu_dims *dims, const void *x, const float *A, const void *B,
+                      const void *C, const float *dt, const float *dt_bias, const float *D,
+                      const void *z, void *state, void *out, int32_t dt_softplus,
+                      const int32_t *state_indices, hipStream_t stream)
+{
+    const char *fn = "ssu_decode";
+    ssu::DecodeParams p = {};
+    const ssu_status st = check_dims(dims, fn, true, state_indices != nullptr, &p);
+    if (st != SSU_OK)
+        return st;
+    if (p.batch == 0)
+        return ok();
+    SSU_REQUIRE_PTR(x, io_bytes(dims->io_dtype), fn);
+    SSU_REQUIRE_PTR(A, 4, fn);
+    SSU_REQUIRE_PTR(B, 16, fn);
+    SSU_REQUIRE_PTR(C, 16, fn);
+    SSU_REQUIRE_PTR(dt, 4, fn);
+    SSU_REQUIRE_PTR(state, 16, fn);
+    SSU_REQUIRE_PTR(out, io_bytes(dims->io_dtype), fn);
+    SSU_OPTIONAL_PTR(dt_bias, 4, fn);
+    SSU_OPTIONAL_PTR(D, 4, fn);
+    SSU_OPTIONAL_PTR(z, io_bytes(dims->io_dtype), fn);
+    SSU_OPTIONAL_PTR(state_indices, 4, fn);
+    p.x = x;
+    p.A = A;
+    p.B = B;
+    p.C = C;
+    p.dt = dt;
+    p.dt_bias = dt_bias;
+    p.D = D;
+    p.z = z;
+    p.state = state;
+    p.out = out;
+    p.idx = state_indices;
+    p.dt_softplus = dt_softplus ? 1 : 0;
+    return hip_status(ssu::launch_decode(p, stream), "ssu_decode launch");
+}
+
+ssu_status ssu_prefill(const ssu_dims *dims, int32_t seq_len, const void *x, const float *A,
+                       const void *B, const void *C, const float *dt, const float *dt_bias,
+                       const float *D, const void *z, void *state, void *out,
+                       int32_t dt_softplus, const int32_t *context_lengths,
+                       const int32_t *state_indices, float *replay_dA, float *replay_u,
+                       float *replay_B, float *replay_dt, hipStream_t stream)
+{
+    const char *fn = "ssu_prefill";
+    ssu::PrefillParams p = {};
+    const ssu_status st = check_dims(dims, fn, true, state_indices != nullptr, &p.d);
+    if (st != SSU_OK)
+        return st;
+    if (seq_len < 0)
+        return fail(SSU_EINVAL, "%s: seq_len %d < 0", fn, seq_len);
+    const int nstash = (replay_dA != nullptr) + (replay_u != nullptr) + (replay_B != nullptr) +
+                       (replay_dt != nullptr);
+    if (nstash != 0 && nstash != 4)
+        return fail(SSU_EINVAL, "%s: replay stash must be all four buffers or none (%d given)",
+                    fn, nstash);
+    if (p.d.batch == 0 || seq_len == 0)
+        return ok();
+    if ((int64_t)p.d.batch * seq_len * p.d.nheads * p.d.dim > ((int64_t)1 << 40))
+        return fail(SSU_ENOTSUP, "%s: problem too large", fn);
+    SSU_REQUIRE_PTR(x, io_bytes(dims->io_dtype), fn);
+    SSU_REQUIRE_PTR(A, 4, fn);
+    SSU_REQUIRE_PTR(B, 16, fn);
+    SSU_REQUIRE_PTR(C, 16, fn);
+    SSU_REQUIRE_PTR(dt, 4, fn);
+    SSU_REQUIRE_PTR(state, 16, fn);
+    SSU_REQUIRE_PTR(out, io_bytes(dims->io_dtype), fn);
+    SSU_OPTIONAL_PTR(dt_bias, 4, fn);
+    SSU_OPTIONAL_PTR(D, 4, fn);
+    SSU_OPTIONAL_PTR(z, io_bytes(dims->io_dtype), fn);
+    SSU_OPTIONAL_PTR(context_lengths, 4, fn);
+    SSU_OPTIONAL_PTR(state_indices, 4, fn);
+    SSU_OPTIONAL_PTR(replay_dA, 4, fn);
+    SSU_OPTIONAL_PTR(replay_u, 4, fn);
+    SSU_OPTIONAL_PTR(replay_B, 16, fn);
+    SSU_OPTIONAL_PTR(replay_dt, 4, fn);
+    p.d.x = x;
+    p.d.A = A;
+    p.d.B = B;
+    p.d.C = C;
+    p.d.dt = dt;
+    p.d.dt_bias = dt_bias;
+    p.d.D = D;
+    p.d.z = z;
+    p.d.state = state;
+    p.d.out = out;
+    p.d.idx = state_indices;
+    p.d.dt_softplus = dt_softplus ? 1 : 0;
+    p.seq_len = seq_len;
+    p.ctx = context_lengths;
+    p.st_dA = replay_dA;
+    p.st_u = replay_u;
+    p.st_B = replay_B;
+    p.st_dt = replay_dt;
+    return hip_status(ssu::launch_prefill(p, stream), "ssu_prefill launch");
+}
+
+ssu_status ssu_replay(const ssu_dims *dims, int32_t seq_len, void *state,
+                      const float *replay_dA, const float *replay_u, const float *replay_B,
+                      const float *replay_dt, const int32_t *accepted_lengths,
+                      const int32_t *state_indices, int32_t active_batch, hipStream_t stream)
+{
+    const char *fn = "ssu_replay";
+    ssu::DecodeParams d = {};
+    const ssu_status st = check_dims(dims, fn, false, state_indices != nullptr, &d);
+    if (st != SSU_OK)
+        return st;
+    if (seq_len < 0)
+        return fail(SSU_EINVAL, "%s: seq_len %d < 0", fn, seq_len);
+    if (active_batch < 0 || active_batch > d.batch)
+        return fail(SSU_EINVAL, "%s: active_batch %d outside [0, batch %d]", fn, active_batch,
+                    d.batch);
+    if (!state_indices && active_batch > dims->pool_rows)
+        return fail(SSU_EINVAL, "%s: active_batch %d > pool_rows %d with no state_indices", fn,
+                    active_batch, dims->pool_rows);
+    if (active_batch == 0 || seq_len == 0)
+        return ok();
+    SSU_REQUIRE_PTR(state, 16, fn);
+    SSU_REQUIRE_PTR(replay_dA, 4, fn);
+    SSU_REQUIRE_PTR(replay_u, 4, fn);
+    SSU_REQUIRE_PTR(replay_B, 16, fn);
+    SSU_REQUIRE_PTR(replay_dt, 4, fn);
+    SSU_REQUIRE_PTR(accepted_lengths, 4, fn);
+    SSU_OPTIONAL_PTR(state_indices, 4, fn);
+    ssu::ReplayParams p = {};
+    p.state = state;
+    p.dA = replay_dA;
+    p.u = replay_u;
+    p.B = replay_B;
+    p.dt = replay_dt;
+    p.accepted = accepted_lengths;
+    p.idx = state_indices;
+    p.row_stride = d.row_stride;
+    p.active_batch = active_batch;
+    p.seq_len = seq_len;
+    p.nheads = d.nheads;
+    p.dim = d.dim;
+    p.dstate = d.dstate;
+    p.ngroups = d.ngroups;
+    p.state_dtype = d.state_dtype;
+    return hip_status(ssu::launch_replay(p, stream), "ssu_replay launch");
+}
+
+}  // extern "C"
+
+// ---------------------------------------------------------------------------
+// Recurrent-state pool
+// ---------------------------------------------------------------------------
+struct ssu_pool {
+    std::vector<ssu_state_spec> specs;
+    std::vector<size_t> bytes_per_slot;  // per state
+    std::vector<void *> slabs;           // per state, slot_count * bytes_per_slot[i] bytes
+    int32_t slot_count = 0;
+};
+
+namespace {
+
+ssu_status check_specs(const ssu_state_spec *specs, int32_t n, const char *fn,
+                       std::vector<size_t> *per_state)
+{
+    if (n < 0)
+        return fail(SSU_EINVAL, "%s: n_specs %d < 0", fn, n);
+    if (n > 0 && !specs)
+        return fail(SSU_EINVAL, "%s: specs is NULL", fn);
+    per_state->clear();
+    for (int32_t i = 0; i < n; ++i) {
+        const ssu_state_spec &s = specs[i];
+        if (s.layer < 0)
+            return fail(SSU_EINVAL, "%s: spec %d names negative layer %d", fn, i, s.layer);
+        if (s.rank < 1 || s.rank > 4)
+            return fail(SSU_EINVAL, "%s: spec %d has rank %d (1..4)", fn, i, s.rank);
+        const size_t eb = dtype_bytes(s.dtype);
+        if (eb == 0)
+            return fail(SSU_EINVAL, "%s: spec %d has unknown dtype %d", fn, i, s.dtype);
+        uint64_t vol = 1;
+        for (int k = 0; k < s.rank; ++k) {
+            if (s.shape[k] <= 0)
+                return fail(SSU_EINVAL, "%s: spec %d has non-positive per-slot volume", fn, i);
+            if (vol > (UINT64_MAX / 16) / (uint64_t)s.shape[k])
+                return fail(SSU_EINVAL, "%s: spec %d volume overflows", fn, i);
+            vol *= (uint64_t)s.shape[k];
+        }
+        for (int32_t j = 0; j < i; ++j)
+            if (specs[j].kind == s.kind && specs[j].layer == s.layer)
+                return fail(SSU_EINVAL, "%s: spec %d repeats {kind %d, layer %d} of spec %d", fn,
+                            i, s.kind, s.layer, j);
+        per_state->push_back((size_t)vol * eb);
+    }
+    return SSU_OK;
+}
+
+bool slot_ok(const ssu_pool *p, int32_t slot) { return slot >= 0 && slot < p->slot_count; }
+
+}  // namespace
+
+extern "C" {
+
+ssu_status ssu_pool_bytes_per_slot(const ssu_state_spec *specs, int32_t n_specs, size_t *out)
+{
+    const char *fn = "ssu_pool_bytes_per_slot";
+    if (!out)
+        return fail(SSU_EINVAL, "%s: out is NULL", fn);
+    std::vector<size_t> per;
+    const ssu_status st = check_specs(specs, n_specs, fn, &per);
+    if (st != SSU_OK)
+        return st;
+    size_t total = 0;
+    for (size_t b : per)
+        total += b;
+    *out = total;
+    return ok();
+}
+
+ssu_status ssu_pool_alloc(const ssu_state_spec *specs, int32_t n_specs, int32_t slot_count,
+                          hipStream_t stream, ssu_pool **out)
+{
+    const char *fn = "ssu_pool_alloc";
+    if (!out)
+        return fail(SSU_EINVAL, "%s: out is NULL", fn);
+    *out = nullptr;
+    if (slot_count < 0)
+        return fail(SSU_EINVAL, "%s: slot_count %d < 0", fn, slot_count);
+    std::vector<size_t> per;
+    ssu_status st = check_specs(specs, n_specs, fn, &per);
+    if (st != SSU_OK)
+        return st;
+    ssu_pool *p = new (std::nothrow) ssu_pool();
+    if (!p)
+        return fail(SSU_ENOMEM, "%s: host allocation failed", fn);
+    p->specs.assign(specs, specs + n_specs);
+    p->bytes_per_slot = per;
+    p->slot_count = slot_count;
+    p->slabs.assign(n_specs, nullptr);
+    if (slot_count > 0) {
+        std::vector<ssu::Segment> segs;
+        for (int32_t i = 0; i < n_specs; ++i) {
+            const size_t bytes = per[i] * (size_t)slot_count;
+            const hipError_t e = hipMalloc(&p->slabs[i], bytes);
+            if (e != hipSuccess) {
+                p->slabs[i] = nullptr;
+                ssu_pool_free(p);
+                return fail(e == hipErrorOutOfMemory ? SSU_ENOMEM : SSU_EHIP,
+                            "%s: hipMalloc of %zu bytes for state %d: %s", fn, bytes, i,
+                            hipGetErrorString(e));
+            }
+            segs.push_back({p->slabs[i], nullptr, (uint64_t)bytes});
+        }
+        const hipError_t e = ssu::launch_segments(segs.data(), (int)segs.size(), stream);
+        if (e != hipSuccess) {
+            ssu_pool_free(p);
+            return hip_status(e, "ssu_pool_alloc zero fill");
+        }
+    }
+    *out = p;
+    return ok();
+}
+
+ssu_status ssu_pool_free(ssu_pool *pool)
+{
+    if (!pool)
+        return ok();
+    bool any = false;
+    for (void *s : pool->slabs)
+        any = any || s;
+    hipError_t first = hipSuccess;
+    if (any)
+        first = hipDeviceSynchronize();  // the slabs may still be in use by queued work
+    for (void *s : pool->slabs) {
+        if (s) {
+            const hipError_t e = hipFree(s);
+            if (first == hipSuccess)
+                first = e;
+        }
+    }
+    delete pool;
+    return hip_status(first, "ssu_pool_free");
+}
+
+ssu_status ssu_pool_info(const ssu_pool *pool, int32_t *num_states, int32_t *slot_count)
+{
+    if (!pool)
+        return fail(SSU_EINVAL, "ssu_pool_info: pool is NULL");
+    if (num_states)
+        *num_states = (int32_t)pool->specs.size();
+    if (slot_count)
+        *slot_count = pool->slot_count;
+    return ok();
+}
+
+ssu_status ssu_pool_state_ptr(const ssu_pool *pool, int32_t state_idx, void **dev_ptr)
+{
+    if (!pool || !dev_ptr)
+        return fail(SSU_EINVAL, "ssu_pool_state_ptr: NULL argument");
+    if (state_idx < 0 || state_idx >= (int32_t)pool->specs.size())
+        return fail(SSU_EINVAL, "ssu_pool_state_ptr: state %d outside [0, %zu)", state_idx,
+                    pool->specs.size());
+    *dev_ptr = pool->slabs[state_idx];
+    return ok();
+}
+
+ssu_status ssu_pool_state_bytes_per_slot(const ssu_pool *pool, int32_t state_idx, size_t *out)
+{
+    if (!pool || !out)
+        return fail(SSU_EINVAL, "ssu_pool_state_bytes_per_slot: NULL argument");
+    if (state_idx < 0 || state_idx >= (int32_t)pool->specs.size())
+        return fail(SSU_EINVAL, "ssu_pool_state_bytes_per_slot: state %d outside [0, %zu)",
+                    state_idx, pool->specs.size());
+    *out = pool->bytes_per_slot[state_idx];
+    return ok();
+}
+
+ssu_status ssu_pool_find_state(const ssu_pool *pool, int32_t kind, int32_t layer,
+                               int32_t *state_idx)
+{
+    if (!pool || !state_idx)
+        return fail(SSU_EINVAL, "ssu_pool_find_state: NULL argument");
+    *state_idx = -1;
+    for (size_t i = 0; i < pool->specs.size(); ++i)
+        if (pool->specs[i].kind == kind && pool->specs[i].layer == layer)
+            *state_idx = (int32_t)i;
+    return ok();
+}
+
+ssu_status ssu_pool_clear_slot(ssu_pool *pool, int32_t slot, hipStream_t stream)
+{
+    const char *fn = "ssu_pool_clear_slot";
+    if (!pool)
+        return fail(SSU_EINVAL, "%s: pool is NULL", fn);
+    if (slot < -1 || slot >= pool->slot_count || (slot == -1 && pool->slot_count < 0))
+        return fail(SSU_EINVAL, "%s: slot %d outside [-1, %d)", fn, slot, pool->slot_count);
+    if (pool->slot_count == 0)
+        return ok();
+    std::vector<ssu::Segment> segs;
+    for (size_t i = 0; i < pool->specs.size(); ++i) {
+        uint8_t *base = static_cast<uint8_t *>(pool->slabs[i]);
+        const size_t b = pool->bytes_per_slot[i];
+        if (slot < 0)
+            segs.push_back({base, nullptr, (uint64_t)(b * (size_t)pool->slot_count)});
+        else
+            segs.push_back({base + b * (size_t)slot, nullptr, (uint64_t)b});
+    }
+    return hip_status(ssu::launch_segments(segs.data(), (int)segs.size(), stream), fn);
+}
+
+ssu_status ssu_pool_clear(ssu_pool *pool, hipStream_t stream)
+{
+    if (!pool)
+        return fail(SSU_EINVAL, "ssu_pool_clear: pool is NULL");
+    return ssu_pool_clear_slot(pool, -1, stream);
+}
+
+ssu_status ssu_pool_capture(const ssu_pool *pool, int32_t slot, void *const *dst,
+                            const size_t *dst_bytes, int32_t n, hipStream_t stream)
+{
+    const char *fn = "ssu_pool_capture";
+    if (!pool)
+        return fail(SSU_EINVAL, "%s: pool is NULL", fn);
+    if (!slot_ok(pool, slot))
+        return fail(SSU_EINVAL, "%s: slot %d outside [0, %d)", fn, slot, pool->slot_count);
+    if (n != (int32_t)pool->specs.size())
+        return fail(SSU_EINVAL, "%s: %d buffers given for %zu states", fn, n, pool->specs.size());
+    if (n > 0 && (!dst || !dst_bytes))
+        return fail(SSU_EINVAL, "%s: dst or dst_bytes is NULL", fn);
+    for (int32_t i = 0; i < n; ++i) {
+        if (!dst[i])
+            return fail(SSU_EINVAL, "%s: dst[%d] is NULL", fn, i);
+        if (dst_bytes[i] != pool->bytes_per_slot[i])
+            return fail(SSU_EINVAL, "%s: dst_bytes[%d] = %zu, state holds %zu bytes per slot", fn,
+                        i, dst_bytes[i], pool->bytes_per_slot[i]);
+    }
+    std::vector<ssu::Segment> segs;
+    for (int32_t i = 0; i < n; ++i) {
+        const uint8_t *base = static_cast<const uint8_t *>(pool->slabs[i]);
+        segs.push_back({dst[i], base + pool->bytes_per_slot[i] * (size_t)slot,
+                        (uint64_t)pool->bytes_per_slot[i]});
+    }
+    return hip_status(ssu::launch_segments(segs.data(), (int)segs.size(), stream), fn);
+}
+
+ssu_status ssu_pool_restore(ssu_pool *pool, int32_t slot, const void *const *src,
+                            const size_t *src_bytes, int32_t n_saved, hipStream_t stream)
+{
+    const char *fn = "ssu_pool_restore";
+    if (!pool)
+        return fail(SSU_EINVAL, "%s: pool is NULL", fn);
+    if (!slot_ok(pool, slot))
+        return fail(SSU_EINVAL, "%s: slot %d outside [0, %d)", fn, slot, pool->slot_count);
+    if (n_saved < 0 || n_saved > (int32_t)pool->specs.size())
+        return fail(SSU_EINVAL, "%s: n_saved %d outside [0, %zu]", fn, n_saved,
+                    pool->specs.size());
+    if (n_saved > 0 && (!src || !src_bytes))
+        return fail(SSU_EINVAL, "%s: src or src_bytes is NULL", fn);
+    for (int32_t i = 0; i < n_saved; ++i) {  // validate everything before any write
+        if (!src[i])
+            return fail(SSU_EINVAL, "%s: src[%d] is NULL", fn, i);
+        if (src_bytes[i] != pool->bytes_per_slot[i])
+            return fail(SSU_EINVAL, "%s: src_bytes[%d] = %zu, state holds %zu bytes per slot", fn,
+                        i, src_bytes[i], pool->bytes_per_slot[i]);
+    }
+    std::vector<ssu::Segment> segs;
+    for (size_t i = 0; i < pool->specs.size(); ++i) {
+        uint8_t *base = static_cast<uint8_t *>(pool->slabs[i]);
+        segs.push_back({base + pool->bytes_per_slot[i] * (size_t)slot,
+                        (int32_t)i < n_saved ? src[i] : nullptr,
+                        (uint64_t)pool->bytes_per_slot[i]});
+    }
+    return hip_status(ssu::launch_segments(segs.data(), (int)segs.size(), stream), fn);
+}
+
+ssu_status ssu_pool_copy_slot_from(ssu_pool *pool, const ssu_pool *source, int32_t dst_slot,
+                                   int32_t src_slot, hipStream_t stream)
+{
+    const char *fn = "ssu_pool_copy_slot_from";
+    if (!pool || !source)
+        return fail(SSU_EINVAL, "%s: pool is NULL", fn);
+    if (pool->specs.size() != source->specs.size())
+        return fail(SSU_EINVAL, "%s: pools hold %zu and %zu states", fn, pool->specs.size(),
+                    source->specs.size());
+    for (size_t i = 0; i < pool->specs.size(); ++i) {
+        const ssu_state_spec &a = pool->specs[i], &b = source->specs[i];
+        bool same = a.kind == b.kind && a.layer == b.layer && a.rank == b.rank &&
+                    a.dtype == b.dtype;
+        for (int k = 0; same && k < a.rank; ++k)
+            same = a.shape[k] == b.shape[k];
+        if (!same)
+            return fail(SSU_EINVAL, "%s: state %zu differs between the pools", fn, i);
+    }
+    if (!slot_ok(pool, dst_slot))
+        return fail(SSU_EINVAL, "%s: destination slot %d outside [0, %d)", fn, dst_slot,
+                    pool->slot_count);
+    if (!slot_ok(source, src_slot))
+        return fail(SSU_EINVAL, "%s: source slot %d outside [0, %d)", fn, src_slot,
+                    source->slot_count);
+    std::vector<ssu::Segment> segs;
+    for (size_t i = 0; i < pool->specs.size(); ++i) {
+        const size_t b = pool->bytes_per_slot[i];
+        segs.push_back({static_cast<uint8_t *>(pool->slabs[i]) + b * (size_t)dst_slot,
+                        static_cast<const uint8_t *>(source->slabs[i]) + b * (size_t)src_slot,
+                        (uint64_t)b});
+    }
+    return hip_status(ssu::launch_segments(segs.data(), (int)segs.size(), stream), fn);
+}
+
+}  // extern "C"

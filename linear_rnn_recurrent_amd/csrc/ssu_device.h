@@ -1,0 +1,229 @@
+// Device-side helpers shared by the SSU kernels: dtype conversions, 16-byte
+// state-vector loads/stores, small wave64 lane reductions.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace ssu {
+
+enum : int { kF32 = 0, kF16 = 1, kBF16 = 2 };
+
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+
+// Storage tag for a bf16 state element (no arithmetic is done on it).
+struct bf16_t {
+    uint16_t bits;
+};
+
+__device__ __forceinline__ float bf16_to_f32(uint32_t bits16) { return __uint_as_float(bits16 << 16); }
+
+// Round to nearest even; NaN stays a (quiet) NaN.
+__device__ __forceinline__ uint32_t f32_to_bf16(float f)
+{
+    uint32_t u = __float_as_uint(f);
+    if ((u & 0x7fffffffu) > 0x7f800000u)
+        return (u >> 16) | 0x40u;
+    u += 0x7fffu + ((u >> 16) & 1u);
+    return u >> 16;
+}
+
+__device__ __forceinline__ float f16_to_f32(uint32_t bits16)
+{
+    return (float)__builtin_bit_cast(_Float16, (uint16_t)bits16);
+}
+
+// fptrunc in the default round-to-nearest-even mode.
+__device__ __forceinline__ uint32_t f32_to_f16(float f)
+{
+    return __builtin_bit_cast(uint16_t, (_Float16)f);
+}
+
+__device__ __forceinline__ float lo16(uint32_t w, int dt)
+{
+    return dt == kBF16 ? __uint_as_float(w << 16) : f16_to_f32(w & 0xffffu);
+}
+__device__ __forceinline__ float hi16(uint32_t w, int dt)
+{
+    return dt == kBF16 ? __uint_as_float(w & 0xffff0000u) : f16_to_f32(w >> 16);
+}
+
+// Scalar element of an x/z/out tensor in io dtype.
+__device__ __forceinline__ float ld_io(const void *p, int64_t i, int dt)
+{
+    if (dt == kF32)
+        return static_cast<const float *>(p)[i];
+    const uint32_t h = static_cast<const uint16_t *>(p)[i];
+    return dt == kBF16 ? bf16_to_f32(h) : f16_to_f32(h);
+}
+
+__device__ __forceinline__ void st_io(void *p, int64_t i, float v, int dt)
+{
+    if (dt == kF32)
+        static_cast<float *>(p)[i] = v;
+    else
+        static_cast<uint16_t *>(p)[i] = (uint16_t)(dt == kBF16 ? f32_to_bf16(v) : f32_to_f16(v));
+}
+
+// N consecutive elements (N a multiple of 4) of a B/C-like tensor at element
+// offset i, which is a multiple of 4 (of 8 when N is); the base is 16-byte
+// aligned. When i is the same on every lane the loads are wave-uniform and the
+// compiler keeps them on the scalar unit.
+template <int N>
+__device__ __forceinline__ void ld_vec(const void *p, int64_t i, int dt, float (&v)[N])
+{
+    static_assert(N % 4 == 0, "N must be a multiple of 4");
+    if (dt == kF32) {
+        const u32x4 *q = reinterpret_cast<const u32x4 *>(static_cast<const float *>(p) + i);
+#pragma unroll
+        for (int k = 0; k < N / 4; ++k) {
+            const u32x4 w = q[k];
+#pragma unroll
+            for (int j = 0; j < 4; ++j)
+                v[4 * k + j] = __uint_as_float(w[j]);
+        }
+    } else if constexpr (N % 8 != 0) {
+        const u32x2 w = *reinterpret_cast<const u32x2 *>(static_cast<const uint16_t *>(p) + i);
+#pragma unroll
+        for (int j = 0; j < 2; ++j) {
+            v[2 * j] = lo16(w[j], dt);
+            v[2 * j + 1] = hi16(w[j], dt);
+        }
+    } else {
+        const u32x4 *q = reinterpret_cast<const u32x4 *>(static_cast<const uint16_t *>(p) + i);
+#pragma unroll
+        for (int k = 0; k < N / 8; ++k) {
+            const u32x4 w = q[k];
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                v[8 * k + 2 * j] = lo16(w[j], dt);
+                v[8 * k + 2 * j + 1] = hi16(w[j], dt);
+            }
+        }
+    }
+}
+
+// N consecutive B/C elements of storage type BT (float, _Float16 or bf16_t)
+// at element offset i (a multiple of 8; base 16-byte aligned). Used with a
+// wave-uniform offset inside the prefill token loop, where the dtype is a
+// template parameter so that only one conversion path is emitted.
+template <typename BT, int N>
+__device__ __forceinline__ void ld_bc(const void *p, int64_t i, float (&v)[N])
+{
+    static_assert(N % 8 == 0, "N must be a multiple of 8");
+    if constexpr (sizeof(BT) == 4) {
+        const u32x4 *q = reinterpret_cast<const u32x4 *>(static_cast<const float *>(p) + i);
+#pragma unroll
+        for (int k = 0; k < N / 4; ++k) {
+            const u32x4 w = q[k];
+#pragma unroll
+            for (int j = 0; j < 4; ++j)
+                v[4 * k + j] = __uint_as_float(w[j]);
+        }
+    } else {
+        const u32x4 *q = reinterpret_cast<const u32x4 *>(static_cast<const uint16_t *>(p) + i);
+#pragma unroll
+        for (int k = 0; k < N / 8; ++k) {
+            const u32x4 w = q[k];
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                if constexpr (sizeof(BT) == 2 && __is_same(BT, bf16_t)) {
+                    v[8 * k + 2 * j] = __uint_as_float(w[j] << 16);
+                    v[8 * k + 2 * j + 1] = __uint_as_float(w[j] & 0xffff0000u);
+                } else {
+                    v[8 * k + 2 * j] = f16_to_f32(w[j] & 0xffffu);
+                    v[8 * k + 2 * j + 1] = f16_to_f32(w[j] >> 16);
+                }
+            }
+        }
+    }
+}
+
+__device__ __forceinline__ int clamp_len(int v, int hi) { return v < 0 ? 0 : (v > hi ? hi : v); }
+
+// 16-byte state vectors: 4 fp32 or 8 fp16/bf16 elements.
+template <typename ST>
+struct SV;
+
+template <>
+struct SV<float> {
+    static constexpr int VEC = 4;
+    __device__ static __forceinline__ void unpack(const u32x4 w, float (&v)[4])
+    {
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+            v[j] = __uint_as_float(w[j]);
+    }
+    __device__ static __forceinline__ u32x4 pack(const float (&v)[4])
+    {
+        u32x4 w;
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+            w[j] = __float_as_uint(v[j]);
+        return w;
+    }
+};
+
+template <>
+struct SV<_Float16> {
+    static constexpr int VEC = 8;
+    __device__ static __forceinline__ void unpack(const u32x4 w, float (&v)[8])
+    {
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            v[2 * j] = f16_to_f32(w[j] & 0xffffu);
+            v[2 * j + 1] = f16_to_f32(w[j] >> 16);
+        }
+    }
+    __device__ static __forceinline__ u32x4 pack(const float (&v)[8])
+    {
+        u32x4 w;
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+            w[j] = f32_to_f16(v[2 * j]) | (f32_to_f16(v[2 * j + 1]) << 16);
+        return w;
+    }
+};
+
+template <>
+struct SV<bf16_t> {
+    static constexpr int VEC = 8;
+    __device__ static __forceinline__ void unpack(const u32x4 w, float (&v)[8])
+    {
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            v[2 * j] = __uint_as_float(w[j] << 16);
+            v[2 * j + 1] = __uint_as_float(w[j] & 0xffff0000u);
+        }
+    }
+    __device__ static __forceinline__ u32x4 pack(const float (&v)[8])
+    {
+        u32x4 w;
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+            w[j] = f32_to_bf16(v[2 * j]) | (f32_to_bf16(v[2 * j + 1]) << 16);
+        return w;
+    }
+};
+
+__device__ __forceinline__ float softplus_f32(float v)
+{
+    // log(1 + e^v); above 20 the correction e^-v is below fp32 resolution of v
+    return v > 20.0f ? v : log1pf(expf(v));
+}
+
+__device__ __forceinline__ float silu_f32(float z) { return z / (1.0f + expf(-z)); }
+
+// Sum over aligned groups of W consecutive lanes (W a power of two <= 64);
+// every lane of a group receives the group sum.
+template <int W>
+__device__ __forceinline__ float group_sum(float v)
+{
+#pragma unroll
+    for (int m = 1; m < W; m <<= 1)
+        v += __shfl_xor(v, m, 64);
+    return v;
+}
+
+}  // namespace ssu

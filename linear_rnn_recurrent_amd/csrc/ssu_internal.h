@@ -1,0 +1,61 @@
+// Internal interface between the C-ABI layer (ssu_api.cpp) and the kernel
+// launchers (*.hip). Plain structs of device pointers and sizes; the host code
+// has validated every field before a launcher sees it.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "ssu.h"
+
+namespace ssu {
+
+struct DecodeParams {
+    const void *x;
+    const float *A;
+    const void *B;
+    const void *C;
+    const float *dt;
+    const float *dt_bias;
+    const float *D;
+    const void *z;
+    void *state;
+    void *out;
+    const int32_t *idx;
+    int64_t row_stride;  // elements
+    int32_t batch, nheads, dim, dstate, ngroups;
+    int32_t state_dtype, io_dtype, bc_dtype;
+    int32_t dt_softplus;
+};
+
+struct PrefillParams {
+    DecodeParams d;  // x/z/out/dt/B/C carry the extra seq_len axis
+    int32_t seq_len;
+    const int32_t *ctx;
+    float *st_dA, *st_u, *st_B, *st_dt;  // all set or all null
+};
+
+struct ReplayParams {
+    void *state;
+    const float *dA, *u, *B, *dt;
+    const int32_t *accepted;
+    const int32_t *idx;
+    int64_t row_stride;
+    int32_t active_batch, seq_len, nheads, dim, dstate, ngroups;
+    int32_t state_dtype;
+};
+
+// One byte range to copy (src != null) or zero (src == null).
+struct Segment {
+    void *dst;
+    const void *src;
+    uint64_t bytes;
+};
+
+hipError_t launch_decode(const DecodeParams &p, hipStream_t stream);
+hipError_t launch_prefill(const PrefillParams &p, hipStream_t stream);
+hipError_t launch_replay(const ReplayParams &p, hipStream_t stream);
+// Copies/zeroes up to any number of segments; one launch per 32 segments.
+hipError_t launch_segments(const Segment *segs, int n, hipStream_t stream);
+
+}  // namespace ssu

@@ -1,0 +1,418 @@
+"""Python binding of libssu (ctypes). Argument marshalling only.
+
+Each function takes torch tensors that live on the GPU, checks that their
+shapes agree (the C library cannot see shapes), and calls the C entry point of
+the same name on torch's current stream. All computation happens in the HIP
+kernels of libssu.so; there is no fallback. If the library has not been built
+the first call raises RuntimeError (build it with
+`python -m linear_rnn_recurrent_amd.build`).
+"""
+import ctypes
+import os
+from typing import Optional, Sequence
+
+import torch
+
+LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libssu.so")
+
+SSU_OK, SSU_EINVAL, SSU_ENOTSUP, SSU_EHIP, SSU_ENOMEM = 0, 1, 2, 3, 4
+SSU_F32, SSU_F16, SSU_BF16, SSU_U8 = 0, 1, 2, 3
+_DT = {torch.float32: SSU_F32, torch.float16: SSU_F16, torch.bfloat16: SSU_BF16,
+       torch.uint8: SSU_U8}
+
+EXPORTS = ("ssu_decode", "ssu_prefill", "ssu_replay", "ssu_pool_bytes_per_slot",
+           "ssu_pool_alloc", "ssu_pool_free", "ssu_pool_info", "ssu_pool_state_ptr",
+           "ssu_pool_state_bytes_per_slot", "ssu_pool_find_state", "ssu_pool_clear",
+           "ssu_pool_clear_slot", "ssu_pool_capture", "ssu_pool_restore",
+           "ssu_pool_copy_slot_from", "ssu_last_error", "ssu_version")
+
+
+class SsuError(RuntimeError):
+    def __init__(self, status, msg):
+        super().__init__(f"[ssu status {status}] {msg}")
+        self.status = status
+
+
+class ssu_dims(ctypes.Structure):
+    _fields_ = [("batch", ctypes.c_int32), ("nheads", ctypes.c_int32), ("dim", ctypes.c_int32),
+                ("dstate", ctypes.c_int32), ("ngroups", ctypes.c_int32),
+                ("pool_rows", ctypes.c_int32), ("state_row_stride", ctypes.c_int64),
+                ("state_dtype", ctypes.c_int32), ("io_dtype", ctypes.c_int32),
+                ("bc_dtype", ctypes.c_int32), ("reserved", ctypes.c_int32)]
+
+
+class ssu_state_spec(ctypes.Structure):
+    _fields_ = [("kind", ctypes.c_int32), ("layer", ctypes.c_int32), ("rank", ctypes.c_int32),
+                ("dtype", ctypes.c_int32), ("shape", ctypes.c_int64 * 4)]
+
+
+_LIB = None
+_P = ctypes.c_void_p
+_I32 = ctypes.c_int32
+
+
+def load_library(path: Optional[str] = None):
+    """Load libssu.so (once) and declare the C signatures."""
+    global _LIB
+    if _LIB is not None and path is None:
+        return _LIB
+    p = path or LIB_PATH
+    if not os.path.exists(p):
+        raise RuntimeError(f"libssu.so not found at {p}: build it with "
+                           "`python -m linear_rnn_recurrent_amd.build`")
+    lib = ctypes.CDLL(p)
+    D = ctypes.POINTER(ssu_dims)
+    S = ctypes.POINTER(ssu_state_spec)
+    sig = {
+        "ssu_decode": [D, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _I32, _P, _P],
+        "ssu_prefill": [D, _I32, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _I32, _P, _P,
+                        _P, _P, _P, _P, _P],
+        "ssu_replay": [D, _I32, _P, _P, _P, _P, _P, _P, _P, _I32, _P],
+        "ssu_pool_bytes_per_slot": [S, _I32, ctypes.POINTER(ctypes.c_size_t)],
+        "ssu_pool_alloc": [S, _I32, _I32, _P, ctypes.POINTER(_P)],
+        "ssu_pool_free": [_P],
+        "ssu_pool_info": [_P, ctypes.POINTER(_I32), ctypes.POINTER(_I32)],
+        "ssu_pool_state_ptr": [_P, _I32, ctypes.POINTER(_P)],
+        "ssu_pool_state_bytes_per_slot": [_P, _I32, ctypes.POINTER(ctypes.c_size_t)],
+        "ssu_pool_find_state": [_P, _I32, _I32, ctypes.POINTER(_I32)],
+        "ssu_pool_clear": [_P, _P],
+        "ssu_pool_clear_slot": [_P, _I32, _P],
+        "ssu_pool_capture": [_P, _I32, ctypes.POINTER(_P), ctypes.POINTER(ctypes.c_size_t),
+                             _I32, _P],
+        "ssu_pool_restore": [_P, _I32, ctypes.POINTER(_P), ctypes.POINTER(ctypes.c_size_t),
+                             _I32, _P],
+        "ssu_pool_copy_slot_from": [_P, _P, _I32, _I32, _P],
+    }
+    for name, args in sig.items():
+        f = getattr(lib, name)
+        f.argtypes = args
+        f.restype = ctypes.c_int32
+    lib.ssu_last_error.argtypes = []
+    lib.ssu_last_error.restype = ctypes.c_char_p
+    lib.ssu_version.argtypes = []
+    lib.ssu_version.restype = ctypes.c_int32
+    if path is None:
+        _LIB = lib
+    return lib
+
+
+def _check(status):
+    if status != SSU_OK:
+        raise SsuError(status, load_library().ssu_last_error().decode())
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(device, stream):
+    if stream is not None:
+        return ctypes.c_void_p(stream if isinstance(stream, int) else stream.cuda_stream)
+    return ctypes.c_void_p(torch.cuda.current_stream(device).cuda_stream)
+
+
+def _need(cond, msg):
+    if not cond:
+        raise ValueError(msg)
+
+
+def _dev(t, name, dtypes=None, shape=None):
+    _need(t.is_cuda, f"{name} must be a GPU tensor")
+    if dtypes is not None:
+        _need(t.dtype in dtypes, f"{name} has dtype {t.dtype}, expected one of {dtypes}")
+    if shape is not None:
+        _need(tuple(t.shape) == tuple(shape), f"{name} has shape {tuple(t.shape)}, expected {tuple(shape)}")
+    return t
+
+
+def _dense(t, name, dtypes=None, shape=None):
+    _dev(t, name, dtypes, shape)
+    _need(t.is_contiguous(), f"{name} must be contiguous")
+    return t
+
+
+_FLOAT = (torch.float32, torch.float16, torch.bfloat16)
+
+
+def _state_geometry(state, nheads, dim, dstate):
+    """state: [rows, nheads, dim, dstate] with dense rows; stride(0) may be padded."""
+    _dev(state, "state", _FLOAT)
+    _need(state.dim() == 4 and tuple(state.shape[1:]) == (nheads, dim, dstate),
+          f"state has shape {tuple(state.shape)}, expected [rows, {nheads}, {dim}, {dstate}]")
+    st = state.stride()
+    _need(st[3] == 1 and st[2] == dstate and st[1] == dim * dstate,
+          "state rows must be dense ([nheads, dim, dstate] contiguous)")
+    _need(st[0] >= nheads * dim * dstate or state.shape[0] == 1, "state row stride too small")
+    stride = st[0] if state.shape[0] > 1 else nheads * dim * dstate
+    return state.shape[0], stride
+
+
+def _dims(batch, nheads, dim, dstate, ngroups, pool_rows, row_stride, state_dtype,
+          io_dtype, bc_dtype):
+    return ssu_dims(batch, nheads, dim, dstate, ngroups, pool_rows, row_stride,
+                    _DT[state_dtype], _DT[io_dtype], _DT[bc_dtype], 0)
+
+
+def _opt_idx(t, name, n):
+    if t is None:
+        return None
+    return _dense(t, name, (torch.int32,), (n,))
+
+
+def ssu_decode(x, A, B, C, dt, state, out, *, dt_bias=None, D=None, z=None,
+               dt_softplus=True, state_indices=None, stream=None):
+    """One decode step; updates `state` in place and writes `out`.
+
+    x, z, out [batch, nheads, dim]; A, dt_bias, D [nheads] fp32; dt [batch, nheads] fp32;
+    B, C [batch, ngroups, dstate]; state [rows, nheads, dim, dstate];
+    state_indices [batch] int32 (negative = padding row).
+    """
+    lib = load_library()
+    _dense(x, "x", _FLOAT)
+    _need(x.dim() == 3, "x must be [batch, nheads, dim]")
+    batch, nheads, dim = x.shape
+    _dense(B, "B", _FLOAT)
+    _need(B.dim() == 3 and B.shape[0] == batch, "B must be [batch, ngroups, dstate]")
+    ngroups, dstate = B.shape[1], B.shape[2]
+    _dense(C, "C", (B.dtype,), B.shape)
+    _dense(A, "A", (torch.float32,), (nheads,))
+    _dense(dt, "dt", (torch.float32,), (batch, nheads))
+    if dt_bias is not None:
+        _dense(dt_bias, "dt_bias", (torch.float32,), (nheads,))
+    if D is not None:
+        _dense(D, "D", (torch.float32,), (nheads,))
+    if z is not None:
+        _dense(z, "z", (x.dtype,), x.shape)
+    _dense(out, "out", (x.dtype,), x.shape)
+    rows, stride = _state_geometry(state, nheads, dim, dstate)
+    _opt_idx(state_indices, "state_indices", batch)
+    d = _dims(batch, nheads, dim, dstate, ngroups, rows, stride, state.dtype, x.dtype, B.dtype)
+    with torch.cuda.device(x.device):
+        _check(lib.ssu_decode(ctypes.byref(d), _ptr(x), _ptr(A), _ptr(B), _ptr(C), _ptr(dt),
+                              _ptr(dt_bias), _ptr(D), _ptr(z), _ptr(state), _ptr(out),
+                              1 if dt_softplus else 0, _ptr(state_indices),
+                              _stream(x.device, stream)))
+    return out
+
+
+def ssu_prefill(x, A, B, C, dt, state, out, *, dt_bias=None, D=None, z=None,
+                dt_softplus=True, context_lengths=None, state_indices=None,
+                replay_dA=None, replay_u=None, replay_B=None, replay_dt=None, stream=None):
+    """All seq_len tokens in one launch.
+
+    x, z, out [batch, seq_len, nheads, dim]; dt [batch, seq_len, nheads];
+    B, C [batch, seq_len, ngroups, dstate]; context_lengths [batch] int32.
+    Replay stash (fp32, all four or none): replay_dA, replay_dt [batch, seq_len, nheads],
+    replay_u [batch, seq_len, nheads, dim], replay_B [batch, seq_len, ngroups, dstate].
+    """
+    lib = load_library()
+    _dense(x, "x", _FLOAT)
+    _need(x.dim() == 4, "x must be [batch, seq_len, nheads, dim]")
+    batch, seq_len, nheads, dim = x.shape
+    _dense(B, "B", _FLOAT)
+    _need(B.dim() == 4 and tuple(B.shape[:2]) == (batch, seq_len),
+          "B must be [batch, seq_len, ngroups, dstate]")
+    ngroups, dstate = B.shape[2], B.shape[3]
+    _dense(C, "C", (B.dtype,), B.shape)
+    _dense(A, "A", (torch.float32,), (nheads,))
+    _dense(dt, "dt", (torch.float32,), (batch, seq_len, nheads))
+    if dt_bias is not None:
+        _dense(dt_bias, "dt_bias", (torch.float32,), (nheads,))
+    if D is not None:
+        _dense(D, "D", (torch.float32,), (nheads,))
+    if z is not None:
+        _dense(z, "z", (x.dtype,), x.shape)
+    _dense(out, "out", (x.dtype,), x.shape)
+    rows, stride = _state_geometry(state, nheads, dim, dstate)
+    _opt_idx(state_indices, "state_indices", batch)
+    _opt_idx(context_lengths, "context_lengths", batch)
+    stash = (replay_dA, replay_u, replay_B, replay_dt)
+    if any(s is not None for s in stash):
+        _dense(replay_dA, "replay_dA", (torch.float32,), (batch, seq_len, nheads))
+        _dense(replay_dt, "replay_dt", (torch.float32,), (batch, seq_len, nheads))
+        _dense(replay_u, "replay_u", (torch.float32,), x.shape)
+        _dense(replay_B, "replay_B", (torch.float32,), B.shape)
+    d = _dims(batch, nheads, dim, dstate, ngroups, rows, stride, state.dtype, x.dtype, B.dtype)
+    with torch.cuda.device(x.device):
+        _check(lib.ssu_prefill(ctypes.byref(d), seq_len, _ptr(x), _ptr(A), _ptr(B), _ptr(C),
+                               _ptr(dt), _ptr(dt_bias), _ptr(D), _ptr(z), _ptr(state),
+                               _ptr(out), 1 if dt_softplus else 0, _ptr(context_lengths),
+                               _ptr(state_indices), *[_ptr(s) for s in stash],
+                               _stream(x.device, stream)))
+    return out
+
+
+def ssu_replay(state, replay_dA, replay_u, replay_B, replay_dt, accepted_lengths, *,
+               state_indices=None, active_batch=None, stream=None):
+    """Apply the first accepted_lengths[b] stashed tokens to the state, in place.
+
+    replay_dA, replay_dt [batch, seq_len, nheads]; replay_u [batch, seq_len, nheads, dim];
+    replay_B [batch, seq_len, ngroups, dstate]; accepted_lengths, state_indices [batch] int32.
+    Rows b >= active_batch (default batch) are never read.
+    """
+    lib = load_library()
+    _dense(replay_dA, "replay_dA", (torch.float32,))
+    _need(replay_dA.dim() == 3, "replay_dA must be [batch, seq_len, nheads]")
+    batch, seq_len, nheads = replay_dA.shape
+    _dense(replay_u, "replay_u", (torch.float32,))
+    _need(replay_u.dim() == 4 and tuple(replay_u.shape[:3]) == (batch, seq_len, nheads),
+          "replay_u must be [batch, seq_len, nheads, dim]")
+    dim = replay_u.shape[3]
+    _dense(replay_B, "replay_B", (torch.float32,))
+    _need(replay_B.dim() == 4 and tuple(replay_B.shape[:2]) == (batch, seq_len),
+          "replay_B must be [batch, seq_len, ngroups, dstate]")
+    ngroups, dstate = replay_B.shape[2], replay_B.shape[3]
+    _dense(replay_dt, "replay_dt", (torch.float32,), (batch, seq_len, nheads))
+    _dense(accepted_lengths, "accepted_lengths", (torch.int32,), (batch,))
+    _opt_idx(state_indices, "state_indices", batch)
+    rows, stride = _state_geometry(state, nheads, dim, dstate)
+    if active_batch is None:
+        active_batch = batch
+    d = _dims(batch, nheads, dim, dstate, ngroups, rows, stride, state.dtype, torch.float32,
+              torch.float32)
+    with torch.cuda.device(state.device):
+        _check(lib.ssu_replay(ctypes.byref(d), seq_len, _ptr(state), _ptr(replay_dA),
+                              _ptr(replay_u), _ptr(replay_B), _ptr(replay_dt),
+                              _ptr(accepted_lengths), _ptr(state_indices), int(active_batch),
+                              _stream(state.device, stream)))
+
+
+# ---------------------------------------------------------------------------
+# Recurrent-state pool
+# ---------------------------------------------------------------------------
+class DeviceArray:
+    """Non-owning view of pool memory: enough of the tensor protocol for the SSU
+    entry points (data_ptr, shape, stride, dtype, device) plus
+    __cuda_array_interface__ for zero-copy interop."""
+
+    _TYPESTR = {torch.float32: "<f4", torch.float16: "<f2", torch.bfloat16: "<V2",
+                torch.uint8: "|u1"}
+
+    def __init__(self, ptr, shape, dtype, device, owner):
+        self._ptr, self.shape, self.dtype, self.device = ptr, tuple(shape), dtype, device
+        self._owner = owner  # keeps the pool alive
+        st, acc = [], 1
+        for s in reversed(self.shape):
+            st.append(acc)
+            acc *= s
+        self._stride = tuple(reversed(st))
+        self.is_cuda = True
+
+    def data_ptr(self):
+        return self._ptr
+
+    def stride(self):
+        return self._stride
+
+    def dim(self):
+        return len(self.shape)
+
+    @property
+    def __cuda_array_interface__(self):
+        return {"shape": self.shape, "typestr": self._TYPESTR[self.dtype],
+                "data": (self._ptr, False), "version": 3, "strides": None}
+
+
+class SsuPool:
+    """Owning handle of an ssu_pool: one zeroed [slot_count] + shape slab per spec.
+
+    specs: sequence of (kind, layer, shape, dtype) with dtype a torch dtype
+    (float32, float16, bfloat16 or uint8).
+    """
+
+    def __init__(self, specs: Sequence, slot_count: int, *, stream=None, device=None):
+        self._lib = load_library()
+        self.device = (torch.device("cuda", torch.cuda.current_device()) if device is None
+                       else torch.device(device))
+        arr = (ssu_state_spec * max(len(specs), 1))()
+        self.specs = []
+        for i, (kind, layer, shape, dtype) in enumerate(specs):
+            shape = tuple(int(s) for s in shape)
+            _need(1 <= len(shape) <= 4, "spec shape must have 1..4 entries")
+            arr[i].kind, arr[i].layer, arr[i].rank = kind, layer, len(shape)
+            arr[i].dtype = _DT[dtype]
+            for k, s in enumerate(shape):
+                arr[i].shape[k] = s
+            self.specs.append((kind, layer, shape, dtype))
+        self._h = ctypes.c_void_p()
+        with torch.cuda.device(self.device):
+            _check(self._lib.ssu_pool_alloc(arr, len(specs), slot_count,
+                                            _stream(self.device, stream), ctypes.byref(self._h)))
+        self.slot_count = slot_count
+
+    @staticmethod
+    def bytes_per_slot(specs):
+        lib = load_library()
+        arr = (ssu_state_spec * max(len(specs), 1))()
+        for i, (kind, layer, shape, dtype) in enumerate(specs):
+            arr[i].kind, arr[i].layer, arr[i].rank = kind, layer, len(shape)
+            arr[i].dtype = _DT.get(dtype, 99)
+            for k, s in enumerate(shape):
+                arr[i].shape[k] = s
+        out = ctypes.c_size_t()
+        _check(lib.ssu_pool_bytes_per_slot(arr, len(specs), ctypes.byref(out)))
+        return out.value
+
+    def close(self):
+        if getattr(self, "_h", None) and self._h.value:
+            _check(self._lib.ssu_pool_free(self._h))
+            self._h = ctypes.c_void_p()
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
+
+    @property
+    def num_states(self):
+        n, s = ctypes.c_int32(), ctypes.c_int32()
+        _check(self._lib.ssu_pool_info(self._h, ctypes.byref(n), ctypes.byref(s)))
+        return n.value
+
+    def state_bytes_per_slot(self, i):
+        out = ctypes.c_size_t()
+        _check(self._lib.ssu_pool_state_bytes_per_slot(self._h, i, ctypes.byref(out)))
+        return out.value
+
+    def find_state(self, kind, layer):
+        out = ctypes.c_int32()
+        _check(self._lib.ssu_pool_find_state(self._h, kind, layer, ctypes.byref(out)))
+        return out.value
+
+    def state(self, i):
+        """DeviceArray view of state i, shaped [slot_count] + spec shape."""
+        p = ctypes.c_void_p()
+        _check(self._lib.ssu_pool_state_ptr(self._h, i, ctypes.byref(p)))
+        kind, layer, shape, dtype = self.specs[i]
+        return DeviceArray(p.value or 0, (self.slot_count,) + shape, dtype, self.device, self)
+
+    def clear(self, stream=None):
+        _check(self._lib.ssu_pool_clear(self._h, _stream(self.device, stream)))
+
+    def clear_slot(self, slot, stream=None):
+        _check(self._lib.ssu_pool_clear_slot(self._h, slot, _stream(self.device, stream)))
+
+    def capture(self, slot, dst=None, stream=None):
+        """Copy one slot of every state into `dst` (list of GPU tensors, allocated
+        here when None) and return it."""
+        if dst is None:
+            dst = [torch.empty((1,) + shape, dtype=dtype, device=self.device)
+                   for (_, _, shape, dtype) in self.specs]
+        n = len(dst)
+        ptrs = (ctypes.c_void_p * max(n, 1))(*[t.data_ptr() for t in dst])
+        sizes = (ctypes.c_size_t * max(n, 1))(*[t.numel() * t.element_size() for t in dst])
+        _check(self._lib.ssu_pool_capture(self._h, slot, ptrs, sizes, n,
+                                          _stream(self.device, stream)))
+        return dst
+
+    def restore(self, saved, slot, stream=None):
+        n = len(saved)
+        ptrs = (ctypes.c_void_p * max(n, 1))(*[t.data_ptr() for t in saved])
+        sizes = (ctypes.c_size_t * max(n, 1))(*[t.numel() * t.element_size() for t in saved])
+        _check(self._lib.ssu_pool_restore(self._h, slot, ptrs, sizes, n,
+                                          _stream(self.device, stream)))
+
+    def copy_slot_from(self, source: "SsuPool", dst_slot, src_slot, stream=None):
+        _check(self._lib.ssu_pool_copy_slot_from(self._h, source._h, dst_slot, src_slot,
+                                                 _stream(self.device, stream)))

@@ -40,6 +40,8 @@ def _lib():
         lib.oracle_ssu_replay.argtypes = [i32] * 6 + [i64] + [_F64P] * 5 + [_I32P, _I32P]
         for f in (lib.oracle_ssu_decode, lib.oracle_ssu_prefill, lib.oracle_ssu_replay):
             f.restype = None
+        lib.oracle_num_threads.argtypes = []
+        lib.oracle_num_threads.restype = ctypes.c_int32
         _LIB = lib
     return _LIB
 
@@ -123,3 +125,8 @@ def replay(state, dA, u, Bst, DT, accepted_lengths, *, state_indices=None,
     ix = _i32(state_indices)
     _lib().oracle_ssu_replay(active_batch, seq_len, nheads, dim, dstate, ngroups, rs,
                              st[1], *[k[1] for k in keep], ac[1], ix[1])
+
+
+def num_threads():
+    """OpenMP threads the oracle's loops run on."""
+    return int(_lib().oracle_num_threads())

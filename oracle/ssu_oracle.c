@@ -44,6 +44,9 @@
 #include <math.h>
 #include <stdint.h>
 #include <string.h>
+#ifdef _OPENMP
+#include <omp.h>
+#endif
 
 static double softplus(double v)
 {
@@ -220,4 +223,14 @@ void oracle_ssu_replay(int32_t active_batch, int32_t seq_len, int32_t nheads,
             }
         }
     }
+}
+
+/* Threads the OpenMP loops above use (reported beside the oracle's timing). */
+int32_t oracle_num_threads(void)
+{
+#ifdef _OPENMP
+    return (int32_t)omp_get_max_threads();
+#else
+    return 1;
+#endif
 }

@@ -1,0 +1,250 @@
+"""C-ABI checks that need no GPU: the library loads, exports every entry point
+include/ssu.h declares, agrees with the header on struct layouts, and rejects
+bad arguments on the host (every such path returns before any HIP call)."""
+import ctypes
+import os
+import re
+import subprocess
+
+import pytest
+
+from linear_rnn_recurrent_amd import ssu as S
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "ssu.h")
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(S.LIB_PATH):
+        from linear_rnn_recurrent_amd import build
+        build.build()
+    return S.load_library()
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    return re.findall(r"^(?:ssu_status|const char \*|int32_t)\s*(ssu_\w+)\s*\(", text, re.M)
+
+
+def test_header_declares_the_entry_points():
+    names = declared_functions()
+    assert set(names) == set(S.EXPORTS), set(names) ^ set(S.EXPORTS)
+
+
+def test_library_exports_every_declared_symbol(lib):
+    nm = subprocess.run(["nm", "-D", "--defined-only", S.LIB_PATH], capture_output=True,
+                        text=True, check=True).stdout
+    exported = set(re.findall(r" T (ssu_\w+)$", nm, re.M))
+    for name in declared_functions():
+        assert name in exported, name
+        assert hasattr(lib, name)
+
+
+def test_library_links_hip_runtime_only():
+    ldd = subprocess.run(["ldd", S.LIB_PATH], capture_output=True, text=True).stdout
+    assert "amdhip64" in ldd
+    assert "torch" not in ldd and "python" not in ldd
+
+
+def test_struct_layout_matches_header(tmp_path):
+    src = tmp_path / "sz.c"
+    src.write_text('#include "ssu.h"\n#include <stdio.h>\n#include <stddef.h>\n'
+                   'int main(void){printf("%zu %zu %zu %zu\\n", sizeof(ssu_dims),'
+                   ' offsetof(ssu_dims, state_row_stride), sizeof(ssu_state_spec),'
+                   ' offsetof(ssu_state_spec, shape));return 0;}\n')
+    exe = tmp_path / "sz"
+    subprocess.run(["gcc", "-D__HIP_PLATFORM_AMD__", "-I", os.path.join(ROOT, "include"),
+                    "-I", "/opt/rocm/include", str(src), "-o", str(exe)], check=True)
+    got = [int(v) for v in subprocess.run([str(exe)], capture_output=True, text=True,
+                                          check=True).stdout.split()]
+    assert got == [ctypes.sizeof(S.ssu_dims), S.ssu_dims.state_row_stride.offset,
+                   ctypes.sizeof(S.ssu_state_spec), S.ssu_state_spec.shape.offset]
+
+
+def test_version(lib):
+    assert lib.ssu_version() == 10000
+
+
+# ---------------------------------------------------------------------------
+# Host-side validation (no GPU needed: nothing reaches the HIP runtime)
+# ---------------------------------------------------------------------------
+FAKE = 0x100000  # a 16-byte aligned non-null pointer value, never dereferenced
+
+
+def dims(**kw):
+    d = dict(batch=2, nheads=4, dim=16, dstate=16, ngroups=1, pool_rows=4, state_row_stride=0,
+             state_dtype=0, io_dtype=0, bc_dtype=0, reserved=0)
+    d.update(kw)
+    return S.ssu_dims(**d)
+
+
+def decode(lib, d, **ptrs):
+    p = dict(x=FAKE, A=FAKE, B=FAKE, C=FAKE, dt=FAKE, dt_bias=None, D=None, z=None,
+             state=FAKE, out=FAKE, idx=None)
+    p.update(ptrs)
+    return lib.ssu_decode(None if d is None else ctypes.byref(d), p["x"], p["A"], p["B"],
+                          p["C"], p["dt"], p["dt_bias"], p["D"], p["z"], p["state"], p["out"],
+                          1, p["idx"], None)
+
+
+def err(lib):
+    return lib.ssu_last_error().decode()
+
+
+@pytest.mark.parametrize("kw,status,needle", [
+    (dict(reserved=1), 1, "reserved"),
+    (dict(batch=-1), 1, "batch"),
+    (dict(nheads=0), 1, "> 0"),
+    (dict(dim=0), 1, "> 0"),
+    (dict(ngroups=3), 1, "multiple of ngroups"),
+    (dict(pool_rows=0), 1, "pool_rows"),
+    (dict(dstate=24), 2, "dstate"),
+    (dict(dstate=512), 2, "dstate"),
+    (dict(dim=5000), 2, "dim"),
+    (dict(state_dtype=7), 2, "dtype"),
+    (dict(io_dtype=3), 2, "dtype"),
+    (dict(state_row_stride=100), 1, "state_row_stride"),
+    (dict(state_row_stride=4 * 16 * 16 + 1), 1, "multiple of 16"),
+    (dict(batch=5), 1, "pool_rows"),
+])
+def test_decode_rejects_bad_dims(lib, kw, status, needle):
+    assert decode(lib, dims(**kw)) == status
+    assert needle in err(lib)
+
+
+def test_decode_null_dims_and_pointers(lib):
+    assert decode(lib, None) == 1 and "dims is NULL" in err(lib)
+    for name in ("x", "A", "B", "C", "dt", "state", "out"):
+        assert decode(lib, dims(), **{name: None}) == 1
+        assert f"'{name}'" in err(lib)
+    assert decode(lib, dims(), x=FAKE + 2) == 1 and "4-byte aligned" in err(lib)
+    assert decode(lib, dims(), z=FAKE + 2) == 1 and "aligned" in err(lib)
+    assert decode(lib, dims(), B=FAKE + 4) == 1 and "16-byte aligned" in err(lib)
+    assert decode(lib, dims(), state=FAKE + 8) == 1 and "16-byte aligned" in err(lib)
+    assert decode(lib, dims(), idx=FAKE + 2) == 1 and "'state_indices'" in err(lib)
+    assert decode(lib, dims(io_dtype=2), x=FAKE + 1) == 1 and "2-byte aligned" in err(lib)
+
+
+def test_decode_empty_batch_is_a_noop(lib):
+    assert decode(lib, dims(batch=0), x=None, state=None) == 0
+    assert err(lib) == ""
+
+
+def test_decode_indices_lift_the_pool_rows_bound(lib):
+    # batch 5 > pool_rows 4 is fine with indices; it then fails on the next check (null x),
+    # which proves the bound was not applied and no launch happened.
+    assert decode(lib, dims(batch=5), idx=FAKE, x=None) == 1 and "'x'" in err(lib)
+
+
+def prefill(lib, d, seq_len=8, stash=(None, None, None, None), **ptrs):
+    p = dict(x=FAKE, A=FAKE, B=FAKE, C=FAKE, dt=FAKE, state=FAKE, out=FAKE)
+    p.update(ptrs)
+    return lib.ssu_prefill(ctypes.byref(d), seq_len, p["x"], p["A"], p["B"], p["C"], p["dt"],
+                           None, None, None, p["state"], p["out"], 1, None, None, *stash, None)
+
+
+def test_prefill_validation(lib):
+    assert prefill(lib, dims(), seq_len=-1) == 1 and "seq_len" in err(lib)
+    assert prefill(lib, dims(), stash=(FAKE, None, None, None)) == 1 and "all four" in err(lib)
+    assert prefill(lib, dims(), stash=(FAKE, FAKE, FAKE, None)) == 1
+    assert prefill(lib, dims(), seq_len=0, x=None) == 0
+    assert prefill(lib, dims(), x=None) == 1 and "'x'" in err(lib)
+    assert prefill(lib, dims(dstate=48)) == 2
+
+
+def replay(lib, d, seq_len=4, active=2, **ptrs):
+    p = dict(state=FAKE, dA=FAKE, u=FAKE, B=FAKE, dt=FAKE, acc=FAKE, idx=None)
+    p.update(ptrs)
+    return lib.ssu_replay(ctypes.byref(d), seq_len, p["state"], p["dA"], p["u"], p["B"],
+                          p["dt"], p["acc"], p["idx"], active, None)
+
+
+def test_replay_validation(lib):
+    assert replay(lib, dims(), active=3) == 1 and "active_batch" in err(lib)
+    assert replay(lib, dims(), active=-1) == 1
+    assert replay(lib, dims(batch=8, pool_rows=4), active=6) == 1 and "pool_rows" in err(lib)
+    assert replay(lib, dims(), seq_len=-2) == 1
+    assert replay(lib, dims(), active=0, state=None) == 0
+    for name in ("state", "dA", "u", "B", "dt", "acc"):
+        assert replay(lib, dims(), **{name: None}) == 1, name
+
+
+def spec_array(specs):
+    arr = (S.ssu_state_spec * max(len(specs), 1))()
+    for i, (kind, layer, shape, dt) in enumerate(specs):
+        arr[i].kind, arr[i].layer, arr[i].rank, arr[i].dtype = kind, layer, len(shape), dt
+        for k, s in enumerate(shape):
+            arr[i].shape[k] = s
+    return arr
+
+
+def test_pool_bytes_per_slot(lib):
+    specs = [(0, 0, (80, 64, 128), 0), (1, 0, (8192, 3), 2), (0, 1, (7,), 3)]
+    out = ctypes.c_size_t()
+    assert lib.ssu_pool_bytes_per_slot(spec_array(specs), 3, ctypes.byref(out)) == 0
+    assert out.value == 80 * 64 * 128 * 4 + 8192 * 3 * 2 + 7
+    assert lib.ssu_pool_bytes_per_slot(spec_array([]), 0, ctypes.byref(out)) == 0
+    assert out.value == 0
+
+
+@pytest.mark.parametrize("specs,needle", [
+    ([(0, -1, (4,), 0)], "negative layer"),
+    ([(0, 0, (4, 0), 0)], "non-positive"),
+    ([(0, 0, (4,), 9)], "dtype"),
+    ([(0, 0, (4,), 0), (1, 0, (4,), 0), (0, 0, (8,), 0)], "repeats"),
+])
+def test_pool_rejects_bad_specs(lib, specs, needle):
+    out = ctypes.c_size_t()
+    assert lib.ssu_pool_bytes_per_slot(spec_array(specs), len(specs), ctypes.byref(out)) == 1
+    assert needle in err(lib)
+    h = ctypes.c_void_p(123)
+    assert lib.ssu_pool_alloc(spec_array(specs), len(specs), 4, None, ctypes.byref(h)) == 1
+    assert h.value is None
+
+
+def test_pool_rank_checks(lib):
+    arr = spec_array([(0, 0, (4,), 0)])
+    arr[0].rank = 5
+    out = ctypes.c_size_t()
+    assert lib.ssu_pool_bytes_per_slot(arr, 1, ctypes.byref(out)) == 1 and "rank" in err(lib)
+
+
+def test_empty_pool_needs_no_device(lib):
+    """slot_count == 0 allocates nothing, so the whole lifecycle runs on the host."""
+    specs = [(0, 0, (80, 64, 128), 0), (1, 0, (128, 3), 2)]
+    h = ctypes.c_void_p()
+    assert lib.ssu_pool_alloc(spec_array(specs), 2, 0, None, ctypes.byref(h)) == 0
+    n, sc = ctypes.c_int32(), ctypes.c_int32()
+    assert lib.ssu_pool_info(h, ctypes.byref(n), ctypes.byref(sc)) == 0
+    assert (n.value, sc.value) == (2, 0)
+    idx = ctypes.c_int32()
+    assert lib.ssu_pool_find_state(h, 1, 0, ctypes.byref(idx)) == 0 and idx.value == 1
+    assert lib.ssu_pool_find_state(h, 1, 5, ctypes.byref(idx)) == 0 and idx.value == -1
+    b = ctypes.c_size_t()
+    assert lib.ssu_pool_state_bytes_per_slot(h, 1, ctypes.byref(b)) == 0 and b.value == 768
+    assert lib.ssu_pool_state_bytes_per_slot(h, 2, ctypes.byref(b)) == 1
+    p = ctypes.c_void_p(1)
+    assert lib.ssu_pool_state_ptr(h, 0, ctypes.byref(p)) == 0 and p.value is None
+    assert lib.ssu_pool_clear_slot(h, -1, None) == 0          # nothing to clear
+    assert lib.ssu_pool_clear_slot(h, 0, None) == 1 and "slot" in err(lib)
+    assert lib.ssu_pool_clear_slot(h, -2, None) == 1
+    ptrs = (ctypes.c_void_p * 2)(FAKE, FAKE)
+    sizes = (ctypes.c_size_t * 2)(80 * 64 * 128 * 4, 768)
+    assert lib.ssu_pool_capture(h, 0, ptrs, sizes, 2, None) == 1 and "slot" in err(lib)
+    assert lib.ssu_pool_restore(h, 0, ptrs, sizes, 2, None) == 1 and "slot" in err(lib)
+    assert lib.ssu_pool_free(h) == 0
+    assert lib.ssu_pool_free(None) == 0
+
+
+def test_null_pool_arguments(lib):
+    assert lib.ssu_pool_clear(None, None) == 1
+    assert lib.ssu_pool_clear_slot(None, 0, None) == 1
+    assert lib.ssu_pool_info(None, None, None) == 1
+    assert lib.ssu_pool_alloc(spec_array([]), 0, 0, None, None) == 1
+    assert lib.ssu_pool_copy_slot_from(None, None, 0, 0, None) == 1
+
+
+def test_python_binding_fails_loudly_without_library(tmp_path):
+    with pytest.raises(RuntimeError, match="not found"):
+        S.load_library(str(tmp_path / "missing.so"))
