@@ -150,10 +150,12 @@ def cpu_baseline(kind, w, seconds, bytes_per_call, units_per_call):
 def main():
     ap = argparse.ArgumentParser(description=__doc__.splitlines()[0])
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=400)
-    ap.add_argument("--warmup", type=int, default=40)
+    ap.add_argument("--steps", type=int, default=1000)
+    ap.add_argument("--warmup", type=int, default=100)
     ap.add_argument("--config", type=int, default=1, choices=[1, 2, 3, 4])
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
+    ap.add_argument("--prewarm-ms", type=float, default=300.0,
+                    help="untimed launches before the warm-up steps, to reach steady clocks")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     args = ap.parse_args()
     world = int(os.environ.get("WORLD_SIZE", "1"))
@@ -227,6 +229,15 @@ def main():
         kkey = "replay_config4"
         bound, peak, unit = "hbm", HBM_PEAK_GBS, "GB/s"
 
+    # Bring the GPU to its steady clocks before the W warm-up steps: a few
+    # milliseconds of launches are not enough for the clocks to ramp.
+    t_pre = time.perf_counter()
+    n_pre = 0
+    while (time.perf_counter() - t_pre) * 1e3 < args.prewarm_ms:
+        for _ in range(20):
+            step(n_pre)
+            n_pre += 1
+        torch.cuda.synchronize()
     for i in range(args.warmup):
         step(i)
     torch.cuda.synchronize()
@@ -288,6 +299,7 @@ def main():
         "roofline": {"bound": bound, "achieved": round(achieved, 3), "peak": round(peak, 3),
                      "unit": unit, "frac": round(achieved / peak, 4), "traffic": traffic},
         "wall_s_timed": round(wall, 3),
+        "prewarm": {"ms": args.prewarm_ms, "launches": n_pre},
     }
     if not args.no_cpu_baseline:
         print(f"[bench] timing the fp64 oracle for about {args.cpu_seconds:.0f} s",

@@ -66,6 +66,84 @@ __device__ __forceinline__ void st_io(void *p, int64_t i, float v, int dt)
         static_cast<uint16_t *>(p)[i] = (uint16_t)(dt == kBF16 ? f32_to_bf16(v) : f32_to_f16(v));
 }
 
+// Typed scalar element access for x/z/out tensors whose dtype is a template
+// parameter (float, _Float16 or bf16_t): one load or store, no branch.
+template <typename T>
+__device__ __forceinline__ float ld_elem(const void *p, int64_t i)
+{
+    if constexpr (sizeof(T) == 4) {
+        return static_cast<const float *>(p)[i];
+    } else {
+        const uint32_t h = static_cast<const uint16_t *>(p)[i];
+        if constexpr (__is_same(T, bf16_t))
+            return bf16_to_f32(h);
+        else
+            return f16_to_f32(h);
+    }
+}
+
+template <typename T>
+__device__ __forceinline__ void st_elem(void *p, int64_t i, float v)
+{
+    if constexpr (sizeof(T) == 4)
+        static_cast<float *>(p)[i] = v;
+    else if constexpr (__is_same(T, bf16_t))
+        static_cast<uint16_t *>(p)[i] = (uint16_t)f32_to_bf16(v);
+    else
+        static_cast<uint16_t *>(p)[i] = (uint16_t)f32_to_f16(v);
+}
+
+// N consecutive B/C elements (N a multiple of 4) of storage type T at element
+// offset i (a multiple of N; base 16-byte aligned), loaded as whole vectors
+// before any conversion so that the loads are all in flight together.
+template <typename T, int N>
+__device__ __forceinline__ void ld_typed(const void *p, int64_t i, float (&v)[N])
+{
+    static_assert(N % 4 == 0, "N must be a multiple of 4");
+    if constexpr (sizeof(T) == 4) {
+        const u32x4 *q = reinterpret_cast<const u32x4 *>(static_cast<const float *>(p) + i);
+        u32x4 w[N / 4];
+#pragma unroll
+        for (int k = 0; k < N / 4; ++k)
+            w[k] = q[k];
+#pragma unroll
+        for (int k = 0; k < N / 4; ++k)
+#pragma unroll
+            for (int j = 0; j < 4; ++j)
+                v[4 * k + j] = __uint_as_float(w[k][j]);
+    } else if constexpr (N % 8 != 0) {
+        const u32x2 w = *reinterpret_cast<const u32x2 *>(static_cast<const uint16_t *>(p) + i);
+#pragma unroll
+        for (int j = 0; j < 2; ++j) {
+            if constexpr (__is_same(T, bf16_t)) {
+                v[2 * j] = __uint_as_float(w[j] << 16);
+                v[2 * j + 1] = __uint_as_float(w[j] & 0xffff0000u);
+            } else {
+                v[2 * j] = f16_to_f32(w[j] & 0xffffu);
+                v[2 * j + 1] = f16_to_f32(w[j] >> 16);
+            }
+        }
+    } else {
+        const u32x4 *q = reinterpret_cast<const u32x4 *>(static_cast<const uint16_t *>(p) + i);
+        u32x4 w[N / 8];
+#pragma unroll
+        for (int k = 0; k < N / 8; ++k)
+            w[k] = q[k];
+#pragma unroll
+        for (int k = 0; k < N / 8; ++k)
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                if constexpr (__is_same(T, bf16_t)) {
+                    v[8 * k + 2 * j] = __uint_as_float(w[k][j] << 16);
+                    v[8 * k + 2 * j + 1] = __uint_as_float(w[k][j] & 0xffff0000u);
+                } else {
+                    v[8 * k + 2 * j] = f16_to_f32(w[k][j] & 0xffffu);
+                    v[8 * k + 2 * j + 1] = f16_to_f32(w[k][j] >> 16);
+                }
+            }
+    }
+}
+
 // N consecutive elements (N a multiple of 4) of a B/C-like tensor at element
 // offset i, which is a multiple of 4 (of 8 when N is); the base is 16-byte
 // aligned. When i is the same on every lane the loads are wave-uniform and the

@@ -7,11 +7,13 @@
 // A row whose accepted count is 0, or whose state index is negative, is left
 // untouched; entries at b >= activeBatchSize are never read.
 //
-// Mapping on gfx950: the same tile mapping as decode (one 256-thread
-// workgroup per (batch row, head); lanes along dstate with 16-byte vectors; all
-// state loads of a tile in flight before the first FMA). The k <= seq_len
-// stashed tokens are applied while the tile sits in registers, so the state is
-// read and written once whatever k is: the kernel is bound by HBM bandwidth.
+// Mapping on gfx950: the decode mapping (the (batch row, head) tile split over
+// workgroups of about 8 KiB of state; lanes along dstate with 16-byte vectors;
+// non-temporal state traffic). The k <= seq_len stashed tokens are applied
+// while the tile sits in registers, so the state is read and written once
+// whatever k is: the kernel is bound by HBM bandwidth. When seq_len <= MAXT
+// the stash values of every token are loaded together with the state, before
+// any of them is used (tokens past k re-read token k-1 and are not applied).
 #include "ssu_device.h"
 #include "ssu_internal.h"
 
@@ -20,10 +22,11 @@ namespace {
 
 struct ReplayShape {
     int64_t row_stride;
-    int32_t seq_len, nheads, dim, ngroups, heads_per_group;
+    int32_t seq_len, nheads, dim, ngroups, heads_per_group, parts;
 };
 
-template <typename ST, int NS, int PASSES>
+// MAXT > 0: seq_len <= MAXT, all stash loads hoisted; MAXT == 0: any seq_len.
+template <typename ST, int NS, int PASSES, int MAXT>
 __global__ __launch_bounds__(256) void ssu_replay_kernel(
     ST *__restrict__ state, const float *__restrict__ sdA, const float *__restrict__ su,
     const float *__restrict__ sB, const float *__restrict__ sdt,
@@ -33,13 +36,16 @@ __global__ __launch_bounds__(256) void ssu_replay_kernel(
     constexpr int LPR = NS / VEC;
     constexpr int RPW = 64 / LPR;
     constexpr int RPP = 4 * RPW;
+    constexpr int ROWS = PASSES * RPP;
 
-    const int tile = blockIdx.x;
+    const int tile = blockIdx.x / sh.parts;
+    const int part = blockIdx.x - tile * sh.parts;
     const int b = tile / sh.nheads;
     const int h = tile - b * sh.nheads;
     const int lane = threadIdx.x & 63;
     const int sub = lane & (LPR - 1);
     const int rsub = (threadIdx.x >> 6) * RPW + lane / LPR;
+    const int r0 = part * ROWS;
 
     const int row = idx ? idx[b] : b;
     const int k = min(accepted[b], sh.seq_len);
@@ -50,36 +56,67 @@ __global__ __launch_bounds__(256) void ssu_replay_kernel(
     const int64_t bT = (int64_t)b * sh.seq_len;
     ST *tp = state + (int64_t)row * sh.row_stride + (int64_t)h * Dm * NS + sub * VEC;
 
-    for (int r0 = 0; r0 < Dm; r0 += PASSES * RPP) {
-        float s[PASSES][VEC];
+    u32x4 raw[PASSES];
 #pragma unroll
-        for (int p = 0; p < PASSES; ++p) {
-            const int r = r0 + p * RPP + rsub;
-            const u32x4 w = r < Dm ? *reinterpret_cast<const u32x4 *>(tp + (int64_t)r * NS)
-                                   : u32x4{0u, 0u, 0u, 0u};
-            SV<ST>::unpack(w, s[p]);
+    for (int p = 0; p < PASSES; ++p) {
+        const int r = min(r0 + p * RPP + rsub, Dm - 1);
+        raw[p] = __builtin_nontemporal_load(reinterpret_cast<const u32x4 *>(tp + (int64_t)r * NS));
+    }
+    float s[PASSES][VEC];
+    if constexpr (MAXT > 0) {
+        float ut[MAXT][PASSES], bt[MAXT][VEC], at[MAXT], dtt[MAXT];
+#pragma unroll
+        for (int t = 0; t < MAXT; ++t) {
+            const int64_t bth = (bT + min(t, k - 1)) * H + h;
+#pragma unroll
+            for (int p = 0; p < PASSES; ++p)
+                ut[t][p] = su[bth * Dm + min(r0 + p * RPP + rsub, Dm - 1)];
+            ld_typed<float, VEC>(sB, ((bT + min(t, k - 1)) * sh.ngroups + g) * NS + sub * VEC,
+                                 bt[t]);
+            at[t] = sdA[bth];
+            dtt[t] = sdt[bth];
         }
+#pragma unroll
+        for (int p = 0; p < PASSES; ++p)
+            SV<ST>::unpack(raw[p], s[p]);
+#pragma unroll
+        for (int t = 0; t < MAXT; ++t) {
+            if (t < k) {
+                const float a = expf(at[t]);
+#pragma unroll
+                for (int p = 0; p < PASSES; ++p) {
+                    const float dtx = dtt[t] * ut[t][p];
+#pragma unroll
+                    for (int e = 0; e < VEC; ++e)
+                        s[p][e] = fmaf(dtx, bt[t][e], s[p][e] * a);
+                }
+            }
+        }
+    } else {
+#pragma unroll
+        for (int p = 0; p < PASSES; ++p)
+            SV<ST>::unpack(raw[p], s[p]);
         for (int t = 0; t < k; ++t) {
             const int64_t bth = (bT + t) * H + h;
             const float a = expf(sdA[bth]);
             const float dtv = sdt[bth];
             float bv[VEC];
-            ld_vec<VEC>(sB, ((bT + t) * sh.ngroups + g) * NS + sub * VEC, kF32, bv);
+            ld_typed<float, VEC>(sB, ((bT + t) * sh.ngroups + g) * NS + sub * VEC, bv);
 #pragma unroll
             for (int p = 0; p < PASSES; ++p) {
-                const int r = r0 + p * RPP + rsub;
-                const float dtx = dtv * (r < Dm ? su[bth * Dm + r] : 0.0f);
+                const float dtx = dtv * su[bth * Dm + min(r0 + p * RPP + rsub, Dm - 1)];
 #pragma unroll
                 for (int e = 0; e < VEC; ++e)
                     s[p][e] = fmaf(dtx, bv[e], s[p][e] * a);
             }
         }
+    }
 #pragma unroll
-        for (int p = 0; p < PASSES; ++p) {
-            const int r = r0 + p * RPP + rsub;
-            if (r < Dm)
-                *reinterpret_cast<u32x4 *>(tp + (int64_t)r * NS) = SV<ST>::pack(s[p]);
-        }
+    for (int p = 0; p < PASSES; ++p) {
+        const int r = r0 + p * RPP + rsub;
+        if (r < Dm)
+            __builtin_nontemporal_store(SV<ST>::pack(s[p]),
+                                        reinterpret_cast<u32x4 *>(tp + (int64_t)r * NS));
     }
 }
 
@@ -88,7 +125,7 @@ hipError_t launch_ns(const ReplayParams &p, hipStream_t stream)
 {
     constexpr int VEC = SV<ST>::VEC;
     constexpr int RPP = 4 * (64 / (NS / VEC));
-    const int need = (p.dim + RPP - 1) / RPP;
+    const int passes = p.dim > RPP ? 2 : 1;
     ReplayShape sh;
     sh.row_stride = p.row_stride;
     sh.seq_len = p.seq_len;
@@ -96,20 +133,33 @@ hipError_t launch_ns(const ReplayParams &p, hipStream_t stream)
     sh.dim = p.dim;
     sh.ngroups = p.ngroups;
     sh.heads_per_group = p.nheads / p.ngroups;
-    const dim3 grid((unsigned)((int64_t)p.active_batch * p.nheads));
+    sh.parts = (p.dim + passes * RPP - 1) / (passes * RPP);
+    const int64_t blocks = (int64_t)p.active_batch * p.nheads * sh.parts;
+    if (blocks > 0x7fffffff)
+        return hipErrorInvalidConfiguration;
+    const dim3 grid((unsigned)blocks);
     ST *st = static_cast<ST *>(p.state);
     (void)hipGetLastError();
-#define SSU_LAUNCH_REPLAY(PS)                                                                  \
-    hipLaunchKernelGGL((ssu_replay_kernel<ST, NS, PS>), grid, dim3(256), 0, stream, st, p.dA, \
+#define SSU_LAUNCH_REPLAY(PS, MT)                                                                \
+    hipLaunchKernelGGL((ssu_replay_kernel<ST, NS, PS, MT>), grid, dim3(256), 0, stream, st, p.dA, \
                        p.u, p.B, p.dt, p.accepted, p.idx, sh)
-    if (need >= 8)
-        SSU_LAUNCH_REPLAY(8);
-    else if (need >= 4)
-        SSU_LAUNCH_REPLAY(4);
-    else if (need >= 2)
-        SSU_LAUNCH_REPLAY(2);
-    else
-        SSU_LAUNCH_REPLAY(1);
+#define SSU_LAUNCH_REPLAY_T(PS)           \
+    if (p.seq_len <= 1)                   \
+        SSU_LAUNCH_REPLAY(PS, 1);         \
+    else if (p.seq_len <= 2)              \
+        SSU_LAUNCH_REPLAY(PS, 2);         \
+    else if (p.seq_len <= 4)              \
+        SSU_LAUNCH_REPLAY(PS, 4);         \
+    else if (p.seq_len <= 8)              \
+        SSU_LAUNCH_REPLAY(PS, 8);         \
+    else                                  \
+        SSU_LAUNCH_REPLAY(PS, 0);
+    if (passes == 2) {
+        SSU_LAUNCH_REPLAY_T(2)
+    } else {
+        SSU_LAUNCH_REPLAY_T(1)
+    }
+#undef SSU_LAUNCH_REPLAY_T
 #undef SSU_LAUNCH_REPLAY
     return hipGetLastError();
 }
