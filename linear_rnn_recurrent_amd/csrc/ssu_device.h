@@ -144,6 +144,69 @@ __device__ __forceinline__ void ld_typed(const void *p, int64_t i, float (&v)[N]
     }
 }
 
+// Raw (unconverted) loads for prefetching: the value is kept as bits until it
+// is converted, so no wait is forced at the load. raw4: 4 consecutive elements
+// (element offset a multiple of 4, base 16-byte aligned).
+template <typename T>
+struct Raw4 {
+    typedef u32x2 type;  // four 16-bit elements
+};
+template <>
+struct Raw4<float> {
+    typedef u32x4 type;
+};
+
+template <typename T>
+__device__ __forceinline__ typename Raw4<T>::type ld_raw4(const void *p, int64_t i)
+{
+    if constexpr (sizeof(T) == 4)
+        return *reinterpret_cast<const u32x4 *>(static_cast<const float *>(p) + i);
+    else
+        return *reinterpret_cast<const u32x2 *>(static_cast<const uint16_t *>(p) + i);
+}
+
+template <typename T>
+__device__ __forceinline__ void cvt_raw4(const typename Raw4<T>::type w, float (&v)[4])
+{
+    if constexpr (sizeof(T) == 4) {
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+            v[j] = __uint_as_float(w[j]);
+    } else {
+#pragma unroll
+        for (int j = 0; j < 2; ++j) {
+            if constexpr (__is_same(T, bf16_t)) {
+                v[2 * j] = __uint_as_float(w[j] << 16);
+                v[2 * j + 1] = __uint_as_float(w[j] & 0xffff0000u);
+            } else {
+                v[2 * j] = f16_to_f32(w[j] & 0xffffu);
+                v[2 * j + 1] = f16_to_f32(w[j] >> 16);
+            }
+        }
+    }
+}
+
+// One element as raw bits (zero-extended for 16-bit types), and its conversion.
+template <typename T>
+__device__ __forceinline__ uint32_t ld_raw1(const void *p, int64_t i)
+{
+    if constexpr (sizeof(T) == 4)
+        return static_cast<const uint32_t *>(p)[i];
+    else
+        return static_cast<const uint16_t *>(p)[i];
+}
+
+template <typename T>
+__device__ __forceinline__ float cvt_raw1(uint32_t w)
+{
+    if constexpr (sizeof(T) == 4)
+        return __uint_as_float(w);
+    else if constexpr (__is_same(T, bf16_t))
+        return __uint_as_float(w << 16);
+    else
+        return f16_to_f32(w);
+}
+
 // N consecutive elements (N a multiple of 4) of a B/C-like tensor at element
 // offset i, which is a multiple of 4 (of 8 when N is); the base is 16-byte
 // aligned. When i is the same on every lane the loads are wave-uniform and the

@@ -57,6 +57,9 @@ hipError_t launch_decode_f32(const DecodeParams &p, hipStream_t stream);
 hipError_t launch_decode_f16(const DecodeParams &p, hipStream_t stream);
 hipError_t launch_decode_bf16(const DecodeParams &p, hipStream_t stream);
 hipError_t launch_prefill(const PrefillParams &p, hipStream_t stream);
+hipError_t launch_prefill_f32(const PrefillParams &p, hipStream_t stream);
+hipError_t launch_prefill_f16(const PrefillParams &p, hipStream_t stream);
+hipError_t launch_prefill_bf16(const PrefillParams &p, hipStream_t stream);
 hipError_t launch_replay(const ReplayParams &p, hipStream_t stream);
 // Copies/zeroes up to any number of segments; one launch per 32 segments.
 hipError_t launch_segments(const Segment *segs, int n, hipStream_t stream);
