@@ -109,6 +109,24 @@ ssu_status check_dims(const ssu_dims *d, const char *fn, bool need_pool_rows_for
 
 size_t io_bytes(int32_t dt) { return dt == SSU_F32 ? 4 : 2; }
 
+// Compute units of the current device, cached per device (a host-side attribute
+// query; no device work, no synchronisation). 0 if the query fails.
+int32_t current_cu_count()
+{
+    static int32_t cache[64] = {0};
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0)
+        return 0;
+    if (dev < 64 && cache[dev] > 0)
+        return cache[dev];
+    int n = 0;
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
+        return 0;
+    if (dev < 64)
+        cache[dev] = n;
+    return n;
+}
+
 // Tensors read with 16-byte vector loads (state, B, C, replay_B) must be 16-byte
 // aligned; every other tensor only needs the alignment of its element type.
 #define SSU_REQUIRE_PTR(p, align, fn)                                                   \
@@ -230,6 +248,8 @@ ssu_status ssu_prefill(const ssu_dims *dims, int32_t seq_len, const void *x, con
     p.st_u = replay_u;
     p.st_B = replay_B;
     p.st_dt = replay_dt;
+    p.cu_count = current_cu_count();
+    p.waves_per_wg = 0;
     return hip_status(ssu::launch_prefill(p, stream), "ssu_prefill launch");
 }
 

@@ -33,6 +33,8 @@ struct PrefillParams {
     int32_t seq_len;
     const int32_t *ctx;
     float *st_dA, *st_u, *st_B, *st_dt;  // all set or all null
+    int32_t cu_count;                    // compute units of the device (workgroup ordering)
+    int32_t waves_per_wg;                // 0: choose from the grid size; 4 or 8: forced
 };
 
 struct ReplayParams {
