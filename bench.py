@@ -10,9 +10,14 @@ last-level cache cannot serve them.
 
     python bench.py [--steps K] [--warmup W] [--config {1,2,3,4}]
 
---config 2/3/4 time prefill / padded decode / MTP replay instead; those pools
-fit in the last-level cache, so each timed launch there is preceded by a 1 GiB
-write that evicts it, and only the kernel itself is timed.
+--config 2/3/4 time prefill / padded decode / MTP replay instead. Their pools
+are smaller than the last-level cache, so the steps rotate over replicas of
+the pool (and, for prefill, of every input) that together exceed it; every
+configuration is timed as back-to-back launches on one stream.
+
+The K timed steps are captured once as a HIP graph and replayed (--no-graph
+launches them one by one from Python instead, which leaves gaps for kernels
+shorter than the binding's per-call host time).
 
 Prints one JSON line: value = algorithmic GB/s (bytes the method must move,
 each element counted once, divided by the average launch time measured with
@@ -157,6 +162,11 @@ def main():
     ap.add_argument("--prewarm-ms", type=float, default=300.0,
                     help="untimed launches before the warm-up steps, to reach steady clocks")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-graph", action="store_true",
+                    help="launch the timed steps one by one from Python instead of one HIP graph")
+    ap.add_argument("--copy-mib", type=int, default=0,
+                    help="after the timed steps, one plain device copy of this many MiB "
+                         "(a known-size kernel for scaling memory-traffic counters)")
     args = ap.parse_args()
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
@@ -173,26 +183,39 @@ def main():
     w = inputs.config(args.config)
     T = {k: (None if v is None else v.to(dev)) for k, v in w.tensors.items()}
     stream = torch.cuda.current_stream(dev)
-    flush = None
+
+    def replicas(names, n):
+        """n copies of the named tensors (replica 0 is the original)."""
+        reps = [T]
+        for _ in range(n - 1):
+            r = dict(T)
+            for k in names:
+                if T[k] is not None:
+                    r[k] = T[k].clone()
+            reps.append(r)
+        return reps
 
     if args.config in (1, 3):
         kind = "decode"
         B = T["x"].shape[0]
         if args.config == 1:
             idx_sets = [s.to(dev) for s in inputs.rotation_index_sets(w.dims["pool_rows"], B, seed=1)]
+            reps = [dict(T, state_indices=ix) for ix in idx_sets]
+            rot = "steps rotate 4 disjoint 64-row index sets over the pool"
         else:
-            idx_sets = [T["state_indices"]]
-            flush = torch.empty(1 << 28, dtype=torch.float32, device=dev)
-        live = int((idx_sets[0] >= 0).sum().item())
+            reps = replicas(["state"], 4)
+            rot = "steps rotate 4 replicas of the pool"
+        live = int((reps[0]["state_indices"] >= 0).sum().item())
         nbytes = decode_bytes(T, live)
         units = live * T["x"].shape[1]
         out = torch.empty_like(T["x"])
 
         def step(i):
-            ssu_decode(T["x"], T["A"], T["B"], T["C"], T["dt"], T["state"], out,
-                       dt_bias=T["dt_bias"], D=T["D"], z=T["z"], dt_softplus=w.dt_softplus,
-                       state_indices=idx_sets[i % len(idx_sets)])
-        src = source_hash("ssu_decode.hip", "ssu_device.h")
+            R = reps[i % len(reps)]
+            ssu_decode(R["x"], R["A"], R["B"], R["C"], R["dt"], R["state"], out,
+                       dt_bias=R["dt_bias"], D=R["D"], z=R["z"], dt_softplus=w.dt_softplus,
+                       state_indices=R["state_indices"])
+        src = source_hash("ssu_decode_impl.h", "ssu_device.h")
         kkey = f"decode_config{args.config}"
         bound, peak, unit = "hbm", HBM_PEAK_GBS, "GB/s"
     elif args.config == 2:
@@ -200,14 +223,16 @@ def main():
         L = T["context_lengths"].clamp(0, T["x"].shape[1]).cpu().tolist()
         nbytes = prefill_bytes(T, L)
         units = sum(L) * T["x"].shape[2]
-        out = torch.empty_like(T["x"])
-        flush = torch.empty(1 << 28, dtype=torch.float32, device=dev)
+        reps = replicas(["x", "z", "B", "C", "dt", "state"], 2)
+        outs = [torch.empty_like(T["x"]) for _ in reps]
+        rot = "steps alternate 2 replicas of the pool and of every input and output"
 
         def step(i):
-            ssu_prefill(T["x"], T["A"], T["B"], T["C"], T["dt"], T["state"], out,
-                        dt_bias=T["dt_bias"], D=T["D"], z=T["z"], dt_softplus=w.dt_softplus,
-                        context_lengths=T["context_lengths"], state_indices=T["state_indices"])
-        src = source_hash("ssu_prefill.hip", "ssu_device.h")
+            R = reps[i % len(reps)]
+            ssu_prefill(R["x"], R["A"], R["B"], R["C"], R["dt"], R["state"], outs[i % len(reps)],
+                        dt_bias=R["dt_bias"], D=R["D"], z=R["z"], dt_softplus=w.dt_softplus,
+                        context_lengths=R["context_lengths"], state_indices=R["state_indices"])
+        src = source_hash("ssu_prefill_impl.h", "ssu_device.h")
         kkey = "prefill_config2"
         elems = sum(L) * T["x"].shape[2] * T["x"].shape[3] * T["B"].shape[3]
         bound, peak, unit = "alu", VALU_PEAK_TOPS, "TOP/s"
@@ -219,11 +244,13 @@ def main():
                   for a, i in zip(acc, idx)]
         nbytes = replay_bytes(T, k_rows)
         units = sum(k_rows) * T["replay_dA"].shape[2]
-        flush = torch.empty(1 << 28, dtype=torch.float32, device=dev)
+        reps = replicas(["state"], 8)
+        rot = "steps rotate 8 replicas of the pool"
 
         def step(i):
-            ssu_replay(T["state"], T["replay_dA"], T["replay_u"], T["replay_B"], T["replay_dt"],
-                       T["accepted_lengths"], state_indices=T["state_indices"],
+            R = reps[i % len(reps)]
+            ssu_replay(R["state"], R["replay_dA"], R["replay_u"], R["replay_B"], R["replay_dt"],
+                       R["accepted_lengths"], state_indices=R["state_indices"],
                        active_batch=w.active_batch)
         src = source_hash("ssu_replay.hip", "ssu_device.h")
         kkey = "replay_config4"
@@ -244,30 +271,33 @@ def main():
     print(f"[bench] config {args.config} ({kind}) warmed up, timing {args.steps} steps",
           file=sys.stderr, flush=True)
 
+    graph = None
+    if not args.no_graph:
+        # The K timed steps as one HIP graph: launches go back to back with no
+        # host work between them, as in a captured serving loop.
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph):
+            for i in range(args.steps):
+                step(args.warmup + i)
+        torch.cuda.synchronize()
+        graph.replay()                      # untimed: first replay uploads the graph
+        torch.cuda.synchronize()
+        stream = torch.cuda.current_stream(dev)
+
     wall0 = time.perf_counter()
-    if flush is None:
-        # back-to-back launches on one stream; events on that same stream
-        ev0 = torch.cuda.Event(enable_timing=True)
-        ev1 = torch.cuda.Event(enable_timing=True)
-        ev0.record(stream)
+    # back-to-back launches on one stream; events recorded on that same stream
+    ev0 = torch.cuda.Event(enable_timing=True)
+    ev1 = torch.cuda.Event(enable_timing=True)
+    ev0.record(stream)
+    if graph is not None:
+        graph.replay()
+    else:
         for i in range(args.steps):
             step(args.warmup + i)
-        ev1.record(stream)
-        torch.cuda.synchronize()
-        total_ms = ev0.elapsed_time(ev1)
-    else:
-        # evict the last-level cache before every launch; time the kernel alone
-        evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-               for _ in range(args.steps)]
-        for i, (e0, e1) in enumerate(evs):
-            flush.fill_(float(i))
-            e0.record(stream)
-            step(args.warmup + i)
-            e1.record(stream)
-        torch.cuda.synchronize()
-        total_ms = sum(e0.elapsed_time(e1) for e0, e1 in evs)
-    wall = time.perf_counter() - wall0
+    ev1.record(stream)
     torch.cuda.synchronize()
+    total_ms = ev0.elapsed_time(ev1)
+    wall = time.perf_counter() - wall0
 
     ms = total_ms / args.steps
     gbs = nbytes / (ms * 1e-3) / 1e9
@@ -289,18 +319,25 @@ def main():
         "vs_baseline": None,
         "dtype": "f32",
         "data": "synthetic",
-        "config": {"workload": inputs.CONFIG_NAMES[args.config]
-                   + ("; steps rotate 4 disjoint 64-row index sets over the pool"
-                      if args.config == 1 else "; LLC evicted before each timed launch"),
+        "config": {"workload": inputs.CONFIG_NAMES[args.config] + "; " + rot,
                    "kernel": kind, "algorithmic_bytes_per_step": nbytes,
                    "token_head_updates_per_step": units},
         "hbm_frac": round(gbs / HBM_PEAK_GBS, 4),
         "token_head_updates_per_s": round(units / (ms * 1e-3), 1),
         "roofline": {"bound": bound, "achieved": round(achieved, 3), "peak": round(peak, 3),
                      "unit": unit, "frac": round(achieved / peak, 4), "traffic": traffic},
+        "launch": "eager" if graph is None else "hip graph of the K steps",
         "wall_s_timed": round(wall, 3),
         "prewarm": {"ms": args.prewarm_ms, "launches": n_pre},
     }
+    if args.copy_mib > 0:
+        cal_src = torch.ones(args.copy_mib << 18, dtype=torch.float32, device=dev)
+        cal_dst = torch.empty_like(cal_src)
+        torch.cuda.synchronize()
+        cal_dst.copy_(cal_src)
+        torch.cuda.synchronize()
+        rec["copy_calibration_bytes"] = cal_src.numel() * 4
+        del cal_src, cal_dst
     if not args.no_cpu_baseline:
         print(f"[bench] timing the fp64 oracle for about {args.cpu_seconds:.0f} s",
               file=sys.stderr, flush=True)
