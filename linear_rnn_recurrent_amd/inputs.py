@@ -19,6 +19,11 @@ Replay stash (the stash a verify prefill would have written):
   u          ~ N(0, 1), replayB ~ N(0, std 1/sqrt(dstate))
 Values are drawn in float64 (float32 for the large state pools), rounded to
 fp32, then cast on the CPU by torch (round to nearest even) to bf16/fp16.
+Draft trees (one per batch row, nodes in topological order, node 0 a root):
+  'random': node n > 0 hangs under a uniformly drawn earlier node whose depth
+            is below max_depth - 1 (a random recursive tree, depth ~ ln n);
+  'chain' : parent n - 1 (a linear draft); 'star': every node a root.
+  depths  : the exact hop count of every node, unless a test overrides it.
 """
 from dataclasses import dataclass, field
 from typing import Dict, Optional
@@ -31,7 +36,7 @@ DTYPES = {"f32": torch.float32, "f16": torch.float16, "bf16": torch.bfloat16}
 
 @dataclass
 class Workload:
-    """One batch of inputs.  `kind` is 'decode', 'prefill' or 'replay'."""
+    """One batch of inputs.  `kind` is 'decode', 'prefill', 'replay' or 'tree'."""
     name: str
     kind: str
     dims: Dict[str, int]
@@ -184,6 +189,75 @@ def replay_workload(*, active_batch, seq_len, nheads, dim, dstate, ngroups, pool
     dims = dict(batch=active_batch, nheads=nheads, dim=dim, dstate=dstate, ngroups=ngroups,
                 pool_rows=pool_rows, seq_len=seq_len)
     return Workload(name, "replay", dims, T, False, active_batch=active_batch)
+
+
+def random_tree(rng, num_nodes, shape="random", max_depth=None):
+    """Parent ids and depths (hops to the root) of one draft tree."""
+    parents = np.full(num_nodes, -1, dtype=np.int32)
+    depth = np.zeros(num_nodes, dtype=np.int32)
+    for n in range(1, num_nodes):
+        if shape == "star":
+            continue
+        if shape == "chain":
+            p = n - 1
+        else:
+            ok = np.arange(n) if max_depth is None else np.nonzero(depth[:n] < max_depth - 1)[0]
+            p = int(ok[rng.integers(ok.size)])
+        parents[n] = p
+        depth[n] = depth[p] + 1
+    return parents, depth
+
+
+def tree_workload(*, batch, num_nodes, nheads, dim, dstate, ngroups, pool_rows, seed,
+                  state_dtype="f32", io_dtype="bf16", bc_dtype="bf16", bc_std=None,
+                  shape="random", max_depth=None, indices="perm", n_live=None,
+                  with_z=False, with_D=True, with_bias=True, dt_softplus=True,
+                  with_depths=True, name="tree"):
+    """Tree-verify inputs: per-node tensors in the prefill layouts (the node axis
+    in place of the token axis) and int32 parent_ids / depths [batch, num_nodes].
+    shape: 'random', 'chain', 'star' or a [batch, num_nodes] parent-id array."""
+    rng = np.random.default_rng(seed)
+    if bc_std is None:
+        bc_std = 1.0
+    A, dt_bias, D = _head_params(rng, nheads)
+    state = _pool(rng, (pool_rows, nheads, dim, dstate), state_dtype)
+    x = rng.standard_normal((batch, num_nodes, nheads, dim))
+    z = rng.standard_normal((batch, num_nodes, nheads, dim))
+    Bm = rng.standard_normal((batch, num_nodes, ngroups, dstate)) * bc_std
+    Cm = rng.standard_normal((batch, num_nodes, ngroups, dstate)) * bc_std
+    dt = rng.standard_normal((batch, num_nodes, nheads)) * 0.5
+    if isinstance(shape, str):
+        trees = [random_tree(rng, num_nodes, shape, max_depth) for _ in range(batch)]
+        par = np.stack([t[0] for t in trees]) if batch else np.zeros((0, num_nodes), np.int32)
+        dep = np.stack([t[1] for t in trees]) if batch else np.zeros((0, num_nodes), np.int32)
+    else:
+        par = np.asarray(shape, dtype=np.int32).reshape(batch, num_nodes)
+        dep = np.zeros_like(par)
+        for b in range(batch):
+            for n in range(num_nodes):
+                p = par[b, n]
+                dep[b, n] = dep[b, p] + 1 if 0 <= p < n else 0
+    if isinstance(indices, str) and indices == "perm":
+        idx = rng.permutation(pool_rows)[:batch].astype(np.int32)
+    elif isinstance(indices, str) and indices == "none":
+        idx = None
+    else:
+        idx = np.asarray(indices, dtype=np.int32)
+    if idx is not None and n_live is not None:
+        idx = idx.copy()
+        idx[n_live:] = -1
+    T = {
+        "x": _t(x, io_dtype), "z": _t(z, io_dtype) if with_z else None,
+        "B": _t(Bm, bc_dtype), "C": _t(Cm, bc_dtype), "dt": _t(dt, "f32"),
+        "A": _t(A, "f32"), "dt_bias": _t(dt_bias, "f32") if with_bias else None,
+        "D": _t(D, "f32") if with_D else None, "state": state,
+        "state_indices": None if idx is None else torch.from_numpy(idx),
+        "parent_ids": torch.from_numpy(np.ascontiguousarray(par)),
+        "depths": torch.from_numpy(np.ascontiguousarray(dep)) if with_depths else None,
+    }
+    dims = dict(batch=batch, nheads=nheads, dim=dim, dstate=dstate, ngroups=ngroups,
+                pool_rows=pool_rows, seq_len=num_nodes, num_nodes=num_nodes)
+    return Workload(name, "tree", dims, T, dt_softplus)
 
 
 # ---------------------------------------------------------------------------

@@ -10,7 +10,9 @@ shape list; invokeSelectiveStateUpdatePrefill; MambaReplayLayerInfo):
 
   decode : x [b,h,d]  B,C [b,g,n]  dt [b,h]  z/out [b,h,d]
   prefill: x [b,t,h,d]  B,C [b,t,g,n]  dt [b,t,h]  z/out [b,t,h,d]
-  replay : dA,DT [b,t,h]  u [b,t,h,d]  Bst [b,t,g,n]
+  replay : dA,DT [b,t,h]  u [b,t,h,d]  Bst [b,t,g,n]  node_ids [b, max_accept_len]
+  tree   : prefill layouts with the node axis in place of t; parent_ids and
+           depths [b, num_nodes] (invokeSelectiveStateUpdateDDTree)
   state  : [rows, h, d, n], or a flat buffer with `row_stride` elements per row
 
 `state`, `out` and the stash arrays are updated in place.
@@ -37,8 +39,12 @@ def _lib():
         lib.oracle_ssu_decode.argtypes = [i32] * 5 + [i64] + [_F64P] * 10 + [i32, _I32P]
         lib.oracle_ssu_prefill.argtypes = ([i32] * 6 + [i64] + [_F64P] * 10 + [i32, _I32P, _I32P]
                                            + [_F64P] * 5)
-        lib.oracle_ssu_replay.argtypes = [i32] * 6 + [i64] + [_F64P] * 5 + [_I32P, _I32P]
-        for f in (lib.oracle_ssu_decode, lib.oracle_ssu_prefill, lib.oracle_ssu_replay):
+        lib.oracle_ssu_replay.argtypes = ([i32] * 6 + [i64] + [_F64P] * 5 + [_I32P] * 3
+                                          + [i32])
+        lib.oracle_ssu_tree.argtypes = ([i32] * 6 + [i64] + [_F64P] * 10 + [i32] + [_I32P] * 3
+                                        + [_F64P] * 5)
+        for f in (lib.oracle_ssu_decode, lib.oracle_ssu_prefill, lib.oracle_ssu_replay,
+                  lib.oracle_ssu_tree):
             f.restype = None
         lib.oracle_num_threads.argtypes = []
         lib.oracle_num_threads.restype = ctypes.c_int32
@@ -112,7 +118,8 @@ def prefill(x, A, B, C, dt, state, out, *, dt_bias=None, D=None, z=None,
 
 
 def replay(state, dA, u, Bst, DT, accepted_lengths, *, state_indices=None,
-           active_batch=None, row_stride=None):
+           active_batch=None, row_stride=None, node_ids=None):
+    """node_ids: None (token t is stash entry t) or int32 [b, max_accept_len]."""
     nb, seq_len, nheads = dA.shape
     dim = u.shape[3]
     ngroups, dstate = Bst.shape[2], Bst.shape[3]
@@ -123,8 +130,42 @@ def replay(state, dA, u, Bst, DT, accepted_lengths, *, state_indices=None,
     st = _f64(state, "state", True)
     ac = _i32(accepted_lengths)
     ix = _i32(state_indices)
+    ni = _i32(node_ids)
+    max_accept = 0 if node_ids is None else ni[0].shape[1]
     _lib().oracle_ssu_replay(active_batch, seq_len, nheads, dim, dstate, ngroups, rs,
-                             st[1], *[k[1] for k in keep], ac[1], ix[1])
+                             st[1], *[k[1] for k in keep], ac[1], ix[1], ni[1], max_accept)
+
+
+MAX_NODES = 128
+
+
+def tree(x, A, B, C, dt, state, out, parent_ids, *, depths=None, dt_bias=None, D=None, z=None,
+         dt_softplus=True, state_indices=None, stash=None, row_stride=None):
+    """Tree verify: x [b,n,h,d], B/C [b,n,g,s], dt [b,n,h], parent_ids/depths [b,n].
+
+    `state` is only read. stash: None or dict of float64 arrays 'dA', 'u', 'B',
+    'dt' (filled in for every node of every live row)."""
+    batch, num_nodes, nheads, dim = x.shape
+    if num_nodes > MAX_NODES:
+        raise ValueError(f"a draft tree holds at most {MAX_NODES} nodes")
+    ngroups, dstate = B.shape[2], B.shape[3]
+    rs = _row_stride(state, nheads, dim, dstate, row_stride)
+    keep = [_f64(v, k) for k, v in (("x", x), ("A", A), ("B", B), ("C", C), ("dt", dt),
+                                     ("dt_bias", dt_bias), ("D", D), ("z", z))]
+    st = _f64(state, "state")
+    ot = _f64(out, "out", True)
+    ix = _i32(state_indices)
+    pa = _i32(parent_ids)
+    dp = _i32(depths)
+    scratch = np.empty(batch * nheads * (dim * dstate + dim), dtype=np.float64)
+    if stash is not None:
+        sd = [_f64(stash[k], "stash " + k, True) for k in ("dA", "u", "B", "dt")]
+        sp = [s[1] for s in sd]
+    else:
+        sp = [None] * 4
+    _lib().oracle_ssu_tree(batch, num_nodes, nheads, dim, dstate, ngroups, rs,
+                           *[k[1] for k in keep[:8]], st[1], ot[1], 1 if dt_softplus else 0,
+                           ix[1], pa[1], dp[1], *sp, scratch.ctypes.data_as(_F64P))
 
 
 def num_threads():

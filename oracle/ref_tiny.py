@@ -10,7 +10,13 @@ Definitions followed (TensorRT-Edge-LLM "Selective State Update" page):
       output    = sum_i new_state_i * C_i + D * x, then * silu(z) if z is given
   * invokeSelectiveStateUpdatePrefill: all seq_len tokens in order; with the
     replay stash the committed state stays read-only.
-  * MambaReplayLayerInfo: replay the first acceptedLengths[b] stashed tokens.
+  * MambaReplayLayerInfo: replay the first acceptedLengths[b] stashed tokens;
+    invokeMambaReplayReconstructBatched: optionally through acceptedNodeIds.
+  * invokeSelectiveStateUpdateDDTree: every node's output after the recurrence
+    along its ancestor path.  Here the path's state is written in its unrolled
+    form (products of the decays along the path), not replayed step by step,
+    so that this file and the C oracle reach the tree outputs by different
+    formulas.
 Padding rows (negative index) follow the FlashInfer gdn_fused_decode_step page,
 parameter state_indices.
 
@@ -133,8 +139,9 @@ def prefill(x, A, B, C, dt, state, out, dt_bias=None, D=None, z=None,
 
 
 def replay(state, dA, u, Bst, DT, accepted_lengths, state_indices=None,
-           active_batch=None):
-    """dA, DT [b,t,h]; u [b,t,h,d]; Bst [b,t,g,n]; state [rows,h,d,n]."""
+           active_batch=None, node_ids=None):
+    """dA, DT [b,t,h]; u [b,t,h,d]; Bst [b,t,g,n]; state [rows,h,d,n];
+    node_ids None or [b, max_accept_len] (stash entry of each accepted token)."""
     nb_stash, nt, nh = dA.shape
     nd = u.shape[3]
     ng, ns = Bst.shape[2], Bst.shape[3]
@@ -142,15 +149,88 @@ def replay(state, dA, u, Bst, DT, accepted_lengths, state_indices=None,
     nb = nb_stash if active_batch is None else active_batch
     for b in range(nb):
         r = _row(state_indices, b)
-        steps = min(int(accepted_lengths[b]), nt)
+        cap = nt if node_ids is None else node_ids.shape[1]
+        steps = min(int(accepted_lengths[b]), cap)
         if r < 0 or steps <= 0:
             continue
+        order = []
+        for t in range(steps):
+            pos = t if node_ids is None else int(node_ids[b, t])
+            if not 0 <= pos < nt:
+                break
+            order.append(pos)
         for h in range(nh):
             grp = h // per_group
-            for t in range(steps):
+            for t in order:
                 dec = math.exp(float(dA[b, t, h]))
                 for d in range(nd):
                     for n in range(ns):
                         state[r, h, d, n] = (float(state[r, h, d, n]) * dec
                                              + float(Bst[b, t, grp, n]) * float(DT[b, t, h])
                                              * float(u[b, t, h, d]))
+
+
+def ancestors(parent_ids, depths, b, node):
+    """Nodes whose tokens the recurrence of `node` runs over, node first, then
+    its parent, and so on: at most depths[b, node] hops (any number without
+    depths), ending at a negative parent id or one not smaller than the node
+    it belongs to."""
+    chain = [node]
+    limit = node if depths is None else int(depths[b, node])
+    while len(chain) <= limit:
+        nxt = int(parent_ids[b, chain[-1]])
+        if nxt < 0 or nxt >= chain[-1]:
+            break
+        chain.append(nxt)
+    return chain
+
+
+def tree(x, A, B, C, dt, state, out, parent_ids, depths=None, dt_bias=None, D=None, z=None,
+         dt_softplus=True, state_indices=None, stash=None):
+    """Tree verify. x, z, out [b,m,h,d]; B, C [b,m,g,n]; dt [b,m,h]; parent_ids,
+    depths [b,m]. state [rows,h,d,n] is read only.
+
+    For a node whose chain (node first) is c_0 .. c_k with decays a_i and inputs
+    dt'_i x_i B_i, the state after the chain is
+        (a_0 a_1 ... a_k) S0 + sum_i (a_0 ... a_{i-1}) dt'_i x_i B_i^T
+    and the node's output is C_0 . state + D x_0, gated by silu(z_0)."""
+    nb, nm, nh, nd = x.shape
+    ng, ns = B.shape[2], B.shape[3]
+    per_group = nh // ng
+    for b in range(nb):
+        r = _row(state_indices, b)
+        if r < 0:
+            for m in range(nm):
+                for h in range(nh):
+                    for d in range(nd):
+                        out[b, m, h, d] = 0.0
+            continue
+        for h in range(nh):
+            grp = h // per_group
+            bias = None if dt_bias is None else dt_bias[h]
+            dtp = [_dt_proc(dt[b, m, h], bias, dt_softplus) for m in range(nm)]
+            dec = [math.exp(float(A[h]) * v) for v in dtp]
+            for m in range(nm):
+                chain = ancestors(parent_ids, depths, b, m)
+                for d in range(nd):
+                    total = 0.0
+                    for n in range(ns):
+                        later = 1.0   # product of the decays of the chain nodes after c_i
+                        acc = 0.0
+                        for c in chain:
+                            acc += later * dtp[c] * float(x[b, c, h, d]) * float(B[b, c, grp, n])
+                            later *= dec[c]
+                        acc += later * float(state[r, h, d, n])
+                        total += acc * float(C[b, m, grp, n])
+                    if D is not None:
+                        total += float(D[h]) * float(x[b, m, h, d])
+                    if z is not None:
+                        total *= _gate(float(z[b, m, h, d]))
+                    out[b, m, h, d] = total
+                if stash is not None:
+                    stash['dA'][b, m, h] = float(A[h]) * dtp[m]
+                    stash['dt'][b, m, h] = dtp[m]
+                    for d in range(nd):
+                        stash['u'][b, m, h, d] = float(x[b, m, h, d])
+                    for n in range(ns):
+                        stash['B'][b, m, grp, n] = float(B[b, m, grp, n])

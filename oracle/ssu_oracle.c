@@ -29,6 +29,13 @@
  *  replay  -- same page, struct MambaReplayLayerInfo: re-run the recurrence
  *             over the first acceptedLengths[b] stashed tokens, in place, for
  *             b < activeBatchSize; accepted == 0 leaves the row untouched.
+ *             With acceptedNodeIds (invokeMambaReplayReconstructBatched) token
+ *             t of row b is the stash entry of node acceptedNodeIds[b, t].
+ *  tree    -- same page, invokeSelectiveStateUpdateDDTree: for every node of
+ *             a draft tree, walk treeParentIds from the node to the root,
+ *             replay the decode step along that path (root first) from the
+ *             committed state, which stays read-only, and emit the node's
+ *             output; stash the node's own dA, x, B and dt'.
  *
  * Readings where the pages are silent (each is listed with its reason in the
  * design notes): the bias is added before softplus; head h reads group
@@ -36,6 +43,12 @@
  * applies exp(dA); tokens t >= clamp(contextLengths[b], 0, seq_len) produce
  * zero outputs and zero stash entries and do not touch the state; replay runs
  * min(acceptedLengths[b], seq_len) tokens and skips negative row indices.
+ * Tree readings: a node's parent id is that of an earlier node (smaller id) or
+ * negative for a node whose predecessor is the committed state; treeDepths[n]
+ * bounds the number of parent hops of the walk (NULL: no bound); a parent id
+ * that is not smaller than the current node ends the walk there.  Replay with
+ * node ids runs min(acceptedLengths[b], maxAcceptLen) tokens and stops at the
+ * first id outside [0, seq_len).
  *
  * Parity pins: tests/test_oracle_pins.py checks this file against hand-derived
  * closed forms, invariants, the unrolled-sum form of the recurrence and an
@@ -47,6 +60,9 @@
 #ifdef _OPENMP
 #include <omp.h>
 #endif
+
+/* Node budget of one draft tree (the page's shared speculative verify budget). */
+#define ORACLE_MAX_NODES 128
 
 static double softplus(double v)
 {
@@ -197,7 +213,8 @@ void oracle_ssu_replay(int32_t active_batch, int32_t seq_len, int32_t nheads,
                        int32_t dim, int32_t dstate, int32_t ngroups,
                        int64_t row_stride, double *state, const double *st_dA,
                        const double *st_u, const double *st_B, const double *st_dt,
-                       const int32_t *accepted_lengths, const int32_t *state_indices)
+                       const int32_t *accepted_lengths, const int32_t *state_indices,
+                       const int32_t *node_ids, int32_t max_accept_len)
 {
     const int hpg = nheads / ngroups;
     const int64_t tile = (int64_t)dim * dstate;
@@ -205,21 +222,113 @@ void oracle_ssu_replay(int32_t active_batch, int32_t seq_len, int32_t nheads,
     for (int b = 0; b < active_batch; ++b) {
         for (int h = 0; h < nheads; ++h) {
             const int64_t s = state_indices ? state_indices[b] : b;
+            const int limit = node_ids ? max_accept_len : seq_len;
             int k = accepted_lengths[b];
-            if (k > seq_len) k = seq_len;
+            if (k > limit) k = limit;
             if (s < 0 || k <= 0)
                 continue;
             const int g = h / hpg;
             double *st = state + s * row_stride + h * tile;
             for (int t = 0; t < k; ++t) {
-                const int64_t bth = ((int64_t)b * seq_len + t) * nheads + h;
-                const int64_t btg = ((int64_t)b * seq_len + t) * ngroups + g;
+                /* stash position of the t-th accepted token */
+                int pos = t;
+                if (node_ids) {
+                    pos = node_ids[(int64_t)b * max_accept_len + t];
+                    if (pos < 0 || pos >= seq_len)
+                        break;
+                }
+                const int64_t bth = ((int64_t)b * seq_len + pos) * nheads + h;
+                const int64_t btg = ((int64_t)b * seq_len + pos) * ngroups + g;
                 const double decay = exp(st_dA[bth]);
                 for (int d = 0; d < dim; ++d)
                     for (int n = 0; n < dstate; ++n)
                         st[(int64_t)d * dstate + n] =
                             st[(int64_t)d * dstate + n] * decay +
                             st_B[btg * dstate + n] * st_dt[bth] * st_u[bth * dim + d];
+            }
+        }
+    }
+}
+
+/* Root-to-node path of node n of one tree: path[0] is the node reached last by
+ * the walk up treeParentIds, path[len-1] = n.  The walk takes at most
+ * depths[n] hops (any number when depths is NULL) and stops at a parent id that
+ * is negative or not smaller than the current node.  Returns len (<= n + 1). */
+static int tree_path(const int32_t *parents, const int32_t *depths, int n, int *path)
+{
+    int up[ORACLE_MAX_NODES];
+    int len = 0;
+    int j = n;
+    const int cap = depths ? depths[n] : n;
+    up[len++] = j;
+    while (len - 1 < cap) {
+        const int p = parents[j];
+        if (p < 0 || p >= j)
+            break;
+        j = p;
+        up[len++] = j;
+    }
+    for (int i = 0; i < len; ++i)
+        path[i] = up[len - 1 - i];
+    return len;
+}
+
+void oracle_ssu_tree(int32_t batch, int32_t num_nodes, int32_t nheads, int32_t dim,
+                     int32_t dstate, int32_t ngroups, int64_t row_stride,
+                     const double *x, const double *A, const double *B, const double *C,
+                     const double *dt, const double *dt_bias, const double *D,
+                     const double *z, const double *state, double *out,
+                     int32_t dt_softplus, const int32_t *state_indices,
+                     const int32_t *parent_ids, const int32_t *depths, double *st_dA,
+                     double *st_u, double *st_B, double *st_dt, double *scratch)
+{
+    /* scratch: batch*nheads*(dim*dstate + dim) doubles: a private copy of the
+     * head's committed state per walk, and the outputs of the path's inner
+     * nodes (discarded). num_nodes <= ORACLE_MAX_NODES. */
+    const int hpg = nheads / ngroups;
+    const int64_t tile = (int64_t)dim * dstate;
+    const int stash = st_dA != 0;
+#pragma omp parallel for collapse(2) schedule(dynamic, 1)
+    for (int b = 0; b < batch; ++b) {
+        for (int h = 0; h < nheads; ++h) {
+            const int64_t s = state_indices ? state_indices[b] : b;
+            const int g = h / hpg;
+            const int32_t *par = parent_ids + (int64_t)b * num_nodes;
+            const int32_t *dep = depths ? depths + (int64_t)b * num_nodes : 0;
+            if (s < 0) {
+                for (int n = 0; n < num_nodes; ++n)
+                    for (int d = 0; d < dim; ++d)
+                        out[(((int64_t)b * num_nodes + n) * nheads + h) * dim + d] = 0.0;
+                continue;
+            }
+            double *priv = scratch + ((int64_t)b * nheads + h) * (tile + dim);
+            double *inner = priv + tile;
+            const double *st0 = state + s * row_stride + h * tile;
+            int path[ORACLE_MAX_NODES];
+            for (int n = 0; n < num_nodes; ++n) {
+                const int len = tree_path(par, dep, n, path);
+                memcpy(priv, st0, sizeof(double) * tile);
+                for (int i = 0; i < len; ++i) {
+                    const int j = path[i];
+                    const int64_t bjh = ((int64_t)b * num_nodes + j) * nheads + h;
+                    const int64_t bjg = ((int64_t)b * num_nodes + j) * ngroups + g;
+                    const double dtp = processed_dt(dt[bjh], dt_bias, h, dt_softplus);
+                    head_step(dim, dstate, priv, x + bjh * dim, B + bjg * dstate,
+                              C + bjg * dstate, dtp, exp(A[h] * dtp), D ? D[h] : 0.0, D != 0,
+                              z ? z + bjh * dim : 0, i == len - 1 ? out + bjh * dim : inner);
+                }
+                if (stash) {
+                    const int64_t bnh = ((int64_t)b * num_nodes + n) * nheads + h;
+                    const int64_t bng = ((int64_t)b * num_nodes + n) * ngroups + g;
+                    const double dtp = processed_dt(dt[bnh], dt_bias, h, dt_softplus);
+                    st_dA[bnh] = A[h] * dtp;
+                    st_dt[bnh] = dtp;
+                    for (int d = 0; d < dim; ++d)
+                        st_u[bnh * dim + d] = x[bnh * dim + d];
+                    if (h % hpg == 0)
+                        for (int k = 0; k < dstate; ++k)
+                            st_B[bng * dstate + k] = B[bng * dstate + k];
+                }
             }
         }
     }

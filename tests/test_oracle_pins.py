@@ -44,7 +44,8 @@ def _ev(v):
 def _inputs(case):
     out = {}
     for k, v in case["inputs"].items():
-        if k in ("state_indices", "context_lengths", "accepted_lengths"):
+        if k in ("state_indices", "context_lengths", "accepted_lengths", "parent_ids", "depths",
+                 "node_ids"):
             out[k] = np.array(v, dtype=np.int32)
         else:
             out[k] = np.array(_ev(v), dtype=np.float64)
@@ -78,10 +79,25 @@ def _run_case(case, impl):
         res = {"state": st, "out": out}
         if stash is not None:
             res.update({"stash_" + k: v for k, v in stash.items()})
+    elif case["kind"] == "tree":
+        out = np.zeros(a["x"].shape)
+        st = a["state"].copy()
+        stash = None
+        if case.get("stash"):
+            b, m, h, d = a["x"].shape
+            stash = {"dA": np.full((b, m, h), 99.0), "dt": np.full((b, m, h), 99.0),
+                     "u": np.full((b, m, h, d), 99.0),
+                     "B": np.full((b, m) + a["B"].shape[2:], 99.0)}
+        impl.tree(a["x"], a["A"], a["B"], a["C"], a["dt"], st, out, a["parent_ids"],
+                  depths=a.get("depths"), dt_bias=a.get("dt_bias"), D=a.get("D"), z=a.get("z"),
+                  dt_softplus=sp, state_indices=a.get("state_indices"), stash=stash)
+        res = {"state": st, "out": out}
+        if stash is not None:
+            res.update({"stash_" + k: v for k, v in stash.items()})
     else:
         st = a["state"].copy()
         impl.replay(st, a["dA"], a["u"], a["Bst"], a["DT"], a["accepted_lengths"],
-                    state_indices=a.get("state_indices"))
+                    state_indices=a.get("state_indices"), node_ids=a.get("node_ids"))
         res = {"state": st}
     return res
 
