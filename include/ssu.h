@@ -7,6 +7,8 @@
  *          mamba_ssm::invokeSelectiveStateUpdate (decode, "Computes" paragraph
  *          and shape list), invokeSelectiveStateUpdatePrefill (prefill loop,
  *          replay stash), struct MambaReplayLayerInfo (replay reconstruct),
+ *          invokeMambaReplayReconstructBatched (acceptedNodeIds, maxAcceptLen),
+ *          invokeSelectiveStateUpdateDDTree (tree verify),
  *          invokeMambaStateClear (slot clear, slot -1 = all).
  *   [PAD]  FlashInfer, "flashinfer.gdn_fused_decode_step" page, parameters
  *          ssm_state (paged pool, padded row stride) and state_indices
@@ -119,19 +121,59 @@ ssu_status ssu_prefill(const ssu_dims *dims, int32_t seq_len, const void *x, con
                        const int32_t *state_indices, float *replay_dA, float *replay_u,
                        float *replay_B, float *replay_dt, hipStream_t stream);
 
-/* ssu_replay -- commit accepted draft tokens [SSU MambaReplayLayerInfo]:
- * for b < active_batch with r = state_indices[b] >= 0 and
- * k = min(accepted_lengths[b], seq_len) > 0, apply k tokens in place:
- *   state[r,h,d,n] = state[r,h,d,n]*exp(replay_dA[b,t,h])
- *                    + replay_B[b,t,g,n]*replay_dt[b,t,h]*replay_u[b,t,h,d]
+/* ssu_replay -- commit accepted draft tokens [SSU MambaReplayLayerInfo,
+ * invokeMambaReplayReconstructBatched]: for b < active_batch with
+ * r = state_indices[b] >= 0, apply k tokens in place, in order:
+ *   state[r,h,d,n] = state[r,h,d,n]*exp(replay_dA[b,p,h])
+ *                    + replay_B[b,p,g,n]*replay_dt[b,p,h]*replay_u[b,p,h,d]
+ * where token t reads stash position p = t and k = min(accepted_lengths[b], seq_len)
+ * when accepted_node_ids is NULL; otherwise p = accepted_node_ids[b, t]
+ * ([dims->batch, max_accept_len] int32, the accepted path of a tree verify,
+ * root first), k = min(accepted_lengths[b], max_accept_len), and the row stops
+ * before the first p outside [0, seq_len).
  * Stash layouts as ssu_prefill with dims->batch rows (the allocation);
  * accepted_lengths and state_indices [dims->batch] int32. Entries at
  * b >= active_batch are never read; rows with k == 0 are left untouched.
- * Requires 0 <= active_batch <= dims->batch. state_indices may be NULL (r = b). */
+ * Requires 0 <= active_batch <= dims->batch, and max_accept_len >= 1 when
+ * accepted_node_ids is given (ignored otherwise). state_indices may be NULL (r = b). */
 ssu_status ssu_replay(const ssu_dims *dims, int32_t seq_len, void *state,
                       const float *replay_dA, const float *replay_u, const float *replay_B,
                       const float *replay_dt, const int32_t *accepted_lengths,
-                      const int32_t *state_indices, int32_t active_batch, hipStream_t stream);
+                      const int32_t *state_indices, int32_t active_batch,
+                      const int32_t *accepted_node_ids, int32_t max_accept_len,
+                      hipStream_t stream);
+
+/* Most nodes one draft tree may hold (the verify budget of the tree kernel) [SSU]. */
+#define SSU_MAX_TREE_NODES 128
+
+/* ssu_tree_verify -- tree speculative verify [SSU invokeSelectiveStateUpdateDDTree].
+ * Every batch row b carries a draft tree of num_nodes nodes
+ * (0 <= num_nodes <= SSU_MAX_TREE_NODES) in topological order: the parent of
+ * node m is parent_ids[b,m] < m, or negative when m hangs directly under the
+ * committed state. The path of m is m, its parent, the parent's parent, ...,
+ * taking at most depths[b,m] hops (any number when depths is NULL) and ending
+ * at a parent id that is negative or not smaller than the node it belongs to.
+ * The decode step of ssu_decode runs along the path, root first, starting
+ * from pool row r = state_indices[b] (or b), and out[b,m] is the output of the
+ * step of node m itself. The pool is only read: the committed state never
+ * changes.
+ * Layouts: x, z, out [batch, num_nodes, nheads, dim] (io_dtype);
+ * dt [batch, num_nodes, nheads]; B, C [batch, num_nodes, ngroups, dstate]
+ * (bc_dtype); parent_ids, depths [batch, num_nodes] int32; A, dt_bias, D
+ * [nheads]; state [pool_rows, nheads, dim, dstate] (state_dtype).
+ * Replay stash (all four or none): as ssu_prefill with the node axis in place
+ * of the token axis, holding every node's own A[h]*dt', dt', x and B; commit an
+ * accepted path with ssu_replay and accepted_node_ids.
+ * z is optional (NULL: no gate; the page's form of this kernel has none), as
+ * are dt_bias, D, depths and state_indices.
+ * Padding rows (r < 0): out[b] = +0.0, stash rows untouched. */
+ssu_status ssu_tree_verify(const ssu_dims *dims, int32_t num_nodes, const void *x,
+                           const float *A, const void *B, const void *C, const float *dt,
+                           const float *dt_bias, const float *D, const void *z,
+                           const void *state, void *out, int32_t dt_softplus,
+                           const int32_t *state_indices, const int32_t *parent_ids,
+                           const int32_t *depths, float *replay_dA, float *replay_u,
+                           float *replay_B, float *replay_dt, hipStream_t stream);
 
 /* ------------------------------------------------------------------------
  * Recurrent-state pool [RSM]: one zeroed, contiguous slab per state spec,

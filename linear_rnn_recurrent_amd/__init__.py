@@ -1,11 +1,12 @@
-"""Selective state update (Mamba-style SSM decode, prefill and MTP replay) over a
-paged recurrent-state pool, as hand-written HIP kernels for AMD Instinct MI355X.
+"""Selective state update (Mamba-style SSM decode, prefill, MTP replay and tree
+verify) over a paged recurrent-state pool, as hand-written HIP kernels for AMD
+Instinct MI355X.
 
 The compute lives in libssu.so (C ABI declared in include/ssu.h); this package
 only marshals torch GPU tensors into those calls.
 """
 from .ssu import (SsuError, SsuPool, DeviceArray, load_library, ssu_decode, ssu_prefill,
-                  ssu_replay, LIB_PATH, EXPORTS)
+                  ssu_replay, ssu_tree_verify, LIB_PATH, EXPORTS)
 
 __all__ = ["SsuError", "SsuPool", "DeviceArray", "load_library", "ssu_decode", "ssu_prefill",
-           "ssu_replay", "LIB_PATH", "EXPORTS"]
+           "ssu_replay", "ssu_tree_verify", "LIB_PATH", "EXPORTS"]

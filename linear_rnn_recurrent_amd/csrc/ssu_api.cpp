@@ -151,7 +151,7 @@ extern "C" {
 
 const char *ssu_last_error(void) { return g_last_error.c_str(); }
 
-int32_t ssu_version(void) { return 10000; }
+int32_t ssu_version(void) { return 10100; }
 
 ssu_status ssu_decode(const ssu_dims *dims, const void *x, const float *A, const void *B,
                       const void *C, const float *dt, const float *dt_bias, const float *D,
@@ -256,7 +256,9 @@ ssu_status ssu_prefill(const ssu_dims *dims, int32_t seq_len, const void *x, con
 ssu_status ssu_replay(const ssu_dims *dims, int32_t seq_len, void *state,
                       const float *replay_dA, const float *replay_u, const float *replay_B,
                       const float *replay_dt, const int32_t *accepted_lengths,
-                      const int32_t *state_indices, int32_t active_batch, hipStream_t stream)
+                      const int32_t *state_indices, int32_t active_batch,
+                      const int32_t *accepted_node_ids, int32_t max_accept_len,
+                      hipStream_t stream)
 {
     const char *fn = "ssu_replay";
     ssu::DecodeParams d = {};
@@ -271,6 +273,9 @@ ssu_status ssu_replay(const ssu_dims *dims, int32_t seq_len, void *state,
     if (!state_indices && active_batch > dims->pool_rows)
         return fail(SSU_EINVAL, "%s: active_batch %d > pool_rows %d with no state_indices", fn,
                     active_batch, dims->pool_rows);
+    if (accepted_node_ids && max_accept_len < 1)
+        return fail(SSU_EINVAL, "%s: max_accept_len %d < 1 with accepted_node_ids", fn,
+                    max_accept_len);
     if (active_batch == 0 || seq_len == 0)
         return ok();
     SSU_REQUIRE_PTR(state, 16, fn);
@@ -280,6 +285,7 @@ ssu_status ssu_replay(const ssu_dims *dims, int32_t seq_len, void *state,
     SSU_REQUIRE_PTR(replay_dt, 4, fn);
     SSU_REQUIRE_PTR(accepted_lengths, 4, fn);
     SSU_OPTIONAL_PTR(state_indices, 4, fn);
+    SSU_OPTIONAL_PTR(accepted_node_ids, 4, fn);
     ssu::ReplayParams p = {};
     p.state = state;
     p.dA = replay_dA;
@@ -296,7 +302,73 @@ ssu_status ssu_replay(const ssu_dims *dims, int32_t seq_len, void *state,
     p.dstate = d.dstate;
     p.ngroups = d.ngroups;
     p.state_dtype = d.state_dtype;
+    p.node_ids = accepted_node_ids;
+    p.max_accept_len = accepted_node_ids ? max_accept_len : 0;
     return hip_status(ssu::launch_replay(p, stream), "ssu_replay launch");
+}
+
+ssu_status ssu_tree_verify(const ssu_dims *dims, int32_t num_nodes, const void *x,
+                           const float *A, const void *B, const void *C, const float *dt,
+                           const float *dt_bias, const float *D, const void *z,
+                           const void *state, void *out, int32_t dt_softplus,
+                           const int32_t *state_indices, const int32_t *parent_ids,
+                           const int32_t *depths, float *replay_dA, float *replay_u,
+                           float *replay_B, float *replay_dt, hipStream_t stream)
+{
+    const char *fn = "ssu_tree_verify";
+    ssu::TreeParams p = {};
+    const ssu_status st = check_dims(dims, fn, true, state_indices != nullptr, &p.d);
+    if (st != SSU_OK)
+        return st;
+    if (num_nodes < 0 || num_nodes > SSU_MAX_TREE_NODES)
+        return fail(SSU_EINVAL, "%s: num_nodes %d outside [0, %d]", fn, num_nodes,
+                    SSU_MAX_TREE_NODES);
+    const int nstash = (replay_dA != nullptr) + (replay_u != nullptr) + (replay_B != nullptr) +
+                       (replay_dt != nullptr);
+    if (nstash != 0 && nstash != 4)
+        return fail(SSU_EINVAL, "%s: replay stash must be all four buffers or none (%d given)",
+                    fn, nstash);
+    if (p.d.batch == 0 || num_nodes == 0)
+        return ok();
+    if ((int64_t)p.d.batch * num_nodes * p.d.nheads * p.d.dim > ((int64_t)1 << 40))
+        return fail(SSU_ENOTSUP, "%s: problem too large", fn);
+    SSU_REQUIRE_PTR(x, io_bytes(dims->io_dtype), fn);
+    SSU_REQUIRE_PTR(A, 4, fn);
+    SSU_REQUIRE_PTR(B, 16, fn);
+    SSU_REQUIRE_PTR(C, 16, fn);
+    SSU_REQUIRE_PTR(dt, 4, fn);
+    SSU_REQUIRE_PTR(state, 16, fn);
+    SSU_REQUIRE_PTR(out, io_bytes(dims->io_dtype), fn);
+    SSU_REQUIRE_PTR(parent_ids, 4, fn);
+    SSU_OPTIONAL_PTR(dt_bias, 4, fn);
+    SSU_OPTIONAL_PTR(D, 4, fn);
+    SSU_OPTIONAL_PTR(z, io_bytes(dims->io_dtype), fn);
+    SSU_OPTIONAL_PTR(state_indices, 4, fn);
+    SSU_OPTIONAL_PTR(depths, 4, fn);
+    SSU_OPTIONAL_PTR(replay_dA, 4, fn);
+    SSU_OPTIONAL_PTR(replay_u, 4, fn);
+    SSU_OPTIONAL_PTR(replay_B, 16, fn);
+    SSU_OPTIONAL_PTR(replay_dt, 4, fn);
+    p.d.x = x;
+    p.d.A = A;
+    p.d.B = B;
+    p.d.C = C;
+    p.d.dt = dt;
+    p.d.dt_bias = dt_bias;
+    p.d.D = D;
+    p.d.z = z;
+    p.d.state = const_cast<void *>(state);  // read only
+    p.d.out = out;
+    p.d.idx = state_indices;
+    p.d.dt_softplus = dt_softplus ? 1 : 0;
+    p.num_nodes = num_nodes;
+    p.parents = parent_ids;
+    p.depths = depths;
+    p.st_dA = replay_dA;
+    p.st_u = replay_u;
+    p.st_B = replay_B;
+    p.st_dt = replay_dt;
+    return hip_status(ssu::launch_tree(p, stream), "ssu_tree_verify launch");
 }
 
 }  // extern "C"

@@ -42,9 +42,18 @@ struct ReplayParams {
     const float *dA, *u, *B, *dt;
     const int32_t *accepted;
     const int32_t *idx;
+    const int32_t *node_ids;  // null: token t is stash position t
     int64_t row_stride;
     int32_t active_batch, seq_len, nheads, dim, dstate, ngroups;
     int32_t state_dtype;
+    int32_t max_accept_len;   // row length of node_ids
+};
+
+struct TreeParams {
+    DecodeParams d;  // x/z/out/dt/B/C carry the node axis; the state is only read
+    int32_t num_nodes;
+    const int32_t *parents, *depths;
+    float *st_dA, *st_u, *st_B, *st_dt;  // all set or all null
 };
 
 // One byte range to copy (src != null) or zero (src == null).
@@ -63,6 +72,10 @@ hipError_t launch_prefill_f32(const PrefillParams &p, hipStream_t stream);
 hipError_t launch_prefill_f16(const PrefillParams &p, hipStream_t stream);
 hipError_t launch_prefill_bf16(const PrefillParams &p, hipStream_t stream);
 hipError_t launch_replay(const ReplayParams &p, hipStream_t stream);
+hipError_t launch_tree(const TreeParams &p, hipStream_t stream);
+hipError_t launch_tree_f32(const TreeParams &p, hipStream_t stream);
+hipError_t launch_tree_f16(const TreeParams &p, hipStream_t stream);
+hipError_t launch_tree_bf16(const TreeParams &p, hipStream_t stream);
 // Copies/zeroes up to any number of segments; one launch per 32 segments.
 hipError_t launch_segments(const Segment *segs, int n, hipStream_t stream);
 

@@ -41,6 +41,7 @@
 
 #include "ssu_device.h"
 #include "ssu_internal.h"
+#include "ssu_rowblock.h"
 
 namespace ssu {
 namespace {
@@ -52,10 +53,6 @@ struct PrefillShape {
 };
 
 constexpr int kPrefillTC = 8;  // tokens per staged chunk
-
-// Position of row r (0..63) of a row block in the LDS x / partial-sum arrays:
-// lane rr of a quarter reads its rows rr, rr+16, rr+32, rr+48 as one float4.
-__device__ __forceinline__ int xpos(int r) { return (r & 15) * 4 + (r >> 4); }
 
 // Per-token operands of one lane: (dt', decay), its four x values and its
 // slice of B and C, all read from LDS (16-byte broadcast reads).
@@ -105,10 +102,8 @@ __device__ __forceinline__ void apply_renorm(float (&S)[4][NSL], const float2 f)
 // renormalisation) and o.va = (dt'/P_t, P_t). The update is one FMA per
 // element, S~ += (dt'/P_t) x B, and so is the partial output sum of S~ C (the
 // factor P_t is applied once per output in the epilogue). token_fma returns
-// the lane's partials of its rows rr + 16 i; quarter_reduce then sums them over
-// the four quarters of the wave with two swap-and-add steps (32-lane halves,
-// then 16-lane rows), leaving in lane rr + 16 q the wave's partial of row
-// rr + 16 q.
+// the lane's partials of its rows rr + 16 i, which quarter_reduce sums over the
+// four quarters of the wave.
 template <int NSL>
 __device__ __forceinline__ float4 token_fma(float (&S)[4][NSL], const Operands<NSL> &o)
 {
@@ -123,19 +118,6 @@ __device__ __forceinline__ float4 token_fma(float (&S)[4][NSL], const Operands<N
         }
     }
     return make_float4(p[0], p[1], p[2], p[3]);
-}
-
-__device__ __forceinline__ float quarter_reduce(const float4 p)
-{
-    const auto s02 = __builtin_amdgcn_permlane32_swap(__float_as_uint(p.x), __float_as_uint(p.z),
-                                                      false, false);
-    const auto s13 = __builtin_amdgcn_permlane32_swap(__float_as_uint(p.y), __float_as_uint(p.w),
-                                                      false, false);
-    const float u0 = __uint_as_float(s02[0]) + __uint_as_float(s02[1]);
-    const float u1 = __uint_as_float(s13[0]) + __uint_as_float(s13[1]);
-    const auto w = __builtin_amdgcn_permlane16_swap(__float_as_uint(u0), __float_as_uint(u1),
-                                                    false, false);
-    return __uint_as_float(w[0]) + __uint_as_float(w[1]);
 }
 
 template <typename ST, typename IOT, typename BCT, int NS, int NW>

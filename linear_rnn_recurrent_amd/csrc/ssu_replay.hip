@@ -5,7 +5,10 @@
 // acceptedLengths[b] stashed tokens, in place, for b < activeBatchSize:
 //   state <- state * exp(dA_t) + B_t * dt_t * u_t
 // A row whose accepted count is 0, or whose state index is negative, is left
-// untouched; entries at b >= activeBatchSize are never read.
+// untouched; entries at b >= activeBatchSize are never read. With
+// acceptedNodeIds (invokeMambaReplayReconstructBatched) token t of row b is the
+// stash entry of node acceptedNodeIds[b, t]; the count is capped at
+// maxAcceptLen and the row ends before the first id outside the stash.
 //
 // Mapping on gfx950: the decode mapping (the (batch row, head) tile split over
 // workgroups of about 8 KiB of state; lanes along dstate with 16-byte vectors;
@@ -23,14 +26,17 @@ namespace {
 struct ReplayShape {
     int64_t row_stride;
     int32_t seq_len, nheads, dim, ngroups, heads_per_group, parts;
+    int32_t max_accept;  // row length of the node-id array (IDS only)
 };
 
-// MAXT > 0: seq_len <= MAXT, all stash loads hoisted; MAXT == 0: any seq_len.
-template <typename ST, int NS, int PASSES, int MAXT>
+// MAXT > 0: at most MAXT tokens per row, all stash loads hoisted; MAXT == 0:
+// any count. IDS: stash positions come from the node-id array.
+template <typename ST, int NS, int PASSES, int MAXT, bool IDS>
 __global__ __launch_bounds__(256) void ssu_replay_kernel(
     ST *__restrict__ state, const float *__restrict__ sdA, const float *__restrict__ su,
     const float *__restrict__ sB, const float *__restrict__ sdt,
-    const int32_t *__restrict__ accepted, const int32_t *__restrict__ idx, const ReplayShape sh)
+    const int32_t *__restrict__ accepted, const int32_t *__restrict__ idx,
+    const int32_t *__restrict__ node_ids, const ReplayShape sh)
 {
     constexpr int VEC = SV<ST>::VEC;
     constexpr int LPR = NS / VEC;
@@ -48,7 +54,7 @@ __global__ __launch_bounds__(256) void ssu_replay_kernel(
     const int r0 = part * ROWS;
 
     const int row = idx ? idx[b] : b;
-    const int k = min(accepted[b], sh.seq_len);
+    const int k = min(accepted[b], IDS ? sh.max_accept : sh.seq_len);
     if (row < 0 || k <= 0)
         return;
     const int g = h / sh.heads_per_group;
@@ -64,24 +70,41 @@ __global__ __launch_bounds__(256) void ssu_replay_kernel(
     }
     float s[PASSES][VEC];
     if constexpr (MAXT > 0) {
+        // stash position of every token slot (slots past k repeat token k-1);
+        // kk = the tokens actually applied
+        int pos[MAXT];
+        int kk = k;
+#pragma unroll
+        for (int t = 0; t < MAXT; ++t) {
+            const int tc = min(t, k - 1);
+            int p = tc;
+            if constexpr (IDS) {
+                p = node_ids[(int64_t)b * sh.max_accept + tc];
+                const bool inside = p >= 0 && p < sh.seq_len;
+                kk = inside ? kk : min(kk, tc);
+                p = inside ? p : 0;
+            }
+            pos[t] = p;
+        }
         float ut[MAXT][PASSES], bt[MAXT][VEC], at[MAXT], dtt[MAXT];
 #pragma unroll
         for (int t = 0; t < MAXT; ++t) {
-            const int64_t bth = (bT + min(t, k - 1)) * H + h;
+            const int64_t bth = (bT + pos[t]) * H + h;
 #pragma unroll
             for (int p = 0; p < PASSES; ++p)
                 ut[t][p] = su[bth * Dm + min(r0 + p * RPP + rsub, Dm - 1)];
-            ld_typed<float, VEC>(sB, ((bT + min(t, k - 1)) * sh.ngroups + g) * NS + sub * VEC,
-                                 bt[t]);
+            ld_typed<float, VEC>(sB, ((bT + pos[t]) * sh.ngroups + g) * NS + sub * VEC, bt[t]);
             at[t] = sdA[bth];
             dtt[t] = sdt[bth];
         }
 #pragma unroll
         for (int p = 0; p < PASSES; ++p)
             SV<ST>::unpack(raw[p], s[p]);
+        if (kk <= 0)
+            return;  // the first node id is outside the stash: nothing to commit
 #pragma unroll
         for (int t = 0; t < MAXT; ++t) {
-            if (t < k) {
+            if (t < kk) {
                 const float a = expf(at[t]);
 #pragma unroll
                 for (int p = 0; p < PASSES; ++p) {
@@ -96,12 +119,19 @@ __global__ __launch_bounds__(256) void ssu_replay_kernel(
 #pragma unroll
         for (int p = 0; p < PASSES; ++p)
             SV<ST>::unpack(raw[p], s[p]);
-        for (int t = 0; t < k; ++t) {
-            const int64_t bth = (bT + t) * H + h;
+        int t = 0;
+        for (; t < k; ++t) {
+            int ps = t;
+            if constexpr (IDS) {
+                ps = node_ids[(int64_t)b * sh.max_accept + t];
+                if (ps < 0 || ps >= sh.seq_len)
+                    break;
+            }
+            const int64_t bth = (bT + ps) * H + h;
             const float a = expf(sdA[bth]);
             const float dtv = sdt[bth];
             float bv[VEC];
-            ld_typed<float, VEC>(sB, ((bT + t) * sh.ngroups + g) * NS + sub * VEC, bv);
+            ld_typed<float, VEC>(sB, ((bT + ps) * sh.ngroups + g) * NS + sub * VEC, bv);
 #pragma unroll
             for (int p = 0; p < PASSES; ++p) {
                 const float dtx = dtv * su[bth * Dm + min(r0 + p * RPP + rsub, Dm - 1)];
@@ -110,6 +140,8 @@ __global__ __launch_bounds__(256) void ssu_replay_kernel(
                     s[p][e] = fmaf(dtx, bv[e], s[p][e] * a);
             }
         }
+        if (t == 0)
+            return;  // nothing committed
     }
 #pragma unroll
     for (int p = 0; p < PASSES; ++p) {
@@ -134,26 +166,34 @@ hipError_t launch_ns(const ReplayParams &p, hipStream_t stream)
     sh.ngroups = p.ngroups;
     sh.heads_per_group = p.nheads / p.ngroups;
     sh.parts = (p.dim + passes * RPP - 1) / (passes * RPP);
+    sh.max_accept = p.max_accept_len;
     const int64_t blocks = (int64_t)p.active_batch * p.nheads * sh.parts;
     if (blocks > 0x7fffffff)
         return hipErrorInvalidConfiguration;
     const dim3 grid((unsigned)blocks);
     ST *st = static_cast<ST *>(p.state);
     (void)hipGetLastError();
-#define SSU_LAUNCH_REPLAY(PS, MT)                                                                \
-    hipLaunchKernelGGL((ssu_replay_kernel<ST, NS, PS, MT>), grid, dim3(256), 0, stream, st, p.dA, \
-                       p.u, p.B, p.dt, p.accepted, p.idx, sh)
+#define SSU_LAUNCH_REPLAY(PS, MT, ID)                                                         \
+    hipLaunchKernelGGL((ssu_replay_kernel<ST, NS, PS, MT, ID>), grid, dim3(256), 0, stream, st, \
+                       p.dA, p.u, p.B, p.dt, p.accepted, p.idx, p.node_ids, sh)
 #define SSU_LAUNCH_REPLAY_T(PS)           \
-    if (p.seq_len <= 1)                   \
-        SSU_LAUNCH_REPLAY(PS, 1);         \
+    if (p.node_ids) {                     \
+        if (p.max_accept_len <= 4)        \
+            SSU_LAUNCH_REPLAY(PS, 4, true);  \
+        else if (p.max_accept_len <= 8)   \
+            SSU_LAUNCH_REPLAY(PS, 8, true);  \
+        else                              \
+            SSU_LAUNCH_REPLAY(PS, 0, true);  \
+    } else if (p.seq_len <= 1)            \
+        SSU_LAUNCH_REPLAY(PS, 1, false);  \
     else if (p.seq_len <= 2)              \
-        SSU_LAUNCH_REPLAY(PS, 2);         \
+        SSU_LAUNCH_REPLAY(PS, 2, false);  \
     else if (p.seq_len <= 4)              \
-        SSU_LAUNCH_REPLAY(PS, 4);         \
+        SSU_LAUNCH_REPLAY(PS, 4, false);  \
     else if (p.seq_len <= 8)              \
-        SSU_LAUNCH_REPLAY(PS, 8);         \
+        SSU_LAUNCH_REPLAY(PS, 8, false);  \
     else                                  \
-        SSU_LAUNCH_REPLAY(PS, 0);
+        SSU_LAUNCH_REPLAY(PS, 0, false);
     if (passes == 2) {
         SSU_LAUNCH_REPLAY_T(2)
     } else {

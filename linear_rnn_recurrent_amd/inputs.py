@@ -300,6 +300,19 @@ def config(i: int, seed: Optional[int] = None) -> Workload:
     raise ValueError(f"no configuration {i}")
 
 
+TREE_NAME = ("tree verify B16 M128 (random draft tree, depth < 16) H80 Dm64 N128 G1, "
+             "fp32 pool P64")
+
+
+def tree_config(seed: int = 5, num_nodes: int = 128) -> Workload:
+    """Tree-verify workload: 16 requests, each with a random draft tree of the
+    full 128-node verify budget, on the decode model shape (H80 Dm64 N128 G1)."""
+    return tree_workload(batch=16, num_nodes=num_nodes, nheads=80, dim=64, dstate=128,
+                         ngroups=1, pool_rows=64, seed=seed, state_dtype="f32",
+                         io_dtype="bf16", bc_dtype="bf16", bc_std=1.0 / np.sqrt(128),
+                         shape="random", max_depth=16, with_z=False, name=TREE_NAME)
+
+
 def rotation_index_sets(pool_rows: int, batch: int, seed: int):
     """Disjoint index sets that together cover the whole pool (one per step)."""
     rng = np.random.default_rng(seed)

@@ -20,7 +20,7 @@ SSU_F32, SSU_F16, SSU_BF16, SSU_U8 = 0, 1, 2, 3
 _DT = {torch.float32: SSU_F32, torch.float16: SSU_F16, torch.bfloat16: SSU_BF16,
        torch.uint8: SSU_U8}
 
-EXPORTS = ("ssu_decode", "ssu_prefill", "ssu_replay", "ssu_pool_bytes_per_slot",
+EXPORTS = ("ssu_decode", "ssu_prefill", "ssu_replay", "ssu_tree_verify", "ssu_pool_bytes_per_slot",
            "ssu_pool_alloc", "ssu_pool_free", "ssu_pool_info", "ssu_pool_state_ptr",
            "ssu_pool_state_bytes_per_slot", "ssu_pool_find_state", "ssu_pool_clear",
            "ssu_pool_clear_slot", "ssu_pool_capture", "ssu_pool_restore",
@@ -67,7 +67,9 @@ def load_library(path: Optional[str] = None):
         "ssu_decode": [D, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _I32, _P, _P],
         "ssu_prefill": [D, _I32, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _I32, _P, _P,
                         _P, _P, _P, _P, _P],
-        "ssu_replay": [D, _I32, _P, _P, _P, _P, _P, _P, _P, _I32, _P],
+        "ssu_replay": [D, _I32, _P, _P, _P, _P, _P, _P, _P, _I32, _P, _I32, _P],
+        "ssu_tree_verify": [D, _I32, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _I32, _P, _P, _P,
+                            _P, _P, _P, _P, _P],
         "ssu_pool_bytes_per_slot": [S, _I32, ctypes.POINTER(ctypes.c_size_t)],
         "ssu_pool_alloc": [S, _I32, _I32, _P, ctypes.POINTER(_P)],
         "ssu_pool_free": [_P],
@@ -243,12 +245,14 @@ def ssu_prefill(x, A, B, C, dt, state, out, *, dt_bias=None, D=None, z=None,
 
 
 def ssu_replay(state, replay_dA, replay_u, replay_B, replay_dt, accepted_lengths, *,
-               state_indices=None, active_batch=None, stream=None):
-    """Apply the first accepted_lengths[b] stashed tokens to the state, in place.
+               state_indices=None, active_batch=None, accepted_node_ids=None, stream=None):
+    """Apply accepted stashed tokens to the state, in place.
 
     replay_dA, replay_dt [batch, seq_len, nheads]; replay_u [batch, seq_len, nheads, dim];
     replay_B [batch, seq_len, ngroups, dstate]; accepted_lengths, state_indices [batch] int32.
-    Rows b >= active_batch (default batch) are never read.
+    accepted_node_ids [batch, max_accept_len] int32: token t of row b is stash entry
+    accepted_node_ids[b, t] (default: entry t). Rows b >= active_batch (default batch)
+    are never read.
     """
     lib = load_library()
     _dense(replay_dA, "replay_dA", (torch.float32,))
@@ -265,6 +269,12 @@ def ssu_replay(state, replay_dA, replay_u, replay_B, replay_dt, accepted_lengths
     _dense(replay_dt, "replay_dt", (torch.float32,), (batch, seq_len, nheads))
     _dense(accepted_lengths, "accepted_lengths", (torch.int32,), (batch,))
     _opt_idx(state_indices, "state_indices", batch)
+    max_accept = 0
+    if accepted_node_ids is not None:
+        _dense(accepted_node_ids, "accepted_node_ids", (torch.int32,))
+        _need(accepted_node_ids.dim() == 2 and accepted_node_ids.shape[0] == batch,
+              "accepted_node_ids must be [batch, max_accept_len]")
+        max_accept = accepted_node_ids.shape[1]
     rows, stride = _state_geometry(state, nheads, dim, dstate)
     if active_batch is None:
         active_batch = batch
@@ -274,7 +284,56 @@ def ssu_replay(state, replay_dA, replay_u, replay_B, replay_dt, accepted_lengths
         _check(lib.ssu_replay(ctypes.byref(d), seq_len, _ptr(state), _ptr(replay_dA),
                               _ptr(replay_u), _ptr(replay_B), _ptr(replay_dt),
                               _ptr(accepted_lengths), _ptr(state_indices), int(active_batch),
+                              _ptr(accepted_node_ids), int(max_accept),
                               _stream(state.device, stream)))
+
+
+def ssu_tree_verify(x, A, B, C, dt, state, out, parent_ids, *, depths=None, dt_bias=None,
+                    D=None, z=None, dt_softplus=True, state_indices=None, replay_dA=None,
+                    replay_u=None, replay_B=None, replay_dt=None, stream=None):
+    """Every node of a draft tree per batch row, from the read-only committed state.
+
+    x, z, out [batch, num_nodes, nheads, dim]; dt [batch, num_nodes, nheads];
+    B, C [batch, num_nodes, ngroups, dstate]; parent_ids, depths [batch, num_nodes] int32.
+    Replay stash (fp32, all four or none) in the ssu_prefill layouts with the node axis.
+    """
+    lib = load_library()
+    _dense(x, "x", _FLOAT)
+    _need(x.dim() == 4, "x must be [batch, num_nodes, nheads, dim]")
+    batch, num_nodes, nheads, dim = x.shape
+    _dense(B, "B", _FLOAT)
+    _need(B.dim() == 4 and tuple(B.shape[:2]) == (batch, num_nodes),
+          "B must be [batch, num_nodes, ngroups, dstate]")
+    ngroups, dstate = B.shape[2], B.shape[3]
+    _dense(C, "C", (B.dtype,), B.shape)
+    _dense(A, "A", (torch.float32,), (nheads,))
+    _dense(dt, "dt", (torch.float32,), (batch, num_nodes, nheads))
+    _dense(parent_ids, "parent_ids", (torch.int32,), (batch, num_nodes))
+    if depths is not None:
+        _dense(depths, "depths", (torch.int32,), (batch, num_nodes))
+    if dt_bias is not None:
+        _dense(dt_bias, "dt_bias", (torch.float32,), (nheads,))
+    if D is not None:
+        _dense(D, "D", (torch.float32,), (nheads,))
+    if z is not None:
+        _dense(z, "z", (x.dtype,), x.shape)
+    _dense(out, "out", (x.dtype,), x.shape)
+    rows, stride = _state_geometry(state, nheads, dim, dstate)
+    _opt_idx(state_indices, "state_indices", batch)
+    stash = (replay_dA, replay_u, replay_B, replay_dt)
+    if any(s is not None for s in stash):
+        _dense(replay_dA, "replay_dA", (torch.float32,), (batch, num_nodes, nheads))
+        _dense(replay_dt, "replay_dt", (torch.float32,), (batch, num_nodes, nheads))
+        _dense(replay_u, "replay_u", (torch.float32,), x.shape)
+        _dense(replay_B, "replay_B", (torch.float32,), B.shape)
+    d = _dims(batch, nheads, dim, dstate, ngroups, rows, stride, state.dtype, x.dtype, B.dtype)
+    with torch.cuda.device(x.device):
+        _check(lib.ssu_tree_verify(ctypes.byref(d), num_nodes, _ptr(x), _ptr(A), _ptr(B),
+                                   _ptr(C), _ptr(dt), _ptr(dt_bias), _ptr(D), _ptr(z),
+                                   _ptr(state), _ptr(out), 1 if dt_softplus else 0,
+                                   _ptr(state_indices), _ptr(parent_ids), _ptr(depths),
+                                   *[_ptr(s) for s in stash], _stream(x.device, stream)))
+    return out
 
 
 # ---------------------------------------------------------------------------

@@ -3,7 +3,7 @@ import numpy as np
 import torch
 
 import oracle
-from linear_rnn_recurrent_amd import ssu_decode, ssu_prefill, ssu_replay
+from linear_rnn_recurrent_amd import ssu_decode, ssu_prefill, ssu_replay, ssu_tree_verify
 
 # Tolerances: max|got - ref| <= tol * (1 + |ref|), elementwise.
 TOL_F32 = 2e-5      # fp32 state and fp32 outputs
@@ -109,7 +109,7 @@ def run_replay(w, **over):
     T.update(over)
     ssu_replay(T["state"], T["replay_dA"], T["replay_u"], T["replay_B"], T["replay_dt"],
                T["accepted_lengths"], state_indices=T["state_indices"],
-               active_batch=w.active_batch)
+               active_batch=w.active_batch, accepted_node_ids=T.get("node_ids"))
     return T["state"]
 
 
@@ -119,8 +119,42 @@ def oracle_replay(w, **over):
     st = a["state"].copy()
     oracle.replay(st, a["replay_dA"], a["replay_u"], a["replay_B"], a["replay_dt"],
                   a["accepted_lengths"], state_indices=a["state_indices"],
-                  active_batch=w.active_batch)
+                  active_batch=w.active_batch, node_ids=a.get("node_ids"))
     return st
+
+
+def _nan_stash(b, m, h, d, bshape, device):
+    return {"replay_dA": torch.full((b, m, h), float("nan"), device=device),
+            "replay_dt": torch.full((b, m, h), float("nan"), device=device),
+            "replay_u": torch.full((b, m, h, d), float("nan"), device=device),
+            "replay_B": torch.full(tuple(bshape), float("nan"), device=device)}
+
+
+def run_tree(w, stash=False, **over):
+    T = {k: gpu(v) for k, v in w.tensors.items()}
+    T.update(over)
+    out = torch.full_like(T["x"], float("nan"))
+    b, m, h, d = T["x"].shape
+    S = _nan_stash(b, m, h, d, T["B"].shape, "cuda") if stash else {}
+    ssu_tree_verify(T["x"], T["A"], T["B"], T["C"], T["dt"], T["state"], out, T["parent_ids"],
+                    depths=T["depths"], dt_bias=T["dt_bias"], D=T["D"], z=T["z"],
+                    dt_softplus=w.dt_softplus, state_indices=T["state_indices"], **S)
+    return T["state"], out, S
+
+
+def oracle_tree(w, stash=False, **over):
+    a = {k: f64(v) for k, v in w.tensors.items()}
+    a.update(over)
+    out = np.zeros(a["x"].shape)
+    S = None
+    if stash:
+        b, m, h, d = a["x"].shape
+        S = {"dA": np.full((b, m, h), np.nan), "dt": np.full((b, m, h), np.nan),
+             "u": np.full((b, m, h, d), np.nan), "B": np.full(a["B"].shape, np.nan)}
+    oracle.tree(a["x"], a["A"], a["B"], a["C"], a["dt"], a["state"], out, a["parent_ids"],
+                depths=a["depths"], dt_bias=a["dt_bias"], D=a["D"], z=a["z"],
+                dt_softplus=w.dt_softplus, state_indices=a["state_indices"], stash=S)
+    return out, S
 
 
 def touched_rows(idx, n_rows):

@@ -63,7 +63,7 @@ def test_struct_layout_matches_header(tmp_path):
 
 
 def test_version(lib):
-    assert lib.ssu_version() == 10000
+    assert lib.ssu_version() == 10100
 
 
 # ---------------------------------------------------------------------------
@@ -153,11 +153,11 @@ def test_prefill_validation(lib):
     assert prefill(lib, dims(dstate=48)) == 2
 
 
-def replay(lib, d, seq_len=4, active=2, **ptrs):
+def replay(lib, d, seq_len=4, active=2, ids=None, max_accept=0, **ptrs):
     p = dict(state=FAKE, dA=FAKE, u=FAKE, B=FAKE, dt=FAKE, acc=FAKE, idx=None)
     p.update(ptrs)
     return lib.ssu_replay(ctypes.byref(d), seq_len, p["state"], p["dA"], p["u"], p["B"],
-                          p["dt"], p["acc"], p["idx"], active, None)
+                          p["dt"], p["acc"], p["idx"], active, ids, max_accept, None)
 
 
 def test_replay_validation(lib):
@@ -168,6 +168,40 @@ def test_replay_validation(lib):
     assert replay(lib, dims(), active=0, state=None) == 0
     for name in ("state", "dA", "u", "B", "dt", "acc"):
         assert replay(lib, dims(), **{name: None}) == 1, name
+
+
+def test_replay_node_id_validation(lib):
+    assert replay(lib, dims(), ids=FAKE, max_accept=0) == 1 and "max_accept_len" in err(lib)
+    assert replay(lib, dims(), ids=FAKE, max_accept=-3) == 1 and "max_accept_len" in err(lib)
+    # ignored without ids: fails later on the null state, not on max_accept_len
+    assert replay(lib, dims(), max_accept=-3, state=None) == 1 and "'state'" in err(lib)
+    assert replay(lib, dims(), ids=FAKE + 2, max_accept=4) == 1
+    assert "'accepted_node_ids'" in err(lib) and "4-byte aligned" in err(lib)
+
+
+def tree(lib, d, num_nodes=8, stash=(None, None, None, None), **ptrs):
+    p = dict(x=FAKE, A=FAKE, B=FAKE, C=FAKE, dt=FAKE, state=FAKE, out=FAKE, par=FAKE,
+             dep=None, idx=None)
+    p.update(ptrs)
+    return lib.ssu_tree_verify(ctypes.byref(d), num_nodes, p["x"], p["A"], p["B"], p["C"],
+                               p["dt"], None, None, None, p["state"], p["out"], 1, p["idx"],
+                               p["par"], p["dep"], *stash, None)
+
+
+def test_tree_verify_validation(lib):
+    assert tree(lib, dims(), num_nodes=-1) == 1 and "num_nodes" in err(lib)
+    assert tree(lib, dims(), num_nodes=129) == 1 and "num_nodes" in err(lib)
+    assert tree(lib, dims(), stash=(FAKE, FAKE, None, FAKE)) == 1 and "all four" in err(lib)
+    assert tree(lib, dims(), num_nodes=0, x=None) == 0 and err(lib) == ""
+    assert tree(lib, dims(batch=0), x=None) == 0
+    for name in ("x", "A", "B", "C", "dt", "state", "out", "par"):
+        assert tree(lib, dims(), **{name: None}) == 1, name
+    assert tree(lib, dims(), par=None) == 1 and "'parent_ids'" in err(lib)
+    assert tree(lib, dims(), dep=FAKE + 1) == 1 and "'depths'" in err(lib)
+    assert tree(lib, dims(), C=FAKE + 8) == 1 and "16-byte aligned" in err(lib)
+    assert tree(lib, dims(), stash=(FAKE, FAKE, FAKE + 4, FAKE)) == 1 and "'replay_B'" in err(lib)
+    assert tree(lib, dims(batch=5)) == 1 and "pool_rows" in err(lib)
+    assert tree(lib, dims(dstate=48)) == 2
 
 
 def spec_array(specs):

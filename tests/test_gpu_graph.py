@@ -6,7 +6,8 @@ calls run eagerly."""
 import pytest
 import torch
 
-from linear_rnn_recurrent_amd import SsuPool, inputs, ssu_decode, ssu_prefill, ssu_replay
+from linear_rnn_recurrent_amd import (SsuPool, inputs, ssu_decode, ssu_prefill, ssu_replay,
+                                      ssu_tree_verify)
 from gpu_helpers import assert_bitwise, gpu
 
 pytestmark = pytest.mark.gpu
@@ -90,5 +91,48 @@ def test_prefill_replay_and_pool_ops_in_graph_match_eager():
         run(st_e, out_e, S_e)
         torch.cuda.synchronize()
         want = [st_e, out_e] + S_e + [saved[0]]
+        for i, (a, e) in enumerate(zip(got, want)):
+            assert_bitwise(a, e, f"tensor {i} after replay {rep}")
+
+
+def test_tree_verify_and_path_commit_in_graph_match_eager():
+    # 128-node trees need more than 64 KiB of LDS: the first (eager) call enables it
+    w = inputs.tree_workload(batch=3, num_nodes=128, nheads=4, dim=64, dstate=128, ngroups=1,
+                             pool_rows=4, seed=103, indices=[2, -1, 0], bc_std=128 ** -0.5)
+    T = {k: gpu(v) for k, v in w.tensors.items()}
+    b, m, h, d = T["x"].shape
+    acc = torch.tensor([3, 2, 4], dtype=torch.int32, device="cuda")
+    ids = torch.tensor([[0, 1, 5, 9], [0, 2, 0, 0], [0, 3, 7, 200]], dtype=torch.int32,
+                       device="cuda")
+
+    def run(st, out, S):
+        ssu_tree_verify(T["x"], T["A"], T["B"], T["C"], T["dt"], st, out, T["parent_ids"],
+                        depths=T["depths"], dt_bias=T["dt_bias"], D=T["D"],
+                        state_indices=T["state_indices"], replay_dA=S[0], replay_u=S[1],
+                        replay_B=S[2], replay_dt=S[3])
+        ssu_replay(st, S[0], S[1], S[2], S[3], acc, state_indices=T["state_indices"],
+                   accepted_node_ids=ids)
+
+    def bufs():
+        return [torch.zeros((b, m, h), device="cuda"), torch.zeros((b, m, h, d), device="cuda"),
+                torch.zeros(tuple(T["B"].shape), device="cuda"), torch.zeros((b, m, h), device="cuda")]
+
+    st_g, out_g, S_g = T["state"].clone(), torch.zeros_like(T["x"]), bufs()
+    run(st_g, out_g, S_g)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        run(st_g, out_g, S_g)
+    torch.cuda.synchronize()
+    for rep in range(3):
+        st_g.copy_(T["state"])
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        got = [st_g.clone(), out_g.clone()] + [s.clone() for s in S_g]
+        st_e, out_e, S_e = T["state"].clone(), torch.zeros_like(T["x"]), bufs()
+        run(st_e, out_e, S_e)
+        torch.cuda.synchronize()
+        want = [st_e, out_e] + S_e
         for i, (a, e) in enumerate(zip(got, want)):
             assert_bitwise(a, e, f"tensor {i} after replay {rep}")
