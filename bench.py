@@ -8,9 +8,10 @@ four disjoint 64-row index sets that together cover the pool, so every step
 streams state rows the previous three steps did not touch and the 256 MB
 last-level cache cannot serve them.
 
-    python bench.py [--steps K] [--warmup W] [--config {1,2,3,4}]
+    python bench.py [--steps K] [--warmup W] [--config {1,2,3,4,5}]
 
---config 2/3/4 time prefill / padded decode / MTP replay instead. Their pools
+--config 2/3/4/5 time prefill / padded decode / MTP replay / tree verify
+(16 requests with 128-node draft trees, replay stash on) instead. Their pools
 are smaller than the last-level cache, so the steps rotate over replicas of
 the pool (and, for prefill, of every input) that together exceed it; every
 configuration is timed as back-to-back launches on one stream.
@@ -81,6 +82,43 @@ def replay_bytes(T, k_rows):
     return total + 8 * len(k_rows)
 
 
+def tree_bytes(T, stash=True):
+    """Algorithmic bytes of one tree-verify launch: committed state of every live
+    row, every node's x, B, C, dt, parent id, depth and output, and the stash."""
+    b, m, h, d = T["x"].shape
+    g, n = T["B"].shape[2], T["B"].shape[3]
+    live = int((T["state_indices"] >= 0).sum().item()) if T["state_indices"] is not None else b
+    s_x = esize(T["x"])
+    per_node = h * d * 2 * s_x + (h * d * s_x if T["z"] is not None else 0) \
+        + 2 * g * n * esize(T["B"]) + 4 * h + 8
+    st = 4 * h * d + 4 * g * n + 8 * h if stash else 0
+    return live * h * d * n * esize(T["state"]) + b * m * per_node + live * m * st + 12 * h
+
+
+def tree_lane_ops(T):
+    """FMAs of the closed form the tree kernel evaluates: S0 . C per (node, row)
+    plus, per path entry, one dstate-long B . C dot and one x term per row."""
+    import numpy as np
+    b, m, h, d = T["x"].shape
+    n = T["B"].shape[3]
+    par = T["parent_ids"].cpu().numpy()
+    dep = T["depths"].cpu().numpy() if T["depths"] is not None else None
+    idx = T["state_indices"].cpu().numpy() if T["state_indices"] is not None else np.arange(b)
+    ops = 0
+    for r in range(b):
+        if idx[r] < 0:
+            continue
+        entries = 0
+        for node in range(m):
+            cap = node if dep is None else int(dep[r, node])
+            j, hops = node, 0
+            while hops < cap and 0 <= par[r, j] < j:
+                j, hops = int(par[r, j]), hops + 1
+            entries += hops + 1
+        ops += h * (m * d * n + entries * (n + d))
+    return ops
+
+
 def source_hash(*names):
     hsh = hashlib.sha256()
     for n in names:
@@ -131,6 +169,17 @@ def cpu_baseline(kind, w, seconds, bytes_per_call, units_per_call):
                            D=a["D"], z=a["z"], dt_softplus=w.dt_softplus,
                            context_lengths=a["context_lengths"], state_indices=a["state_indices"])
         sample = "the full prefill batch of this workload"
+    elif kind == "tree":
+        out = np.zeros(a["x"].shape)
+        b, m, h, d = a["x"].shape
+        S = {"dA": np.zeros((b, m, h)), "dt": np.zeros((b, m, h)), "u": np.zeros((b, m, h, d)),
+             "B": np.zeros(a["B"].shape)}
+
+        def call():
+            oracle.tree(a["x"], a["A"], a["B"], a["C"], a["dt"], a["state"], out, a["parent_ids"],
+                        depths=a["depths"], dt_bias=a["dt_bias"], D=a["D"], z=a["z"],
+                        dt_softplus=w.dt_softplus, state_indices=a["state_indices"], stash=S)
+        sample = "the full tree batch of this workload"
     else:
         st = a["state"].copy()
 
@@ -157,7 +206,7 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=1000)
     ap.add_argument("--warmup", type=int, default=100)
-    ap.add_argument("--config", type=int, default=1, choices=[1, 2, 3, 4])
+    ap.add_argument("--config", type=int, default=1, choices=[1, 2, 3, 4, 5])
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--prewarm-ms", type=float, default=300.0,
                     help="untimed launches before the warm-up steps, to reach steady clocks")
@@ -175,12 +224,14 @@ def main():
         sys.exit(2)
 
     import torch
-    from linear_rnn_recurrent_amd import inputs, load_library, ssu_decode, ssu_prefill, ssu_replay
+    from linear_rnn_recurrent_amd import (inputs, load_library, ssu_decode, ssu_prefill,
+                                          ssu_replay, ssu_tree_verify)
 
     load_library()
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
-    w = inputs.config(args.config)
+    w = inputs.config(args.config) if args.config != 5 else inputs.tree_config()
+    name = inputs.CONFIG_NAMES[args.config] if args.config != 5 else inputs.TREE_NAME
     T = {k: (None if v is None else v.to(dev)) for k, v in w.tensors.items()}
     stream = torch.cuda.current_stream(dev)
 
@@ -232,9 +283,33 @@ def main():
             ssu_prefill(R["x"], R["A"], R["B"], R["C"], R["dt"], R["state"], outs[i % len(reps)],
                         dt_bias=R["dt_bias"], D=R["D"], z=R["z"], dt_softplus=w.dt_softplus,
                         context_lengths=R["context_lengths"], state_indices=R["state_indices"])
-        src = source_hash("ssu_prefill_impl.h", "ssu_device.h")
+        src = source_hash("ssu_prefill_impl.h", "ssu_rowblock.h", "ssu_device.h")
         kkey = "prefill_config2"
         elems = sum(L) * T["x"].shape[2] * T["x"].shape[3] * T["B"].shape[3]
+        bound, peak, unit = "alu", VALU_PEAK_TOPS, "TOP/s"
+    elif args.config == 5:
+        kind = "tree"
+        b, m, h, d = T["x"].shape
+        nbytes = tree_bytes(T)
+        units = int((T["state_indices"] >= 0).sum().item()) * m * h
+        reps = replicas(["x", "B", "C", "dt", "state"], 3)
+        for R in reps:
+            R["out"] = torch.empty_like(T["x"])
+            R["S"] = {"replay_dA": torch.empty((b, m, h), device=dev),
+                      "replay_dt": torch.empty((b, m, h), device=dev),
+                      "replay_u": torch.empty((b, m, h, d), device=dev),
+                      "replay_B": torch.empty(tuple(T["B"].shape), device=dev)}
+        rot = "steps rotate 3 replicas of the pool, of every input and of the outputs and stash"
+
+        def step(i):
+            R = reps[i % len(reps)]
+            ssu_tree_verify(R["x"], R["A"], R["B"], R["C"], R["dt"], R["state"], R["out"],
+                            R["parent_ids"], depths=R["depths"], dt_bias=R["dt_bias"], D=R["D"],
+                            z=R["z"], dt_softplus=w.dt_softplus, state_indices=R["state_indices"],
+                            **R["S"])
+        src = source_hash("ssu_tree_impl.h", "ssu_device.h")
+        kkey = "tree_config5"
+        lane_ops = tree_lane_ops(T)
         bound, peak, unit = "alu", VALU_PEAK_TOPS, "TOP/s"
     else:
         kind = "replay"
@@ -303,6 +378,8 @@ def main():
     gbs = nbytes / (ms * 1e-3) / 1e9
     if bound == "hbm":
         achieved = gbs
+    elif kind == "tree":
+        achieved = lane_ops / (ms * 1e-3) / 1e12        # FMAs of the closed form
     else:
         achieved = 3.0 * elems / (ms * 1e-3) / 1e12     # mul + fma + fma per element-token
     traffic = measured_traffic(kkey, src)
@@ -319,7 +396,7 @@ def main():
         "vs_baseline": None,
         "dtype": "f32",
         "data": "synthetic",
-        "config": {"workload": inputs.CONFIG_NAMES[args.config] + "; " + rot,
+        "config": {"workload": name + "; " + rot,
                    "kernel": kind, "algorithmic_bytes_per_step": nbytes,
                    "token_head_updates_per_step": units},
         "hbm_frac": round(gbs / HBM_PEAK_GBS, 4),

@@ -12,37 +12,44 @@
 // Form used here. Along a path c_k -> ... -> c_1 -> c_0 = m (root first) the
 // recurrence is affine in the state, so the state after m's step is
 //   S_m = w_S S0 + sum_i w_i dt'_{c_i} x_{c_i} B_{c_i}^T,
-//   w_i = exp(sum of A dt' over c_0 .. c_{i-1}),  w_S = exp(sum over c_0 .. c_k),
+//   w_i = prod of exp(A dt') over c_0 .. c_{i-1},  w_S = prod over c_0 .. c_k,
 // and m's output row is
 //   y_m = w_S (S0 C_m) + sum_i [w_i dt'_{c_i} (B_{c_i} . C_m)] x_{c_i} + D x_m.
 // This costs one dstate-long dot per (row, node) for S0 C_m, plus one
 // dstate-long dot per (node, path entry) shared by all rows, instead of a
-// full state update per path entry and row. The exponent sums are formed
-// from m upwards, so each weight carries the rounding of its own few terms
-// (a weight far up the path is small whatever its relative error).
+// full state update per path entry and row. The weights are running products
+// of the per-node decays from m upwards, the same products the step-by-step
+// recurrence forms.
 //
-// Mapping on gfx950 (256 threads, one (batch row, head, block of 64 rows of
-// dim) per workgroup; the prefill's lane layout, state slice in registers):
-//   1. per node (one lane each): dt', A dt', parent id into LDS;
-//   2. per node: walk the parents once to count the path, a workgroup prefix
-//      sum places every node's path entries, a second walk writes each
-//      entry's ancestor id and weight w_i dt'_{c_i} (the path entries of all
-//      nodes fit in M(M+1)/2 slots: a node's path has at most m+1 entries);
-//   3. per path entry: B_{c_i} . C_m over dstate by 4..16 lanes from global
-//      memory (B and C are shared by all heads of a group, so L2 serves
-//      them), folded into the entry's coefficient;
-//   4. C of TC nodes at a time is staged in LDS (register prefetch of the next
-//      chunk); each lane forms its rows' partial S0 . C_m over its dstate
-//      slice, the four quarters of a wave are summed with cross-lane swaps and
-//      the four waves' partials meet in LDS;
-//   5. per (node, row): w_S * (sum of wave partials) + sum over the node's path
-//      entries of coefficient * x (x of every node of the row block sits in
-//      LDS) + D x, gate, store.
+// Mapping on gfx950 (one (batch row, head, block of 64 rows of dim) per
+// 256-thread workgroup):
+//   1. prologue: every global load is issued first: the state slice (straight
+//      into MFMA operand registers), x and B of every node (16-byte vectors,
+//      kept in LDS in their storage dtype), dt / parent / depth per node and C
+//      of the first chunk. Per node a record {exp(A dt'), dt', parent, hop
+//      bound} goes to LDS; then one lane per node walks the parent ids and
+//      writes the node's path (ancestor ids, node first) into a fixed slot of
+//      the triangular table (a node's path has at most m+1 entries);
+//   2. nodes go in chunks of 16 (the N side of one MFMA tile). S0 . C_m is a
+//      dense contraction [64 rows x dstate] x [dstate x nodes] and runs on the
+//      matrix cores in fp32 (v_mfma_f32_16x16x4_f32): wave w owns rows
+//      16w .. 16w+15, lane group g = lane/16 owns the dstate slice
+//      [g dstate/4, (g+1) dstate/4), C of the chunk (LDS, storage dtype, rows
+//      padded against bank conflicts) is the B operand, and the wave's 16 x 16
+//      result stays in its accumulator registers;
+//   3. meanwhile 16 lanes per chunk node go along its path: per entry the
+//      dot B_{c_i} . C_m (dstate split over the lanes, DPP row sums) and the
+//      weight w_i dt'_{c_i} as a running product of the decays in registers,
+//      giving the entry's coefficient; C of the next chunk is loaded into
+//      registers;
+//   4. after one barrier, each lane finishes the outputs it holds in its
+//      accumulators (one node, four consecutive rows): w_S (S0 . C_m) + the
+//      node's path terms + D x, gate, store; the next chunk's C goes to LDS;
+//      a second barrier ends the chunk.
 #pragma once
 
 #include "ssu_device.h"
 #include "ssu_internal.h"
-#include "ssu_rowblock.h"
 
 namespace ssu {
 namespace {
@@ -53,12 +60,14 @@ struct TreeShape {
     int32_t dt_softplus;
 };
 
-constexpr int kTreeTC = 8;  // nodes per staged chunk of C
-constexpr int kTreeNW = 4;  // waves per workgroup
+constexpr int kTreeTC = 16;   // nodes per chunk (the N side of one 16x16 MFMA tile)
+constexpr int kTreeNT = 256;  // threads: four waves of 16 rows each
+
+typedef float f32x4 __attribute__((ext_vector_type(4)));
 
 // Byte offsets of the LDS arrays for a tree of M nodes (host and device).
 struct TreeLds {
-    int xs, cs, ybuf, dtp, dA, wS, par, off, len, ew, ej, en, wsum, total;
+    int xs, bs, cs, rec, path, len, cw, cws, total;
 };
 
 __host__ __device__ inline int tree_lds_take(int &o, int bytes)
@@ -68,62 +77,88 @@ __host__ __device__ inline int tree_lds_take(int &o, int bytes)
     return r;
 }
 
-__host__ __device__ inline TreeLds tree_lds(int M, int NS)
+// Row pitches (bytes) in LDS: one 16-byte pad per row spreads the rows that
+// the lanes of one instruction read together over the banks (B and C rows of
+// dstate elements; x rows of the block's 64 rows of dim).
+__host__ __device__ constexpr int tree_row_bytes(int NS, int bc_bytes) { return NS * bc_bytes + 16; }
+__host__ __device__ constexpr int tree_x_pitch(int io_bytes) { return 64 * io_bytes + 16; }
+
+__host__ __device__ inline TreeLds tree_lds(int M, int NS, int io_bytes, int bc_bytes)
 {
     TreeLds L;
     int o = 0;
-    const int E = M * (M + 1) / 2;
-    L.xs = tree_lds_take(o, M * 64 * 4);                    // x of the row block [M][64]
-    L.cs = tree_lds_take(o, 2 * kTreeTC * NS * 4);          // C chunks [2][TC][NS]
-    L.ybuf = tree_lds_take(o, kTreeTC * kTreeNW * 64 * 4);  // wave partials [TC][NW][64]
-    L.dtp = tree_lds_take(o, M * 4);                        // dt'
-    L.dA = tree_lds_take(o, M * 4);                         // A dt'
-    L.wS = tree_lds_take(o, M * 4);                         // weight of S0 per node
-    L.par = tree_lds_take(o, M * 4);                        // parent id
-    L.off = tree_lds_take(o, M * 4);                        // first path entry
-    L.len = tree_lds_take(o, M * 4);                        // path entries
-    L.ew = tree_lds_take(o, E * 4);                         // entry weight / coefficient
-    L.ej = tree_lds_take(o, E);                             // entry: ancestor id
-    L.en = tree_lds_take(o, E);                             // entry: node id
-    L.wsum = tree_lds_take(o, kTreeNW * 4);                 // per-wave path counts
+    const int rb = tree_row_bytes(NS, bc_bytes);
+    L.xs = tree_lds_take(o, M * tree_x_pitch(io_bytes));  // x [M][64 rows]
+    L.bs = tree_lds_take(o, M * rb);                  // B [M][NS]
+    L.cs = tree_lds_take(o, kTreeTC * rb);            // C of the current chunk [TC][NS]
+    L.rec = tree_lds_take(o, M * 16);                 // node records
+    L.path = tree_lds_take(o, M * (M + 1) / 2);       // path of node m at m(m+1)/2
+    L.len = tree_lds_take(o, M * 4);                  // path lengths
+    L.cw = tree_lds_take(o, kTreeTC * M * 4);         // coefficients of the chunk's entries
+    L.cws = tree_lds_take(o, kTreeTC * 4);            // weights of S0 of the chunk's nodes
     L.total = o;
     return L;
 }
 
-template <int NSL>
-__device__ __forceinline__ void fetch_c(float (&c)[NSL], const float *cp)
+// n consecutive storage-dtype elements (16-bit or fp32) from LDS as fp32;
+// n * element size is a multiple of 8 bytes and the address is aligned to it.
+template <typename T, int N>
+__device__ __forceinline__ void lds_row(const unsigned char *p, float (&f)[N])
 {
-    if constexpr (NSL % 4 == 0) {
+    if constexpr (sizeof(T) == 4) {
+        static_assert(N % 4 == 0, "fp32 rows go in 16-byte pieces");
 #pragma unroll
-        for (int j = 0; j < NSL; j += 4) {
-            const float4 c4 = *reinterpret_cast<const float4 *>(cp + j);
-            c[j] = c4.x;
-            c[j + 1] = c4.y;
-            c[j + 2] = c4.z;
-            c[j + 3] = c4.w;
+        for (int k = 0; k < N; k += 4) {
+            const u32x4 w = *reinterpret_cast<const u32x4 *>(p + 4 * k);
+#pragma unroll
+            for (int e = 0; e < 4; ++e)
+                f[k + e] = __uint_as_float(w[e]);
+        }
+    } else if constexpr (N % 8 == 0) {
+#pragma unroll
+        for (int k = 0; k < N; k += 8) {
+            const u32x4 w = *reinterpret_cast<const u32x4 *>(p + 2 * k);
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                f[k + 2 * e] = cvt_raw1<T>(w[e] & 0xffffu);
+                f[k + 2 * e + 1] = cvt_raw1<T>(w[e] >> 16);
+            }
         }
     } else {
+        static_assert(N == 4, "16-bit rows go in 8- or 16-byte pieces");
+        const u32x2 w = *reinterpret_cast<const u32x2 *>(p);
 #pragma unroll
-        for (int j = 0; j < NSL; ++j)
-            c[j] = cp[j];
+        for (int e = 0; e < 2; ++e) {
+            f[2 * e] = cvt_raw1<T>(w[e] & 0xffffu);
+            f[2 * e + 1] = cvt_raw1<T>(w[e] >> 16);
+        }
     }
 }
 
-// The lane's partial S0 . C over its slice, for its rows rr + 16 i.
-template <int NSL>
-__device__ __forceinline__ float4 rows_dot(const float (&S)[4][NSL], const float (&c)[NSL])
+// Sum over aligned groups of W lanes (W = 4, 8 or 16) with DPP: quad
+// permutations, then the half-row and row mirrors; every lane of a group gets
+// the group's sum. No LDS traffic.
+template <int CTRL>
+__device__ __forceinline__ float dpp_f32(float a)
 {
-    float p[4] = {0.0f, 0.0f, 0.0f, 0.0f};
-#pragma unroll
-    for (int j = 0; j < NSL; ++j)
-#pragma unroll
-        for (int i = 0; i < 4; ++i)
-            p[i] = fmaf(S[i][j], c[j], p[i]);
-    return make_float4(p[0], p[1], p[2], p[3]);
+    return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, a),
+                                                                CTRL, 0xF, 0xF, false));
+}
+
+template <int W>
+__device__ __forceinline__ float row_group_sum(float v)
+{
+    v += dpp_f32<0xB1>(v);  // quad_perm [1,0,3,2]
+    v += dpp_f32<0x4E>(v);  // quad_perm [2,3,0,1]
+    if constexpr (W >= 8)
+        v += dpp_f32<0x141>(v);  // row_half_mirror: lane i <- lane 7 - i of its half row
+    if constexpr (W >= 16)
+        v += dpp_f32<0x140>(v);  // row_mirror: lane i <- lane 15 - i
+    return v;
 }
 
 template <typename ST, typename IOT, typename BCT, int NS>
-__global__ __launch_bounds__(64 * kTreeNW) void ssu_tree_kernel(
+__global__ __launch_bounds__(kTreeNT) void ssu_tree_kernel(
     const void *__restrict__ x, const float *__restrict__ A, const void *__restrict__ Bm,
     const void *__restrict__ Cm, const float *__restrict__ dt, const float *__restrict__ dt_bias,
     const float *__restrict__ Dv, const void *__restrict__ z, const ST *__restrict__ state,
@@ -131,42 +166,36 @@ __global__ __launch_bounds__(64 * kTreeNW) void ssu_tree_kernel(
     const int32_t *__restrict__ depths, float *__restrict__ st_dA, float *__restrict__ st_u,
     float *__restrict__ st_B, float *__restrict__ st_dt, const TreeShape sh)
 {
-    constexpr int NW = kTreeNW;
-    constexpr int NT = 64 * NW;
+    constexpr int NT = kTreeNT;
     constexpr int TC = kTreeTC;
-    constexpr int NSL = NS / (4 * NW);             // dstate columns per lane
-    constexpr int BCN = TC * NS;                   // C elements per chunk
-    constexpr int BCV = (BCN / 4 + NT - 1) / NT;   // 4-element C vectors per thread
-    constexpr int XT_PER = TC * 64 / NT;           // (node, row) outputs per thread per chunk
-    constexpr int EPL = NS / 16 >= 4 ? NS / 16 : 4;  // B/C elements per lane in a path dot
-    constexpr int LPE = NS / EPL;                  // lanes per path entry
-    constexpr int EPP = NT / LPE;                  // path entries per pass
-    static_assert(NSL >= 1 && NS % (4 * NW) == 0, "dstate must split into 16 slices");
-    static_assert(TC % 2 == 0 && XT_PER * NT == TC * 64, "chunk shape");
+    constexpr int KS = NS / 4;                        // dstate columns per lane group
+    constexpr int XB = (int)sizeof(IOT), BB = (int)sizeof(BCT);
+    constexpr int RB = tree_row_bytes(NS, BB);        // LDS row pitch of B and C
+    constexpr int XP = tree_x_pitch(XB);              // LDS row pitch of x
+    constexpr int CV = (TC * NS * BB / 16 + NT - 1) / NT;  // 16-byte C vectors per thread
+    constexpr int XV = 16 / XB;                       // x elements per 16-byte vector
+    constexpr int BVE = 16 / BB;                      // B/C elements per 16-byte vector
+    constexpr int XVEC = (SSU_MAX_TREE_NODES * 64 / XV + NT - 1) / NT;  // x vectors per thread
+    constexpr int NPT = (SSU_MAX_TREE_NODES + NT - 1) / NT;  // node records per thread
+    static_assert(KS % 4 == 0 && (KS * BB) % 8 == 0, "tile shape");
 
     extern __shared__ __attribute__((aligned(16))) unsigned char lds[];
     const int M = sh.num_nodes;
-    const TreeLds L = tree_lds(M, NS);
-    float *xs = reinterpret_cast<float *>(lds + L.xs);
-    float(*Cs)[TC][NS] = reinterpret_cast<float(*)[TC][NS]>(lds + L.cs);
-    float(*ybuf)[NW][64] = reinterpret_cast<float(*)[NW][64]>(lds + L.ybuf);
-    float *n_dtp = reinterpret_cast<float *>(lds + L.dtp);
-    float *n_dA = reinterpret_cast<float *>(lds + L.dA);
-    float *n_wS = reinterpret_cast<float *>(lds + L.wS);
-    int *n_par = reinterpret_cast<int *>(lds + L.par);
-    int *n_off = reinterpret_cast<int *>(lds + L.off);
+    const TreeLds L = tree_lds(M, NS, XB, BB);
+    unsigned char *xs = lds + L.xs;
+    unsigned char *bs = lds + L.bs;
+    unsigned char *cs = lds + L.cs;
+    float4 *rec = reinterpret_cast<float4 *>(lds + L.rec);  // {exp(A dt'), dt', parent, bound}
+    uint8_t *n_path = lds + L.path;                          // triangular path table
     int *n_len = reinterpret_cast<int *>(lds + L.len);
-    float *e_w = reinterpret_cast<float *>(lds + L.ew);
-    uint8_t *e_j = lds + L.ej;
-    uint8_t *e_n = lds + L.en;
-    int *wsum = reinterpret_cast<int *>(lds + L.wsum);
+    float *c_w = reinterpret_cast<float *>(lds + L.cw);      // [TC][M]
+    float *c_wS = reinterpret_cast<float *>(lds + L.cws);    // [TC]
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-    const int q = lane >> 4;
-    const int rr = lane & 15;
-    const int n0 = (wave * 4 + q) * NSL;
+    const int qg = lane >> 4;     // lane group: dstate slice (MFMA A/B), row quad (MFMA D)
+    const int ln = lane & 15;     // MFMA A row / B and D column (node of the chunk)
     const int H = sh.nheads, Dm = sh.dim, G = sh.ngroups;
     const int per_b = H * sh.nrb;
     const int b = blockIdx.x / per_b;
@@ -192,213 +221,320 @@ __global__ __launch_bounds__(64 * kTreeNW) void ssu_tree_kernel(
     const float bias = dt_bias ? dt_bias[h] : 0.0f;
     const float dskip = Dv ? Dv[h] : 0.0f;
 
-    // ---- the committed state slice: rows rbase + rr + 16 i, columns n0 .. n0+NSL-1 ----
-    float S[4][NSL];
-    const ST *sbase = state + (int64_t)srow * sh.row_stride + (int64_t)h * Dm * NS + n0;
+    // ---- 1. prologue: every global load first ----
+    // MFMA A operand: lane (ln, qg) of wave w holds S0[row 16 w + ln][qg KS + s]
+    const int arow = rbase + 16 * wave + ln;
+    float sa[KS];
+    {
+        const ST *sp = state + (int64_t)srow * sh.row_stride + (int64_t)h * Dm * NS +
+                       (int64_t)min(arow, Dm - 1) * NS + qg * KS;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-        const int rc = min(rbase + rr + 16 * i, Dm - 1);
+        for (int s = 0; s < KS; ++s)
+            sa[s] = ld_elem<ST>(sp, s);
+    }
+    // per node: dt, parent id, hop bound
+    float ndt[NPT];
+    int npar[NPT], ncap[NPT];
 #pragma unroll
-        for (int j = 0; j < NSL; ++j)
-            S[i][j] = ld_elem<ST>(sbase, (int64_t)rc * NS + j);
+    for (int k = 0; k < NPT; ++k) {
+        const int m = min(tid + NT * k, M - 1);
+        ndt[k] = dt[(bM + m) * H + h];
+        npar[k] = parents[bM + m];
+        ncap[k] = depths ? depths[bM + m] : m;
     }
-
-    // ---- 1. per node: dt', A dt', parent; x of every node into LDS ----
-    if (tid < M) {
-        float v = dt[(bM + tid) * H + h] + bias;
-        if (sh.dt_softplus)
-            v = softplus_f32(v);
-        n_dtp[tid] = v;
-        n_dA[tid] = Ah * v;
-        n_par[tid] = parents[bM + tid];
-        if (stash && rb == 0) {
-            st_dA[(bM + tid) * H + h] = Ah * v;
-            st_dt[(bM + tid) * H + h] = v;
+    // C of chunk c: 16-byte vectors of the storage dtype (nodes past M clamp to M-1)
+    u32x4 rc[CV];
+    auto load_c = [&](int t0) {
+#pragma unroll
+        for (int k = 0; k < CV; ++k) {
+            const int v = tid + NT * k;               // vector v: node v / (NS/BVE)
+            const int m = min(t0 + v / (NS / BVE), M - 1);
+            rc[k] = *reinterpret_cast<const u32x4 *>(
+                static_cast<const unsigned char *>(Cm) +
+                (((bM + m) * G + g) * NS + BVE * (v % (NS / BVE))) * BB);
+        }
+    };
+    auto store_c = [&]() {
+#pragma unroll
+        for (int k = 0; k < CV; ++k) {
+            const int v = tid + NT * k;
+            if (v < TC * NS / BVE)
+                *reinterpret_cast<u32x4 *>(cs + (v / (NS / BVE)) * RB + (v % (NS / BVE)) * 16) =
+                    rc[k];
+        }
+    };
+    load_c(0);
+    // B of every node (16-byte vectors; vector v: node v / (NS/BVE)), in
+    // batches of 8 per thread; the stash copy of B comes from the first head of
+    // the group
+    constexpr int BPN = NS / BVE;
+    const int nbv = M * BPN;
+    const bool writes_B = stash && rb == 0 && (h % sh.heads_per_group) == 0;
+    u32x4 br[8];
+    auto load_b = [&](int v0) {
+#pragma unroll
+        for (int k = 0; k < 8; ++k) {
+            const int v = min(v0 + tid + NT * k, nbv - 1);
+            br[k] = *reinterpret_cast<const u32x4 *>(
+                static_cast<const unsigned char *>(Bm) +
+                (((bM + v / BPN) * G + g) * NS + BVE * (v % BPN)) * BB);
+        }
+    };
+    auto store_b = [&](int v0) {
+#pragma unroll
+        for (int k = 0; k < 8; ++k) {
+            const int v = v0 + tid + NT * k;
+            if (v < nbv) {
+                *reinterpret_cast<u32x4 *>(bs + (v / BPN) * RB + (v % BPN) * 16) = br[k];
+                if (writes_B) {
+                    float f[BVE];
+                    if constexpr (BB == 4) {
+#pragma unroll
+                        for (int e = 0; e < 4; ++e)
+                            f[e] = __uint_as_float(br[k][e]);
+                    } else {
+#pragma unroll
+                        for (int e = 0; e < 4; ++e) {
+                            f[2 * e] = cvt_raw1<BCT>(br[k][e] & 0xffffu);
+                            f[2 * e + 1] = cvt_raw1<BCT>(br[k][e] >> 16);
+                        }
+                    }
+                    float *dst = st_B + ((bM + v / BPN) * G + g) * NS + BVE * (v % BPN);
+#pragma unroll
+                    for (int e = 0; e < BVE; e += 4)
+                        *reinterpret_cast<float4 *>(dst + e) =
+                            make_float4(f[e], f[e + 1], f[e + 2], f[e + 3]);
+                }
+            }
+        }
+    };
+    // x of every node, rows of the block, as 16-byte vectors when dim allows
+    // (vector v: node v / (64/XV), rows XV*(v % (64/XV)) ..); rows past dim are
+    // 0. Its loads and the first batch of B loads are in flight together.
+    const bool xvec = Dm % XV == 0 && (reinterpret_cast<uintptr_t>(x) & 15) == 0 &&
+                      (!stash || (reinterpret_cast<uintptr_t>(st_u) & 15) == 0);
+    if (xvec) {
+        constexpr int VPN = 64 / XV;  // vectors per node
+        const int nvec = M * VPN;
+        u32x4 xr[XVEC];
+#pragma unroll
+        for (int k = 0; k < XVEC; ++k) {
+            const int v = min(tid + NT * k, nvec - 1);
+            const int r = min(rbase + XV * (v % VPN), Dm - XV);
+            xr[k] = *reinterpret_cast<const u32x4 *>(
+                static_cast<const unsigned char *>(x) +
+                ((((bM + v / VPN) * H + h) * Dm + r) * XB));
+        }
+        load_b(0);
+#pragma unroll
+        for (int k = 0; k < XVEC; ++k) {
+            const int v = tid + NT * k;
+            if (v < nvec) {
+                const int m = v / VPN, rl = XV * (v % VPN);
+                const bool valid = rbase + rl < Dm;
+                u32x4 w = xr[k];
+                if (!valid)
+                    w = u32x4{0u, 0u, 0u, 0u};
+                *reinterpret_cast<u32x4 *>(xs + m * XP + rl * XB) = w;
+                if (stash && valid) {
+                    float f[XV];
+                    if constexpr (XB == 4) {
+#pragma unroll
+                        for (int e = 0; e < 4; ++e)
+                            f[e] = __uint_as_float(w[e]);
+                    } else {
+#pragma unroll
+                        for (int e = 0; e < 4; ++e) {
+                            f[2 * e] = cvt_raw1<IOT>(w[e] & 0xffffu);
+                            f[2 * e + 1] = cvt_raw1<IOT>(w[e] >> 16);
+                        }
+                    }
+                    float *dst = st_u + ((bM + m) * H + h) * Dm + rbase + rl;
+#pragma unroll
+                    for (int e = 0; e < XV; e += 4)
+                        *reinterpret_cast<float4 *>(dst + e) =
+                            make_float4(f[e], f[e + 1], f[e + 2], f[e + 3]);
+                }
+            }
+        }
+    } else {
+        load_b(0);
+        for (int e = tid; e < M * 64; e += NT) {
+            const int m = e >> 6, rl = e & 63, r = rbase + rl;
+            uint32_t w = 0;
+            if (r < Dm) {
+                const int64_t o = ((bM + m) * H + h) * Dm + r;
+                w = ld_raw1<IOT>(x, o);
+                if (stash)
+                    st_u[o] = cvt_raw1<IOT>(w);
+            }
+            if constexpr (XB == 4)
+                *reinterpret_cast<uint32_t *>(xs + m * XP + rl * 4) = w;
+            else
+                *reinterpret_cast<uint16_t *>(xs + m * XP + rl * 2) = (uint16_t)w;
         }
     }
-#pragma unroll 4
-    for (int e = tid; e < M * 64; e += NT) {
-        const int m = e >> 6;
-        const int r = rbase + (e & 63);
-        float v = 0.0f;
-        if (r < Dm) {
-            const int64_t o = ((bM + m) * H + h) * Dm + r;
-            v = ld_elem<IOT>(x, o);
-            if (stash)
-                st_u[o] = v;
-        }
-        xs[m * 64 + xpos(e & 63)] = v;
+    store_b(0);
+    for (int v0 = 8 * NT; v0 < nbv; v0 += 8 * NT) {
+        load_b(v0);
+        store_b(v0);
     }
-    if (stash && rb == 0 && (h % sh.heads_per_group) == 0) {
-        for (int i = tid; i < M * NS; i += NT) {
-            const int64_t o = ((bM + i / NS) * G + g) * NS + (i % NS);
-            st_B[o] = ld_elem<BCT>(Bm, o);
+    // node records {decay exp(A dt'), dt', parent id (-1 unless it precedes the
+    // node), hop bound}
+#pragma unroll
+    for (int k = 0; k < NPT; ++k) {
+        const int m = tid + NT * k;
+        if (m < M) {
+            float v = ndt[k] + bias;
+            if (sh.dt_softplus)
+                v = softplus_f32(v);
+            const int p = npar[k];
+            rec[m] = make_float4(expf(Ah * v), v, __int_as_float(p >= 0 && p < m ? p : -1),
+                                 __int_as_float(ncap[k]));
+            if (stash && rb == 0) {
+                st_dA[(bM + m) * H + h] = Ah * v;
+                st_dt[(bM + m) * H + h] = v;
+            }
         }
     }
+    store_c();
     __syncthreads();
 
-    // ---- 2. the path of every node: length, placement, entries ----
-    int len = 0;
-    if (tid < M) {
-        const int cap = depths ? depths[bM + tid] : tid;
-        int j = tid, hops = 0;
-        while (hops < cap) {
-            const int p = n_par[j];
-            if (p < 0 || p >= j)
+    // ---- the path of every node (one lane per node), node first ----
+    for (int m = tid; m < M; m += NT) {
+        uint8_t *pp = n_path + m * (m + 1) / 2;
+        const int cap = __float_as_int(rec[m].w);
+        int j = m, hops = 0;
+        while (true) {
+            pp[hops] = (uint8_t)j;
+            const int p = __float_as_int(rec[j].z);
+            if (hops >= cap || p < 0)
                 break;
             j = p;
             ++hops;
         }
-        len = hops + 1;
-    }
-    int incl = len;
-#pragma unroll
-    for (int d = 1; d < 64; d <<= 1) {
-        const int o = __shfl_up(incl, d, 64);
-        if (lane >= d)
-            incl += o;
-    }
-    if (lane == 63)
-        wsum[wave] = incl;
-    __syncthreads();
-    int base = 0, total = 0;
-#pragma unroll
-    for (int w = 0; w < NW; ++w) {
-        const int c = wsum[w];
-        base += w < wave ? c : 0;
-        total += c;
-    }
-    if (tid < M) {
-        const int e0 = base + incl - len;
-        n_off[tid] = e0;
-        n_len[tid] = len;
-        int j = tid;
-        float acc = 0.0f;  // sum of A dt' over the path nodes after j
-        for (int k = 0; k < len; ++k) {
-            e_j[e0 + k] = (uint8_t)j;
-            e_n[e0 + k] = (uint8_t)tid;
-            e_w[e0 + k] = expf(acc) * n_dtp[j];
-            acc += n_dA[j];
-            j = n_par[j];
-        }
-        n_wS[tid] = expf(acc);
+        n_len[m] = hops + 1;
     }
     __syncthreads();
-
-    // ---- 3. coefficient of every path entry: weight * (B_ancestor . C_node) ----
-    {
-        const int grp = tid / LPE;
-        const int l = tid - grp * LPE;
-        for (int e0 = 0; e0 < total; e0 += 2 * EPP) {
-            float bv[2][EPL], cv[2][EPL];
-#pragma unroll
-            for (int u = 0; u < 2; ++u) {
-                const int ec = min(e0 + u * EPP + grp, total - 1);
-                const int j = e_j[ec], m = e_n[ec];
-                ld_typed<BCT, EPL>(Bm, ((bM + j) * G + g) * NS + l * EPL, bv[u]);
-                ld_typed<BCT, EPL>(Cm, ((bM + m) * G + g) * NS + l * EPL, cv[u]);
-            }
-#pragma unroll
-            for (int u = 0; u < 2; ++u) {
-                float d = 0.0f;
-#pragma unroll
-                for (int k = 0; k < EPL; ++k)
-                    d = fmaf(bv[u][k], cv[u][k], d);
-                d = group_sum<LPE>(d);
-                const int e = e0 + u * EPP + grp;
-                if (l == 0 && e < total)
-                    e_w[e] *= d;
-            }
-        }
-    }
-
-    // ---- 4./5. S0 . C per node in chunks of TC nodes, then the outputs ----
-    typename Raw4<BCT>::type rC[BCV];
-    auto load_chunk = [&](int t0, int nt) {
-#pragma unroll
-        for (int k = 0; k < BCV; ++k) {
-            const int e = min((tid + NT * k) * 4, nt * NS - 4);
-            rC[k] = ld_raw4<BCT>(Cm, ((bM + t0 + e / NS) * G + g) * NS + (e % NS));
-        }
-    };
-    auto store_chunk = [&](int buf) {
-#pragma unroll
-        for (int k = 0; k < BCV; ++k) {
-            const int e = (tid + NT * k) * 4;
-            if (e < BCN) {
-                float vc[4];
-                cvt_raw4<BCT>(rC[k], vc);
-                *reinterpret_cast<float4 *>(&Cs[buf][e / NS][e % NS]) =
-                    make_float4(vc[0], vc[1], vc[2], vc[3]);
-            }
-        }
-    };
 
     const int nchunks = (M + TC - 1) / TC;
-    load_chunk(0, min(TC, M));
-    store_chunk(0);
-    __syncthreads();
     const void *zsrc = z ? z : x;
+    constexpr int LPN = KS >= 16 ? 16 : KS;   // lanes per chunk node in the path sums
+    constexpr int EPN = NS / LPN;             // dstate elements per lane there
     for (int c = 0; c < nchunks; ++c) {
-        const int buf = c & 1;
         const int t0 = c * TC;
         const int nt = min(TC, M - t0);
+        const int mo = t0 + ln;                       // this lane's output node
+        const int orow = rbase + 16 * wave + 4 * qg;  // and its first output row
+        // gate inputs of this lane's four outputs (raw bits; clamped indices)
+        uint32_t zq[4];
+#pragma unroll
+        for (int v = 0; v < 4; ++v)
+            zq[v] = ld_raw1<IOT>(zsrc, ((bM + min(mo, M - 1)) * H + h) * Dm + min(orow + v, Dm - 1));
         if (c + 1 < nchunks)
-            load_chunk(t0 + TC, min(TC, M - t0 - TC));
-        uint32_t zq[XT_PER];
-#pragma unroll
-        for (int k = 0; k < XT_PER; ++k) {
-            const int e = tid + NT * k;
-            const int tt = min(e >> 6, nt - 1);
-            const int r = min(rbase + (e & 63), Dm - 1);
-            zq[k] = ld_raw1<IOT>(zsrc, ((bM + t0 + tt) * H + h) * Dm + r);
-        }
+            load_c(t0 + TC);
 
-        // Pairs of nodes with ping-pong operands; slots past nt hold clamped
-        // copies of the chunk's last node and their partials are never read.
-        float ca[NSL], cb[NSL];
-        fetch_c<NSL>(ca, &Cs[buf][0][n0]);
-        for (int tt = 0; tt < nt; tt += 2) {
-            fetch_c<NSL>(cb, &Cs[buf][tt + 1][n0]);
-            ybuf[tt][wave][lane] = quarter_reduce(rows_dot<NSL>(S, ca));
-            fetch_c<NSL>(ca, &Cs[buf][min(tt + 2, TC - 1)][n0]);
-            ybuf[tt + 1][wave][lane] = quarter_reduce(rows_dot<NSL>(S, cb));
-        }
-        __syncthreads();
-
+        // S0 . C: 16 rows x 16 nodes per wave on the matrix cores, four
+        // independent accumulators so that the MFMAs issue back to back
+        f32x4 acc4[4];
 #pragma unroll
-        for (int k = 0; k < XT_PER; ++k) {
-            const int e = tid + NT * k;
-            const int tt = e >> 6;  // uniform across the wave
-            const int rl = e & 63;
-            const int r = rbase + rl;
-            if (tt < nt && r < Dm) {
-                const int m = t0 + tt;
-                const int xp = xpos(rl);
-                float y = 0.0f;
+        for (int a4 = 0; a4 < 4; ++a4)
+            acc4[a4] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+        {
+            const unsigned char *cb = cs + ln * RB + qg * KS * BB;
 #pragma unroll
-                for (int w = 0; w < NW; w += 2)
-                    y += ybuf[tt][w][rl] + ybuf[tt][w + 1][rl];
-                y *= n_wS[m];
-                const int off = n_off[m], nl = n_len[m];
-                int k2 = 0;
-                for (; k2 + 1 < nl; k2 += 2) {
-                    const int j0 = e_j[off + k2], j1 = e_j[off + k2 + 1];
-                    const float w0 = e_w[off + k2], w1 = e_w[off + k2 + 1];
-                    const float x0 = xs[j0 * 64 + xp], x1 = xs[j1 * 64 + xp];
-                    y = fmaf(w0, x0, y);
-                    y = fmaf(w1, x1, y);
-                }
-                if (k2 < nl)
-                    y = fmaf(e_w[off + k2], xs[e_j[off + k2] * 64 + xp], y);
-                y += dskip * xs[m * 64 + xp];
-                if (z)
-                    y *= silu_f32(cvt_raw1<IOT>(zq[k]));
-                st_elem<IOT>(out, ((bM + m) * H + h) * Dm + r, y);
+            for (int s0 = 0; s0 < KS; s0 += 4) {
+                float cv[4];
+                lds_row<BCT, 4>(cb + s0 * BB, cv);
+#pragma unroll
+                for (int e = 0; e < 4; ++e)
+                    acc4[e] = __builtin_amdgcn_mfma_f32_16x16x4f32(sa[s0 + e], cv[e], acc4[e], 0, 0, 0);
             }
         }
+
+        // coefficients of the chunk's path entries: LPN lanes per node
+        for (int tt = tid / LPN; tt < TC; tt += NT / LPN) {
+            const int l = tid % LPN;
+            const int m = min(t0 + tt, M - 1);
+            const int nl = tt < nt ? n_len[m] : 0;
+            const uint8_t *pp = n_path + m * (m + 1) / 2;
+            float cv[EPN];
+            lds_row<BCT, EPN>(cs + tt * RB + l * EPN * BB, cv);
+            float wr = 1.0f;
+            // four entries at a time: their ids, then their records and B rows,
+            // then the arithmetic (the weight is a running product in registers)
+            for (int k0 = 0; k0 < nl; k0 += 4) {
+                int jj[4];
+#pragma unroll
+                for (int u = 0; u < 4; ++u)
+                    jj[u] = pp[min(k0 + u, nl - 1)];
+                float4 r[4];
+                float bv[4][EPN];
+#pragma unroll
+                for (int u = 0; u < 4; ++u) {
+                    r[u] = rec[jj[u]];
+                    lds_row<BCT, EPN>(bs + jj[u] * RB + l * EPN * BB, bv[u]);
+                }
+#pragma unroll
+                for (int u = 0; u < 4; ++u) {
+                    if (k0 + u < nl) {  // uniform over the node's lanes
+                        float d = 0.0f;
+#pragma unroll
+                        for (int e = 0; e < EPN; ++e)
+                            d = fmaf(bv[u][e], cv[e], d);
+                        d = row_group_sum<LPN>(d);
+                        if (l == 0)
+                            c_w[tt * M + k0 + u] = wr * r[u].y * d;
+                        wr *= r[u].x;
+                    }
+                }
+            }
+            if (l == 0 && tt < nt)
+                c_wS[tt] = wr;
+        }
+        __syncthreads();
         if (c + 1 < nchunks)
-            store_chunk(buf ^ 1);
+            store_c();  // every read of this chunk's C is done
+
+        // outputs held in the accumulators: node mo, rows orow .. orow+3
+        if (ln < nt) {
+            f32x4 acc = (acc4[0] + acc4[1]) + (acc4[2] + acc4[3]);
+            float y[4];
+            const float wS = c_wS[ln];
+#pragma unroll
+            for (int v = 0; v < 4; ++v)
+                y[v] = acc[v] * wS;
+            const int nl = n_len[mo];
+            const uint8_t *pp = n_path + mo * (mo + 1) / 2;
+            const float *cw = c_w + ln * M;
+            for (int k0 = 0; k0 < nl; k0 += 4) {
+                int jj[4];
+                float co[4], xv[4][4];
+#pragma unroll
+                for (int u = 0; u < 4; ++u) {
+                    jj[u] = pp[min(k0 + u, nl - 1)];
+                    co[u] = cw[min(k0 + u, nl - 1)];
+                }
+#pragma unroll
+                for (int u = 0; u < 4; ++u)
+                    lds_row<IOT, 4>(xs + jj[u] * XP + (orow - rbase) * XB, xv[u]);
+#pragma unroll
+                for (int u = 0; u < 4; ++u)
+#pragma unroll
+                    for (int v = 0; v < 4; ++v)
+                        y[v] = k0 + u < nl ? fmaf(co[u], xv[u][v], y[v]) : y[v];
+            }
+            float xm[4];
+            lds_row<IOT, 4>(xs + mo * XP + (orow - rbase) * XB, xm);
+#pragma unroll
+            for (int v = 0; v < 4; ++v) {
+                float o = y[v] + dskip * xm[v];
+                if (z)
+                    o *= silu_f32(cvt_raw1<IOT>(zq[v]));
+                if (orow + v < Dm)
+                    st_elem<IOT>(out, ((bM + mo) * H + h) * Dm + orow + v, o);
+            }
+        }
         __syncthreads();
     }
 }
@@ -419,7 +555,8 @@ hipError_t launch_tree_cfg(const TreeParams &p, hipStream_t stream)
     const int64_t blocks = (int64_t)d.batch * d.nheads * sh.nrb;
     if (blocks > 0x7fffffff)
         return hipErrorInvalidConfiguration;
-    const TreeLds L = tree_lds(p.num_nodes, NS);
+    constexpr int XB = (int)sizeof(IOT), BB = (int)sizeof(BCT);
+    const TreeLds L = tree_lds(p.num_nodes, NS, XB, BB);
     auto kern = ssu_tree_kernel<ST, IOT, BCT, NS>;
     if (L.total > 64 * 1024) {
         // Above 64 KiB of dynamic LDS the kernel must be allowed it first, once
@@ -431,7 +568,7 @@ hipError_t launch_tree_cfg(const TreeParams &p, hipStream_t stream)
         if (e != hipSuccess)
             return e;
         if (dev < 0 || dev >= 64 || allowed[dev] < L.total) {
-            const int most = tree_lds(SSU_MAX_TREE_NODES, NS).total;
+            const int most = tree_lds(SSU_MAX_TREE_NODES, NS, XB, BB).total;
             e = hipFuncSetAttribute(reinterpret_cast<const void *>(kern),
                                     hipFuncAttributeMaxDynamicSharedMemorySize, most);
             if (e != hipSuccess)
@@ -441,8 +578,8 @@ hipError_t launch_tree_cfg(const TreeParams &p, hipStream_t stream)
         }
     }
     (void)hipGetLastError();
-    hipLaunchKernelGGL(kern, dim3((unsigned)blocks), dim3(64 * kTreeNW), (unsigned)L.total,
-                       stream, d.x, d.A, d.B, d.C, d.dt, d.dt_bias, d.D, d.z,
+    hipLaunchKernelGGL(kern, dim3((unsigned)blocks), dim3(kTreeNT), (unsigned)L.total, stream,
+                       d.x, d.A, d.B, d.C, d.dt, d.dt_bias, d.D, d.z,
                        static_cast<const ST *>(d.state), d.out, d.idx, p.parents, p.depths,
                        p.st_dA, p.st_u, p.st_B, p.st_dt, sh);
     return hipGetLastError();
