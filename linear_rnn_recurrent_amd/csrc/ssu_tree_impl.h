@@ -418,7 +418,6 @@ __global__ __launch_bounds__(kTreeNT) void ssu_tree_kernel(
     __syncthreads();
 
     const int nchunks = (M + TC - 1) / TC;
-    const void *zsrc = z ? z : x;
     constexpr int LPN = KS >= 16 ? 16 : KS;   // lanes per chunk node in the path sums
     constexpr int EPN = NS / LPN;             // dstate elements per lane there
     for (int c = 0; c < nchunks; ++c) {
@@ -427,10 +426,12 @@ __global__ __launch_bounds__(kTreeNT) void ssu_tree_kernel(
         const int mo = t0 + ln;                       // this lane's output node
         const int orow = rbase + 16 * wave + 4 * qg;  // and its first output row
         // gate inputs of this lane's four outputs (raw bits; clamped indices)
-        uint32_t zq[4];
+        uint32_t zq[4] = {0u, 0u, 0u, 0u};
+        if (z) {
 #pragma unroll
-        for (int v = 0; v < 4; ++v)
-            zq[v] = ld_raw1<IOT>(zsrc, ((bM + min(mo, M - 1)) * H + h) * Dm + min(orow + v, Dm - 1));
+            for (int v = 0; v < 4; ++v)
+                zq[v] = ld_raw1<IOT>(z, ((bM + min(mo, M - 1)) * H + h) * Dm + min(orow + v, Dm - 1));
+        }
         if (c + 1 < nchunks)
             load_c(t0 + TC);
 
