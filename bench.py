@@ -8,10 +8,13 @@ four disjoint 64-row index sets that together cover the pool, so every step
 streams state rows the previous three steps did not touch and the 256 MB
 last-level cache cannot serve them.
 
-    python bench.py [--steps K] [--warmup W] [--config {1,2,3,4,5}]
+    python bench.py [--steps K] [--warmup W] [--config {1,2,3,4,5,6,7}]
 
 --config 2/3/4/5 time prefill / padded decode / MTP replay / tree verify
-(16 requests with 128-node draft trees, replay stash on) instead. Their pools
+(16 requests with 128-node draft trees, replay stash on) instead; 6 and 7 the
+layer-batched calls over a 64-layer stack: the MTP replay of config 4 for every
+layer in one launch, and the clear of one resident slot (recurrent and conv
+rows) of every layer in one launch. Their pools
 are smaller than the last-level cache, so the steps rotate over replicas of
 the pool (and, for prefill, of every input) that together exceed it; every
 configuration is timed as back-to-back launches on one stream.
@@ -147,8 +150,10 @@ def cpu_baseline(kind, w, seconds, bytes_per_call, units_per_call):
     import numpy as np
     import oracle
 
+    from linear_rnn_recurrent_amd import inputs as inputs_mod
     a = {k: (None if v is None else (v.double().numpy() if v.is_floating_point() else v.numpy()))
          for k, v in w.tensors.items()}
+    scale = 1.0   # fraction of one step's work a call does
     if kind == "decode":
         idx = a["state_indices"]
         live = idx[idx >= 0]
@@ -181,14 +186,35 @@ def cpu_baseline(kind, w, seconds, bytes_per_call, units_per_call):
                         depths=a["depths"], dt_bias=a["dt_bias"], D=a["D"], z=a["z"],
                         dt_softplus=w.dt_softplus, state_indices=a["state_indices"], stash=S)
         sample = "the full tree batch of this workload"
-    else:
-        st = a["state"].copy()
+    elif kind == "clear_layers":
+        nl = 4
+        rows = a["state"].shape[0]
+        rec_rb = a["state"][0].size * 4
+        conv_rb = inputs_mod.STACK_CONV_ROW_BYTES
+        recs = [np.ones(rows * rec_rb, dtype=np.uint8) for _ in range(nl)]
+        convs = [np.ones(rows * conv_rb, dtype=np.uint8) for _ in range(nl)]
+        slot = [0]
 
         def call():
-            oracle.replay(st, a["replay_dA"], a["replay_u"], a["replay_B"], a["replay_dt"],
-                          a["accepted_lengths"], state_indices=a["state_indices"],
-                          active_batch=w.active_batch)
-        sample = "the full replay batch of this workload"
+            oracle.clear_layers(recs, convs, rows, slot[0] % rows, rec_rb, conv_rb)
+            slot[0] += 1
+        sample = f"{nl} of the {inputs_mod.STACK_LAYERS} layers per call"
+        scale = nl / inputs_mod.STACK_LAYERS
+    else:
+        st = a["state"].copy()
+        reps = 1 if kind == "replay" else 2
+        stacks = [st] + [st.copy() for _ in range(reps - 1)]
+
+        def call():
+            for s_ in stacks:
+                oracle.replay(s_, a["replay_dA"], a["replay_u"], a["replay_B"], a["replay_dt"],
+                              a["accepted_lengths"], state_indices=a["state_indices"],
+                              active_batch=w.active_batch)
+        if kind == "replay":
+            sample = "the full replay batch of this workload"
+        else:
+            sample = f"{reps} of the {inputs_mod.STACK_LAYERS} layers per call"
+            scale = reps / inputs_mod.STACK_LAYERS
     calls, t0 = 0, time.perf_counter()
     while True:
         call()
@@ -196,10 +222,10 @@ def cpu_baseline(kind, w, seconds, bytes_per_call, units_per_call):
         el = time.perf_counter() - t0
         if el >= seconds:
             break
-    gbs = bytes_per_call * calls / el / 1e9
+    gbs = bytes_per_call * scale * calls / el / 1e9
     return {"value": round(gbs, 4), "unit": "GB/s", "cores": oracle.num_threads(), "kind": "oracle",
             "sample": f"{sample}, {calls} call(s) in {el:.1f} s (fp64, OpenMP)",
-            "token_head_updates_per_s": units_per_call * calls / el}
+            "token_head_updates_per_s": units_per_call * scale * calls / el}
 
 
 def main():
@@ -207,7 +233,7 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=1000)
     ap.add_argument("--warmup", type=int, default=100)
-    ap.add_argument("--config", type=int, default=1, choices=[1, 2, 3, 4, 5])
+    ap.add_argument("--config", type=int, default=1, choices=[1, 2, 3, 4, 5, 6, 7])
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--prewarm-ms", type=float, default=300.0,
                     help="untimed launches before the warm-up steps, to reach steady clocks")
@@ -225,14 +251,20 @@ def main():
         sys.exit(2)
 
     import torch
-    from linear_rnn_recurrent_amd import (inputs, load_library, ssu_decode, ssu_prefill,
-                                          ssu_replay, ssu_tree_verify)
+    from linear_rnn_recurrent_amd import (ReplayLayerTable, StateLayerTable, inputs, load_library,
+                                          ssu_decode, ssu_prefill, ssu_replay,
+                                          ssu_replay_layers, ssu_state_clear_layers,
+                                          ssu_tree_verify)
 
     load_library()
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
-    w = inputs.config(args.config) if args.config != 5 else inputs.tree_config()
-    name = inputs.CONFIG_NAMES[args.config] if args.config != 5 else inputs.TREE_NAME
+    if args.config == 5:
+        w, name = inputs.tree_config(), inputs.TREE_NAME
+    elif args.config in (6, 7):
+        w, name = inputs.config(4), inputs.LAYERS_NAME[args.config]
+    else:
+        w, name = inputs.config(args.config), inputs.CONFIG_NAMES[args.config]
     T = {k: (None if v is None else v.to(dev)) for k, v in w.tensors.items()}
     stream = torch.cuda.current_stream(dev)
 
@@ -312,6 +344,47 @@ def main():
         kkey = "tree_config5"
         lane_ops = tree_lane_ops(T)
         bound, peak, unit = "mfma", MFMA_F32_PEAK_TFLOPS, "TFLOP/s"
+    elif args.config == 6:
+        kind = "replay_layers"
+        nl = inputs.STACK_LAYERS
+        acc = T["accepted_lengths"][: w.active_batch].cpu()
+        idx = T["state_indices"][: w.active_batch].cpu()
+        k_rows = [min(int(a), T["replay_dA"].shape[1]) if int(i) >= 0 else 0
+                  for a, i in zip(acc, idx)]
+        nbytes = nl * replay_bytes(T, k_rows)
+        units = nl * sum(k_rows) * T["replay_dA"].shape[2]
+        # every layer its own pool and stash (copies of the config-4 tensors)
+        table = ReplayLayerTable([T["state"].clone() for _ in range(nl)],
+                                 [T["replay_dA"].clone() for _ in range(nl)],
+                                 [T["replay_u"].clone() for _ in range(nl)],
+                                 [T["replay_B"].clone() for _ in range(nl)],
+                                 [T["replay_dt"].clone() for _ in range(nl)])
+        rot = f"one launch replays all {nl} layers ({nl} separate pools, 8 GB in all)"
+
+        def step(i):
+            ssu_replay_layers(table, T["accepted_lengths"], state_indices=T["state_indices"],
+                              active_batch=w.active_batch)
+        src = source_hash("ssu_replay.hip", "ssu_device.h")
+        kkey = "replay_layers_config6"
+        bound, peak, unit = "hbm", HBM_PEAK_GBS, "GB/s"
+    elif args.config == 7:
+        kind = "clear_layers"
+        nl = inputs.STACK_LAYERS
+        rows = T["state"].shape[0]
+        rec_rb = T["state"][0].numel() * T["state"].element_size()
+        conv_rb = inputs.STACK_CONV_ROW_BYTES
+        recs = [torch.ones_like(T["state"]) for _ in range(nl)]
+        convs = [torch.ones(rows * conv_rb, dtype=torch.uint8, device=dev) for _ in range(nl)]
+        table = StateLayerTable(recs, convs)
+        nbytes = nl * (rec_rb + conv_rb)
+        units = nl
+        rot = f"one launch clears one slot of all {nl} layers; steps rotate over the {rows} slots"
+
+        def step(i):
+            ssu_state_clear_layers(table, rows, i % rows, rec_rb, conv_rb)
+        src = source_hash("ssu_pool_kernels.hip", "ssu_device.h")
+        kkey = "clear_layers_config7"
+        bound, peak, unit = "hbm", HBM_PEAK_GBS, "GB/s"
     else:
         kind = "replay"
         acc = T["accepted_lengths"][: w.active_batch].cpu()

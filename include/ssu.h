@@ -9,7 +9,8 @@
  *          replay stash), struct MambaReplayLayerInfo (replay reconstruct),
  *          invokeMambaReplayReconstructBatched (acceptedNodeIds, maxAcceptLen),
  *          invokeSelectiveStateUpdateDDTree (tree verify),
- *          invokeMambaStateClear (slot clear, slot -1 = all).
+ *          struct MambaStateLayerInfo, invokeMambaStateClear (slot clear,
+ *          slot -1 = all, every layer in one launch).
  *   [PAD]  FlashInfer, "flashinfer.gdn_fused_decode_step" page, parameters
  *          ssm_state (paged pool, padded row stride) and state_indices
  *          (negative index = padding row; index >= rows is a caller bug).
@@ -174,6 +175,51 @@ ssu_status ssu_tree_verify(const ssu_dims *dims, int32_t num_nodes, const void *
                            const int32_t *state_indices, const int32_t *parent_ids,
                            const int32_t *depths, float *replay_dA, float *replay_u,
                            float *replay_B, float *replay_dt, hipStream_t stream);
+
+/* One layer's buffers for ssu_replay_layers [SSU MambaReplayLayerInfo:
+ * stateDst, replayDa, replayU, replayB, replayDt]. Layouts and alignment as
+ * for ssu_replay; every layer shares the geometry in ssu_dims. */
+typedef struct ssu_replay_layer {
+    void *state;             /* [pool_rows, nheads, dim, dstate] state_dtype, in place */
+    const float *replay_dA;  /* [dims->batch, seq_len, nheads] */
+    const float *replay_u;   /* [dims->batch, seq_len, nheads, dim] */
+    const float *replay_B;   /* [dims->batch, seq_len, ngroups, dstate] */
+    const float *replay_dt;  /* [dims->batch, seq_len, nheads] */
+} ssu_replay_layer;
+
+/* ssu_replay_layers -- ssu_replay for num_layers layers in one launch
+ * [SSU invokeMambaReplayReconstructBatched]. `layers` is a DEVICE array of
+ * num_layers entries (the caller uploads it once and keeps it while calls that
+ * use it are in flight); accepted_lengths, state_indices, accepted_node_ids
+ * and active_batch are shared by every layer, exactly as in ssu_replay. The
+ * pointers inside `layers` are not validated on the host: each must be
+ * non-null and aligned as ssu_replay requires (undefined behaviour otherwise).
+ * num_layers >= 0 (0: nothing to do). */
+ssu_status ssu_replay_layers(const ssu_dims *dims, int32_t seq_len, const ssu_replay_layer *layers,
+                             int32_t num_layers, const int32_t *accepted_lengths,
+                             const int32_t *state_indices, int32_t active_batch,
+                             const int32_t *accepted_node_ids, int32_t max_accept_len,
+                             hipStream_t stream);
+
+/* One layer's persistent states for ssu_state_clear_layers [SSU
+ * MambaStateLayerInfo: recurrentState, convState]. Either may be NULL (that
+ * buffer is skipped). */
+typedef struct ssu_state_layer {
+    void *recurrent_state; /* resident_rows rows of recurrent_row_bytes bytes */
+    void *conv_state;      /* resident_rows rows of conv_row_bytes bytes */
+} ssu_state_layer;
+
+/* ssu_state_clear_layers -- zero resident row `slot` of both states of every
+ * layer, or every row when slot == -1, in one launch [SSU
+ * invokeMambaStateClear]. `layers` is a DEVICE array of num_layers entries.
+ * Row bytes may be any non-negative count (0: that state is skipped); no
+ * alignment is required. SSU_EINVAL unless num_layers >= 0, resident_rows >= 0,
+ * -1 <= slot < resident_rows (slot -1 allowed with resident_rows == 0) and the
+ * row byte counts are >= 0. */
+ssu_status ssu_state_clear_layers(const ssu_state_layer *layers, int32_t num_layers,
+                                  int32_t resident_rows, int32_t slot,
+                                  int64_t recurrent_row_bytes, int64_t conv_row_bytes,
+                                  hipStream_t stream);
 
 /* ------------------------------------------------------------------------
  * Recurrent-state pool [RSM]: one zeroed, contiguous slab per state spec,

@@ -5,8 +5,10 @@ Instinct MI355X.
 The compute lives in libssu.so (C ABI declared in include/ssu.h); this package
 only marshals torch GPU tensors into those calls.
 """
-from .ssu import (SsuError, SsuPool, DeviceArray, load_library, ssu_decode, ssu_prefill,
-                  ssu_replay, ssu_tree_verify, LIB_PATH, EXPORTS)
+from .ssu import (SsuError, SsuPool, DeviceArray, ReplayLayerTable, StateLayerTable,
+                  load_library, ssu_decode, ssu_prefill, ssu_replay, ssu_tree_verify,
+                  ssu_replay_layers, ssu_state_clear_layers, LIB_PATH, EXPORTS)
 
-__all__ = ["SsuError", "SsuPool", "DeviceArray", "load_library", "ssu_decode", "ssu_prefill",
-           "ssu_replay", "ssu_tree_verify", "LIB_PATH", "EXPORTS"]
+__all__ = ["SsuError", "SsuPool", "DeviceArray", "ReplayLayerTable", "StateLayerTable",
+           "load_library", "ssu_decode", "ssu_prefill", "ssu_replay", "ssu_tree_verify",
+           "ssu_replay_layers", "ssu_state_clear_layers", "LIB_PATH", "EXPORTS"]

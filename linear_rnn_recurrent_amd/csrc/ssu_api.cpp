@@ -307,6 +307,77 @@ ssu_status ssu_replay(const ssu_dims *dims, int32_t seq_len, void *state,
     return hip_status(ssu::launch_replay(p, stream), "ssu_replay launch");
 }
 
+ssu_status ssu_replay_layers(const ssu_dims *dims, int32_t seq_len, const ssu_replay_layer *layers,
+                             int32_t num_layers, const int32_t *accepted_lengths,
+                             const int32_t *state_indices, int32_t active_batch,
+                             const int32_t *accepted_node_ids, int32_t max_accept_len,
+                             hipStream_t stream)
+{
+    const char *fn = "ssu_replay_layers";
+    ssu::DecodeParams d = {};
+    const ssu_status st = check_dims(dims, fn, false, state_indices != nullptr, &d);
+    if (st != SSU_OK)
+        return st;
+    if (seq_len < 0)
+        return fail(SSU_EINVAL, "%s: seq_len %d < 0", fn, seq_len);
+    if (num_layers < 0 || num_layers > 65535)
+        return fail(SSU_EINVAL, "%s: num_layers %d outside [0, 65535]", fn, num_layers);
+    if (active_batch < 0 || active_batch > d.batch)
+        return fail(SSU_EINVAL, "%s: active_batch %d outside [0, batch %d]", fn, active_batch,
+                    d.batch);
+    if (!state_indices && active_batch > dims->pool_rows)
+        return fail(SSU_EINVAL, "%s: active_batch %d > pool_rows %d with no state_indices", fn,
+                    active_batch, dims->pool_rows);
+    if (accepted_node_ids && max_accept_len < 1)
+        return fail(SSU_EINVAL, "%s: max_accept_len %d < 1 with accepted_node_ids", fn,
+                    max_accept_len);
+    if (num_layers == 0 || active_batch == 0 || seq_len == 0)
+        return ok();
+    SSU_REQUIRE_PTR(layers, alignof(ssu_replay_layer), fn);
+    SSU_REQUIRE_PTR(accepted_lengths, 4, fn);
+    SSU_OPTIONAL_PTR(state_indices, 4, fn);
+    SSU_OPTIONAL_PTR(accepted_node_ids, 4, fn);
+    ssu::ReplayParams p = {};
+    p.layers = layers;
+    p.num_layers = num_layers;
+    p.accepted = accepted_lengths;
+    p.idx = state_indices;
+    p.row_stride = d.row_stride;
+    p.active_batch = active_batch;
+    p.seq_len = seq_len;
+    p.nheads = d.nheads;
+    p.dim = d.dim;
+    p.dstate = d.dstate;
+    p.ngroups = d.ngroups;
+    p.state_dtype = d.state_dtype;
+    p.node_ids = accepted_node_ids;
+    p.max_accept_len = accepted_node_ids ? max_accept_len : 0;
+    return hip_status(ssu::launch_replay(p, stream), "ssu_replay_layers launch");
+}
+
+ssu_status ssu_state_clear_layers(const ssu_state_layer *layers, int32_t num_layers,
+                                  int32_t resident_rows, int32_t slot,
+                                  int64_t recurrent_row_bytes, int64_t conv_row_bytes,
+                                  hipStream_t stream)
+{
+    const char *fn = "ssu_state_clear_layers";
+    if (num_layers < 0 || num_layers > 65535)
+        return fail(SSU_EINVAL, "%s: num_layers %d outside [0, 65535]", fn, num_layers);
+    if (resident_rows < 0)
+        return fail(SSU_EINVAL, "%s: resident_rows %d < 0", fn, resident_rows);
+    if (slot < -1 || (slot >= 0 && slot >= resident_rows))
+        return fail(SSU_EINVAL, "%s: slot %d outside [-1, %d)", fn, slot, resident_rows);
+    if (recurrent_row_bytes < 0 || conv_row_bytes < 0)
+        return fail(SSU_EINVAL, "%s: row byte counts must be >= 0 (got %lld, %lld)", fn,
+                    (long long)recurrent_row_bytes, (long long)conv_row_bytes);
+    if (num_layers == 0 || resident_rows == 0)
+        return ok();
+    SSU_REQUIRE_PTR(layers, alignof(ssu_state_layer), fn);
+    return hip_status(ssu::launch_clear_layers(layers, num_layers, resident_rows, slot,
+                                               recurrent_row_bytes, conv_row_bytes, stream),
+                      "ssu_state_clear_layers launch");
+}
+
 ssu_status ssu_tree_verify(const ssu_dims *dims, int32_t num_nodes, const void *x,
                            const float *A, const void *B, const void *C, const float *dt,
                            const float *dt_bias, const float *D, const void *z,

@@ -40,6 +40,8 @@ struct PrefillParams {
 struct ReplayParams {
     void *state;
     const float *dA, *u, *B, *dt;
+    const ssu_replay_layer *layers;  // device array; when set, the five pointers above are unused
+    int32_t num_layers;
     const int32_t *accepted;
     const int32_t *idx;
     const int32_t *node_ids;  // null: token t is stash position t
@@ -73,6 +75,9 @@ hipError_t launch_prefill_f16(const PrefillParams &p, hipStream_t stream);
 hipError_t launch_prefill_bf16(const PrefillParams &p, hipStream_t stream);
 hipError_t launch_replay(const ReplayParams &p, hipStream_t stream);
 hipError_t launch_tree(const TreeParams &p, hipStream_t stream);
+// Zeroes row `slot` (or all rows, slot -1) of both states of every layer.
+hipError_t launch_clear_layers(const ssu_state_layer *layers, int num_layers, int rows, int slot,
+                               int64_t rec_row_bytes, int64_t conv_row_bytes, hipStream_t stream);
 hipError_t launch_tree_f32(const TreeParams &p, hipStream_t stream);
 hipError_t launch_tree_f16(const TreeParams &p, hipStream_t stream);
 hipError_t launch_tree_bf16(const TreeParams &p, hipStream_t stream);

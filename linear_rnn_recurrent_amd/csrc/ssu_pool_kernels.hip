@@ -39,7 +39,64 @@ __global__ __launch_bounds__(256) void ssu_segments_kernel(const SegBatch sb)
         d[i] = s ? s[i] : (uint8_t)0;
 }
 
+// invokeMambaStateClear ("Selective State Update" page): zero row `slot` (or
+// every row, slot -1) of the recurrent (blockIdx.z == 0) and conv (== 1) state
+// of layer blockIdx.y, whose pointers come from a device array of
+// MambaStateLayerInfo-like entries. Any alignment: bytes up to the first
+// 16-byte boundary, then 16-byte stores, then the tail bytes.
+__global__ __launch_bounds__(256) void ssu_clear_layers_kernel(const ssu_state_layer *layers,
+                                                               int rows, int slot,
+                                                               int64_t rec_row_bytes,
+                                                               int64_t conv_row_bytes)
+{
+    const ssu_state_layer ly = layers[blockIdx.y];
+    uint8_t *base = static_cast<uint8_t *>(blockIdx.z ? ly.conv_state : ly.recurrent_state);
+    const uint64_t rb = (uint64_t)(blockIdx.z ? conv_row_bytes : rec_row_bytes);
+    if (base == nullptr || rb == 0)
+        return;
+    uint8_t *d = base + (slot >= 0 ? (uint64_t)slot * rb : 0);
+    const uint64_t n = slot >= 0 ? rb : (uint64_t)rows * rb;
+    const uint64_t mis = (uint64_t)((16 - ((uintptr_t)d & 15)) & 15);
+    const uint64_t head = mis < n ? mis : n;
+    const uint64_t body = (n - head) / 16;
+    const uint64_t first = (uint64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    const uint64_t step = (uint64_t)gridDim.x * blockDim.x;
+    if (first < head)
+        d[first] = 0;
+    // four 16-byte stores per thread per pass, a workgroup's lanes side by side
+    u32x4 *d4 = reinterpret_cast<u32x4 *>(d + head);
+    const uint64_t b0 = (uint64_t)blockIdx.x * blockDim.x * 4 + threadIdx.x;
+    const uint64_t bstep = (uint64_t)gridDim.x * blockDim.x * 4;
+    for (uint64_t i = b0; i < body; i += bstep) {
+#pragma unroll
+        for (int k = 0; k < 4; ++k)
+            if (i + (uint64_t)k * blockDim.x < body)
+                __builtin_nontemporal_store(u32x4{0u, 0u, 0u, 0u}, &d4[i + (uint64_t)k * blockDim.x]);
+    }
+    for (uint64_t i = head + body * 16 + first; i < n; i += step)
+        d[i] = 0;
+}
+
 }  // namespace
+
+hipError_t launch_clear_layers(const ssu_state_layer *layers, int num_layers, int rows, int slot,
+                               int64_t rec_row_bytes, int64_t conv_row_bytes, hipStream_t stream)
+{
+    if (num_layers == 0 || rows == 0)
+        return hipSuccess;
+    if (num_layers > 65535)
+        return hipErrorInvalidConfiguration;
+    const uint64_t rb = (uint64_t)(rec_row_bytes > conv_row_bytes ? rec_row_bytes : conv_row_bytes);
+    const uint64_t maxb = slot >= 0 ? rb : (uint64_t)rows * rb;
+    if (maxb == 0)
+        return hipSuccess;
+    uint64_t blocks = (maxb / 16 + 1023) / 1024;  // 256 threads x 4 vectors each
+    blocks = blocks < 1 ? 1 : (blocks > 2048 ? 2048 : blocks);
+    (void)hipGetLastError();
+    hipLaunchKernelGGL(ssu_clear_layers_kernel, dim3((unsigned)blocks, (unsigned)num_layers, 2),
+                       dim3(256), 0, stream, layers, rows, slot, rec_row_bytes, conv_row_bytes);
+    return hipGetLastError();
+}
 
 hipError_t launch_segments(const Segment *segs, int n, hipStream_t stream)
 {

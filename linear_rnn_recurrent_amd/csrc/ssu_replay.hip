@@ -9,6 +9,9 @@
 // acceptedNodeIds (invokeMambaReplayReconstructBatched) token t of row b is the
 // stash entry of node acceptedNodeIds[b, t]; the count is capped at
 // maxAcceptLen and the row ends before the first id outside the stash.
+// invokeMambaReplayReconstructBatched runs every layer in one launch: the layer
+// is blockIdx.y and its buffers come from a device array of
+// MambaReplayLayerInfo-like entries.
 //
 // Mapping on gfx950: the decode mapping (the (batch row, head) tile split over
 // workgroups of about 8 KiB of state; lanes along dstate with 16-byte vectors;
@@ -36,8 +39,17 @@ __global__ __launch_bounds__(256) void ssu_replay_kernel(
     ST *__restrict__ state, const float *__restrict__ sdA, const float *__restrict__ su,
     const float *__restrict__ sB, const float *__restrict__ sdt,
     const int32_t *__restrict__ accepted, const int32_t *__restrict__ idx,
-    const int32_t *__restrict__ node_ids, const ReplayShape sh)
+    const int32_t *__restrict__ node_ids, const ssu_replay_layer *__restrict__ layers,
+    const ReplayShape sh)
 {
+    if (layers) {  // batched over layers: this workgroup's layer is blockIdx.y
+        const ssu_replay_layer &ly = layers[blockIdx.y];
+        state = static_cast<ST *>(ly.state);
+        sdA = ly.replay_dA;
+        su = ly.replay_u;
+        sB = ly.replay_B;
+        sdt = ly.replay_dt;
+    }
     constexpr int VEC = SV<ST>::VEC;
     constexpr int LPR = NS / VEC;
     constexpr int RPW = 64 / LPR;
@@ -170,12 +182,14 @@ hipError_t launch_ns(const ReplayParams &p, hipStream_t stream)
     const int64_t blocks = (int64_t)p.active_batch * p.nheads * sh.parts;
     if (blocks > 0x7fffffff)
         return hipErrorInvalidConfiguration;
-    const dim3 grid((unsigned)blocks);
+    if (p.layers && (p.num_layers <= 0 || p.num_layers > 65535))
+        return hipErrorInvalidConfiguration;
+    const dim3 grid((unsigned)blocks, p.layers ? (unsigned)p.num_layers : 1u);
     ST *st = static_cast<ST *>(p.state);
     (void)hipGetLastError();
 #define SSU_LAUNCH_REPLAY(PS, MT, ID)                                                         \
     hipLaunchKernelGGL((ssu_replay_kernel<ST, NS, PS, MT, ID>), grid, dim3(256), 0, stream, st, \
-                       p.dA, p.u, p.B, p.dt, p.accepted, p.idx, p.node_ids, sh)
+                       p.dA, p.u, p.B, p.dt, p.accepted, p.idx, p.node_ids, p.layers, sh)
 #define SSU_LAUNCH_REPLAY_T(PS)           \
     if (p.node_ids) {                     \
         if (p.max_accept_len <= 4)        \

@@ -300,6 +300,17 @@ def config(i: int, seed: Optional[int] = None) -> Workload:
     raise ValueError(f"no configuration {i}")
 
 
+# A Mamba2-2.7B-shaped layer stack for the layer-batched calls: 64 layers, and a
+# conv-state row of (d_inner + 2 ngroups dstate) channels x (d_conv - 1) taps in bf16.
+STACK_LAYERS = 64
+STACK_CONV_ROW_BYTES = (5120 + 2 * 128) * 3 * 2
+LAYERS_NAME = {
+    6: "MTP replay of the config-4 batch (active32/48 T4 H80 Dm64 N128 G1, fp32) on each of "
+       "64 layers, one launch",
+    7: "clear of one resident slot of 64 layers (fp32 recurrent rows H80 Dm64 N128 + bf16 conv "
+       "rows 5376 x 3), one launch",
+}
+
 TREE_NAME = ("tree verify B16 M128 (random draft tree, depth < 16) H80 Dm64 N128 G1, "
              "fp32 pool P64")
 

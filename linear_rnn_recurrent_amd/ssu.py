@@ -20,7 +20,8 @@ SSU_F32, SSU_F16, SSU_BF16, SSU_U8 = 0, 1, 2, 3
 _DT = {torch.float32: SSU_F32, torch.float16: SSU_F16, torch.bfloat16: SSU_BF16,
        torch.uint8: SSU_U8}
 
-EXPORTS = ("ssu_decode", "ssu_prefill", "ssu_replay", "ssu_tree_verify", "ssu_pool_bytes_per_slot",
+EXPORTS = ("ssu_decode", "ssu_prefill", "ssu_replay", "ssu_tree_verify", "ssu_replay_layers",
+           "ssu_state_clear_layers", "ssu_pool_bytes_per_slot",
            "ssu_pool_alloc", "ssu_pool_free", "ssu_pool_info", "ssu_pool_state_ptr",
            "ssu_pool_state_bytes_per_slot", "ssu_pool_find_state", "ssu_pool_clear",
            "ssu_pool_clear_slot", "ssu_pool_capture", "ssu_pool_restore",
@@ -39,6 +40,16 @@ class ssu_dims(ctypes.Structure):
                 ("pool_rows", ctypes.c_int32), ("state_row_stride", ctypes.c_int64),
                 ("state_dtype", ctypes.c_int32), ("io_dtype", ctypes.c_int32),
                 ("bc_dtype", ctypes.c_int32), ("reserved", ctypes.c_int32)]
+
+
+class ssu_replay_layer(ctypes.Structure):
+    _fields_ = [("state", ctypes.c_void_p), ("replay_dA", ctypes.c_void_p),
+                ("replay_u", ctypes.c_void_p), ("replay_B", ctypes.c_void_p),
+                ("replay_dt", ctypes.c_void_p)]
+
+
+class ssu_state_layer(ctypes.Structure):
+    _fields_ = [("recurrent_state", ctypes.c_void_p), ("conv_state", ctypes.c_void_p)]
 
 
 class ssu_state_spec(ctypes.Structure):
@@ -70,6 +81,8 @@ def load_library(path: Optional[str] = None):
         "ssu_replay": [D, _I32, _P, _P, _P, _P, _P, _P, _P, _I32, _P, _I32, _P],
         "ssu_tree_verify": [D, _I32, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _I32, _P, _P, _P,
                             _P, _P, _P, _P, _P],
+        "ssu_replay_layers": [D, _I32, _P, _I32, _P, _P, _I32, _P, _I32, _P],
+        "ssu_state_clear_layers": [_P, _I32, _I32, _I32, ctypes.c_int64, ctypes.c_int64, _P],
         "ssu_pool_bytes_per_slot": [S, _I32, ctypes.POINTER(ctypes.c_size_t)],
         "ssu_pool_alloc": [S, _I32, _I32, _P, ctypes.POINTER(_P)],
         "ssu_pool_free": [_P],
@@ -334,6 +347,100 @@ def ssu_tree_verify(x, A, B, C, dt, state, out, parent_ids, *, depths=None, dt_b
                                    _ptr(state_indices), _ptr(parent_ids), _ptr(depths),
                                    *[_ptr(s) for s in stash], _stream(x.device, stream)))
     return out
+
+
+def _device_table(structs, device):
+    """Pack ctypes structs into one device buffer (a uint8 tensor)."""
+    n = len(structs)
+    size = ctypes.sizeof(structs[0]) if n else 0
+    raw = bytearray(size * n)
+    for i, st in enumerate(structs):
+        ctypes.memmove((ctypes.c_char * size).from_buffer(raw, i * size), ctypes.addressof(st), size)
+    host = torch.frombuffer(raw, dtype=torch.uint8) if n else torch.empty(0, dtype=torch.uint8)
+    return host.to(device)
+
+
+class ReplayLayerTable:
+    """Device array of per-layer replay buffers for ssu_replay_layers.
+
+    states[i] [rows, nheads, dim, dstate]; dAs[i], dts[i] [batch, seq_len, nheads];
+    us[i] [batch, seq_len, nheads, dim]; Bs[i] [batch, seq_len, ngroups, dstate] (fp32).
+    Every layer has the same shapes and dtypes. Keeps the tensors alive."""
+
+    def __init__(self, states, dAs, us, Bs, dts):
+        n = len(states)
+        _need(n > 0 and all(len(v) == n for v in (dAs, us, Bs, dts)), "one entry per layer")
+        s0, a0, u0, b0 = states[0], dAs[0], us[0], Bs[0]
+        for i in range(n):
+            _need(states[i].dtype == s0.dtype and states[i].shape == s0.shape and
+                  states[i].stride() == s0.stride(), "every layer's state has the same geometry")
+            _dense(dAs[i], "replay_dA", (torch.float32,), a0.shape)
+            _dense(dts[i], "replay_dt", (torch.float32,), a0.shape)
+            _dense(us[i], "replay_u", (torch.float32,), u0.shape)
+            _dense(Bs[i], "replay_B", (torch.float32,), b0.shape)
+        _need(a0.dim() == 3 and u0.dim() == 4 and b0.dim() == 4, "stash shapes")
+        self.batch, self.seq_len, self.nheads = a0.shape
+        self.dim = u0.shape[3]
+        self.ngroups, self.dstate = b0.shape[2], b0.shape[3]
+        self.rows, self.stride = _state_geometry(s0, self.nheads, self.dim, self.dstate)
+        self.state_dtype = s0.dtype
+        self.keep = (states, dAs, us, Bs, dts)
+        self.num_layers = n
+        self.device = s0.device
+        self.table = _device_table([ssu_replay_layer(states[i].data_ptr(), dAs[i].data_ptr(),
+                                                     us[i].data_ptr(), Bs[i].data_ptr(),
+                                                     dts[i].data_ptr()) for i in range(n)],
+                                   self.device)
+
+
+def ssu_replay_layers(table: ReplayLayerTable, accepted_lengths, *, state_indices=None,
+                      active_batch=None, accepted_node_ids=None, stream=None):
+    """ssu_replay for every layer of `table` in one launch (shared accepted
+    lengths, state indices and node ids)."""
+    lib = load_library()
+    _dense(accepted_lengths, "accepted_lengths", (torch.int32,), (table.batch,))
+    _opt_idx(state_indices, "state_indices", table.batch)
+    max_accept = 0
+    if accepted_node_ids is not None:
+        _dense(accepted_node_ids, "accepted_node_ids", (torch.int32,))
+        _need(accepted_node_ids.dim() == 2 and accepted_node_ids.shape[0] == table.batch,
+              "accepted_node_ids must be [batch, max_accept_len]")
+        max_accept = accepted_node_ids.shape[1]
+    if active_batch is None:
+        active_batch = table.batch
+    d = _dims(table.batch, table.nheads, table.dim, table.dstate, table.ngroups, table.rows,
+              table.stride, table.state_dtype, torch.float32, torch.float32)
+    with torch.cuda.device(table.device):
+        _check(lib.ssu_replay_layers(ctypes.byref(d), table.seq_len, _ptr(table.table),
+                                     table.num_layers, _ptr(accepted_lengths),
+                                     _ptr(state_indices), int(active_batch),
+                                     _ptr(accepted_node_ids), int(max_accept),
+                                     _stream(table.device, stream)))
+
+
+class StateLayerTable:
+    """Device array of per-layer {recurrent, conv} state buffers for
+    ssu_state_clear_layers. Entries may be None (that buffer is skipped)."""
+
+    def __init__(self, recurrent, conv):
+        _need(len(recurrent) == len(conv) and len(recurrent) > 0, "one entry per layer")
+        self.keep = (recurrent, conv)
+        self.num_layers = len(recurrent)
+        dev = next(t.device for t in list(recurrent) + list(conv) if t is not None)
+        self.device = dev
+        self.table = _device_table([ssu_state_layer(0 if r is None else r.data_ptr(),
+                                                    0 if c is None else c.data_ptr())
+                                    for r, c in zip(recurrent, conv)], dev)
+
+
+def ssu_state_clear_layers(table: StateLayerTable, resident_rows, slot, recurrent_row_bytes,
+                           conv_row_bytes, stream=None):
+    """Zero row `slot` (or every row, slot -1) of both states of every layer."""
+    lib = load_library()
+    with torch.cuda.device(table.device):
+        _check(lib.ssu_state_clear_layers(_ptr(table.table), table.num_layers, int(resident_rows),
+                                          int(slot), int(recurrent_row_bytes),
+                                          int(conv_row_bytes), _stream(table.device, stream)))
 
 
 # ---------------------------------------------------------------------------

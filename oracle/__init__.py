@@ -13,6 +13,8 @@ shape list; invokeSelectiveStateUpdatePrefill; MambaReplayLayerInfo):
   replay : dA,DT [b,t,h]  u [b,t,h,d]  Bst [b,t,g,n]  node_ids [b, max_accept_len]
   tree   : prefill layouts with the node axis in place of t; parent_ids and
            depths [b, num_nodes] (invokeSelectiveStateUpdateDDTree)
+  layers : lists of per-layer states / stashes (invokeMambaReplayReconstructBatched,
+           invokeMambaStateClear)
   state  : [rows, h, d, n], or a flat buffer with `row_stride` elements per row
 
 `state`, `out` and the stash arrays are updated in place.
@@ -134,6 +136,34 @@ def replay(state, dA, u, Bst, DT, accepted_lengths, *, state_indices=None,
     max_accept = 0 if node_ids is None else ni[0].shape[1]
     _lib().oracle_ssu_replay(active_batch, seq_len, nheads, dim, dstate, ngroups, rs,
                              st[1], *[k[1] for k in keep], ac[1], ix[1], ni[1], max_accept)
+
+
+def replay_layers(states, stashes, accepted_lengths, *, state_indices=None, active_batch=None,
+                  node_ids=None, row_stride=None):
+    """Replay of every layer (TensorRT-Edge-LLM "Selective State Update" page,
+    invokeMambaReplayReconstructBatched: the MambaReplayLayerInfo replay for each of
+    numLayers layers, with acceptedLengths, stateIndices, activeBatchSize and
+    acceptedNodeIds shared by all layers). states[i] is updated in place; stashes[i]
+    is a dict with 'dA', 'u', 'B', 'dt'."""
+    for st, S in zip(states, stashes):
+        replay(st, S["dA"], S["u"], S["B"], S["dt"], accepted_lengths,
+               state_indices=state_indices, active_batch=active_batch, row_stride=row_stride,
+               node_ids=node_ids)
+
+
+def clear_layers(recurrent, conv, resident_rows, slot, recurrent_row_bytes, conv_row_bytes):
+    """Zero resident row `slot`, or every row when slot == -1, of the recurrent and
+    the conv state of every layer (same page, MambaStateLayerInfo and
+    invokeMambaStateClear). Buffers are uint8 arrays of resident_rows rows of the
+    given byte count (None: absent); updated in place."""
+    for bufs, rb in ((recurrent, recurrent_row_bytes), (conv, conv_row_bytes)):
+        for buf in bufs:
+            if buf is None or rb == 0:
+                continue
+            if slot == -1:
+                buf[: resident_rows * rb] = 0
+            else:
+                buf[slot * rb:(slot + 1) * rb] = 0
 
 
 MAX_NODES = 128

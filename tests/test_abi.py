@@ -282,3 +282,32 @@ def test_null_pool_arguments(lib):
 def test_python_binding_fails_loudly_without_library(tmp_path):
     with pytest.raises(RuntimeError, match="not found"):
         S.load_library(str(tmp_path / "missing.so"))
+
+
+def test_replay_layers_validation(lib):
+    def call(d, num_layers=3, active=2, layers=FAKE, acc=FAKE, ids=None, max_accept=0, seq_len=4):
+        return lib.ssu_replay_layers(ctypes.byref(d), seq_len, layers, num_layers, acc, None,
+                                     active, ids, max_accept, None)
+    assert call(dims(), num_layers=-1) == 1 and "num_layers" in err(lib)
+    assert call(dims(), num_layers=70000) == 1 and "num_layers" in err(lib)
+    assert call(dims(), active=3) == 1 and "active_batch" in err(lib)
+    assert call(dims(), ids=FAKE, max_accept=0) == 1 and "max_accept_len" in err(lib)
+    assert call(dims(), num_layers=0, layers=None) == 0 and err(lib) == ""
+    assert call(dims(), seq_len=0, layers=None) == 0
+    assert call(dims(), layers=None) == 1 and "'layers'" in err(lib)
+    assert call(dims(), layers=FAKE + 4) == 1 and "aligned" in err(lib)
+    assert call(dims(), acc=None) == 1 and "'accepted_lengths'" in err(lib)
+    assert call(dims(dstate=48)) == 2
+
+
+def test_state_clear_layers_validation(lib):
+    def call(num_layers=2, rows=4, slot=1, rb=64, cb=10, layers=FAKE):
+        return lib.ssu_state_clear_layers(layers, num_layers, rows, slot, rb, cb, None)
+    assert call(num_layers=-1) == 1 and "num_layers" in err(lib)
+    assert call(rows=-1) == 1 and "resident_rows" in err(lib)
+    assert call(slot=4) == 1 and "slot" in err(lib)
+    assert call(slot=-2) == 1 and "slot" in err(lib)
+    assert call(rb=-1) == 1 and "row byte" in err(lib)
+    assert call(layers=None) == 1 and "'layers'" in err(lib)
+    assert call(num_layers=0, layers=None) == 0
+    assert call(rows=0, slot=-1, layers=None) == 0

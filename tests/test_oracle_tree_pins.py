@@ -240,3 +240,39 @@ def test_bruteforce_against_pure_python(seed, shape, opts):
         r.append([out] + [S[k] for k in ("dA", "u", "B", "dt")])
     for x, y in zip(*r):
         np.testing.assert_allclose(x, y, rtol=1e-12, atol=1e-13)
+
+
+# ---------------------------------------------------------------------------
+# Layer-batched replay and clear (invokeMambaReplayReconstructBatched,
+# invokeMambaStateClear)
+# ---------------------------------------------------------------------------
+
+def test_clear_layers_hand_case():
+    """3 resident rows; recurrent rows of 8 bytes, conv rows of 5; layer 1 has no conv."""
+    rec = [np.arange(1, 25, dtype=np.uint8), np.arange(101, 125, dtype=np.uint8)]
+    conv = [np.arange(201, 216, dtype=np.uint8), None]
+    oracle.clear_layers(rec, conv, 3, 1, 8, 5)
+    for r0 in rec:
+        assert np.all(r0[8:16] == 0) and np.all(r0[:8] != 0) and np.all(r0[16:] != 0)
+    assert np.all(conv[0][5:10] == 0) and np.all(conv[0][:5] == np.arange(201, 206))
+    assert np.all(conv[0][10:] == np.arange(211, 216))
+    oracle.clear_layers(rec, conv, 3, -1, 8, 5)
+    assert all(np.all(r0 == 0) for r0 in rec) and np.all(conv[0] == 0)
+
+
+def test_replay_layers_is_one_replay_per_layer():
+    ws = [inputs.replay_workload(active_batch=3, seq_len=4, nheads=2, dim=3, dstate=4, ngroups=1,
+                                 pool_rows=4, seed=60 + i, accepted=[4, 1, 0],
+                                 indices=[2, 0, 3]) for i in range(3)]
+    arrs = [_np(w) for w in ws]
+    acc = arrs[0]["accepted_lengths"]
+    idx = arrs[0]["state_indices"]
+    states = [a["state"].copy() for a in arrs]
+    stashes = [{"dA": a["replay_dA"], "u": a["replay_u"], "B": a["replay_B"], "dt": a["replay_dt"]}
+               for a in arrs]
+    oracle.replay_layers(states, stashes, acc, state_indices=idx)
+    for a, st in zip(arrs, states):
+        want = a["state"].copy()
+        ref_tiny.replay(want, a["replay_dA"], a["replay_u"], a["replay_B"], a["replay_dt"], acc,
+                        state_indices=idx)
+        np.testing.assert_allclose(st, want, rtol=1e-13, atol=1e-13)
