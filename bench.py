@@ -8,13 +8,14 @@ four disjoint 64-row index sets that together cover the pool, so every step
 streams state rows the previous three steps did not touch and the 256 MB
 last-level cache cannot serve them.
 
-    python bench.py [--steps K] [--warmup W] [--config {1,2,3,4,5,6,7}]
+    python bench.py [--steps K] [--warmup W] [--config {1,2,3,4,5,6,7,8}]
 
 --config 2/3/4/5 time prefill / padded decode / MTP replay / tree verify
 (16 requests with 128-node draft trees, replay stash on) instead; 6 and 7 the
 layer-batched calls over a 64-layer stack: the MTP replay of config 4 for every
 layer in one launch, and the clear of one resident slot (recurrent and conv
-rows) of every layer in one launch. Their pools
+rows) of every layer in one launch; 8 the gather of the config-1 batch's 64 pool
+rows into a contiguous active batch. Their pools
 are smaller than the last-level cache, so the steps rotate over replicas of
 the pool (and, for prefill, of every input) that together exceed it; every
 configuration is timed as back-to-back launches on one stream.
@@ -186,6 +187,13 @@ def cpu_baseline(kind, w, seconds, bytes_per_call, units_per_call):
                         depths=a["depths"], dt_bias=a["dt_bias"], D=a["D"], z=a["z"],
                         dt_softplus=w.dt_softplus, state_indices=a["state_indices"], stash=S)
         sample = "the full tree batch of this workload"
+    elif kind == "gather":
+        idx = a["state_indices"]
+        pool = a["state"]
+
+        def call():
+            oracle.gather(pool, idx)
+        sample = "the full 64-row gather of this workload"
     elif kind == "clear_layers":
         nl = 4
         rows = a["state"].shape[0]
@@ -233,7 +241,7 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=1000)
     ap.add_argument("--warmup", type=int, default=100)
-    ap.add_argument("--config", type=int, default=1, choices=[1, 2, 3, 4, 5, 6, 7])
+    ap.add_argument("--config", type=int, default=1, choices=[1, 2, 3, 4, 5, 6, 7, 8])
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--prewarm-ms", type=float, default=300.0,
                     help="untimed launches before the warm-up steps, to reach steady clocks")
@@ -254,7 +262,7 @@ def main():
     from linear_rnn_recurrent_amd import (ReplayLayerTable, StateLayerTable, inputs, load_library,
                                           ssu_decode, ssu_prefill, ssu_replay,
                                           ssu_replay_layers, ssu_state_clear_layers,
-                                          ssu_tree_verify)
+                                          ssu_state_gather, ssu_tree_verify)
 
     load_library()
     dev = torch.device("cuda:0")
@@ -263,6 +271,8 @@ def main():
         w, name = inputs.tree_config(), inputs.TREE_NAME
     elif args.config in (6, 7):
         w, name = inputs.config(4), inputs.LAYERS_NAME[args.config]
+    elif args.config == 8:
+        w, name = inputs.config(1), inputs.GATHER_NAME
     else:
         w, name = inputs.config(args.config), inputs.CONFIG_NAMES[args.config]
     T = {k: (None if v is None else v.to(dev)) for k, v in w.tensors.items()}
@@ -384,6 +394,21 @@ def main():
             ssu_state_clear_layers(table, rows, i % rows, rec_rb, conv_rb)
         src = source_hash("ssu_pool_kernels.hip", "ssu_device.h")
         kkey = "clear_layers_config7"
+        bound, peak, unit = "hbm", HBM_PEAK_GBS, "GB/s"
+    elif args.config == 8:
+        kind = "gather"
+        B = T["x"].shape[0]
+        idx_sets = [s.to(dev) for s in inputs.rotation_index_sets(w.dims["pool_rows"], B, seed=1)]
+        active = torch.empty((B,) + tuple(T["state"].shape[1:]), device=dev)
+        row_bytes = T["state"][0].numel() * T["state"].element_size()
+        nbytes = 2 * B * row_bytes
+        units = B
+        rot = "steps rotate 4 disjoint 64-row index sets over the pool"
+
+        def step(i):
+            ssu_state_gather(T["state"], active, idx_sets[i % len(idx_sets)])
+        src = source_hash("ssu_pool_kernels.hip", "ssu_device.h")
+        kkey = "gather_config8"
         bound, peak, unit = "hbm", HBM_PEAK_GBS, "GB/s"
     else:
         kind = "replay"

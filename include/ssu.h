@@ -17,6 +17,8 @@
  *   [RSM]  TensorRT-Edge-LLM, "Recurrent State Manager" page: constructor,
  *          clear, clearSlot, capture, restore, copySlotFrom, bytesPerSlot,
  *          stateBytesPerSlot, findState.
+ *   [DNP]  Smile, "Class DeltaNetStatePool" page: activateStep, scatterActive
+ *          (pack a cohort's home rows into working slots [0, B) and back).
  *
  * Conventions shared by every entry point
  *   - Every tensor pointer is a DEVICE pointer owned by the caller, dense
@@ -220,6 +222,52 @@ ssu_status ssu_state_clear_layers(const ssu_state_layer *layers, int32_t num_lay
                                   int32_t resident_rows, int32_t slot,
                                   int64_t recurrent_row_bytes, int64_t conv_row_bytes,
                                   hipStream_t stream);
+
+/* ------------------------------------------------------------------------
+ * Row movement between a resident pool and contiguous working rows. A row is
+ * row_bytes bytes (the trailing dimensions of one pool row, any dtype); rows
+ * of a buffer are `stride` bytes apart (0 = row_bytes, >= row_bytes
+ * otherwise). Any alignment; 16-byte aligned rows and strides copy fastest.
+ * Index arrays are device int32 arrays; values are not validated on the host.
+ * ---------------------------------------------------------------------- */
+
+/* ssu_state_gather -- active[b] = resident[state_indices[b]] for b < batch
+ * [SSU invokeMambaStateGather]. A negative index is a padding entry [PAD]: its
+ * active row is written as zeros. An index >= resident_rows is undefined. */
+ssu_status ssu_state_gather(const void *resident, int32_t resident_rows, int64_t resident_stride,
+                            void *active, int64_t active_stride, const int32_t *state_indices,
+                            int32_t batch, int64_t row_bytes, hipStream_t stream);
+
+/* ssu_state_scatter -- resident[state_indices[b]] = active[b] for b < batch with
+ * a non-negative index [SSU invokeMambaStateScatter]; padding entries write
+ * nothing. Duplicate live indices are undefined. */
+ssu_status ssu_state_scatter(const void *active, int64_t active_stride, void *resident,
+                             int32_t resident_rows, int64_t resident_stride,
+                             const int32_t *state_indices, int32_t batch, int64_t row_bytes,
+                             hipStream_t stream);
+
+/* ssu_state_pack -- pack a cohort's home rows into the working slots [0, batch)
+ * of the same pool [DNP activateStep]: afterwards slot b holds what row
+ * homes[b] held before the call, for every b. Every source row is read before
+ * any slot is written (a sequential home-to-slot copy would corrupt the cohort
+ * when homes are not in ascending order), and the rows listed in
+ * `bystanders` (live rows of other requests whose home lies in [0, batch);
+ * each < batch, none a home of the cohort) are saved first so that
+ * ssu_state_unpack can put them back. Slots whose home is the slot itself are
+ * not copied. workspace: device buffer of (batch + n_bystanders) * row_bytes
+ * bytes, kept by the caller until the matching ssu_state_unpack. homes must be
+ * distinct and in [0, pool_rows); values are not validated. Two launches. */
+ssu_status ssu_state_pack(void *pool, int32_t pool_rows, int64_t row_stride, int64_t row_bytes,
+                          const int32_t *homes, int32_t batch, const int32_t *bystanders,
+                          int32_t n_bystanders, void *workspace, hipStream_t stream);
+
+/* ssu_state_unpack -- write the working slots [0, batch) back to the homes and
+ * restore the bystander rows saved by ssu_state_pack [DNP scatterActive]; the
+ * same arguments as the pack. Every slot is read before any home is written.
+ * Two launches. */
+ssu_status ssu_state_unpack(void *pool, int32_t pool_rows, int64_t row_stride, int64_t row_bytes,
+                            const int32_t *homes, int32_t batch, const int32_t *bystanders,
+                            int32_t n_bystanders, void *workspace, hipStream_t stream);
 
 /* ------------------------------------------------------------------------
  * Recurrent-state pool [RSM]: one zeroed, contiguous slab per state spec,

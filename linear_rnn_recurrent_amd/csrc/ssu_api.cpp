@@ -378,6 +378,194 @@ ssu_status ssu_state_clear_layers(const ssu_state_layer *layers, int32_t num_lay
                       "ssu_state_clear_layers launch");
 }
 
+namespace {
+
+ssu_status check_rows(const char *fn, int32_t rows, int64_t stride, int64_t row_bytes,
+                      int32_t batch, int64_t *eff_stride)
+{
+    if (rows < 0)
+        return fail(SSU_EINVAL, "%s: row count %d < 0", fn, rows);
+    if (batch < 0 || batch > 65535)
+        return fail(SSU_EINVAL, "%s: batch %d outside [0, 65535]", fn, batch);
+    if (row_bytes < 0)
+        return fail(SSU_EINVAL, "%s: row_bytes %lld < 0", fn, (long long)row_bytes);
+    if (stride != 0 && stride < row_bytes)
+        return fail(SSU_EINVAL, "%s: stride %lld < row_bytes %lld", fn, (long long)stride,
+                    (long long)row_bytes);
+    *eff_stride = stride ? stride : row_bytes;
+    return SSU_OK;
+}
+
+}  // namespace
+
+ssu_status ssu_state_gather(const void *resident, int32_t resident_rows, int64_t resident_stride,
+                            void *active, int64_t active_stride, const int32_t *state_indices,
+                            int32_t batch, int64_t row_bytes, hipStream_t stream)
+{
+    const char *fn = "ssu_state_gather";
+    int64_t rs = 0, as = 0;
+    ssu_status st = check_rows(fn, resident_rows, resident_stride, row_bytes, batch, &rs);
+    if (st != SSU_OK)
+        return st;
+    st = check_rows(fn, batch, active_stride, row_bytes, batch, &as);
+    if (st != SSU_OK)
+        return st;
+    if (batch == 0 || row_bytes == 0)
+        return ok();
+    SSU_REQUIRE_PTR(resident, 1, fn);
+    SSU_REQUIRE_PTR(active, 1, fn);
+    SSU_REQUIRE_PTR(state_indices, 4, fn);
+    ssu::RowMove mv = {};
+    mv.dst = active;
+    mv.src = resident;
+    mv.src_idx = state_indices;
+    mv.dst_stride = as;
+    mv.src_stride = rs;
+    mv.rows = batch;
+    return hip_status(ssu::launch_row_moves(&mv, 1, row_bytes, stream), "ssu_state_gather launch");
+}
+
+ssu_status ssu_state_scatter(const void *active, int64_t active_stride, void *resident,
+                             int32_t resident_rows, int64_t resident_stride,
+                             const int32_t *state_indices, int32_t batch, int64_t row_bytes,
+                             hipStream_t stream)
+{
+    const char *fn = "ssu_state_scatter";
+    int64_t rs = 0, as = 0;
+    ssu_status st = check_rows(fn, resident_rows, resident_stride, row_bytes, batch, &rs);
+    if (st != SSU_OK)
+        return st;
+    st = check_rows(fn, batch, active_stride, row_bytes, batch, &as);
+    if (st != SSU_OK)
+        return st;
+    if (batch == 0 || row_bytes == 0)
+        return ok();
+    SSU_REQUIRE_PTR(active, 1, fn);
+    SSU_REQUIRE_PTR(resident, 1, fn);
+    SSU_REQUIRE_PTR(state_indices, 4, fn);
+    ssu::RowMove mv = {};
+    mv.dst = resident;
+    mv.src = active;
+    mv.dst_idx = state_indices;
+    mv.dst_stride = rs;
+    mv.src_stride = as;
+    mv.rows = batch;
+    return hip_status(ssu::launch_row_moves(&mv, 1, row_bytes, stream), "ssu_state_scatter launch");
+}
+
+namespace {
+
+ssu_status pack_args(const char *fn, void *pool, int32_t pool_rows, int64_t row_stride,
+                     int64_t row_bytes, const int32_t *homes, int32_t batch,
+                     const int32_t *bystanders, int32_t n_bystanders, void *workspace,
+                     int64_t *eff_stride)
+{
+    ssu_status st = check_rows(fn, pool_rows, row_stride, row_bytes, batch, eff_stride);
+    if (st != SSU_OK)
+        return st;
+    if (batch > pool_rows)
+        return fail(SSU_EINVAL, "%s: batch %d > pool_rows %d", fn, batch, pool_rows);
+    if (n_bystanders < 0 || n_bystanders > batch)
+        return fail(SSU_EINVAL, "%s: n_bystanders %d outside [0, batch %d]", fn, n_bystanders,
+                    batch);
+    if (batch == 0 || row_bytes == 0)
+        return SSU_OK;
+    SSU_REQUIRE_PTR(pool, 1, fn);
+    SSU_REQUIRE_PTR(homes, 4, fn);
+    SSU_REQUIRE_PTR(workspace, 1, fn);
+    if (n_bystanders > 0)
+        SSU_REQUIRE_PTR(bystanders, 4, fn);
+    return SSU_OK;
+}
+
+}  // namespace
+
+ssu_status ssu_state_pack(void *pool, int32_t pool_rows, int64_t row_stride, int64_t row_bytes,
+                          const int32_t *homes, int32_t batch, const int32_t *bystanders,
+                          int32_t n_bystanders, void *workspace, hipStream_t stream)
+{
+    const char *fn = "ssu_state_pack";
+    int64_t rs = 0;
+    const ssu_status st = pack_args(fn, pool, pool_rows, row_stride, row_bytes, homes, batch,
+                                    bystanders, n_bystanders, workspace, &rs);
+    if (st != SSU_OK)
+        return st;
+    if (batch == 0 || row_bytes == 0)
+        return ok();
+    uint8_t *ws = static_cast<uint8_t *>(workspace);
+    // 1. read every source: homes -> workspace rows [0, batch), bystanders ->
+    //    workspace rows [batch, batch + n_bystanders)
+    ssu::RowMove in[2] = {};
+    in[0].dst = ws;
+    in[0].src = pool;
+    in[0].src_idx = homes;
+    in[0].skip_same = homes;
+    in[0].dst_stride = row_bytes;
+    in[0].src_stride = rs;
+    in[0].rows = batch;
+    in[1].dst = ws + (int64_t)batch * row_bytes;
+    in[1].src = pool;
+    in[1].src_idx = bystanders;
+    in[1].dst_stride = row_bytes;
+    in[1].src_stride = rs;
+    in[1].rows = n_bystanders;
+    hipError_t e = ssu::launch_row_moves(in, n_bystanders > 0 ? 2 : 1, row_bytes, stream);
+    if (e != hipSuccess)
+        return hip_status(e, "ssu_state_pack launch");
+    // 2. then write the slots
+    ssu::RowMove out = {};
+    out.dst = pool;
+    out.src = ws;
+    out.skip_same = homes;
+    out.dst_stride = rs;
+    out.src_stride = row_bytes;
+    out.rows = batch;
+    return hip_status(ssu::launch_row_moves(&out, 1, row_bytes, stream), "ssu_state_pack launch");
+}
+
+ssu_status ssu_state_unpack(void *pool, int32_t pool_rows, int64_t row_stride, int64_t row_bytes,
+                            const int32_t *homes, int32_t batch, const int32_t *bystanders,
+                            int32_t n_bystanders, void *workspace, hipStream_t stream)
+{
+    const char *fn = "ssu_state_unpack";
+    int64_t rs = 0;
+    const ssu_status st = pack_args(fn, pool, pool_rows, row_stride, row_bytes, homes, batch,
+                                    bystanders, n_bystanders, workspace, &rs);
+    if (st != SSU_OK)
+        return st;
+    if (batch == 0 || row_bytes == 0)
+        return ok();
+    uint8_t *ws = static_cast<uint8_t *>(workspace);
+    // 1. read every slot into the workspace (rows in place are left alone)
+    ssu::RowMove in = {};
+    in.dst = ws;
+    in.src = pool;
+    in.skip_same = homes;
+    in.dst_stride = row_bytes;
+    in.src_stride = rs;
+    in.rows = batch;
+    hipError_t e = ssu::launch_row_moves(&in, 1, row_bytes, stream);
+    if (e != hipSuccess)
+        return hip_status(e, "ssu_state_unpack launch");
+    // 2. write the slots to their homes and the saved bystanders back (disjoint rows)
+    ssu::RowMove out[2] = {};
+    out[0].dst = pool;
+    out[0].src = ws;
+    out[0].dst_idx = homes;
+    out[0].skip_same = homes;
+    out[0].dst_stride = rs;
+    out[0].src_stride = row_bytes;
+    out[0].rows = batch;
+    out[1].dst = pool;
+    out[1].src = ws + (int64_t)batch * row_bytes;
+    out[1].dst_idx = bystanders;
+    out[1].dst_stride = rs;
+    out[1].src_stride = row_bytes;
+    out[1].rows = n_bystanders;
+    return hip_status(ssu::launch_row_moves(out, n_bystanders > 0 ? 2 : 1, row_bytes, stream),
+                      "ssu_state_unpack launch");
+}
+
 ssu_status ssu_tree_verify(const ssu_dims *dims, int32_t num_nodes, const void *x,
                            const float *A, const void *B, const void *C, const float *dt,
                            const float *dt_bias, const float *D, const void *z,

@@ -81,6 +81,19 @@ hipError_t launch_clear_layers(const ssu_state_layer *layers, int num_layers, in
 hipError_t launch_tree_f32(const TreeParams &p, hipStream_t stream);
 hipError_t launch_tree_f16(const TreeParams &p, hipStream_t stream);
 hipError_t launch_tree_bf16(const TreeParams &p, hipStream_t stream);
+// One set of row moves: for b < rows, dst row (dst_idx ? dst_idx[b] : b) gets
+// src row (src_idx ? src_idx[b] : b); a negative destination index skips the
+// row, a negative source index (or src == null) writes zeros; with skip_same,
+// rows where skip_same[b] == b are not touched.
+struct RowMove {
+    void *dst;
+    const void *src;
+    const int32_t *dst_idx, *src_idx, *skip_same;
+    int64_t dst_stride, src_stride;
+    int32_t rows;
+};
+// Up to two row-move sets of row_bytes-byte rows in one launch.
+hipError_t launch_row_moves(const RowMove *moves, int n, int64_t row_bytes, hipStream_t stream);
 // Copies/zeroes up to any number of segments; one launch per 32 segments.
 hipError_t launch_segments(const Segment *segs, int n, hipStream_t stream);
 

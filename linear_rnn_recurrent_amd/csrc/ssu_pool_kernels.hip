@@ -77,7 +77,90 @@ __global__ __launch_bounds__(256) void ssu_clear_layers_kernel(const ssu_state_l
         d[i] = 0;
 }
 
+// Row moves between a pool and working rows (invokeMambaStateGather /
+// invokeMambaStateScatter, "Selective State Update" page; the activateStep /
+// scatterActive packing of the "Class DeltaNetStatePool" page): workgroup
+// (x, y, z) moves bytes [x * kRowChunk, (x+1) * kRowChunk) of row y of move set
+// z. Streaming 16-byte non-temporal loads and stores when both rows are
+// 16-byte aligned, bytes otherwise.
+constexpr int64_t kRowChunk = 64 * 1024;
+
+struct RowMoves {
+    RowMove m[2];
+    int64_t row_bytes;
+};
+
+__global__ __launch_bounds__(256) void ssu_row_moves_kernel(const RowMoves rm)
+{
+    const RowMove mv = rm.m[blockIdx.z];
+    const int b = blockIdx.y;
+    if (b >= mv.rows)
+        return;
+    if (mv.skip_same && mv.skip_same[b] == b)
+        return;
+    const int d = mv.dst_idx ? mv.dst_idx[b] : b;
+    if (d < 0)
+        return;
+    const int s = mv.src ? (mv.src_idx ? mv.src_idx[b] : b) : -1;
+    const uint64_t lo = (uint64_t)blockIdx.x * kRowChunk;
+    const uint64_t n = (uint64_t)rm.row_bytes;
+    if (lo >= n)
+        return;
+    const uint64_t len = n - lo < (uint64_t)kRowChunk ? n - lo : (uint64_t)kRowChunk;
+    uint8_t *dp = static_cast<uint8_t *>(mv.dst) + (uint64_t)d * mv.dst_stride + lo;
+    const uint8_t *sp =
+        s >= 0 ? static_cast<const uint8_t *>(mv.src) + (uint64_t)s * mv.src_stride + lo : nullptr;
+    const bool aligned = (((uintptr_t)dp | (sp ? (uintptr_t)sp : 0)) & 15) == 0;
+    uint64_t done = 0;
+    if (aligned) {
+        const uint64_t nv = len / 16;
+        u32x4 *d4 = reinterpret_cast<u32x4 *>(dp);
+        const u32x4 *s4 = reinterpret_cast<const u32x4 *>(sp);
+        for (uint64_t i = threadIdx.x; i < nv; i += 4 * blockDim.x) {
+            u32x4 v[4];
+#pragma unroll
+            for (int k = 0; k < 4; ++k) {
+                const uint64_t j = i + (uint64_t)k * blockDim.x;
+                v[k] = (s4 && j < nv) ? __builtin_nontemporal_load(&s4[j]) : u32x4{0u, 0u, 0u, 0u};
+            }
+#pragma unroll
+            for (int k = 0; k < 4; ++k) {
+                const uint64_t j = i + (uint64_t)k * blockDim.x;
+                if (j < nv)
+                    __builtin_nontemporal_store(v[k], &d4[j]);
+            }
+        }
+        done = nv * 16;
+    }
+    for (uint64_t i = done + threadIdx.x; i < len; i += blockDim.x)
+        dp[i] = sp ? sp[i] : (uint8_t)0;
+}
+
 }  // namespace
+
+hipError_t launch_row_moves(const RowMove *moves, int n, int64_t row_bytes, hipStream_t stream)
+{
+    if (n < 1 || n > 2)
+        return hipErrorInvalidValue;
+    RowMoves rm = {};
+    int rows = 0;
+    for (int i = 0; i < n; ++i) {
+        rm.m[i] = moves[i];
+        rows = moves[i].rows > rows ? moves[i].rows : rows;
+    }
+    rm.row_bytes = row_bytes;
+    if (rows == 0 || row_bytes == 0)
+        return hipSuccess;
+    if (rows > 65535)
+        return hipErrorInvalidConfiguration;
+    const uint64_t chunks = ((uint64_t)row_bytes + kRowChunk - 1) / kRowChunk;
+    if (chunks > 0x7fffffffull)
+        return hipErrorInvalidConfiguration;
+    (void)hipGetLastError();
+    hipLaunchKernelGGL(ssu_row_moves_kernel, dim3((unsigned)chunks, (unsigned)rows, (unsigned)n),
+                       dim3(256), 0, stream, rm);
+    return hipGetLastError();
+}
 
 hipError_t launch_clear_layers(const ssu_state_layer *layers, int num_layers, int rows, int slot,
                                int64_t rec_row_bytes, int64_t conv_row_bytes, hipStream_t stream)

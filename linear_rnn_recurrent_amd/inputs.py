@@ -311,6 +311,9 @@ LAYERS_NAME = {
        "rows 5376 x 3), one launch",
 }
 
+GATHER_NAME = ("gather of the config-1 batch: 64 rows of H80 Dm64 N128 fp32 (2.6 MB each) from "
+               "the 256-row pool into a contiguous active batch")
+
 TREE_NAME = ("tree verify B16 M128 (random draft tree, depth < 16) H80 Dm64 N128 G1, "
              "fp32 pool P64")
 

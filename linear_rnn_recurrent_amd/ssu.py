@@ -21,7 +21,8 @@ _DT = {torch.float32: SSU_F32, torch.float16: SSU_F16, torch.bfloat16: SSU_BF16,
        torch.uint8: SSU_U8}
 
 EXPORTS = ("ssu_decode", "ssu_prefill", "ssu_replay", "ssu_tree_verify", "ssu_replay_layers",
-           "ssu_state_clear_layers", "ssu_pool_bytes_per_slot",
+           "ssu_state_clear_layers", "ssu_state_gather", "ssu_state_scatter", "ssu_state_pack",
+           "ssu_state_unpack", "ssu_pool_bytes_per_slot",
            "ssu_pool_alloc", "ssu_pool_free", "ssu_pool_info", "ssu_pool_state_ptr",
            "ssu_pool_state_bytes_per_slot", "ssu_pool_find_state", "ssu_pool_clear",
            "ssu_pool_clear_slot", "ssu_pool_capture", "ssu_pool_restore",
@@ -83,6 +84,12 @@ def load_library(path: Optional[str] = None):
                             _P, _P, _P, _P, _P],
         "ssu_replay_layers": [D, _I32, _P, _I32, _P, _P, _I32, _P, _I32, _P],
         "ssu_state_clear_layers": [_P, _I32, _I32, _I32, ctypes.c_int64, ctypes.c_int64, _P],
+        "ssu_state_gather": [_P, _I32, ctypes.c_int64, _P, ctypes.c_int64, _P, _I32,
+                             ctypes.c_int64, _P],
+        "ssu_state_scatter": [_P, ctypes.c_int64, _P, _I32, ctypes.c_int64, _P, _I32,
+                              ctypes.c_int64, _P],
+        "ssu_state_pack": [_P, _I32, ctypes.c_int64, ctypes.c_int64, _P, _I32, _P, _I32, _P, _P],
+        "ssu_state_unpack": [_P, _I32, ctypes.c_int64, ctypes.c_int64, _P, _I32, _P, _I32, _P, _P],
         "ssu_pool_bytes_per_slot": [S, _I32, ctypes.POINTER(ctypes.c_size_t)],
         "ssu_pool_alloc": [S, _I32, _I32, _P, ctypes.POINTER(_P)],
         "ssu_pool_free": [_P],
@@ -441,6 +448,77 @@ def ssu_state_clear_layers(table: StateLayerTable, resident_rows, slot, recurren
         _check(lib.ssu_state_clear_layers(_ptr(table.table), table.num_layers, int(resident_rows),
                                           int(slot), int(recurrent_row_bytes),
                                           int(conv_row_bytes), _stream(table.device, stream)))
+
+
+def _rows(t, name):
+    """(rows, row_bytes, row stride in bytes) of a tensor whose leading dim is the row."""
+    _dev(t, name)
+    _need(t.dim() >= 1, f"{name} needs a leading row dimension")
+    inner = t[0] if t.shape[0] > 0 else t.new_empty(t.shape[1:])
+    _need(inner.is_contiguous(), f"{name} rows must be dense")
+    row_bytes = inner.numel() * t.element_size()
+    stride = t.stride(0) * t.element_size() if t.shape[0] > 1 else row_bytes
+    return t.shape[0], row_bytes, stride
+
+
+def ssu_state_gather(resident, active, state_indices, stream=None):
+    """active[b] = resident[state_indices[b]]; a negative index gives a zero row."""
+    lib = load_library()
+    rr, rb, rs = _rows(resident, "resident")
+    ar, ab, ast = _rows(active, "active")
+    _need(rb == ab and resident.dtype == active.dtype, "resident and active rows must match")
+    _dense(state_indices, "state_indices", (torch.int32,), (ar,))
+    with torch.cuda.device(active.device):
+        _check(lib.ssu_state_gather(_ptr(resident), rr, rs, _ptr(active), ast,
+                                    _ptr(state_indices), ar, rb, _stream(active.device, stream)))
+
+
+def ssu_state_scatter(active, resident, state_indices, stream=None):
+    """resident[state_indices[b]] = active[b] for non-negative indices."""
+    lib = load_library()
+    rr, rb, rs = _rows(resident, "resident")
+    ar, ab, ast = _rows(active, "active")
+    _need(rb == ab and resident.dtype == active.dtype, "resident and active rows must match")
+    _dense(state_indices, "state_indices", (torch.int32,), (ar,))
+    with torch.cuda.device(active.device):
+        _check(lib.ssu_state_scatter(_ptr(active), ast, _ptr(resident), rr, rs,
+                                     _ptr(state_indices), ar, rb, _stream(active.device, stream)))
+
+
+def pack_workspace_bytes(pool, batch, n_bystanders):
+    """Bytes of the workspace ssu_state_pack / ssu_state_unpack need (pool: any
+    tensor whose leading dimension is the row)."""
+    row_bytes = int(torch.Size(pool.shape[1:]).numel()) * pool.element_size()
+    return (batch + n_bystanders) * row_bytes
+
+
+def _pack_call(fn, pool, homes, bystanders, workspace, stream):
+    lib = load_library()
+    rows, rb, rs = _rows(pool, "pool")
+    _dense(homes, "homes", (torch.int32,))
+    _need(homes.dim() == 1, "homes must be 1-D")
+    nb = 0
+    if bystanders is not None:
+        _dense(bystanders, "bystanders", (torch.int32,))
+        nb = bystanders.numel()
+    _dev(workspace, "workspace")
+    _need(workspace.numel() * workspace.element_size() >= (homes.numel() + nb) * rb,
+          "workspace too small")
+    with torch.cuda.device(pool.device):
+        _check(getattr(lib, fn)(_ptr(pool), rows, rs, rb, _ptr(homes), homes.numel(),
+                                _ptr(bystanders) if nb else None, nb, _ptr(workspace),
+                                _stream(pool.device, stream)))
+
+
+def ssu_state_pack(pool, homes, workspace, bystanders=None, stream=None):
+    """Slots [0, len(homes)) of `pool` get the rows homes[b] held (all read first);
+    bystander rows are saved in `workspace` for ssu_state_unpack."""
+    _pack_call("ssu_state_pack", pool, homes, bystanders, workspace, stream)
+
+
+def ssu_state_unpack(pool, homes, workspace, bystanders=None, stream=None):
+    """Slots [0, len(homes)) go back to their homes; bystanders are restored."""
+    _pack_call("ssu_state_unpack", pool, homes, bystanders, workspace, stream)
 
 
 # ---------------------------------------------------------------------------

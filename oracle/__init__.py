@@ -166,6 +166,46 @@ def clear_layers(recurrent, conv, resident_rows, slot, recurrent_row_bytes, conv
                 buf[slot * rb:(slot + 1) * rb] = 0
 
 
+def gather(resident, state_indices):
+    """Active rows from a pool (TensorRT-Edge-LLM "Selective State Update" page,
+    invokeMambaStateGather): row b is resident[state_indices[b]]; a negative index
+    (padding, FlashInfer gdn_fused_decode_step page, state_indices) gives zeros."""
+    out = np.zeros((len(state_indices),) + resident.shape[1:], dtype=resident.dtype)
+    for b, r in enumerate(state_indices):
+        if r >= 0:
+            out[b] = resident[r]
+    return out
+
+
+def scatter(active, resident, state_indices):
+    """invokeMambaStateScatter (same page): resident[state_indices[b]] = active[b] for
+    non-negative indices; `resident` is updated in place."""
+    for b, r in enumerate(state_indices):
+        if r >= 0:
+            resident[r] = active[b]
+
+
+def pack(pool, homes, bystanders):
+    """activateStep (Smile "Class DeltaNetStatePool" page): every source row is read
+    first, then slot b of the pool gets the row homes[b] held; the bystander rows
+    (live rows of other requests with homes in [0, B)) are saved and returned."""
+    src = [pool[h].copy() for h in homes]
+    saved = [pool[r].copy() for r in bystanders]
+    for b, row in enumerate(src):
+        pool[b] = row
+    return saved
+
+
+def unpack(pool, homes, bystanders, saved):
+    """scatterActive (same page): working slots [0, B) go back to their homes (all
+    slots read first), then the saved bystander rows are put back."""
+    slots = [pool[b].copy() for b in range(len(homes))]
+    for b, h in enumerate(homes):
+        pool[h] = slots[b]
+    for r, row in zip(bystanders, saved):
+        pool[r] = row
+
+
 MAX_NODES = 128
 
 

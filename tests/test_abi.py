@@ -311,3 +311,24 @@ def test_state_clear_layers_validation(lib):
     assert call(layers=None) == 1 and "'layers'" in err(lib)
     assert call(num_layers=0, layers=None) == 0
     assert call(rows=0, slot=-1, layers=None) == 0
+
+
+def test_row_movement_validation(lib):
+    g = lambda rr=4, rs=0, as_=0, idx=FAKE, batch=2, rb=64, res=FAKE, act=FAKE: lib.ssu_state_gather(
+        res, rr, rs, act, as_, idx, batch, rb, None)
+    assert g(rr=-1) == 1 and "row count" in err(lib)
+    assert g(batch=70000) == 1 and "batch" in err(lib)
+    assert g(rb=-1) == 1 and "row_bytes" in err(lib)
+    assert g(rs=32) == 1 and "stride" in err(lib)
+    assert g(idx=None) == 1 and "'state_indices'" in err(lib)
+    assert g(batch=0, res=None) == 0 and g(rb=0, res=None) == 0
+    assert lib.ssu_state_scatter(FAKE, 0, FAKE, 4, 0, None, 2, 64, None) == 1
+    p = lambda batch=3, rows=4, nby=0, by=None, ws=FAKE, homes=FAKE: lib.ssu_state_pack(
+        FAKE, rows, 0, 64, homes, batch, by, nby, ws, None)
+    assert p(batch=5) == 1 and "pool_rows" in err(lib)
+    assert p(nby=4) == 1 and "n_bystanders" in err(lib)
+    assert p(nby=1) == 1 and "'bystanders'" in err(lib)
+    assert p(ws=None) == 1 and "'workspace'" in err(lib)
+    assert p(homes=None) == 1 and "'homes'" in err(lib)
+    assert p(batch=0, ws=None) == 0
+    assert lib.ssu_state_unpack(FAKE, 4, 0, 64, FAKE, 3, None, 0, None, None) == 1
