@@ -311,6 +311,54 @@ LAYERS_NAME = {
        "rows 5376 x 3), one launch",
 }
 
+def gdn_workload(*, batch, hidden, num_q_heads, num_v_heads, head_dim, conv_width, pool_rows,
+                 seed, indices="perm", n_live=None, conv_layout="ds", use_qk_l2norm=True,
+                 scale=None, ssm_std=0.1, name="gdn"):
+    """Inputs of the fused gated-delta-rule decode step (bf16 activations and
+    conv pool, fp32 A_log and ssm pool). conv_layout 'ds': conv_state is the
+    dense [P, qkv_dim, W-1] pool; 'sd': the pool holds [P, W-1, qkv_dim] rows and
+    conv_state is its transposed view."""
+    rng = np.random.default_rng(seed)
+    hq, hv, d, w = num_q_heads, num_v_heads, head_dim, conv_width
+    qkv = (2 * hq + hv) * d
+    bf = lambda a: _t(a, "bf16")
+    hs = rng.standard_normal((batch, hidden))
+    w_ba = rng.standard_normal((hidden, 2 * hv)) / np.sqrt(hidden)
+    mixed = rng.standard_normal((batch, qkv))
+    conv_w = rng.standard_normal((qkv, w)) / np.sqrt(w)
+    conv_b = rng.standard_normal(qkv) * 0.1
+    A_log = np.log(rng.uniform(1.0, 16.0, hv))
+    dt_bias = np.log(np.expm1(rng.uniform(1e-3, 0.1, hv)))
+    if conv_layout == "ds":
+        conv_state = bf(rng.standard_normal((pool_rows, qkv, w - 1)))
+    else:
+        conv_state = bf(rng.standard_normal((pool_rows, w - 1, qkv))).transpose(1, 2)
+    ssm = torch.from_numpy((rng.standard_normal((pool_rows, hv, d, d)) * ssm_std).astype(np.float32))
+    if isinstance(indices, str) and indices == "perm":
+        idx = rng.permutation(pool_rows)[:batch].astype(np.int32)
+    else:
+        idx = np.asarray(indices, dtype=np.int32)
+    if n_live is not None:
+        idx = idx.copy()
+        idx[n_live:] = -1
+    T = {"hidden_states": bf(hs), "w_ba": bf(w_ba), "mixed_qkv": bf(mixed), "conv_weight": bf(conv_w),
+         "conv_bias": bf(conv_b), "conv_state": conv_state, "A_log": _t(A_log, "f32"),
+         "dt_bias": bf(dt_bias), "ssm_state": ssm, "state_indices": torch.from_numpy(idx)}
+    dims = dict(batch=batch, hidden=hidden, num_q_heads=hq, num_v_heads=hv, head_dim=d,
+                conv_width=w, pool_rows=pool_rows, use_qk_l2norm=use_qk_l2norm, scale=scale)
+    return Workload(name, "gdn", dims, T, True)
+
+
+GDN_NAME = ("GDN fused decode B64 hidden2048 Hq16 HV32 D128 W4 (Qwen3-Next-shaped linear "
+            "attention layer), fp32 ssm pool P256, bf16 conv pool")
+
+
+def gdn_config(seed: int = 9) -> Workload:
+    """Fused gated-delta-rule decode at a Qwen3-Next-shaped linear-attention layer."""
+    return gdn_workload(batch=64, hidden=2048, num_q_heads=16, num_v_heads=32, head_dim=128,
+                        conv_width=4, pool_rows=256, seed=seed, name=GDN_NAME)
+
+
 GATHER_NAME = ("gather of the config-1 batch: 64 rows of H80 Dm64 N128 fp32 (2.6 MB each) from "
                "the 256-row pool into a contiguous active batch")
 

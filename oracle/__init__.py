@@ -15,6 +15,8 @@ shape list; invokeSelectiveStateUpdatePrefill; MambaReplayLayerInfo):
            depths [b, num_nodes] (invokeSelectiveStateUpdateDDTree)
   layers : lists of per-layer states / stashes (invokeMambaReplayReconstructBatched,
            invokeMambaStateClear)
+  gdn    : the fused gated-delta-rule decode step of FlashInfer's
+           gdn_fused_decode_step page (gdn_oracle.c)
   state  : [rows, h, d, n], or a flat buffer with `row_stride` elements per row
 
 `state`, `out` and the stash arrays are updated in place.
@@ -48,6 +50,10 @@ def _lib():
         for f in (lib.oracle_ssu_decode, lib.oracle_ssu_prefill, lib.oracle_ssu_replay,
                   lib.oracle_ssu_tree):
             f.restype = None
+        lib.oracle_gdn_decode.argtypes = ([i32] * 6 + [_F64P] * 5 + [_F64P] + [i64] * 3
+                                          + [_F64P] * 2 + [ctypes.c_double] + [_F64P] + [i64]
+                                          + [_I32P, i32, _F64P])
+        lib.oracle_gdn_decode.restype = None
         lib.oracle_num_threads.argtypes = []
         lib.oracle_num_threads.restype = ctypes.c_int32
         _LIB = lib
@@ -204,6 +210,43 @@ def unpack(pool, homes, bystanders, saved):
         pool[h] = slots[b]
     for r, row in zip(bystanders, saved):
         pool[r] = row
+
+
+def gdn_decode(hidden_states, w_ba, mixed_qkv, conv_weight, conv_bias, conv_state, A_log,
+               dt_bias, scale, ssm_state, state_indices, *, num_q_heads, use_qk_l2norm=True,
+               out=None, conv_strides=None, ssm_row_stride=None):
+    """Fused gated-delta-rule decode step (FlashInfer "flashinfer.gdn_fused_decode_step"
+    page; formulas in oracle/gdn_oracle.c). Shapes: hidden_states [B, hidden],
+    w_ba [hidden, 2 HV], mixed_qkv [B, (2 Hq + HV) D], conv_weight [qkv_dim, W],
+    conv_bias [qkv_dim], conv_state [P, qkv_dim, W-1] (or a flat buffer with
+    conv_strides = (slot, channel, tap) element strides), A_log / dt_bias [HV],
+    ssm_state [P, HV, D, D] (V-major, K-last). conv_state, ssm_state and out
+    ([B, 1, HV, D]) are updated in place; out is returned."""
+    B, hidden = hidden_states.shape
+    hv = w_ba.shape[1] // 2
+    hq = num_q_heads
+    dhead = conv_weight.shape[0] // (2 * num_q_heads + hv)
+    width = conv_weight.shape[1]
+    keep = [_f64(v, k) for k, v in (("hidden_states", hidden_states), ("w_ba", w_ba),
+                                     ("mixed_qkv", mixed_qkv), ("conv_weight", conv_weight),
+                                     ("conv_bias", conv_bias), ("A_log", A_log),
+                                     ("dt_bias", dt_bias))]
+    cs = _f64(conv_state, "conv_state", True)
+    st = _f64(ssm_state, "ssm_state", True)
+    if out is None:
+        out = np.zeros((B, 1, hv, dhead))
+    ot = _f64(out, "out", True)
+    if conv_strides is None:
+        conv_strides = (conv_state.shape[1] * conv_state.shape[2], conv_state.shape[2], 1)
+    if scale is None or scale == 0.0:
+        scale = 1.0 / np.sqrt(dhead)
+    ix = _i32(state_indices)
+    row_stride = hv * dhead * dhead if ssm_row_stride is None else int(ssm_row_stride)
+    _lib().oracle_gdn_decode(B, hidden, hq, hv, dhead, width, keep[0][1], keep[1][1], keep[2][1],
+                             keep[3][1], keep[4][1], cs[1], *[int(x) for x in conv_strides],
+                             keep[5][1], keep[6][1], float(scale), st[1], row_stride, ix[1],
+                             1 if use_qk_l2norm else 0, ot[1])
+    return out
 
 
 MAX_NODES = 128

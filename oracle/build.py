@@ -7,14 +7,14 @@ import subprocess
 import sys
 
 HERE = os.path.dirname(os.path.abspath(__file__))
-SRC = os.path.join(HERE, "ssu_oracle.c")
+SRCS = [os.path.join(HERE, "ssu_oracle.c"), os.path.join(HERE, "gdn_oracle.c")]
 LIB = os.path.join(HERE, "libssu_oracle.so")
 
 
 def build(verbose=False):
     cmd = ["gcc", "-O2", "-std=c11", "-fPIC", "-shared", "-fopenmp",
            "-ffp-contract=off", "-fno-fast-math", "-Wall", "-Wextra",
-           "-o", LIB + ".tmp", SRC, "-lm"]
+           "-o", LIB + ".tmp"] + SRCS + ["-lm"]
     if verbose:
         print(" ".join(cmd))
     subprocess.run(cmd, check=True)

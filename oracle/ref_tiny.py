@@ -17,6 +17,11 @@ Definitions followed (TensorRT-Edge-LLM "Selective State Update" page):
     form (products of the decays along the path), not replayed step by step,
     so that this file and the C oracle reach the tree outputs by different
     formulas.
+  * FlashInfer "flashinfer.gdn_fused_decode_step": the fused gated-delta-rule
+    decode step (readings as in oracle/gdn_oracle.c). Here the output is formed
+    from the expanded update, o = alpha (S q) + delta (k . q), and the prediction
+    as alpha (S k), instead of from the updated state row, so the two oracles
+    reach the outputs by different formulas.
 Padding rows (negative index) follow the FlashInfer gdn_fused_decode_step page,
 parameter state_indices.
 
@@ -234,3 +239,54 @@ def tree(x, A, B, C, dt, state, out, parent_ids, depths=None, dt_bias=None, D=No
                         stash['u'][b, m, h, d] = float(x[b, m, h, d])
                     for n in range(ns):
                         stash['B'][b, m, grp, n] = float(B[b, m, grp, n])
+
+
+def gdn_decode(hidden_states, w_ba, mixed_qkv, conv_weight, conv_bias, conv_state, A_log,
+               dt_bias, scale, ssm_state, state_indices, num_q_heads, use_qk_l2norm=True):
+    """Returns out [B, 1, HV, D]; conv_state [P, qkv, W-1] and ssm_state
+    [P, HV, D, D] are updated in place."""
+    nb, hidden = hidden_states.shape
+    hv = w_ba.shape[1] // 2
+    hq = num_q_heads
+    qkv, width = conv_weight.shape
+    dh = qkv // (2 * hq + hv)
+    if scale is None or scale == 0.0:
+        scale = 1.0 / math.sqrt(dh)
+    out = [[[[0.0] * dh for _ in range(hv)]] for _ in range(nb)]
+    for b in range(nb):
+        s = int(state_indices[b])
+        if s < 0:
+            continue
+        proj = [sum(float(hidden_states[b, i]) * float(w_ba[i, j]) for i in range(hidden))
+                for j in range(2 * hv)]
+        ch = []
+        for c in range(qkv):
+            taps = [float(conv_state[s, c, j]) for j in range(width - 1)]
+            taps.append(float(mixed_qkv[b, c]))
+            pre = float(conv_bias[c]) + sum(taps[j] * float(conv_weight[c, j]) for j in range(width))
+            ch.append(pre / (1.0 + math.exp(-pre)))
+            for j in range(width - 1):
+                conv_state[s, c, j] = taps[j + 1]
+        heads_q = [ch[h * dh:(h + 1) * dh] for h in range(hq)]
+        heads_k = [ch[(hq + h) * dh:(hq + h + 1) * dh] for h in range(hq)]
+        if use_qk_l2norm:
+            heads_q = [[e / math.sqrt(sum(t * t for t in x) + 1e-6) for e in x] for x in heads_q]
+            heads_k = [[e / math.sqrt(sum(t * t for t in x) + 1e-6) for e in x] for x in heads_k]
+        heads_q = [[e * scale for e in x] for x in heads_q]
+        for h in range(hv):
+            q = heads_q[h // (hv // hq)]
+            k = heads_k[h // (hv // hq)]
+            v = ch[(2 * hq + h) * dh:(2 * hq + h + 1) * dh]
+            beta = 1.0 / (1.0 + math.exp(-proj[h]))
+            sp = _sp(proj[hv + h] + float(dt_bias[h]))
+            alpha = math.exp(-math.exp(float(A_log[h])) * sp)
+            kq = sum(k[i] * q[i] for i in range(dh))
+            for vi in range(dh):
+                row = [float(ssm_state[s, h, vi, i]) for i in range(dh)]
+                sk = sum(row[i] * k[i] for i in range(dh))
+                sq = sum(row[i] * q[i] for i in range(dh))
+                delta = beta * (v[vi] - alpha * sk)
+                out[b][0][h][vi] = alpha * sq + delta * kq
+                for i in range(dh):
+                    ssm_state[s, h, vi, i] = alpha * row[i] + delta * k[i]
+    return out
