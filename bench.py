@@ -8,14 +8,17 @@ four disjoint 64-row index sets that together cover the pool, so every step
 streams state rows the previous three steps did not touch and the 256 MB
 last-level cache cannot serve them.
 
-    python bench.py [--steps K] [--warmup W] [--config {1,2,3,4,5,6,7,8}]
+    python bench.py [--steps K] [--warmup W] [--config {1,2,3,4,5,6,7,8,9}]
 
 --config 2/3/4/5 time prefill / padded decode / MTP replay / tree verify
 (16 requests with 128-node draft trees, replay stash on) instead; 6 and 7 the
 layer-batched calls over a 64-layer stack: the MTP replay of config 4 for every
 layer in one launch, and the clear of one resident slot (recurrent and conv
 rows) of every layer in one launch; 8 the gather of the config-1 batch's 64 pool
-rows into a contiguous active batch. Their pools
+rows into a contiguous active batch; 9 the fused gated-delta-rule decode step
+of a Qwen3-Next-shaped linear-attention layer (B=64, hidden 2048, Hq 16, HV 32,
+D 128, conv width 4) over a 256-slot pool, steps rotating disjoint 64-slot
+index sets as in the default. The other pools
 are smaller than the last-level cache, so the steps rotate over replicas of
 the pool (and, for prefill, of every input) that together exceed it; every
 configuration is timed as back-to-back launches on one stream.
@@ -98,6 +101,19 @@ def tree_bytes(T, stash=True):
         + 2 * g * n * esize(T["B"]) + 4 * h + 8
     st = 4 * h * d + 4 * g * n + 8 * h if stash else 0
     return live * h * d * n * esize(T["state"]) + b * m * per_node + live * m * st + 12 * h
+
+
+def gdn_bytes(T, live):
+    """Algorithmic bytes of one fused gated-delta-rule decode launch: weights once,
+    per live entry its activations, conv-pool taps (read and written) and the
+    HV x D x D fp32 state (read and written); out for every entry."""
+    B, hidden = T["hidden_states"].shape
+    qkv, w = T["conv_weight"].shape
+    P, hv, d, _ = T["ssm_state"].shape
+    e = esize(T["hidden_states"])
+    once = (T["w_ba"].numel() + T["conv_weight"].numel() + qkv) * e + hv * (4 + e)
+    per = (hidden + qkv) * e + 2 * qkv * (w - 1) * e + 2 * hv * d * d * 4
+    return once + live * per + B * (4 + hv * d * e)
 
 
 def tree_lane_ops(T):
@@ -187,6 +203,20 @@ def cpu_baseline(kind, w, seconds, bytes_per_call, units_per_call):
                         depths=a["depths"], dt_bias=a["dt_bias"], D=a["D"], z=a["z"],
                         dt_softplus=w.dt_softplus, state_indices=a["state_indices"], stash=S)
         sample = "the full tree batch of this workload"
+    elif kind == "gdn":
+        idx = a["state_indices"]
+        live = idx[idx >= 0]
+        st = a["ssm_state"][live].copy()            # compact pools of the addressed slots
+        cs = a["conv_state"][live].copy()
+        remap = np.full(idx.shape, -1, dtype=np.int32)
+        remap[idx >= 0] = np.arange(live.size, dtype=np.int32)
+
+        def call():
+            oracle.gdn_decode(a["hidden_states"], a["w_ba"], a["mixed_qkv"], a["conv_weight"],
+                              a["conv_bias"], cs, a["A_log"], a["dt_bias"], w.dims["scale"], st,
+                              remap, num_q_heads=w.dims["num_q_heads"],
+                              use_qk_l2norm=w.dims["use_qk_l2norm"])
+        sample = f"the full {idx.shape[0]}-entry batch of this workload"
     elif kind == "gather":
         idx = a["state_indices"]
         pool = a["state"]
@@ -241,7 +271,7 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=1000)
     ap.add_argument("--warmup", type=int, default=100)
-    ap.add_argument("--config", type=int, default=1, choices=[1, 2, 3, 4, 5, 6, 7, 8])
+    ap.add_argument("--config", type=int, default=1, choices=[1, 2, 3, 4, 5, 6, 7, 8, 9])
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--prewarm-ms", type=float, default=300.0,
                     help="untimed launches before the warm-up steps, to reach steady clocks")
@@ -260,8 +290,8 @@ def main():
 
     import torch
     from linear_rnn_recurrent_amd import (ReplayLayerTable, StateLayerTable, inputs, load_library,
-                                          ssu_decode, ssu_prefill, ssu_replay,
-                                          ssu_replay_layers, ssu_state_clear_layers,
+                                          ssu_decode, ssu_gdn_decode, ssu_prefill,
+                                          ssu_replay, ssu_replay_layers, ssu_state_clear_layers,
                                           ssu_state_gather, ssu_tree_verify)
 
     load_library()
@@ -273,6 +303,8 @@ def main():
         w, name = inputs.config(4), inputs.LAYERS_NAME[args.config]
     elif args.config == 8:
         w, name = inputs.config(1), inputs.GATHER_NAME
+    elif args.config == 9:
+        w, name = inputs.gdn_config(), inputs.GDN_NAME
     else:
         w, name = inputs.config(args.config), inputs.CONFIG_NAMES[args.config]
     T = {k: (None if v is None else v.to(dev)) for k, v in w.tensors.items()}
@@ -350,7 +382,7 @@ def main():
                             R["parent_ids"], depths=R["depths"], dt_bias=R["dt_bias"], D=R["D"],
                             z=R["z"], dt_softplus=w.dt_softplus, state_indices=R["state_indices"],
                             **R["S"])
-        src = source_hash("ssu_tree_impl.h", "ssu_device.h")
+        src = source_hash("ssu_tree_impl.h", "ssu_dpp.h", "ssu_device.h")
         kkey = "tree_config5"
         lane_ops = tree_lane_ops(T)
         bound, peak, unit = "mfma", MFMA_F32_PEAK_TFLOPS, "TFLOP/s"
@@ -409,6 +441,25 @@ def main():
             ssu_state_gather(T["state"], active, idx_sets[i % len(idx_sets)])
         src = source_hash("ssu_pool_kernels.hip", "ssu_device.h")
         kkey = "gather_config8"
+        bound, peak, unit = "hbm", HBM_PEAK_GBS, "GB/s"
+    elif args.config == 9:
+        kind = "gdn"
+        B = T["hidden_states"].shape[0]
+        idx_sets = [s.to(dev) for s in inputs.rotation_index_sets(w.dims["pool_rows"], B, seed=1)]
+        nbytes = gdn_bytes(T, B)
+        units = B * w.dims["num_v_heads"]
+        out = torch.empty((B, 1, w.dims["num_v_heads"], w.dims["head_dim"]), dtype=torch.bfloat16,
+                          device=dev)
+        rot = "steps rotate 4 disjoint 64-slot index sets over both pools"
+
+        def step(i):
+            ssu_gdn_decode(T["hidden_states"], T["w_ba"], T["mixed_qkv"], T["conv_weight"],
+                           T["conv_bias"], T["conv_state"], T["A_log"], T["dt_bias"],
+                           w.dims["scale"], T["ssm_state"], idx_sets[i % len(idx_sets)],
+                           num_q_heads=w.dims["num_q_heads"],
+                           use_qk_l2norm=w.dims["use_qk_l2norm"], out=out)
+        src = source_hash("ssu_gdn.hip", "ssu_dpp.h", "ssu_device.h")
+        kkey = "gdn_config9"
         bound, peak, unit = "hbm", HBM_PEAK_GBS, "GB/s"
     else:
         kind = "replay"

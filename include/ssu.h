@@ -19,6 +19,8 @@
  *          stateBytesPerSlot, findState.
  *   [DNP]  Smile, "Class DeltaNetStatePool" page: activateStep, scatterActive
  *          (pack a cohort's home rows into working slots [0, B) and back).
+ *   [GDN]  FlashInfer, "flashinfer.gdn_fused_decode_step" page: the fused
+ *          gated-delta-rule decode step over paged conv / ssm pools.
  *
  * Conventions shared by every entry point
  *   - Every tensor pointer is a DEVICE pointer owned by the caller, dense
@@ -222,6 +224,50 @@ ssu_status ssu_state_clear_layers(const ssu_state_layer *layers, int32_t num_lay
                                   int32_t resident_rows, int32_t slot,
                                   int64_t recurrent_row_bytes, int64_t conv_row_bytes,
                                   hipStream_t stream);
+
+/* ------------------------------------------------------------------------
+ * Fused gated-delta-rule decode step [GDN]: one token per batch entry.
+ * ---------------------------------------------------------------------- */
+typedef struct ssu_gdn_dims {
+    int32_t batch;
+    int32_t hidden;           /* rows of w_ba */
+    int32_t num_q_heads;      /* Hq: q and k heads */
+    int32_t num_v_heads;      /* HV: value heads, a multiple of Hq */
+    int32_t head_dim;         /* D = K = V, in {32, 64, 128, 256} */
+    int32_t conv_width;       /* W, 1..8 */
+    int32_t pool_rows;        /* P: leading extent of both pools */
+    int32_t use_qk_l2norm;
+    int64_t ssm_row_stride;   /* elements between pool rows of ssm_state; 0 = HV*D*D */
+    int64_t conv_slot_stride; /* conv_state element strides of its logical */
+    int64_t conv_chan_stride; /* [P, qkv_dim, W-1] view: DS-dense pools are    */
+    int64_t conv_tap_stride;  /* (qkv_dim*(W-1), W-1, 1), SD pools (.., 1, qkv_dim) */
+} ssu_gdn_dims;
+
+/* ssu_gdn_decode -- [GDN] with these readings of the steps the page names:
+ *   ba = hidden_states[b] @ w_ba; beta = sigmoid(ba[:, h]);
+ *   alpha = exp(-exp(A_log[h]) * softplus(ba[:, HV+h] + dt_bias[h]));
+ *   conv: window = [conv_state[s, c, 0..W-2], mixed_qkv[b, c]] (oldest first),
+ *         y_c = silu(sum_j window[j] conv_weight[c, j] + conv_bias[c]);
+ *         conv_state[s, c, :] = window[1..];
+ *   q | k | v = y channels [Hq D | Hq D | HV D]; value head h reads q/k head
+ *   h / (HV/Hq); q, k /= sqrt(sum x^2 + 1e-6) when use_qk_l2norm; q *= scale
+ *   (scale <= 0 or NaN selects 1/sqrt(D), as the page treats None and 0.0);
+ *   S = ssm_state[s, h] ([D(v), D(k)], V-major, K-last): S *= alpha;
+ *   S[v][:] += beta * (v[v] - S[v][:].k) k;  out[b, 0, h, v] = S[v][:].q.
+ * s = state_indices[b]; a negative index is a padding entry: no pool access,
+ * out[b] = +0.0. Indices >= P are undefined (the page: a caller bug).
+ * Dtypes as the page: hidden_states [B, hidden], w_ba [hidden, 2 HV],
+ * mixed_qkv [B, qkv_dim], conv_weight [qkv_dim, W], conv_bias [qkv_dim],
+ * conv_state, dt_bias [HV] and out [B, 1, HV, D] bf16; A_log [HV] and
+ * ssm_state [P, HV, D, D] fp32; qkv_dim = (2 Hq + HV) D. All device pointers;
+ * ssm_state 16-byte aligned with a row stride that keeps rows 16-byte
+ * aligned; every other pointer aligned to its element. Both pools are updated
+ * in place. */
+ssu_status ssu_gdn_decode(const ssu_gdn_dims *dims, const void *hidden_states, const void *w_ba,
+                          const void *mixed_qkv, const void *conv_weight, const void *conv_bias,
+                          void *conv_state, const float *A_log, const void *dt_bias, float scale,
+                          float *ssm_state, const int32_t *state_indices, void *out,
+                          hipStream_t stream);
 
 /* ------------------------------------------------------------------------
  * Row movement between a resident pool and contiguous working rows. A row is

@@ -21,7 +21,7 @@ OBJDIR = os.path.join(HERE, "_build")
 SOURCES = ["ssu_api.cpp", "ssu_decode.hip", "ssu_decode_f32.hip", "ssu_decode_f16.hip",
            "ssu_decode_bf16.hip", "ssu_prefill.hip", "ssu_prefill_f32.hip", "ssu_prefill_f16.hip",
            "ssu_prefill_bf16.hip", "ssu_replay.hip", "ssu_tree.hip", "ssu_tree_f32.hip",
-           "ssu_tree_f16.hip", "ssu_tree_bf16.hip", "ssu_pool_kernels.hip"]
+           "ssu_tree_f16.hip", "ssu_tree_bf16.hip", "ssu_gdn.hip", "ssu_pool_kernels.hip"]
 ARCH = "gfx950"
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 CFLAGS = ["-x", "hip", f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC",

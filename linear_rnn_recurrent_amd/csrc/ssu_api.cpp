@@ -1,6 +1,7 @@
 // C ABI of libssu: host-side argument checks, dispatch to the kernel
 // launchers, and the recurrent-state pool. No entry point reads device memory
 // on the host, synchronises, or allocates, except ssu_pool_alloc/ssu_pool_free.
+#include <math.h>
 #include <stdarg.h>
 #include <stdio.h>
 #include <string.h>
@@ -376,6 +377,76 @@ ssu_status ssu_state_clear_layers(const ssu_state_layer *layers, int32_t num_lay
     return hip_status(ssu::launch_clear_layers(layers, num_layers, resident_rows, slot,
                                                recurrent_row_bytes, conv_row_bytes, stream),
                       "ssu_state_clear_layers launch");
+}
+
+ssu_status ssu_gdn_decode(const ssu_gdn_dims *dims, const void *hidden_states, const void *w_ba,
+                          const void *mixed_qkv, const void *conv_weight, const void *conv_bias,
+                          void *conv_state, const float *A_log, const void *dt_bias, float scale,
+                          float *ssm_state, const int32_t *state_indices, void *out,
+                          hipStream_t stream)
+{
+    const char *fn = "ssu_gdn_decode";
+    if (!dims)
+        return fail(SSU_EINVAL, "%s: dims is NULL", fn);
+    const ssu_gdn_dims &d = *dims;
+    if (d.batch < 0 || d.hidden <= 0 || d.num_q_heads <= 0 || d.num_v_heads <= 0 ||
+        d.pool_rows <= 0)
+        return fail(SSU_EINVAL, "%s: batch >= 0, hidden/heads/pool_rows > 0 required", fn);
+    if (d.num_v_heads % d.num_q_heads != 0)
+        return fail(SSU_EINVAL, "%s: num_v_heads %d is not a multiple of num_q_heads %d", fn,
+                    d.num_v_heads, d.num_q_heads);
+    if (d.num_v_heads / d.num_q_heads > 8)
+        return fail(SSU_ENOTSUP, "%s: more than 8 value heads per q/k head", fn);
+    if (d.head_dim != 32 && d.head_dim != 64 && d.head_dim != 128 && d.head_dim != 256)
+        return fail(SSU_ENOTSUP, "%s: head_dim %d not in {32, 64, 128, 256}", fn, d.head_dim);
+    if (d.conv_width < 1 || d.conv_width > 8)
+        return fail(SSU_ENOTSUP, "%s: conv_width %d outside [1, 8]", fn, d.conv_width);
+    const int64_t tile = (int64_t)d.num_v_heads * d.head_dim * d.head_dim;
+    int64_t rs = d.ssm_row_stride ? d.ssm_row_stride : tile;
+    if (rs < tile || (rs * 4) % 16 != 0)
+        return fail(SSU_EINVAL, "%s: ssm_row_stride %lld must be >= HV*D*D and keep rows 16-byte aligned",
+                    fn, (long long)d.ssm_row_stride);
+    if (d.conv_slot_stride < 0 || d.conv_chan_stride < 0 || d.conv_tap_stride < 0)
+        return fail(SSU_EINVAL, "%s: negative conv_state stride", fn);
+    if (d.batch == 0)
+        return ok();
+    SSU_REQUIRE_PTR(hidden_states, 2, fn);
+    SSU_REQUIRE_PTR(w_ba, 2, fn);
+    SSU_REQUIRE_PTR(mixed_qkv, 2, fn);
+    SSU_REQUIRE_PTR(conv_weight, 2, fn);
+    SSU_REQUIRE_PTR(conv_bias, 2, fn);
+    if (d.conv_width > 1)
+        SSU_REQUIRE_PTR(conv_state, 2, fn);
+    SSU_REQUIRE_PTR(A_log, 4, fn);
+    SSU_REQUIRE_PTR(dt_bias, 2, fn);
+    SSU_REQUIRE_PTR(ssm_state, 16, fn);
+    SSU_REQUIRE_PTR(state_indices, 4, fn);
+    SSU_REQUIRE_PTR(out, 2, fn);
+    ssu::GdnParams p = {};
+    p.hs = hidden_states;
+    p.w_ba = w_ba;
+    p.qkv = mixed_qkv;
+    p.conv_w = conv_weight;
+    p.conv_b = conv_bias;
+    p.conv_state = conv_state;
+    p.A_log = A_log;
+    p.dt_bias = dt_bias;
+    p.scale = (scale > 0.0f) ? scale : 1.0f / sqrtf((float)d.head_dim);
+    p.ssm = ssm_state;
+    p.idx = state_indices;
+    p.out = out;
+    p.ssm_row_stride = rs;
+    p.cs_slot = d.conv_slot_stride;
+    p.cs_chan = d.conv_chan_stride;
+    p.cs_tap = d.conv_tap_stride;
+    p.batch = d.batch;
+    p.hidden = d.hidden;
+    p.hq = d.num_q_heads;
+    p.hv = d.num_v_heads;
+    p.dhead = d.head_dim;
+    p.width = d.conv_width;
+    p.use_l2 = d.use_qk_l2norm ? 1 : 0;
+    return hip_status(ssu::launch_gdn(p, stream), "ssu_gdn_decode launch");
 }
 
 namespace {

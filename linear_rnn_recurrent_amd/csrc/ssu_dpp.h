@@ -1,0 +1,29 @@
+// Cross-lane sums with DPP (data-parallel primitives): no LDS traffic.
+#pragma once
+
+#include <hip/hip_runtime.h>
+
+namespace ssu {
+
+template <int CTRL>
+__device__ __forceinline__ float dpp_f32(float a)
+{
+    return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, a),
+                                                                CTRL, 0xF, 0xF, false));
+}
+
+// Sum over aligned groups of W lanes (W = 4, 8 or 16): quad permutations, then
+// the half-row and row mirrors; every lane of a group gets the group's sum.
+template <int W>
+__device__ __forceinline__ float row_group_sum(float v)
+{
+    v += dpp_f32<0xB1>(v);  // quad_perm [1,0,3,2]
+    v += dpp_f32<0x4E>(v);  // quad_perm [2,3,0,1]
+    if constexpr (W >= 8)
+        v += dpp_f32<0x141>(v);  // row_half_mirror: lane i <- lane 7 - i of its half row
+    if constexpr (W >= 16)
+        v += dpp_f32<0x140>(v);  // row_mirror: lane i <- lane 15 - i
+    return v;
+}
+
+}  // namespace ssu

@@ -81,6 +81,20 @@ hipError_t launch_clear_layers(const ssu_state_layer *layers, int num_layers, in
 hipError_t launch_tree_f32(const TreeParams &p, hipStream_t stream);
 hipError_t launch_tree_f16(const TreeParams &p, hipStream_t stream);
 hipError_t launch_tree_bf16(const TreeParams &p, hipStream_t stream);
+struct GdnParams {
+    const void *hs, *w_ba, *qkv, *conv_w, *conv_b;
+    void *conv_state;
+    const float *A_log;
+    const void *dt_bias;
+    float scale;
+    float *ssm;
+    const int32_t *idx;
+    void *out;
+    int64_t ssm_row_stride, cs_slot, cs_chan, cs_tap;
+    int32_t batch, hidden, hq, hv, dhead, width, use_l2;
+};
+hipError_t launch_gdn(const GdnParams &p, hipStream_t stream);
+
 // One set of row moves: for b < rows, dst row (dst_idx ? dst_idx[b] : b) gets
 // src row (src_idx ? src_idx[b] : b); a negative destination index skips the
 // row, a negative source index (or src == null) writes zeros; with skip_same,

@@ -22,7 +22,7 @@ _DT = {torch.float32: SSU_F32, torch.float16: SSU_F16, torch.bfloat16: SSU_BF16,
 
 EXPORTS = ("ssu_decode", "ssu_prefill", "ssu_replay", "ssu_tree_verify", "ssu_replay_layers",
            "ssu_state_clear_layers", "ssu_state_gather", "ssu_state_scatter", "ssu_state_pack",
-           "ssu_state_unpack", "ssu_pool_bytes_per_slot",
+           "ssu_state_unpack", "ssu_gdn_decode", "ssu_pool_bytes_per_slot",
            "ssu_pool_alloc", "ssu_pool_free", "ssu_pool_info", "ssu_pool_state_ptr",
            "ssu_pool_state_bytes_per_slot", "ssu_pool_find_state", "ssu_pool_clear",
            "ssu_pool_clear_slot", "ssu_pool_capture", "ssu_pool_restore",
@@ -51,6 +51,15 @@ class ssu_replay_layer(ctypes.Structure):
 
 class ssu_state_layer(ctypes.Structure):
     _fields_ = [("recurrent_state", ctypes.c_void_p), ("conv_state", ctypes.c_void_p)]
+
+
+class ssu_gdn_dims(ctypes.Structure):
+    _fields_ = [("batch", ctypes.c_int32), ("hidden", ctypes.c_int32),
+                ("num_q_heads", ctypes.c_int32), ("num_v_heads", ctypes.c_int32),
+                ("head_dim", ctypes.c_int32), ("conv_width", ctypes.c_int32),
+                ("pool_rows", ctypes.c_int32), ("use_qk_l2norm", ctypes.c_int32),
+                ("ssm_row_stride", ctypes.c_int64), ("conv_slot_stride", ctypes.c_int64),
+                ("conv_chan_stride", ctypes.c_int64), ("conv_tap_stride", ctypes.c_int64)]
 
 
 class ssu_state_spec(ctypes.Structure):
@@ -89,6 +98,8 @@ def load_library(path: Optional[str] = None):
         "ssu_state_scatter": [_P, ctypes.c_int64, _P, _I32, ctypes.c_int64, _P, _I32,
                               ctypes.c_int64, _P],
         "ssu_state_pack": [_P, _I32, ctypes.c_int64, ctypes.c_int64, _P, _I32, _P, _I32, _P, _P],
+        "ssu_gdn_decode": [ctypes.POINTER(ssu_gdn_dims), _P, _P, _P, _P, _P, _P, _P, _P,
+                           ctypes.c_float, _P, _P, _P, _P],
         "ssu_state_unpack": [_P, _I32, ctypes.c_int64, ctypes.c_int64, _P, _I32, _P, _I32, _P, _P],
         "ssu_pool_bytes_per_slot": [S, _I32, ctypes.POINTER(ctypes.c_size_t)],
         "ssu_pool_alloc": [S, _I32, _I32, _P, ctypes.POINTER(_P)],
@@ -519,6 +530,58 @@ def ssu_state_pack(pool, homes, workspace, bystanders=None, stream=None):
 def ssu_state_unpack(pool, homes, workspace, bystanders=None, stream=None):
     """Slots [0, len(homes)) go back to their homes; bystanders are restored."""
     _pack_call("ssu_state_unpack", pool, homes, bystanders, workspace, stream)
+
+
+def ssu_gdn_decode(hidden_states, w_ba, mixed_qkv, conv_weight, conv_bias, conv_state, A_log,
+                   dt_bias, scale, ssm_state, state_indices, *, num_q_heads, use_qk_l2norm=True,
+                   out=None, stream=None):
+    """Fused gated-delta-rule decode step (one token per batch entry) over paged
+    conv / ssm pools, both updated in place. conv_state: a [P, qkv_dim, W-1]
+    view of any strides (a dense pool, or the transposed view of a
+    [P, W-1, qkv_dim] pool). Returns out [B, 1, HV, D] (bf16)."""
+    lib = load_library()
+    bf = (torch.bfloat16,)
+    _dense(hidden_states, "hidden_states", bf)
+    B, hidden = hidden_states.shape
+    _dense(w_ba, "w_ba", bf)
+    _need(w_ba.dim() == 2 and w_ba.shape[0] == hidden and w_ba.shape[1] % 2 == 0,
+          "w_ba must be [hidden, 2*HV]")
+    hv = w_ba.shape[1] // 2
+    hq = int(num_q_heads)
+    _need(hq > 0 and hv % hq == 0, "num_v_heads must be a multiple of num_q_heads")
+    _dense(conv_weight, "conv_weight", bf)
+    qkv, width = conv_weight.shape
+    _need(qkv % (2 * hq + hv) == 0, "qkv_dim must be (2*Hq + HV)*D")
+    d = qkv // (2 * hq + hv)
+    _dense(mixed_qkv, "mixed_qkv", bf, (B, qkv))
+    _dense(conv_bias, "conv_bias", bf, (qkv,))
+    _dev(conv_state, "conv_state", bf)
+    _need(conv_state.dim() == 3 and tuple(conv_state.shape[1:]) == (qkv, width - 1),
+          "conv_state must be a [P, qkv_dim, W-1] view")
+    _dense(A_log, "A_log", (torch.float32,), (hv,))
+    _dense(dt_bias, "dt_bias", bf, (hv,))
+    _dev(ssm_state, "ssm_state", (torch.float32,))
+    _need(ssm_state.dim() == 4 and tuple(ssm_state.shape[1:]) == (hv, d, d),
+          "ssm_state must be [P, HV, D, D]")
+    st = ssm_state.stride()
+    _need(st[3] == 1 and st[2] == d and st[1] == d * d, "ssm_state rows must be dense")
+    _need(ssm_state.shape[0] == conv_state.shape[0], "both pools have the same slots")
+    _dense(state_indices, "state_indices", (torch.int32,), (B,))
+    if out is None:
+        out = torch.empty((B, 1, hv, d), dtype=torch.bfloat16, device=hidden_states.device)
+    _dense(out, "out", bf, (B, 1, hv, d))
+    cs = conv_state.stride()
+    dims = ssu_gdn_dims(B, hidden, hq, hv, d, width, ssm_state.shape[0],
+                        1 if use_qk_l2norm else 0,
+                        st[0] if ssm_state.shape[0] > 1 else hv * d * d, cs[0], cs[1], cs[2])
+    sc = 0.0 if scale is None else float(scale)
+    with torch.cuda.device(hidden_states.device):
+        _check(lib.ssu_gdn_decode(ctypes.byref(dims), _ptr(hidden_states), _ptr(w_ba),
+                                  _ptr(mixed_qkv), _ptr(conv_weight), _ptr(conv_bias),
+                                  _ptr(conv_state), _ptr(A_log), _ptr(dt_bias), sc,
+                                  _ptr(ssm_state), _ptr(state_indices), _ptr(out),
+                                  _stream(hidden_states.device, stream)))
+    return out
 
 
 # ---------------------------------------------------------------------------
