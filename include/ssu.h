@@ -232,7 +232,7 @@ typedef struct ssu_gdn_dims {
     int32_t batch;
     int32_t hidden;           /* rows of w_ba */
     int32_t num_q_heads;      /* Hq: q and k heads */
-    int32_t num_v_heads;      /* HV: value heads, a multiple of Hq */
+    int32_t num_v_heads;      /* HV: value heads, HV/Hq in {1, 2, 4, 8} (else SSU_ENOTSUP) */
     int32_t head_dim;         /* D = K = V, in {32, 64, 128, 256} */
     int32_t conv_width;       /* W, 1..8 */
     int32_t pool_rows;        /* P: leading extent of both pools */
@@ -261,8 +261,9 @@ typedef struct ssu_gdn_dims {
  * conv_state, dt_bias [HV] and out [B, 1, HV, D] bf16; A_log [HV] and
  * ssm_state [P, HV, D, D] fp32; qkv_dim = (2 Hq + HV) D. All device pointers;
  * ssm_state 16-byte aligned with a row stride that keeps rows 16-byte
- * aligned; every other pointer aligned to its element. Both pools are updated
- * in place. */
+ * aligned; w_ba aligned to 2 HV/Hq bytes (a head group's weights in one row
+ * are read as one chunk); every other pointer aligned to its element
+ * (SSU_EINVAL otherwise). Both pools are updated in place. */
 ssu_status ssu_gdn_decode(const ssu_gdn_dims *dims, const void *hidden_states, const void *w_ba,
                           const void *mixed_qkv, const void *conv_weight, const void *conv_bias,
                           void *conv_state, const float *A_log, const void *dt_bias, float scale,

@@ -395,8 +395,9 @@ ssu_status ssu_gdn_decode(const ssu_gdn_dims *dims, const void *hidden_states, c
     if (d.num_v_heads % d.num_q_heads != 0)
         return fail(SSU_EINVAL, "%s: num_v_heads %d is not a multiple of num_q_heads %d", fn,
                     d.num_v_heads, d.num_q_heads);
-    if (d.num_v_heads / d.num_q_heads > 8)
-        return fail(SSU_ENOTSUP, "%s: more than 8 value heads per q/k head", fn);
+    const int G = d.num_v_heads / d.num_q_heads;
+    if (G != 1 && G != 2 && G != 4 && G != 8)
+        return fail(SSU_ENOTSUP, "%s: num_v_heads / num_q_heads = %d not in {1, 2, 4, 8}", fn, G);
     if (d.head_dim != 32 && d.head_dim != 64 && d.head_dim != 128 && d.head_dim != 256)
         return fail(SSU_ENOTSUP, "%s: head_dim %d not in {32, 64, 128, 256}", fn, d.head_dim);
     if (d.conv_width < 1 || d.conv_width > 8)
@@ -411,7 +412,7 @@ ssu_status ssu_gdn_decode(const ssu_gdn_dims *dims, const void *hidden_states, c
     if (d.batch == 0)
         return ok();
     SSU_REQUIRE_PTR(hidden_states, 2, fn);
-    SSU_REQUIRE_PTR(w_ba, 2, fn);
+    SSU_REQUIRE_PTR(w_ba, 2 * G, fn);
     SSU_REQUIRE_PTR(mixed_qkv, 2, fn);
     SSU_REQUIRE_PTR(conv_weight, 2, fn);
     SSU_REQUIRE_PTR(conv_bias, 2, fn);

@@ -26,4 +26,16 @@ __device__ __forceinline__ float row_group_sum(float v)
     return v;
 }
 
+// Sum over the whole 64-lane wave, returned wave-uniform: row sums by DPP,
+// then the four rows' sums read from lanes 0, 16, 32 and 48.
+__device__ __forceinline__ float wave_sum(float v)
+{
+    v = row_group_sum<16>(v);
+    const int u = __builtin_bit_cast(int, v);
+    return (__builtin_bit_cast(float, __builtin_amdgcn_readlane(u, 0)) +
+            __builtin_bit_cast(float, __builtin_amdgcn_readlane(u, 16))) +
+           (__builtin_bit_cast(float, __builtin_amdgcn_readlane(u, 32)) +
+            __builtin_bit_cast(float, __builtin_amdgcn_readlane(u, 48)));
+}
+
 }  // namespace ssu

@@ -332,3 +332,19 @@ def test_row_movement_validation(lib):
     assert p(homes=None) == 1 and "'homes'" in err(lib)
     assert p(batch=0, ws=None) == 0
     assert lib.ssu_state_unpack(FAKE, 4, 0, 64, FAKE, 3, None, 0, None, None) == 1
+
+
+def test_gdn_decode_validation(lib):
+    def call(hq=2, hv=4, d=128, w=4, rs=0, w_ba=FAKE, hs=FAKE, batch=2):
+        dd = S.ssu_gdn_dims(batch, 64, hq, hv, d, w, 4, 1, rs, 3 * (2 * hq + hv) * d, 3, 1)
+        return lib.ssu_gdn_decode(ctypes.byref(dd), hs, w_ba, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE,
+                                  ctypes.c_float(0.0), FAKE, FAKE, FAKE, None)
+    assert call(hv=3) == 1 and "multiple" in err(lib)
+    assert call(hq=1, hv=3) == 2 and "{1, 2, 4, 8}" in err(lib)
+    assert call(hq=1, hv=16) == 2
+    assert call(d=96) == 2 and "head_dim" in err(lib)
+    assert call(w=9) == 2 and "conv_width" in err(lib)
+    assert call(rs=4 * 128 * 128 - 4) == 1 and "ssm_row_stride" in err(lib)
+    assert call(w_ba=FAKE + 2) == 1 and "'w_ba'" in err(lib)          # G = 2: 4-byte chunks
+    assert call(hs=None) == 1 and "'hidden_states'" in err(lib)
+    assert call(batch=0, hs=None, w_ba=None) == 0

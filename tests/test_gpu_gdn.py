@@ -76,7 +76,7 @@ def test_qwen_shaped_layer_full_size():
 
 
 @pytest.mark.parametrize("head_dim", [32, 64, 128, 256])
-@pytest.mark.parametrize("hq,hv", [(2, 2), (2, 4), (1, 8)])
+@pytest.mark.parametrize("hq,hv", [(2, 2), (2, 4), (1, 4), (1, 8)])
 def test_head_dim_and_gqa(head_dim, hq, hv):
     w = inputs.gdn_workload(batch=3, hidden=96, num_q_heads=hq, num_v_heads=hv,
                             head_dim=head_dim, conv_width=4, pool_rows=5, seed=head_dim + hv)
