@@ -290,7 +290,8 @@ def main():
 
     import torch
     from linear_rnn_recurrent_amd import (ReplayLayerTable, StateLayerTable, inputs, load_library,
-                                          ssu_decode, ssu_gdn_decode, ssu_prefill,
+                                          gdn_workspace_bytes, ssu_decode, ssu_gdn_decode,
+                                          ssu_prefill,
                                           ssu_replay, ssu_replay_layers, ssu_state_clear_layers,
                                           ssu_state_gather, ssu_tree_verify)
 
@@ -450,6 +451,9 @@ def main():
         units = B * w.dims["num_v_heads"]
         out = torch.empty((B, 1, w.dims["num_v_heads"], w.dims["head_dim"]), dtype=torch.bfloat16,
                           device=dev)
+        ws = torch.empty(gdn_workspace_bytes(B, w.dims["hidden"], w.dims["num_q_heads"],
+                                             w.dims["num_v_heads"], w.dims["head_dim"]),
+                         dtype=torch.uint8, device=dev)
         rot = "steps rotate 4 disjoint 64-slot index sets over both pools"
 
         def step(i):
@@ -457,7 +461,7 @@ def main():
                            T["conv_bias"], T["conv_state"], T["A_log"], T["dt_bias"],
                            w.dims["scale"], T["ssm_state"], idx_sets[i % len(idx_sets)],
                            num_q_heads=w.dims["num_q_heads"],
-                           use_qk_l2norm=w.dims["use_qk_l2norm"], out=out)
+                           use_qk_l2norm=w.dims["use_qk_l2norm"], out=out, workspace=ws)
         src = source_hash("ssu_gdn.hip", "ssu_dpp.h", "ssu_device.h")
         kkey = "gdn_config9"
         bound, peak, unit = "hbm", HBM_PEAK_GBS, "GB/s"

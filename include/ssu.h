@@ -261,14 +261,25 @@ typedef struct ssu_gdn_dims {
  * conv_state, dt_bias [HV] and out [B, 1, HV, D] bf16; A_log [HV] and
  * ssm_state [P, HV, D, D] fp32; qkv_dim = (2 Hq + HV) D. All device pointers;
  * ssm_state 16-byte aligned with a row stride that keeps rows 16-byte
- * aligned; w_ba aligned to 2 HV/Hq bytes (a head group's weights in one row
- * are read as one chunk); every other pointer aligned to its element
- * (SSU_EINVAL otherwise). Both pools are updated in place. */
+ * aligned; w_ba 4-byte aligned; every other pointer aligned to its element
+ * (SSU_EINVAL otherwise). Both pools are updated in place. HV <= 256.
+ * workspace: caller-owned device scratch of at least ssu_gdn_workspace_bytes
+ * (dims) bytes, 16-byte aligned (it carries the normalised q/k, v and the
+ * b/a projection partial sums from the first of the two launches to the
+ * second); its contents on
+ * entry are ignored and on return unspecified. Calls that share a workspace
+ * must be ordered (one stream). */
 ssu_status ssu_gdn_decode(const ssu_gdn_dims *dims, const void *hidden_states, const void *w_ba,
                           const void *mixed_qkv, const void *conv_weight, const void *conv_bias,
                           void *conv_state, const float *A_log, const void *dt_bias, float scale,
                           float *ssm_state, const int32_t *state_indices, void *out,
-                          hipStream_t stream);
+                          void *workspace, int64_t workspace_bytes, hipStream_t stream);
+
+/* Bytes of workspace ssu_gdn_decode needs for these dims:
+ * 4 * B * (2 Hq D + HV D + 2 HV ceil(hidden / 256)); -1 if dims is NULL or
+ * has a non-positive hidden, head count or head_dim, or a negative batch.
+ * No HIP call. */
+int64_t ssu_gdn_workspace_bytes(const ssu_gdn_dims *dims);
 
 /* ------------------------------------------------------------------------
  * Row movement between a resident pool and contiguous working rows. A row is

@@ -379,11 +379,20 @@ ssu_status ssu_state_clear_layers(const ssu_state_layer *layers, int32_t num_lay
                       "ssu_state_clear_layers launch");
 }
 
+int64_t ssu_gdn_workspace_bytes(const ssu_gdn_dims *dims)
+{
+    if (!dims || dims->batch < 0 || dims->hidden <= 0 || dims->num_q_heads <= 0 ||
+        dims->num_v_heads <= 0 || dims->head_dim <= 0)
+        return -1;
+    return 4 * ssu::gdn_workspace_floats(dims->batch, dims->hidden, dims->num_q_heads,
+                                         dims->num_v_heads, dims->head_dim);
+}
+
 ssu_status ssu_gdn_decode(const ssu_gdn_dims *dims, const void *hidden_states, const void *w_ba,
                           const void *mixed_qkv, const void *conv_weight, const void *conv_bias,
                           void *conv_state, const float *A_log, const void *dt_bias, float scale,
                           float *ssm_state, const int32_t *state_indices, void *out,
-                          hipStream_t stream)
+                          void *workspace, int64_t workspace_bytes, hipStream_t stream)
 {
     const char *fn = "ssu_gdn_decode";
     if (!dims)
@@ -398,6 +407,8 @@ ssu_status ssu_gdn_decode(const ssu_gdn_dims *dims, const void *hidden_states, c
     const int G = d.num_v_heads / d.num_q_heads;
     if (G != 1 && G != 2 && G != 4 && G != 8)
         return fail(SSU_ENOTSUP, "%s: num_v_heads / num_q_heads = %d not in {1, 2, 4, 8}", fn, G);
+    if (d.num_v_heads > 256)
+        return fail(SSU_ENOTSUP, "%s: num_v_heads %d > 256", fn, d.num_v_heads);
     if (d.head_dim != 32 && d.head_dim != 64 && d.head_dim != 128 && d.head_dim != 256)
         return fail(SSU_ENOTSUP, "%s: head_dim %d not in {32, 64, 128, 256}", fn, d.head_dim);
     if (d.conv_width < 1 || d.conv_width > 8)
@@ -412,7 +423,7 @@ ssu_status ssu_gdn_decode(const ssu_gdn_dims *dims, const void *hidden_states, c
     if (d.batch == 0)
         return ok();
     SSU_REQUIRE_PTR(hidden_states, 2, fn);
-    SSU_REQUIRE_PTR(w_ba, 2 * G, fn);
+    SSU_REQUIRE_PTR(w_ba, 4, fn);
     SSU_REQUIRE_PTR(mixed_qkv, 2, fn);
     SSU_REQUIRE_PTR(conv_weight, 2, fn);
     SSU_REQUIRE_PTR(conv_bias, 2, fn);
@@ -423,7 +434,13 @@ ssu_status ssu_gdn_decode(const ssu_gdn_dims *dims, const void *hidden_states, c
     SSU_REQUIRE_PTR(ssm_state, 16, fn);
     SSU_REQUIRE_PTR(state_indices, 4, fn);
     SSU_REQUIRE_PTR(out, 2, fn);
+    SSU_REQUIRE_PTR(workspace, 16, fn);
+    const int64_t need = ssu_gdn_workspace_bytes(dims);
+    if (workspace_bytes < need)
+        return fail(SSU_EINVAL, "%s: workspace_bytes %lld < %lld required", fn,
+                    (long long)workspace_bytes, (long long)need);
     ssu::GdnParams p = {};
+    p.workspace = workspace;
     p.hs = hidden_states;
     p.w_ba = w_ba;
     p.qkv = mixed_qkv;

@@ -6,20 +6,30 @@
 // negative state_indices are padding entries (no pool access, zero output).
 // The formulas (the page names the steps only) are those stated in ssu.h.
 //
-// Mapping on gfx950. One 256-thread workgroup per (batch entry, q/k head h)
-// owns every channel that head's outputs depend on: the D q and D k channels
-// of h and the D v channels of each of its G = HV/Hq value heads, so each
-// conv-state channel is read and written by exactly one workgroup. The state
-// of the G value heads (G x D x D fp32, 128 KiB at D = 128, G = 2) dominates
-// the traffic and is streamed once: 16 lanes per state row (D/16 columns
-// each, interleaved in 16-byte chunks so that every non-temporal vector load
-// or store covers whole cache lines), four rows per wave, 16 rows
-// per workgroup pass. The first passes' loads are issued before anything
-// else, so they are in flight while the workgroup does its setup (the b/a
-// dot products for its G value heads, the conv update of its (2+G) D
-// channels, the q/k norms); later passes are prefetched a group of passes
-// ahead. Per row: decay, the prediction S.k, the delta update, the output S.q
-// -- the two row dots summed over the 16 lanes with DPP.
+// Mapping on gfx950: two launches on the caller's stream.
+//
+// 1. gdn_prep: everything but the state. Workgroup (b, h) of the first B*Hq
+//    owns every conv channel that q/k head h's outputs depend on (its D q and
+//    D k channels and the D v channels of its G = HV/Hq value heads), so each
+//    conv-state channel is read, shifted and written by exactly one thread;
+//    it also takes the q/k L2 norms and writes q*scale/|q|, k/|k| and v to the
+//    workspace. The remaining workgroups, one per (b, chunk of 256 hidden
+//    rows), compute partial sums of the b/a projection (hidden x 2HV) over
+//    their rows, reading the weight in whole rows (it is [hidden, 2HV]
+//    row-major: a per-head column slice would touch a cache line per row for
+//    a few useful bytes), one round of loads per thread.
+// 2. gdn_stream: the state, all but a few percent of the bytes. Every wave is
+//    independent (no barrier, no LDS): it owns a few rows of one value head's
+//    D x D fp32 state, 8 (or 16) lanes per row with the columns interleaved
+//    in 16-byte chunks so that every non-temporal vector load or store covers
+//    whole cache lines; it issues its state loads first, then reads its q/k
+//    slices, v values and the b/a partial sums from the workspace (cache
+//    hits), forms its head's gates, and per row applies decay, prediction,
+//    delta update and output (row dots summed over the row's lanes with DPP).
+// Splitting the step in two lets the state stream run as many small,
+// barrier-free waves that the dispatcher overlaps freely; in one launch each
+// workgroup had to finish its latency-bound setup before streaming, and the
+// workgroups sharing a CU spent much of the launch out of phase.
 #include "ssu_device.h"
 #include "ssu_dpp.h"
 #include "ssu_internal.h"
@@ -28,406 +38,463 @@ namespace ssu {
 namespace {
 
 constexpr int kGdnNT = 256;
+constexpr int kProjRows = 256;  // hidden rows per projection workgroup
 
-struct GdnShape {
-    int64_t ssm_row_stride, cs_slot, cs_chan, cs_tap;
-    int32_t hidden, hq, hv, width, use_l2, G;
+struct GdnPrepShape {
+    int64_t cs_slot, cs_chan, cs_tap;
+    int32_t batch, hidden, hq, hv, width, use_l2, proj_vec, nck;
     float scale;
 };
 
-// The G (a power of two) consecutive bf16 weights of one head group in one
-// projection row, as one load of 2 G bytes.
-template <int GM> struct BaChunk;
-template <> struct BaChunk<1> { typedef uint16_t T; };
-template <> struct BaChunk<2> { typedef uint32_t T; };
-template <> struct BaChunk<4> { typedef u32x2 T; };
-template <> struct BaChunk<8> { typedef u32x4 T; };
-
-template <int GM, int G>
-__device__ __forceinline__ float ba_col(const typename BaChunk<GM>::T &w)
+// Workspace layout (fp32): qk [B][Hq][2][D] (q*scale/|q|, k/|k|), v [B][HV][D],
+// part [B][NCK][2HV] (b/a projection partial sums per chunk of 256 rows).
+__host__ __device__ inline int64_t ws_v_off(int64_t B, int64_t hq, int64_t d) { return B * hq * 2 * d; }
+__host__ __device__ inline int64_t ws_p_off(int64_t B, int64_t hq, int64_t hv, int64_t d)
 {
-    if constexpr (GM == 1) {
-        return bf16_to_f32(w);
-    } else if constexpr (GM == 2) {
-        return G == 0 ? __uint_as_float(w << 16) : __uint_as_float(w & 0xFFFF0000u);
-    } else {
-        const uint32_t x = w[G / 2];
-        return (G & 1) ? __uint_as_float(x & 0xFFFF0000u) : __uint_as_float(x << 16);
-    }
+    return ws_v_off(B, hq, d) + B * hv * d;
 }
 
-// A state row of D = 16 EPL fp32 is spread over 16 lanes. Column layout: a
-// lane's e-th float is column col_of(l16, e); for EPL >= 4 its k-th 16-byte
-// vector holds columns 64 k + 4 l16 .. + 3, so the 16 lanes of a row cover
-// 256 consecutive bytes with each vector load or store (whole cache lines);
-// for EPL = 2 a lane holds columns 2 l16, 2 l16 + 1.
-template <int EPL>
-__device__ __forceinline__ int col_of(int l16, int e)
+// ---------------------------------------------------------------------------
+// gdn_prep, b/a projection role: workgroup (b, chunk ck of 256 hidden rows),
+// all 2HV columns. Thread t owns column chunk cc = t % NCH (CWC columns, one
+// 16- or 4-byte load per row) and row phase rp = t / NCH; the partial sums are
+// combined over the row phases through LDS and written per chunk.
+// ---------------------------------------------------------------------------
+template <int CWC>
+__device__ __forceinline__ void proj_row(const uint16_t *p, float (&w)[CWC])
 {
-    return EPL >= 4 ? (e / 4) * 64 + l16 * 4 + (e % 4) : l16 * 2 + e;
-}
-
-// p: the row's first element plus the lane's base offset lane_off<EPL>(l16)
-template <int EPL>
-__device__ __forceinline__ int lane_off(int l16) { return EPL >= 4 ? l16 * 4 : l16 * 2; }
-
-template <int EPL>
-__device__ __forceinline__ void ld_row(const float *p, float (&x)[EPL])
-{
-    if constexpr (EPL % 4 == 0) {
+    if constexpr (CWC == 8) {
+        const u32x4 v = *reinterpret_cast<const u32x4 *>(p);
 #pragma unroll
-        for (int e = 0; e < EPL; e += 4) {
-            const u32x4 w = __builtin_nontemporal_load(reinterpret_cast<const u32x4 *>(p + e * 16));
-#pragma unroll
-            for (int j = 0; j < 4; ++j)
-                x[e + j] = __uint_as_float(w[j]);
+        for (int j = 0; j < 4; ++j) {
+            w[2 * j] = __uint_as_float(v[j] << 16);
+            w[2 * j + 1] = __uint_as_float(v[j] & 0xFFFF0000u);
         }
     } else {
-        static_assert(EPL == 2, "rows split into 2, 4, 8 or 16 columns per lane");
-        const u32x2 w = __builtin_nontemporal_load(reinterpret_cast<const u32x2 *>(p));
-        x[0] = __uint_as_float(w[0]);
-        x[1] = __uint_as_float(w[1]);
+        const uint32_t v = *reinterpret_cast<const uint32_t *>(p);
+        w[0] = __uint_as_float(v << 16);
+        w[1] = __uint_as_float(v & 0xFFFF0000u);
     }
 }
 
-template <int EPL>
-__device__ __forceinline__ void st_row(float *p, const float (&x)[EPL])
-{
-    if constexpr (EPL % 4 == 0) {
-#pragma unroll
-        for (int e = 0; e < EPL; e += 4)
-            __builtin_nontemporal_store(
-                u32x4{__float_as_uint(x[e]), __float_as_uint(x[e + 1]), __float_as_uint(x[e + 2]),
-                      __float_as_uint(x[e + 3])},
-                reinterpret_cast<u32x4 *>(p + e * 16));
-    } else {
-        __builtin_nontemporal_store(u32x2{__float_as_uint(x[0]), __float_as_uint(x[1])},
-                                    reinterpret_cast<u32x2 *>(p));
-    }
-}
-
-// Workgroups per CU the register budget is held to: four keep a B = 64,
-// Hq = 16 launch (1024 workgroups) resident in one round; the wide-window and
-// D = 64, G = 8 variants need more registers than that allows.
-template <int D, int GM, int WM>
-constexpr int gdn_min_blocks() { return (WM > 4 || (D == 64 && GM == 8)) ? 1 : 4; }
-
-// D: head dim; GM: value heads per q/k head (G = GM, a power of two); WM: conv width bound (the runtime width W <= WM; WM = 1
-// exactly when W = 1, so the other instantiations always have a tap to read).
-template <int D, int GM, int WM>
-__global__ __launch_bounds__(kGdnNT, (gdn_min_blocks<D, GM, WM>())) void ssu_gdn_kernel(
-    const uint16_t *__restrict__ hs, const uint16_t *__restrict__ w_ba,
-    const uint16_t *__restrict__ mixed_qkv, const uint16_t *__restrict__ conv_w,
-    const uint16_t *__restrict__ conv_b, uint16_t *__restrict__ conv_state,
-    const float *__restrict__ A_log, const uint16_t *__restrict__ dt_bias, float *__restrict__ ssm,
-    const int32_t *__restrict__ idx, uint16_t *__restrict__ out, const GdnShape sh)
+template <int CWC>
+__device__ void gdn_projection(int b, int ck, const uint16_t *__restrict__ hs,
+                               const uint16_t *__restrict__ w_ba, float *__restrict__ part_out,
+                               const GdnPrepShape &sh, float *lds)
 {
     constexpr int NT = kGdnNT;
-    constexpr int EPL = D / 16;                             // state columns per lane
-    constexpr int PF = EPL >= 16 ? 2 : (EPL >= 8 ? 4 : 8);  // passes of loads in flight
-    constexpr int KV = GM <= 2 ? 16 : (GM == 4 ? 8 : 4);     // projection rows per lane per batch
-    constexpr int CPT = ((2 + GM) * D + NT - 1) / NT;       // owned channels per thread (bound)
-    constexpr int CB = CPT < 2 ? CPT : 2;                   // channels per load batch
-    constexpr int NTAP = WM > 1 ? WM - 1 : 1;
-    constexpr int NRED = 2 * GM + 2;                        // b, a dots; |q|^2, |k|^2
-    __shared__ float ych[(2 + GM) * D];                     // conv outputs: q | k | v of G heads
-    __shared__ float red[NT / 64][NRED];                    // per-wave partial sums
-
+    constexpr int U = 8;             // rows in flight per thread
     const int tid = threadIdx.x;
-    const int lane = tid & 63;
-    const int wave = tid >> 6;
-    constexpr int G = GM;
-    const int Hq = sh.hq, HV = sh.hv, W = sh.width, hidden = sh.hidden;
-    const int b = blockIdx.x / Hq;
-    const int h = blockIdx.x - b * Hq;
-    const int hv0 = h * G;
-    const int nch = (2 + G) * D;
-    const int HD = Hq * D;
-    const int s = idx[b];
-    const int64_t out0 = ((int64_t)b * HV + hv0) * D;
-
-    if (s < 0) {  // padding entry (uniform over the workgroup): no pool access, zero output
-        for (int i = tid; i < G * D; i += NT)
-            out[out0 + i] = 0;
-        return;
+    const int NC = 2 * sh.hv;
+    const int NCH = NC / CWC;        // column chunks (<= NT)
+    const int RPH = NT / NCH;        // row phases
+    const int cc = tid % NCH, rp = tid / NCH;
+    const bool active = rp < RPH;
+    const int r0 = ck * kProjRows;
+    const int cn = min(kProjRows, sh.hidden - r0);
+    float *hid = lds;                // this chunk's hidden values
+    float *part = lds + kProjRows;   // [RPH][NC] partial sums
+    if (tid < cn)
+        hid[tid] = bf16_to_f32(hs[(int64_t)b * sh.hidden + r0 + tid]);
+    float acc[CWC];
+#pragma unroll
+    for (int j = 0; j < CWC; ++j)
+        acc[j] = 0.0f;
+    const uint16_t *wb = w_ba + (int64_t)r0 * NC + cc * CWC;
+    __syncthreads();
+    if (active) {
+        for (int ra = rp; ra < cn; ra += U * RPH) {
+            float w[U][CWC];
+#pragma unroll
+            for (int u = 0; u < U; ++u)
+                proj_row<CWC>(wb + (int64_t)min(ra + u * RPH, cn - 1) * NC, w[u]);
+#pragma unroll
+            for (int u = 0; u < U; ++u) {
+                const int r = ra + u * RPH;
+                const float x = r < cn ? hid[r] : 0.0f;
+#pragma unroll
+                for (int j = 0; j < CWC; ++j)
+                    acc[j] = fmaf(x, w[u][j], acc[j]);
+            }
+        }
+#pragma unroll
+        for (int j = 0; j < CWC; ++j)
+            part[rp * NC + cc * CWC + j] = acc[j];
     }
+    __syncthreads();
+    for (int t = tid; t < NC; t += NT) {
+        float v = 0.0f;
+        for (int r = 0; r < RPH; ++r)
+            v += part[r * NC + t];
+        part_out[((int64_t)b * sh.nck + ck) * NC + t] = v;
+    }
+}
 
-    // ---- issue every setup load before any use: b/a rows, conv inputs ----
-    const uint16_t *hsb = hs + (int64_t)b * hidden;
-    const int64_t wrow = 2 * (int64_t)HV;
-    // Lane pairs share a projection row (one cache line): the even lane reads
-    // the G beta-gate weights of this head group, the odd lane the G decay
-    // weights, each as one chunk.
-    typedef typename BaChunk<GM>::T WT;
-    const int part = tid & 1;
-    const int rlane = tid >> 1;
-    uint32_t hx[KV];
-    WT wv[KV];
-    auto load_ba = [&](int i0) {
-#pragma unroll
-        for (int k = 0; k < KV; ++k) {
-            const int ic = min(i0 + rlane + (NT / 2) * k, hidden - 1);
-            hx[k] = hsb[ic];
-            wv[k] = *reinterpret_cast<const WT *>(w_ba + ic * wrow + part * HV + hv0);
-        }
-    };
-    float acc[GM];
-#pragma unroll
-    for (int g = 0; g < GM; ++g)
-        acc[g] = 0.0f;
-    auto fma_ba = [&](int i0) {
-#pragma unroll
-        for (int k = 0; k < KV; ++k) {
-            const float x = (i0 + rlane + (NT / 2) * k < hidden) ? bf16_to_f32(hx[k]) : 0.0f;
-            acc[0] = fmaf(x, ba_col<GM, 0>(wv[k]), acc[0]);
-            if constexpr (GM > 1)
-                acc[1] = fmaf(x, ba_col<GM, 1>(wv[k]), acc[1]);
-            if constexpr (GM > 2) {
-                acc[2] = fmaf(x, ba_col<GM, 2>(wv[k]), acc[2]);
-                acc[3] = fmaf(x, ba_col<GM, 3>(wv[k]), acc[3]);
-            }
-            if constexpr (GM > 4) {
-                acc[4] = fmaf(x, ba_col<GM, 4>(wv[k]), acc[4]);
-                acc[5] = fmaf(x, ba_col<GM, 5>(wv[k]), acc[5]);
-                acc[6] = fmaf(x, ba_col<GM, 6>(wv[k]), acc[6]);
-                acc[7] = fmaf(x, ba_col<GM, 7>(wv[k]), acc[7]);
-            }
-        }
-    };
+// ---------------------------------------------------------------------------
+// gdn_prep, conv role: workgroup (b, h). D: head dim; GM: G (a power of two);
+// WM: conv width bound (W <= WM; WM = 1 exactly when W = 1, so the other
+// instantiations always have a tap to read).
+// ---------------------------------------------------------------------------
+template <int D, int GM, int WM>
+__device__ void gdn_conv(int b, int h, const uint16_t *__restrict__ mixed_qkv,
+                         const uint16_t *__restrict__ conv_w, const uint16_t *__restrict__ conv_b,
+                         uint16_t *__restrict__ conv_state, int s, float *__restrict__ ws,
+                         const GdnPrepShape &sh, float *lds)
+{
+    constexpr int NT = kGdnNT;
+    constexpr int G = GM;
+    constexpr int NCH = (2 + G) * D;          // owned channels
+    constexpr int CPT = (NCH + NT - 1) / NT;  // channels per thread
+    constexpr int NTAP = WM > 1 ? WM - 1 : 1;
+    const int tid = threadIdx.x;
+    const int lane = tid & 63, wave = tid >> 6;
+    const int Hq = sh.hq, HV = sh.hv, W = sh.width;
+    const int hv0 = h * G;
+    const int HD = Hq * D;
+    const int64_t qkv_dim = 2 * (int64_t)HD + (int64_t)HV * D;
     auto chan = [&](int j) {
         return j < D ? h * D + j : (j < 2 * D ? HD + h * D + (j - D) : 2 * HD + hv0 * D + (j - 2 * D));
     };
-    const int64_t qkv_dim = 2 * (int64_t)HD + (int64_t)HV * D;
-    uint32_t cbias[CB], cx[CB], cwt[CB][WM], ctap[CB][NTAP];
-    auto load_conv = [&](int j0) {
+    // every load first (pool taps from HBM, the rest from cache), then the math
+    uint32_t cbias[CPT], cx[CPT], cwt[CPT][WM], ctap[CPT][NTAP];
 #pragma unroll
-        for (int k = 0; k < CB; ++k) {
-            const int c = chan(min(j0 + tid + NT * k, nch - 1));
-            cbias[k] = conv_b[c];
-            cx[k] = mixed_qkv[b * qkv_dim + c];
+    for (int k = 0; k < CPT; ++k) {
+        const int c = chan(min(tid + NT * k, NCH - 1));
+        if constexpr (WM > 1) {  // here W >= 2: every tap index is in the pool
+            const uint16_t *cs = conv_state + (int64_t)s * sh.cs_slot + (int64_t)c * sh.cs_chan;
 #pragma unroll
-            for (int t = 0; t < WM; ++t)
-                cwt[k][t] = conv_w[(int64_t)c * W + min(t, W - 1)];
-            if constexpr (WM > 1) {  // here W >= 2: every tap index is in the pool
-                const uint16_t *cs = conv_state + (int64_t)s * sh.cs_slot + (int64_t)c * sh.cs_chan;
-#pragma unroll
-                for (int t = 0; t < NTAP; ++t)
-                    ctap[k][t] = cs[min(t, W - 2) * sh.cs_tap];
-            }
+            for (int t = 0; t < NTAP; ++t)
+                ctap[k][t] = cs[min(t, W - 2) * sh.cs_tap];
         }
-    };
+        cbias[k] = conv_b[c];
+        cx[k] = mixed_qkv[b * qkv_dim + c];
+#pragma unroll
+        for (int t = 0; t < WM; ++t)
+            cwt[k][t] = conv_w[(int64_t)c * W + min(t, W - 1)];
+    }
+    float y[CPT];
     float ssq = 0.0f, ssk = 0.0f;
-    auto conv_step = [&](int j0) {
 #pragma unroll
-        for (int k = 0; k < CB; ++k) {
-            const int j = j0 + tid + NT * k;
-            if (j < nch) {
-                const int c = chan(j);
-                float y = bf16_to_f32(cbias[k]);
-                float wl = 0.0f;
+    for (int k = 0; k < CPT; ++k) {
+        const int j = tid + NT * k;
+        float acc = bf16_to_f32(cbias[k]);
+        float wl = 0.0f;
 #pragma unroll
-                for (int t = 0; t < WM; ++t) {
-                    if (WM > 1 && t < W - 1 && t < NTAP)
-                        y = fmaf(bf16_to_f32(ctap[k][t < NTAP ? t : 0]), bf16_to_f32(cwt[k][t]), y);
-                    if (t == W - 1)
-                        wl = bf16_to_f32(cwt[k][t]);
-                }
-                y = fmaf(bf16_to_f32(cx[k]), wl, y);
-                // the pool keeps the last W-1 raw inputs: tap t <- tap t+1, newest last
-                if constexpr (WM > 1) {
-                    uint16_t *cs = conv_state + (int64_t)s * sh.cs_slot + (int64_t)c * sh.cs_chan;
+        for (int t = 0; t < WM; ++t) {
+            if (WM > 1 && t < W - 1 && t < NTAP)
+                acc = fmaf(bf16_to_f32(ctap[k][t < NTAP ? t : 0]), bf16_to_f32(cwt[k][t]), acc);
+            if (t == W - 1)
+                wl = bf16_to_f32(cwt[k][t]);
+        }
+        acc = fmaf(bf16_to_f32(cx[k]), wl, acc);
+        y[k] = silu_f32(acc);
+        if (j < NCH) {
+            // the pool keeps the last W-1 raw inputs: tap t <- tap t+1, newest last
+            if constexpr (WM > 1) {
+                uint16_t *cs = conv_state + (int64_t)s * sh.cs_slot + (int64_t)chan(j) * sh.cs_chan;
 #pragma unroll
-                    for (int t = 0; t < NTAP; ++t) {
-                        if (t < W - 1) {
-                            const uint32_t v = (t + 1 < NTAP && t + 1 < W - 1)
-                                                   ? ctap[k][t + 1 < NTAP ? t + 1 : 0]
-                                                   : cx[k];
-                            cs[t * sh.cs_tap] = (uint16_t)v;
-                        }
+                for (int t = 0; t < NTAP; ++t) {
+                    if (t < W - 1) {
+                        const uint32_t v = (t + 1 < NTAP && t + 1 < W - 1)
+                                               ? ctap[k][t + 1 < NTAP ? t + 1 : 0]
+                                               : cx[k];
+                        cs[t * sh.cs_tap] = (uint16_t)v;
                     }
                 }
-                const float ys = silu_f32(y);
-                ych[j] = ys;
-                const float y2 = ys * ys;
-                ssq += j < D ? y2 : 0.0f;
-                ssk += (j >= D && j < 2 * D) ? y2 : 0.0f;
             }
+            const float y2 = y[k] * y[k];
+            ssq += j < D ? y2 : 0.0f;
+            ssk += (j >= D && j < 2 * D) ? y2 : 0.0f;
         }
-    };
-    load_conv(0);  // pool taps first: they come from HBM, the projection from cache
-    load_ba(0);
-
-    // ---- then the first passes of state loads: in flight during the setup math ----
-    const int l16 = lane & 15;
-    const int rsub = wave * 4 + (lane >> 4);  // row within a 16-row pass
-    const int NP = G * D / 16;                // passes
-    float *ssm_h = ssm + (int64_t)s * sh.ssm_row_stride + (int64_t)hv0 * D * D + lane_off<EPL>(l16);
-    auto row_ptr = [&](int p) { return ssm_h + (int64_t)(16 * p + rsub) * D; };
-    float cur[PF][EPL];
-    // vmcnt retires in order: the state loads go strictly after the setup
-    // loads, so waiting for a setup value never waits for the state
-    __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-    for (int k = 0; k < PF; ++k)
-        ld_row<EPL>(row_ptr(min(k, NP - 1)), cur[k]);
-    __builtin_amdgcn_sched_barrier(0);
-
-    fma_ba(0);
-    for (int i0 = (NT / 2) * KV; i0 < hidden; i0 += (NT / 2) * KV) {
-        load_ba(i0);
-        fma_ba(i0);
     }
-    conv_step(0);
-    for (int j0 = NT * CB; j0 < nch; j0 += NT * CB) {
-        load_conv(j0);
-        conv_step(j0);
-    }
-
-    // ---- one exchange: per-wave partial sums; every wave finishes them itself ----
-    {
-        float red_w[NRED];
-#pragma unroll
-        for (int g = 0; g < GM; ++g) {
-            red_w[g] = wave_sum(part ? 0.0f : acc[g]);       // beta-gate input
-            red_w[GM + g] = wave_sum(part ? acc[g] : 0.0f);  // decay input
-        }
-        red_w[2 * GM] = wave_sum(ssq);
-        red_w[2 * GM + 1] = wave_sum(ssk);
-        if (lane == 0) {
-#pragma unroll
-            for (int i = 0; i < NRED; ++i)
-                red[wave][i] = red_w[i];
-        }
+    const float wq = wave_sum(ssq), wk = wave_sum(ssk);
+    if (lane == 0) {
+        lds[2 * wave] = wq;
+        lds[2 * wave + 1] = wk;
     }
     __syncthreads();
-    float alpha[GM], beta[GM];
+    const float sq = (lds[0] + lds[2]) + (lds[4] + lds[6]);
+    const float sk = (lds[1] + lds[3]) + (lds[5] + lds[7]);
+    const float iq = (sh.use_l2 ? 1.0f / sqrtf(sq + 1e-6f) : 1.0f) * sh.scale;
+    const float ik = sh.use_l2 ? 1.0f / sqrtf(sk + 1e-6f) : 1.0f;
+    float *qk = ws + ((int64_t)b * Hq + h) * 2 * D;
+    float *vv = ws + ws_v_off(sh.batch, Hq, D) + ((int64_t)b * HV + hv0) * D;
 #pragma unroll
-    for (int g = 0; g < GM; ++g) {
-        const float bb = (red[0][g] + red[1][g]) + (red[2][g] + red[3][g]);
-        const float aa = (red[0][GM + g] + red[1][GM + g]) + (red[2][GM + g] + red[3][GM + g]);
-        const int hh = hv0 + g;
-        const float sp = softplus_f32(aa + bf16_to_f32(dt_bias[hh]));
-        alpha[g] = expf(-expf(A_log[hh]) * sp);
-        beta[g] = 1.0f / (1.0f + expf(-bb));
-    }
-    float qv[EPL], kv[EPL];
-    {
-        const float sq = (red[0][2 * GM] + red[1][2 * GM]) + (red[2][2 * GM] + red[3][2 * GM]);
-        const float sk =
-            (red[0][2 * GM + 1] + red[1][2 * GM + 1]) + (red[2][2 * GM + 1] + red[3][2 * GM + 1]);
-        const float iq = (sh.use_l2 ? 1.0f / sqrtf(sq + 1e-6f) : 1.0f) * sh.scale;
-        const float ik = sh.use_l2 ? 1.0f / sqrtf(sk + 1e-6f) : 1.0f;
-#pragma unroll
-        for (int e = 0; e < EPL; ++e) {
-            qv[e] = ych[col_of<EPL>(l16, e)] * iq;
-            kv[e] = ych[D + col_of<EPL>(l16, e)] * ik;
-        }
-    }
-
-    // ---- stream the state: PF passes at a time, the next group in flight ----
-    for (int p0 = 0; p0 < NP; p0 += PF) {
-        float nxt[PF][EPL];
-        const bool more = p0 + PF < NP;
-        if (more) {
-#pragma unroll
-            for (int k = 0; k < PF; ++k)
-                ld_row<EPL>(row_ptr(min(p0 + PF + k, NP - 1)), nxt[k]);
-        }
-#pragma unroll
-        for (int k = 0; k < PF; ++k) {
-            const int p = p0 + k;
-            if (p < NP) {
-                const int g = p / (D / 16);           // value head of this pass (uniform)
-                const int v = 16 * (p - g * (D / 16)) + rsub;
-                float al = alpha[0], be = beta[0];
-#pragma unroll
-                for (int gg = 1; gg < GM; ++gg) {
-                    if (g == gg) {
-                        al = alpha[gg];
-                        be = beta[gg];
-                    }
-                }
-                float pk = 0.0f;
-#pragma unroll
-                for (int e = 0; e < EPL; ++e) {
-                    cur[k][e] *= al;
-                    pk = fmaf(cur[k][e], kv[e], pk);
-                }
-                pk = row_group_sum<16>(pk);
-                const float delta = be * (ych[(2 + g) * D + v] - pk);
-                float po = 0.0f;
-#pragma unroll
-                for (int e = 0; e < EPL; ++e) {
-                    cur[k][e] = fmaf(delta, kv[e], cur[k][e]);
-                    po = fmaf(cur[k][e], qv[e], po);
-                }
-                po = row_group_sum<16>(po);
-                st_row<EPL>(row_ptr(p), cur[k]);
-                if (l16 == 0)
-                    out[out0 + g * D + v] = (uint16_t)f32_to_bf16(po);
-            }
-        }
-        if (more) {
-#pragma unroll
-            for (int k = 0; k < PF; ++k)
-#pragma unroll
-                for (int e = 0; e < EPL; ++e)
-                    cur[k][e] = nxt[k][e];
-        }
+    for (int k = 0; k < CPT; ++k) {
+        const int j = tid + NT * k;
+        if (j < D)
+            qk[j] = y[k] * iq;
+        else if (j < 2 * D)
+            qk[j] = y[k] * ik;
+        else if (j < NCH)
+            vv[j - 2 * D] = y[k];
     }
 }
 
 template <int D, int GM, int WM>
-hipError_t launch_dgw(const GdnParams &p, const GdnShape &sh, hipStream_t stream)
+__global__ __launch_bounds__(kGdnNT) void gdn_prep_kernel(
+    const uint16_t *__restrict__ hs, const uint16_t *__restrict__ w_ba,
+    const uint16_t *__restrict__ mixed_qkv, const uint16_t *__restrict__ conv_w,
+    const uint16_t *__restrict__ conv_b, uint16_t *__restrict__ conv_state,
+    const int32_t *__restrict__ idx, float *__restrict__ ws, const GdnPrepShape sh)
 {
-    const int64_t blocks = (int64_t)p.batch * p.hq;
+    __shared__ float lds[kProjRows + kGdnNT * 8];
+    const int B = sh.batch;
+    const int nconv = B * sh.hq;
+    if ((int)blockIdx.x >= nconv) {  // projection role (uniform over the workgroup)
+        const int j = blockIdx.x - nconv;
+        const int b = j / sh.nck, ck = j - b * sh.nck;
+        if (idx[b] < 0)
+            return;
+        float *part = ws + ws_p_off(B, sh.hq, sh.hv, D);
+        if (sh.proj_vec)
+            gdn_projection<8>(b, ck, hs, w_ba, part, sh, lds);
+        else
+            gdn_projection<2>(b, ck, hs, w_ba, part, sh, lds);
+        return;
+    }
+    const int b = blockIdx.x / sh.hq;
+    const int h = blockIdx.x - b * sh.hq;
+    const int s = idx[b];
+    if (s < 0)  // padding entry: no pool access; the stream writes its zero output
+        return;
+    gdn_conv<D, GM, WM>(b, h, mixed_qkv, conv_w, conv_b, conv_state, s, ws, sh, lds);
+}
+
+// ---------------------------------------------------------------------------
+// gdn_stream
+// ---------------------------------------------------------------------------
+// A state row (D fp32) is spread over LPR lanes (8; 16 at D = 256), EPL = D /
+// LPR floats each, as NV = EPL / 4 16-byte vectors: lane l's vector v holds
+// columns 4 LPR v + 4 l .. + 3, so each vector access of a row's LPR lanes
+// covers 16 LPR >= 128 consecutive bytes (whole cache lines). One wave
+// instruction serves RPI = 64 / LPR rows; a wave runs PW such passes.
+template <int D>
+struct StreamCfg {
+    static constexpr int LPR = D == 256 ? 16 : 8;
+    static constexpr int EPL = D / LPR;
+    static constexpr int NV = EPL / 4;
+    static constexpr int RPI = 64 / LPR;
+    static constexpr int PW = D == 32 ? 1 : 2;
+    static constexpr int RPW = RPI * PW;   // rows per wave
+    static constexpr int RPB = 4 * RPW;    // rows per workgroup
+    static constexpr int NPH = D / RPB;    // workgroups per value head
+    static_assert(NV >= 1 && NPH >= 1 && NPH * RPB == D, "stream tiling");
+};
+
+// p: the row's first element + 4 l
+template <int NV, int LPR>
+__device__ __forceinline__ void ld_row(const float *p, float (&x)[4 * NV])
+{
+#pragma unroll
+    for (int v = 0; v < NV; ++v) {
+        const u32x4 w = __builtin_nontemporal_load(reinterpret_cast<const u32x4 *>(p + v * 4 * LPR));
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+            x[4 * v + j] = __uint_as_float(w[j]);
+    }
+}
+
+template <int NV, int LPR>
+__device__ __forceinline__ void st_row(float *p, const float (&x)[4 * NV])
+{
+#pragma unroll
+    for (int v = 0; v < NV; ++v)
+        __builtin_nontemporal_store(
+            u32x4{__float_as_uint(x[4 * v]), __float_as_uint(x[4 * v + 1]),
+                  __float_as_uint(x[4 * v + 2]), __float_as_uint(x[4 * v + 3])},
+            reinterpret_cast<u32x4 *>(p + v * 4 * LPR));
+}
+
+// the same column layout for a (cached) D-vector in the workspace
+template <int NV, int LPR>
+__device__ __forceinline__ void ld_vec(const float *p, float (&x)[4 * NV])
+{
+#pragma unroll
+    for (int v = 0; v < NV; ++v) {
+        const float4 w = *reinterpret_cast<const float4 *>(p + v * 4 * LPR);
+        x[4 * v] = w.x;
+        x[4 * v + 1] = w.y;
+        x[4 * v + 2] = w.z;
+        x[4 * v + 3] = w.w;
+    }
+}
+
+// exp via the hardware exp2 (relative error a few 1e-7 over the gates' range)
+__device__ __forceinline__ float fast_exp(float x) { return __builtin_amdgcn_exp2f(x * 1.4426950408889634f); }
+
+// bf16 bits of f, round to nearest even, NaN kept quiet; selects, no branch
+__device__ __forceinline__ uint32_t bf16_bits(float f)
+{
+    const uint32_t u = __float_as_uint(f);
+    const uint32_t r = (u + 0x7fffu + ((u >> 16) & 1u)) >> 16;
+    return (u & 0x7fffffffu) > 0x7f800000u ? ((u >> 16) | 0x40u) : r;
+}
+
+struct GdnStreamShape {
+    int64_t ssm_row_stride;
+    int32_t batch, hq, hv, nck;
+};
+
+// Per row, with x the state row before the step, a = alpha, k / q the
+// normalised key / scaled query: pk = x.k and po = x.q (both reduced over the
+// row's lanes together), delta = beta (v - a pk), out = a po + delta (k.q),
+// x' = a x + delta k -- the same values as decaying the row, predicting,
+// updating and then reading the output, with the two reductions independent.
+template <int D>
+__global__ __launch_bounds__(kGdnNT) void gdn_stream_kernel(
+    float *__restrict__ ssm, const int32_t *__restrict__ idx, const float *__restrict__ ws,
+    const float *__restrict__ A_log, const uint16_t *__restrict__ dt_bias,
+    uint16_t *__restrict__ out, const GdnStreamShape sh)
+{
+    using C = StreamCfg<D>;
+    constexpr int LPR = C::LPR, EPL = C::EPL, NV = C::NV, PW = C::PW, RPI = C::RPI;
+    const int tid = threadIdx.x;
+    const int lane = tid & 63, wave = tid >> 6;
+    const int l = lane & (LPR - 1);
+    const int HV = sh.hv;
+    const int bh = blockIdx.x / C::NPH;  // b * HV + hv
+    const int part = blockIdx.x - bh * C::NPH;
+    const int b = bh / HV, hv = bh - b * HV;
+    const int h = hv / (HV / sh.hq);     // q/k head of this value head
+    const int row0 = part * C::RPB + wave * C::RPW + lane / LPR;  // rows row0 + RPI p
+    const int s = idx[b];
+    uint16_t *ob = out + (int64_t)bh * D;
+    if (s < 0) {  // padding entry: zero output
+        if (l == 0) {
+#pragma unroll
+            for (int p = 0; p < PW; ++p)
+                ob[row0 + RPI * p] = 0;
+        }
+        return;
+    }
+    float *st = ssm + (int64_t)s * sh.ssm_row_stride + (int64_t)hv * D * D + 4 * l;
+    float x[PW][EPL];
+#pragma unroll
+    for (int p = 0; p < PW; ++p)
+        ld_row<NV, LPR>(st + (int64_t)(row0 + RPI * p) * D, x[p]);
+    const float *qk = ws + ((int64_t)b * sh.hq + h) * 2 * D + 4 * l;
+    float qv[EPL], kv[EPL];
+    ld_vec<NV, LPR>(qk, qv);
+    ld_vec<NV, LPR>(qk + D, kv);
+    const float *vvp = ws + ws_v_off(sh.batch, sh.hq, D) + (int64_t)bh * D + row0;
+    float vrow[PW];
+#pragma unroll
+    for (int p = 0; p < PW; ++p)
+        vrow[p] = vvp[RPI * p];
+    // gates: b/a sums of this value head over the projection chunks
+    const float *pp = ws + ws_p_off(sh.batch, sh.hq, HV, D) + (int64_t)b * sh.nck * 2 * HV + hv;
+    float pb = 0.0f, pa = 0.0f;
+    for (int j = lane; j < sh.nck; j += 64) {
+        pb += pp[(int64_t)j * 2 * HV];
+        pa += pp[(int64_t)j * 2 * HV + HV];
+    }
+    pb = wave_sum(pb);
+    pa = wave_sum(pa);
+    const float t = pa + bf16_to_f32(dt_bias[hv]);
+    const float sp = t > 20.0f ? t : __builtin_amdgcn_logf(1.0f + fast_exp(t)) * 0.6931471805599453f;
+    const float alpha = fast_exp(-fast_exp(A_log[hv]) * sp);
+    const float beta = __builtin_amdgcn_rcpf(1.0f + fast_exp(-pb));
+    float kq = 0.0f;
+#pragma unroll
+    for (int e = 0; e < EPL; ++e)
+        kq = fmaf(kv[e], qv[e], kq);
+    kq = row_group_sum<LPR>(kq);
+#pragma unroll
+    for (int p = 0; p < PW; ++p) {
+        float pk = 0.0f, po = 0.0f;
+#pragma unroll
+        for (int e = 0; e < EPL; ++e) {
+            pk = fmaf(x[p][e], kv[e], pk);
+            po = fmaf(x[p][e], qv[e], po);
+        }
+        pk = row_group_sum<LPR>(pk);
+        po = row_group_sum<LPR>(po);
+        const float delta = beta * (vrow[p] - alpha * pk);
+        const float o = fmaf(alpha, po, delta * kq);
+#pragma unroll
+        for (int e = 0; e < EPL; ++e)
+            x[p][e] = fmaf(delta, kv[e], alpha * x[p][e]);
+        st_row<NV, LPR>(st + (int64_t)(row0 + RPI * p) * D, x[p]);
+        const uint32_t o16 = bf16_bits(o);
+        if (l == 0)
+            ob[row0 + RPI * p] = (uint16_t)o16;
+    }
+}
+
+template <int D, int GM, int WM>
+hipError_t launch_prep(const GdnParams &p, const GdnPrepShape &sh, hipStream_t stream)
+{
+    const int64_t blocks = (int64_t)p.batch * p.hq + (int64_t)p.batch * sh.nck;
     if (blocks > 0x7fffffff)
         return hipErrorInvalidConfiguration;
-    (void)hipGetLastError();
-    hipLaunchKernelGGL((ssu_gdn_kernel<D, GM, WM>), dim3((unsigned)blocks), dim3(kGdnNT), 0,
+    hipLaunchKernelGGL((gdn_prep_kernel<D, GM, WM>), dim3((unsigned)blocks), dim3(kGdnNT), 0,
                        stream, static_cast<const uint16_t *>(p.hs),
                        static_cast<const uint16_t *>(p.w_ba), static_cast<const uint16_t *>(p.qkv),
                        static_cast<const uint16_t *>(p.conv_w),
                        static_cast<const uint16_t *>(p.conv_b),
-                       static_cast<uint16_t *>(p.conv_state), p.A_log,
-                       static_cast<const uint16_t *>(p.dt_bias), p.ssm, p.idx,
-                       static_cast<uint16_t *>(p.out), sh);
+                       static_cast<uint16_t *>(p.conv_state), p.idx,
+                       static_cast<float *>(p.workspace), sh);
     return hipGetLastError();
 }
 
 template <int D, int GM>
-hipError_t launch_dg(const GdnParams &p, const GdnShape &sh, hipStream_t stream)
+hipError_t launch_prep_g(const GdnParams &p, const GdnPrepShape &sh, hipStream_t stream)
 {
     if (p.width == 1)
-        return launch_dgw<D, GM, 1>(p, sh, stream);
-    return p.width <= 4 ? launch_dgw<D, GM, 4>(p, sh, stream) : launch_dgw<D, GM, 8>(p, sh, stream);
+        return launch_prep<D, GM, 1>(p, sh, stream);
+    return p.width <= 4 ? launch_prep<D, GM, 4>(p, sh, stream) : launch_prep<D, GM, 8>(p, sh, stream);
 }
 
 template <int D>
 hipError_t launch_d(const GdnParams &p, hipStream_t stream)
 {
-    GdnShape sh;
-    sh.ssm_row_stride = p.ssm_row_stride;
+    GdnPrepShape sh;
     sh.cs_slot = p.cs_slot;
     sh.cs_chan = p.cs_chan;
     sh.cs_tap = p.cs_tap;
+    sh.batch = p.batch;
     sh.hidden = p.hidden;
     sh.hq = p.hq;
     sh.hv = p.hv;
     sh.width = p.width;
     sh.use_l2 = p.use_l2;
-    sh.G = p.hv / p.hq;
+    sh.proj_vec = (p.hv % 4 == 0 && (reinterpret_cast<uintptr_t>(p.w_ba) & 15) == 0) ? 1 : 0;
     sh.scale = p.scale;
-    switch (sh.G) {
-    case 1: return launch_dg<D, 1>(p, sh, stream);
-    case 2: return launch_dg<D, 2>(p, sh, stream);
-    case 4: return launch_dg<D, 4>(p, sh, stream);
-    case 8: return launch_dg<D, 8>(p, sh, stream);
+    sh.nck = (p.hidden + kProjRows - 1) / kProjRows;
+    (void)hipGetLastError();
+    hipError_t e;
+    switch (p.hv / p.hq) {
+    case 1: e = launch_prep_g<D, 1>(p, sh, stream); break;
+    case 2: e = launch_prep_g<D, 2>(p, sh, stream); break;
+    case 4: e = launch_prep_g<D, 4>(p, sh, stream); break;
+    case 8: e = launch_prep_g<D, 8>(p, sh, stream); break;
     default: return hipErrorInvalidValue;
     }
+    if (e != hipSuccess)
+        return e;
+    GdnStreamShape ss;
+    ss.ssm_row_stride = p.ssm_row_stride;
+    ss.batch = p.batch;
+    ss.hq = p.hq;
+    ss.hv = p.hv;
+    ss.nck = sh.nck;
+    const int64_t blocks = (int64_t)p.batch * p.hv * StreamCfg<D>::NPH;
+    if (blocks > 0x7fffffff)
+        return hipErrorInvalidConfiguration;
+    hipLaunchKernelGGL((gdn_stream_kernel<D>), dim3((unsigned)blocks), dim3(kGdnNT), 0, stream,
+                       p.ssm, p.idx, static_cast<const float *>(p.workspace), p.A_log,
+                       static_cast<const uint16_t *>(p.dt_bias), static_cast<uint16_t *>(p.out), ss);
+    return hipGetLastError();
 }
 
 }  // namespace
+
+int64_t gdn_workspace_floats(int64_t batch, int64_t hidden, int64_t hq, int64_t hv, int64_t d)
+{
+    const int64_t nck = (hidden + kProjRows - 1) / kProjRows;
+    return ws_p_off(batch, hq, hv, d) + batch * nck * 2 * hv;
+}
 
 hipError_t launch_gdn(const GdnParams &p, hipStream_t stream)
 {

@@ -90,9 +90,11 @@ struct GdnParams {
     float *ssm;
     const int32_t *idx;
     void *out;
+    void *workspace;  // gdn_workspace_floats() fp32, 16-byte aligned
     int64_t ssm_row_stride, cs_slot, cs_chan, cs_tap;
     int32_t batch, hidden, hq, hv, dhead, width, use_l2;
 };
+int64_t gdn_workspace_floats(int64_t batch, int64_t hidden, int64_t hq, int64_t hv, int64_t d);
 hipError_t launch_gdn(const GdnParams &p, hipStream_t stream);
 
 // One set of row moves: for b < rows, dst row (dst_idx ? dst_idx[b] : b) gets

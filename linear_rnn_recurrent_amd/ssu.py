@@ -22,7 +22,8 @@ _DT = {torch.float32: SSU_F32, torch.float16: SSU_F16, torch.bfloat16: SSU_BF16,
 
 EXPORTS = ("ssu_decode", "ssu_prefill", "ssu_replay", "ssu_tree_verify", "ssu_replay_layers",
            "ssu_state_clear_layers", "ssu_state_gather", "ssu_state_scatter", "ssu_state_pack",
-           "ssu_state_unpack", "ssu_gdn_decode", "ssu_pool_bytes_per_slot",
+           "ssu_state_unpack", "ssu_gdn_decode", "ssu_gdn_workspace_bytes",
+           "ssu_pool_bytes_per_slot",
            "ssu_pool_alloc", "ssu_pool_free", "ssu_pool_info", "ssu_pool_state_ptr",
            "ssu_pool_state_bytes_per_slot", "ssu_pool_find_state", "ssu_pool_clear",
            "ssu_pool_clear_slot", "ssu_pool_capture", "ssu_pool_restore",
@@ -99,7 +100,7 @@ def load_library(path: Optional[str] = None):
                               ctypes.c_int64, _P],
         "ssu_state_pack": [_P, _I32, ctypes.c_int64, ctypes.c_int64, _P, _I32, _P, _I32, _P, _P],
         "ssu_gdn_decode": [ctypes.POINTER(ssu_gdn_dims), _P, _P, _P, _P, _P, _P, _P, _P,
-                           ctypes.c_float, _P, _P, _P, _P],
+                           ctypes.c_float, _P, _P, _P, _P, ctypes.c_int64, _P],
         "ssu_state_unpack": [_P, _I32, ctypes.c_int64, ctypes.c_int64, _P, _I32, _P, _I32, _P, _P],
         "ssu_pool_bytes_per_slot": [S, _I32, ctypes.POINTER(ctypes.c_size_t)],
         "ssu_pool_alloc": [S, _I32, _I32, _P, ctypes.POINTER(_P)],
@@ -120,6 +121,8 @@ def load_library(path: Optional[str] = None):
         f = getattr(lib, name)
         f.argtypes = args
         f.restype = ctypes.c_int32
+    lib.ssu_gdn_workspace_bytes.argtypes = [ctypes.POINTER(ssu_gdn_dims)]
+    lib.ssu_gdn_workspace_bytes.restype = ctypes.c_int64
     lib.ssu_last_error.argtypes = []
     lib.ssu_last_error.restype = ctypes.c_char_p
     lib.ssu_version.argtypes = []
@@ -534,11 +537,13 @@ def ssu_state_unpack(pool, homes, workspace, bystanders=None, stream=None):
 
 def ssu_gdn_decode(hidden_states, w_ba, mixed_qkv, conv_weight, conv_bias, conv_state, A_log,
                    dt_bias, scale, ssm_state, state_indices, *, num_q_heads, use_qk_l2norm=True,
-                   out=None, stream=None):
+                   out=None, workspace=None, stream=None):
     """Fused gated-delta-rule decode step (one token per batch entry) over paged
     conv / ssm pools, both updated in place. conv_state: a [P, qkv_dim, W-1]
     view of any strides (a dense pool, or the transposed view of a
-    [P, W-1, qkv_dim] pool). Returns out [B, 1, HV, D] (bf16)."""
+    [P, W-1, qkv_dim] pool). workspace: a uint8 GPU tensor of at least
+    gdn_workspace_bytes(...) bytes (allocated here when None). Returns
+    out [B, 1, HV, D] (bf16)."""
     lib = load_library()
     bf = (torch.bfloat16,)
     _dense(hidden_states, "hidden_states", bf)
@@ -575,13 +580,24 @@ def ssu_gdn_decode(hidden_states, w_ba, mixed_qkv, conv_weight, conv_bias, conv_
                         1 if use_qk_l2norm else 0,
                         st[0] if ssm_state.shape[0] > 1 else hv * d * d, cs[0], cs[1], cs[2])
     sc = 0.0 if scale is None else float(scale)
+    need = int(lib.ssu_gdn_workspace_bytes(ctypes.byref(dims)))
+    if workspace is None:
+        workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=hidden_states.device)
+    _dense(workspace, "workspace", (torch.uint8,))
     with torch.cuda.device(hidden_states.device):
         _check(lib.ssu_gdn_decode(ctypes.byref(dims), _ptr(hidden_states), _ptr(w_ba),
                                   _ptr(mixed_qkv), _ptr(conv_weight), _ptr(conv_bias),
                                   _ptr(conv_state), _ptr(A_log), _ptr(dt_bias), sc,
                                   _ptr(ssm_state), _ptr(state_indices), _ptr(out),
+                                  _ptr(workspace), workspace.numel(),
                                   _stream(hidden_states.device, stream)))
     return out
+
+
+def gdn_workspace_bytes(batch, hidden, num_q_heads, num_v_heads, head_dim):
+    """Bytes of the workspace ssu_gdn_decode needs (no GPU needed)."""
+    d = ssu_gdn_dims(batch, hidden, num_q_heads, num_v_heads, head_dim, 1, 1, 1, 0, 0, 0, 0)
+    return int(load_library().ssu_gdn_workspace_bytes(ctypes.byref(d)))
 
 
 # ---------------------------------------------------------------------------

@@ -24,7 +24,8 @@ def lib():
 
 def declared_functions():
     text = open(HEADER).read()
-    return re.findall(r"^(?:ssu_status|const char \*|int32_t)\s*(ssu_\w+)\s*\(", text, re.M)
+    return re.findall(r"^(?:ssu_status|const char \*|int32_t|int64_t)\s*(ssu_\w+)\s*\(", text,
+                      re.M)
 
 
 def test_header_declares_the_entry_points():
@@ -335,16 +336,25 @@ def test_row_movement_validation(lib):
 
 
 def test_gdn_decode_validation(lib):
-    def call(hq=2, hv=4, d=128, w=4, rs=0, w_ba=FAKE, hs=FAKE, batch=2):
+    need = 4 * 2 * (2 * 2 * 128 + 4 * 128 + 2 * 4 * 1)  # hidden 64: one 256-row chunk
+
+    def call(hq=2, hv=4, d=128, w=4, rs=0, w_ba=FAKE, hs=FAKE, batch=2, ws=FAKE, ws_bytes=need):
         dd = S.ssu_gdn_dims(batch, 64, hq, hv, d, w, 4, 1, rs, 3 * (2 * hq + hv) * d, 3, 1)
         return lib.ssu_gdn_decode(ctypes.byref(dd), hs, w_ba, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE,
-                                  ctypes.c_float(0.0), FAKE, FAKE, FAKE, None)
+                                  ctypes.c_float(0.0), FAKE, FAKE, FAKE, ws, ws_bytes, None)
     assert call(hv=3) == 1 and "multiple" in err(lib)
     assert call(hq=1, hv=3) == 2 and "{1, 2, 4, 8}" in err(lib)
     assert call(hq=1, hv=16) == 2
     assert call(d=96) == 2 and "head_dim" in err(lib)
     assert call(w=9) == 2 and "conv_width" in err(lib)
     assert call(rs=4 * 128 * 128 - 4) == 1 and "ssm_row_stride" in err(lib)
-    assert call(w_ba=FAKE + 2) == 1 and "'w_ba'" in err(lib)          # G = 2: 4-byte chunks
+    assert call(w_ba=FAKE + 2) == 1 and "'w_ba'" in err(lib)
+    assert call(hq=128, hv=512) == 2 and "256" in err(lib)
+    assert call(ws=None) == 1 and "'workspace'" in err(lib)
+    assert call(ws=FAKE + 8) == 1 and "'workspace'" in err(lib)
+    assert call(ws_bytes=need - 4) == 1 and "workspace_bytes" in err(lib)
     assert call(hs=None) == 1 and "'hidden_states'" in err(lib)
-    assert call(batch=0, hs=None, w_ba=None) == 0
+    assert call(batch=0, hs=None, w_ba=None, ws=None) == 0
+    dd = S.ssu_gdn_dims(2, 64, 2, 4, 128, 4, 4, 1, 0, 0, 0, 0)
+    assert lib.ssu_gdn_workspace_bytes(ctypes.byref(dd)) == need
+    assert lib.ssu_gdn_workspace_bytes(None) == -1
