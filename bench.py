@@ -290,7 +290,8 @@ def main():
 
     import torch
     from linear_rnn_recurrent_amd import (ReplayLayerTable, StateLayerTable, inputs, load_library,
-                                          gdn_workspace_bytes, ssu_decode, ssu_gdn_decode,
+                                          gdn_workspace_bytes, tree_workspace_bytes,
+                                          ssu_decode, ssu_gdn_decode,
                                           ssu_prefill,
                                           ssu_replay, ssu_replay_layers, ssu_state_clear_layers,
                                           ssu_state_gather, ssu_tree_verify)
@@ -376,13 +377,15 @@ def main():
                       "replay_u": torch.empty((b, m, h, d), device=dev),
                       "replay_B": torch.empty(tuple(T["B"].shape), device=dev)}
         rot = "steps rotate 3 replicas of the pool, of every input and of the outputs and stash"
+        tws = torch.empty(tree_workspace_bytes(b, T["B"].shape[2], m), dtype=torch.uint8,
+                          device=dev)
 
         def step(i):
             R = reps[i % len(reps)]
             ssu_tree_verify(R["x"], R["A"], R["B"], R["C"], R["dt"], R["state"], R["out"],
                             R["parent_ids"], depths=R["depths"], dt_bias=R["dt_bias"], D=R["D"],
                             z=R["z"], dt_softplus=w.dt_softplus, state_indices=R["state_indices"],
-                            **R["S"])
+                            workspace=tws, **R["S"])
         src = source_hash("ssu_tree_impl.h", "ssu_dpp.h", "ssu_device.h")
         kkey = "tree_config5"
         lane_ops = tree_lane_ops(T)

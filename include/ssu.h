@@ -171,14 +171,25 @@ ssu_status ssu_replay(const ssu_dims *dims, int32_t seq_len, void *state,
  * accepted path with ssu_replay and accepted_node_ids.
  * z is optional (NULL: no gate; the page's form of this kernel has none), as
  * are dt_bias, D, depths and state_indices.
- * Padding rows (r < 0): out[b] = +0.0, stash rows untouched. */
+ * Padding rows (r < 0): out[b] = +0.0, stash rows untouched.
+ * workspace: caller-owned device scratch of at least
+ * ssu_tree_workspace_bytes(dims, num_nodes) bytes, 16-byte aligned (it
+ * carries the B . C dots of every node pair, shared by all heads, from the
+ * first of the two launches to the second); contents on entry ignored, on
+ * return unspecified; calls sharing a workspace must be ordered (one stream). */
 ssu_status ssu_tree_verify(const ssu_dims *dims, int32_t num_nodes, const void *x,
                            const float *A, const void *B, const void *C, const float *dt,
                            const float *dt_bias, const float *D, const void *z,
                            const void *state, void *out, int32_t dt_softplus,
                            const int32_t *state_indices, const int32_t *parent_ids,
                            const int32_t *depths, float *replay_dA, float *replay_u,
-                           float *replay_B, float *replay_dt, hipStream_t stream);
+                           float *replay_B, float *replay_dt, void *workspace,
+                           int64_t workspace_bytes, hipStream_t stream);
+
+/* Bytes of workspace ssu_tree_verify needs: 4 * batch * ngroups * num_nodes^2;
+ * -1 if dims is NULL or num_nodes is outside [0, SSU_MAX_TREE_NODES] or
+ * batch / ngroups is out of range. No HIP call. */
+int64_t ssu_tree_workspace_bytes(const ssu_dims *dims, int32_t num_nodes);
 
 /* One layer's buffers for ssu_replay_layers [SSU MambaReplayLayerInfo:
  * stateDst, replayDa, replayU, replayB, replayDt]. Layouts and alignment as

@@ -9,11 +9,12 @@ from .ssu import (SsuError, SsuPool, DeviceArray, ReplayLayerTable, StateLayerTa
                   load_library, ssu_decode, ssu_prefill, ssu_replay, ssu_tree_verify,
                   ssu_replay_layers, ssu_state_clear_layers, ssu_state_gather,
                   ssu_state_scatter, ssu_state_pack, ssu_state_unpack, pack_workspace_bytes,
-                  ssu_gdn_decode, gdn_workspace_bytes,
+                  ssu_gdn_decode, gdn_workspace_bytes, tree_workspace_bytes,
                   LIB_PATH, EXPORTS)
 
 __all__ = ["SsuError", "SsuPool", "DeviceArray", "ReplayLayerTable", "StateLayerTable",
            "load_library", "ssu_decode", "ssu_prefill", "ssu_replay", "ssu_tree_verify",
            "ssu_replay_layers", "ssu_state_clear_layers", "ssu_state_gather", "ssu_state_scatter",
            "ssu_state_pack", "ssu_state_unpack", "pack_workspace_bytes", "ssu_gdn_decode", "gdn_workspace_bytes",
+           "tree_workspace_bytes",
            "LIB_PATH", "EXPORTS"]

@@ -655,13 +655,22 @@ ssu_status ssu_state_unpack(void *pool, int32_t pool_rows, int64_t row_stride, i
                       "ssu_state_unpack launch");
 }
 
+int64_t ssu_tree_workspace_bytes(const ssu_dims *dims, int32_t num_nodes)
+{
+    if (!dims || num_nodes < 0 || num_nodes > SSU_MAX_TREE_NODES || dims->batch < 0 ||
+        dims->ngroups <= 0)
+        return -1;
+    return (int64_t)4 * dims->batch * dims->ngroups * num_nodes * num_nodes;
+}
+
 ssu_status ssu_tree_verify(const ssu_dims *dims, int32_t num_nodes, const void *x,
                            const float *A, const void *B, const void *C, const float *dt,
                            const float *dt_bias, const float *D, const void *z,
                            const void *state, void *out, int32_t dt_softplus,
                            const int32_t *state_indices, const int32_t *parent_ids,
                            const int32_t *depths, float *replay_dA, float *replay_u,
-                           float *replay_B, float *replay_dt, hipStream_t stream)
+                           float *replay_B, float *replay_dt, void *workspace,
+                           int64_t workspace_bytes, hipStream_t stream)
 {
     const char *fn = "ssu_tree_verify";
     ssu::TreeParams p = {};
@@ -697,6 +706,12 @@ ssu_status ssu_tree_verify(const ssu_dims *dims, int32_t num_nodes, const void *
     SSU_OPTIONAL_PTR(replay_u, 4, fn);
     SSU_OPTIONAL_PTR(replay_B, 16, fn);
     SSU_OPTIONAL_PTR(replay_dt, 4, fn);
+    SSU_REQUIRE_PTR(workspace, 16, fn);
+    const int64_t need = ssu_tree_workspace_bytes(dims, num_nodes);
+    if (workspace_bytes < need)
+        return fail(SSU_EINVAL, "%s: workspace_bytes %lld < %lld required", fn,
+                    (long long)workspace_bytes, (long long)need);
+    p.gram = static_cast<float *>(workspace);
     p.d.x = x;
     p.d.A = A;
     p.d.B = B;

@@ -12,6 +12,27 @@ __device__ __forceinline__ float dpp_f32(float a)
                                                                 CTRL, 0xF, 0xF, false));
 }
 
+// dpp_f32 with a fill value: lanes whose source lies outside their row of 16
+// get `fill` (row shifts leave the first lanes of a row without a source).
+template <int CTRL>
+__device__ __forceinline__ float dpp_f32_fill(float fill, float a)
+{
+    return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(__builtin_bit_cast(int, fill),
+                                                                __builtin_bit_cast(int, a), CTRL,
+                                                                0xF, 0xF, false));
+}
+
+// Inclusive running product along each row of 16 lanes (lane i of a row gets
+// the product of lanes 0..i): four row shifts, Hillis-Steele.
+__device__ __forceinline__ float row_prefix_prod16(float v)
+{
+    v *= dpp_f32_fill<0x111>(1.0f, v);  // row_shr:1
+    v *= dpp_f32_fill<0x112>(1.0f, v);  // row_shr:2
+    v *= dpp_f32_fill<0x114>(1.0f, v);  // row_shr:4
+    v *= dpp_f32_fill<0x118>(1.0f, v);  // row_shr:8
+    return v;
+}
+
 // Sum over aligned groups of W lanes (W = 4, 8 or 16): quad permutations, then
 // the half-row and row mirrors; every lane of a group gets the group's sum.
 template <int W>

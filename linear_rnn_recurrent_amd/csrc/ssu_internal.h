@@ -56,6 +56,7 @@ struct TreeParams {
     int32_t num_nodes;
     const int32_t *parents, *depths;
     float *st_dA, *st_u, *st_B, *st_dt;  // all set or all null
+    float *gram;  // workspace: [batch][ngroups][M][M] fp32, B_j . C_m for j <= m
 };
 
 // One byte range to copy (src != null) or zero (src == null).

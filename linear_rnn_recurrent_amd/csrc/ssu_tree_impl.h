@@ -21,31 +21,37 @@
 // of the per-node decays from m upwards, the same products the step-by-step
 // recurrence forms.
 //
+// The dots B_{c_i} . C_m depend on the batch row and group only, so a first
+// launch (ssu_tree_gram_kernel) forms G[b,g][m][j] = B_j . C_m for every
+// j <= m (ancestors precede their node) once, for all heads, into a caller
+// workspace, and copies B to the stash. The main launch then writes, per node
+// and head, the dense coefficient matrix Q[m][j] = w_j dt'_j G[m][j] (zero off
+// the path), and the path sum becomes a second matrix product Q . X.
+//
 // Mapping on gfx950 (one (batch row, head, block of 64 rows of dim) per
 // 256-thread workgroup):
 //   1. prologue: every global load is issued first: the state slice (straight
-//      into MFMA operand registers), x and B of every node (16-byte vectors,
-//      kept in LDS in their storage dtype), dt / parent / depth per node and C
-//      of the first chunk. Per node a record {exp(A dt'), dt', parent, hop
-//      bound} goes to LDS; then one lane per node walks the parent ids and
-//      writes the node's path (ancestor ids, node first) into a fixed slot of
-//      the triangular table (a node's path has at most m+1 entries);
+//      into MFMA operand registers), x of every node (16-byte vectors, kept in
+//      LDS in their storage dtype), dt / parent / depth per node and C of the
+//      first chunk. Per node a record {exp(A dt'), dt', parent, hop bound}
+//      goes to LDS; one lane per node walks the parent ids and writes the
+//      node's path (ancestor ids, node first) into a fixed slot of a
+//      triangular table; each lane then keeps the x values it feeds to the
+//      path product in registers;
 //   2. nodes go in chunks of 16 (the N side of one MFMA tile). S0 . C_m is a
-//      dense contraction [64 rows x dstate] x [dstate x nodes] and runs on the
-//      matrix cores in fp32 (v_mfma_f32_16x16x4_f32): wave w owns rows
-//      16w .. 16w+15, lane group g = lane/16 owns the dstate slice
-//      [g dstate/4, (g+1) dstate/4), C of the chunk (LDS, storage dtype, rows
-//      padded against bank conflicts) is the B operand, and the wave's 16 x 16
-//      result stays in its accumulator registers;
-//   3. meanwhile 16 lanes per chunk node go along its path: per entry the
-//      dot B_{c_i} . C_m (dstate split over the lanes, DPP row sums) and the
-//      weight w_i dt'_{c_i} as a running product of the decays in registers,
-//      giving the entry's coefficient; C of the next chunk is loaded into
-//      registers;
-//   4. after one barrier, each lane finishes the outputs it holds in its
-//      accumulators (one node, four consecutive rows): w_S (S0 . C_m) + the
-//      node's path terms + D x, gate, store; the next chunk's C goes to LDS;
-//      a second barrier ends the chunk.
+//      dense contraction [64 rows x dstate] x [dstate x nodes] on the matrix
+//      cores in fp32 (v_mfma_f32_16x16x4_f32): wave w owns rows 16w .. 16w+15,
+//      lane group g = lane/16 the dstate slice [g dstate/4, (g+1) dstate/4),
+//      C of the chunk (LDS) is the B operand;
+//   3. the 16 lanes of each chunk node take one path entry each: its decay,
+//      dt' and G value (prefetched from the workspace a chunk ahead), the
+//      weights as a running product across the lanes (DPP prefix product),
+//      giving Q[m][j] (written into a zeroed LDS matrix, transposed) and the
+//      weight w_S of S0 for the node;
+//   4. after one barrier the accumulators are scaled by w_S per node and the
+//      path terms are added on the matrix cores: acc += X . Q^T over the
+//      source nodes j < the chunk's end (ancestors only), with X from the
+//      registers of step 1; then D x, gate, store.
 #pragma once
 
 #include "ssu_device.h"
@@ -68,7 +74,7 @@ typedef float f32x4 __attribute__((ext_vector_type(4)));
 
 // Byte offsets of the LDS arrays for a tree of M nodes (host and device).
 struct TreeLds {
-    int xs, bs, cs, rec, path, len, cw, cws, total;
+    int xs, cs, rec, path, len, qt, cws, total;
 };
 
 __host__ __device__ inline int tree_lds_take(int &o, int bytes)
@@ -79,10 +85,12 @@ __host__ __device__ inline int tree_lds_take(int &o, int bytes)
 }
 
 // Row pitches (bytes) in LDS: one 16-byte pad per row spreads the rows that
-// the lanes of one instruction read together over the banks (B and C rows of
+// the lanes of one instruction read together over the banks (C rows of
 // dstate elements; x rows of the block's 64 rows of dim).
 __host__ __device__ constexpr int tree_row_bytes(int NS, int bc_bytes) { return NS * bc_bytes + 16; }
 __host__ __device__ constexpr int tree_x_pitch(int io_bytes) { return 64 * io_bytes + 16; }
+// source-node rows of the coefficient matrix: every chunk's range, padded
+__host__ __device__ constexpr int tree_q_rows(int M) { return (M + 15) & ~15; }
 
 __host__ __device__ inline TreeLds tree_lds(int M, int NS, int io_bytes, int bc_bytes)
 {
@@ -90,21 +98,21 @@ __host__ __device__ inline TreeLds tree_lds(int M, int NS, int io_bytes, int bc_
     int o = 0;
     const int rb = tree_row_bytes(NS, bc_bytes);
     L.xs = tree_lds_take(o, M * tree_x_pitch(io_bytes));  // x [M][64 rows]
-    L.bs = tree_lds_take(o, M * rb);                  // B [M][NS]
-    L.cs = tree_lds_take(o, kTreeTC * rb);            // C of the current chunk [TC][NS]
-    L.rec = tree_lds_take(o, M * 16);                 // node records
-    L.path = tree_lds_take(o, M * (M + 1) / 2);       // path of node m at m(m+1)/2
-    L.len = tree_lds_take(o, M * 4);                  // path lengths
-    L.cw = tree_lds_take(o, kTreeTC * M * 4);         // coefficients of the chunk's entries
-    L.cws = tree_lds_take(o, kTreeTC * 4);            // weights of S0 of the chunk's nodes
+    L.cs = tree_lds_take(o, kTreeTC * rb);                // C of the current chunk [TC][NS]
+    L.rec = tree_lds_take(o, M * 16);                     // node records
+    L.path = tree_lds_take(o, M * (M + 1) / 2);           // path of node m at m(m+1)/2
+    L.len = tree_lds_take(o, M * 4);                      // path lengths
+    L.qt = tree_lds_take(o, 2 * tree_q_rows(M) * kTreeTC * 4);  // Q^T [source][chunk node], x2
+    L.cws = tree_lds_take(o, kTreeTC * 4);                // weights of S0 of the chunk's nodes
     L.total = o;
     return L;
 }
 
-// n consecutive storage-dtype elements (16-bit or fp32) from LDS as fp32;
-// n * element size is a multiple of 8 bytes and the address is aligned to it.
+// n consecutive storage-dtype elements (16-bit or fp32) as fp32, from LDS or
+// global memory; n * element size is a multiple of 8 bytes and the address is
+// aligned to it.
 template <typename T, int N>
-__device__ __forceinline__ void lds_row(const unsigned char *p, float (&f)[N])
+__device__ __forceinline__ void ld_row_f32(const unsigned char *p, float (&f)[N])
 {
     if constexpr (sizeof(T) == 4) {
         static_assert(N % 4 == 0, "fp32 rows go in 16-byte pieces");
@@ -136,47 +144,103 @@ __device__ __forceinline__ void lds_row(const unsigned char *p, float (&f)[N])
     }
 }
 
-// Sum over aligned groups of W lanes (W = 4, 8 or 16) with DPP: quad
-// permutations, then the half-row and row mirrors; every lane of a group gets
-// the group's sum. No LDS traffic.
+// G[b,g][m][j] = B_j . C_m (fp32) for j <= m, on the matrix cores: one
+// workgroup per (b, g, block of 16 nodes m); wave w computes the 16 x 16 tiles
+// of source blocks jb = w, w+4, .. <= the node block (v_mfma_f32_16x16x4_f32,
+// lane group q summing the dstate slice [q NS/4, (q+1) NS/4)); and the stash
+// copy of B (fp32) of the block's nodes. Padded batch rows are skipped (their
+// stash stays untouched).
+template <typename BCT, int NS>
+__global__ __launch_bounds__(kTreeNT) void ssu_tree_gram_kernel(
+    const void *__restrict__ Bm, const void *__restrict__ Cm, const int32_t *__restrict__ idx,
+    float *__restrict__ gram, float *__restrict__ st_B, int32_t M, int32_t G)
+{
+    constexpr int KS = NS / 4;
+    constexpr int BB = (int)sizeof(BCT);
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wave = tid >> 6;
+    const int qg = lane >> 4, ln = lane & 15;
+    const int nmb = (M + 15) / 16;
+    const int bg = blockIdx.x / nmb;
+    const int mb = blockIdx.x - bg * nmb;
+    const int b = bg / G, g = bg - b * G;
+    if (idx && idx[b] < 0)
+        return;
+    const int m0 = 16 * mb;
+    auto row = [&](const void *base, int node) {  // this lane's dstate slice of a node's row
+        return static_cast<const unsigned char *>(base) +
+               ((((int64_t)b * M + min(node, M - 1)) * G + g) * NS + qg * KS) * BB;
+    };
+    float ca[KS];
+    ld_row_f32<BCT, KS>(row(Cm, m0 + ln), ca);
+    for (int jb = wave; jb <= mb; jb += 4) {
+        float bv[KS];
+        ld_row_f32<BCT, KS>(row(Bm, 16 * jb + ln), bv);
+        f32x4 acc = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+        for (int k = 0; k < KS; ++k)
+            acc = __builtin_amdgcn_mfma_f32_16x16x4f32(ca[k], bv[k], acc, 0, 0, 0);
+        // acc[v] = C_{m0 + 4 qg + v} . B_{16 jb + ln}
+        const int j = 16 * jb + ln;
+#pragma unroll
+        for (int v = 0; v < 4; ++v) {
+            const int m = m0 + 4 * qg + v;
+            if (m < M && j <= m)
+                gram[((int64_t)bg * M + m) * M + j] = acc[v];
+        }
+    }
+    if (st_B) {
+        for (int e = tid; e < 16 * NS; e += kTreeNT) {
+            const int r = m0 + e / NS;
+            if (r < M) {
+                const int64_t o = (((int64_t)b * M + r) * G + g) * NS + e % NS;
+                st_B[o] = cvt_raw1<BCT>(ld_raw1<BCT>(Bm, o));
+            }
+        }
+    }
+}
+
 template <typename ST, typename IOT, typename BCT, int NS>
 __global__ __launch_bounds__(kTreeNT) void ssu_tree_kernel(
-    const void *__restrict__ x, const float *__restrict__ A, const void *__restrict__ Bm,
-    const void *__restrict__ Cm, const float *__restrict__ dt, const float *__restrict__ dt_bias,
-    const float *__restrict__ Dv, const void *__restrict__ z, const ST *__restrict__ state,
-    void *__restrict__ out, const int32_t *__restrict__ idx, const int32_t *__restrict__ parents,
-    const int32_t *__restrict__ depths, float *__restrict__ st_dA, float *__restrict__ st_u,
-    float *__restrict__ st_B, float *__restrict__ st_dt, const TreeShape sh)
+    const void *__restrict__ x, const float *__restrict__ A, const void *__restrict__ Cm,
+    const float *__restrict__ dt, const float *__restrict__ dt_bias, const float *__restrict__ Dv,
+    const void *__restrict__ z, const ST *__restrict__ state, void *__restrict__ out,
+    const int32_t *__restrict__ idx, const int32_t *__restrict__ parents,
+    const int32_t *__restrict__ depths, const float *__restrict__ gram,
+    float *__restrict__ st_dA, float *__restrict__ st_u, float *__restrict__ st_dt,
+    const TreeShape sh)
 {
     constexpr int NT = kTreeNT;
     constexpr int TC = kTreeTC;
+    constexpr int MX = SSU_MAX_TREE_NODES;
     constexpr int KS = NS / 4;                        // dstate columns per lane group
     constexpr int XB = (int)sizeof(IOT), BB = (int)sizeof(BCT);
-    constexpr int RB = tree_row_bytes(NS, BB);        // LDS row pitch of B and C
+    constexpr int RB = tree_row_bytes(NS, BB);        // LDS row pitch of C
     constexpr int XP = tree_x_pitch(XB);              // LDS row pitch of x
     constexpr int CV = (TC * NS * BB / 16 + NT - 1) / NT;  // 16-byte C vectors per thread
     constexpr int XV = 16 / XB;                       // x elements per 16-byte vector
-    constexpr int BVE = 16 / BB;                      // B/C elements per 16-byte vector
-    constexpr int XVEC = (SSU_MAX_TREE_NODES * 64 / XV + NT - 1) / NT;  // x vectors per thread
-    constexpr int NPT = (SSU_MAX_TREE_NODES + NT - 1) / NT;  // node records per thread
+    constexpr int BVE = 16 / BB;                      // C elements per 16-byte vector
+    constexpr int XVEC = (MX * 64 / XV + NT - 1) / NT;  // x vectors per thread
+    constexpr int NPT = (MX + NT - 1) / NT;           // node records per thread
     static_assert(KS % 4 == 0 && (KS * BB) % 8 == 0, "tile shape");
 
     extern __shared__ __attribute__((aligned(16))) unsigned char lds[];
     const int M = sh.num_nodes;
     const TreeLds L = tree_lds(M, NS, XB, BB);
+    const int RM = tree_q_rows(M);
     unsigned char *xs = lds + L.xs;
-    unsigned char *bs = lds + L.bs;
     unsigned char *cs = lds + L.cs;
     float4 *rec = reinterpret_cast<float4 *>(lds + L.rec);  // {exp(A dt'), dt', parent, bound}
     uint8_t *n_path = lds + L.path;                          // triangular path table
     int *n_len = reinterpret_cast<int *>(lds + L.len);
-    float *c_w = reinterpret_cast<float *>(lds + L.cw);      // [TC][M]
+    float *qt = reinterpret_cast<float *>(lds + L.qt);       // 2 x [RM][TC]
     float *c_wS = reinterpret_cast<float *>(lds + L.cws);    // [TC]
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-    const int qg = lane >> 4;     // lane group: dstate slice (MFMA A/B), row quad (MFMA D)
+    const int qg = lane >> 4;     // lane group: dstate slice / source node (MFMA A/B), row quad (D)
     const int ln = lane & 15;     // MFMA A row / B and D column (node of the chunk)
     const int H = sh.nheads, Dm = sh.dim, G = sh.ngroups;
     const int per_b = H * sh.nrb;
@@ -199,6 +263,7 @@ __global__ __launch_bounds__(kTreeNT) void ssu_tree_kernel(
 
     const bool stash = st_dA != nullptr;
     const int g = h / sh.heads_per_group;
+    const float *gbg = gram + ((int64_t)b * G + g) * M * M;  // G[m][j] of this (b, g)
     const float Ah = A[h];
     const float bias = dt_bias ? dt_bias[h] : 0.0f;
     const float dskip = Dv ? Dv[h] : 0.0f;
@@ -246,53 +311,8 @@ __global__ __launch_bounds__(kTreeNT) void ssu_tree_kernel(
         }
     };
     load_c(0);
-    // B of every node (16-byte vectors; vector v: node v / (NS/BVE)), in
-    // batches of 8 per thread; the stash copy of B comes from the first head of
-    // the group
-    constexpr int BPN = NS / BVE;
-    const int nbv = M * BPN;
-    const bool writes_B = stash && rb == 0 && (h % sh.heads_per_group) == 0;
-    u32x4 br[8];
-    auto load_b = [&](int v0) {
-#pragma unroll
-        for (int k = 0; k < 8; ++k) {
-            const int v = min(v0 + tid + NT * k, nbv - 1);
-            br[k] = *reinterpret_cast<const u32x4 *>(
-                static_cast<const unsigned char *>(Bm) +
-                (((bM + v / BPN) * G + g) * NS + BVE * (v % BPN)) * BB);
-        }
-    };
-    auto store_b = [&](int v0) {
-#pragma unroll
-        for (int k = 0; k < 8; ++k) {
-            const int v = v0 + tid + NT * k;
-            if (v < nbv) {
-                *reinterpret_cast<u32x4 *>(bs + (v / BPN) * RB + (v % BPN) * 16) = br[k];
-                if (writes_B) {
-                    float f[BVE];
-                    if constexpr (BB == 4) {
-#pragma unroll
-                        for (int e = 0; e < 4; ++e)
-                            f[e] = __uint_as_float(br[k][e]);
-                    } else {
-#pragma unroll
-                        for (int e = 0; e < 4; ++e) {
-                            f[2 * e] = cvt_raw1<BCT>(br[k][e] & 0xffffu);
-                            f[2 * e + 1] = cvt_raw1<BCT>(br[k][e] >> 16);
-                        }
-                    }
-                    float *dst = st_B + ((bM + v / BPN) * G + g) * NS + BVE * (v % BPN);
-#pragma unroll
-                    for (int e = 0; e < BVE; e += 4)
-                        *reinterpret_cast<float4 *>(dst + e) =
-                            make_float4(f[e], f[e + 1], f[e + 2], f[e + 3]);
-                }
-            }
-        }
-    };
     // x of every node, rows of the block, as 16-byte vectors when dim allows
-    // (vector v: node v / (64/XV), rows XV*(v % (64/XV)) ..); rows past dim are
-    // 0. Its loads and the first batch of B loads are in flight together.
+    // (vector v: node v / (64/XV), rows XV*(v % (64/XV)) ..); rows past dim are 0
     const bool xvec = Dm % XV == 0 && (reinterpret_cast<uintptr_t>(x) & 15) == 0 &&
                       (!stash || (reinterpret_cast<uintptr_t>(st_u) & 15) == 0);
     if (xvec) {
@@ -307,7 +327,6 @@ __global__ __launch_bounds__(kTreeNT) void ssu_tree_kernel(
                 static_cast<const unsigned char *>(x) +
                 ((((bM + v / VPN) * H + h) * Dm + r) * XB));
         }
-        load_b(0);
 #pragma unroll
         for (int k = 0; k < XVEC; ++k) {
             const int v = tid + NT * k;
@@ -340,7 +359,6 @@ __global__ __launch_bounds__(kTreeNT) void ssu_tree_kernel(
             }
         }
     } else {
-        load_b(0);
         for (int e = tid; e < M * 64; e += NT) {
             const int m = e >> 6, rl = e & 63, r = rbase + rl;
             uint32_t w = 0;
@@ -355,11 +373,6 @@ __global__ __launch_bounds__(kTreeNT) void ssu_tree_kernel(
             else
                 *reinterpret_cast<uint16_t *>(xs + m * XP + rl * 2) = (uint16_t)w;
         }
-    }
-    store_b(0);
-    for (int v0 = 8 * NT; v0 < nbv; v0 += 8 * NT) {
-        load_b(v0);
-        store_b(v0);
     }
     // node records {decay exp(A dt'), dt', parent id (-1 unless it precedes the
     // node), hop bound}
@@ -380,6 +393,13 @@ __global__ __launch_bounds__(kTreeNT) void ssu_tree_kernel(
         }
     }
     store_c();
+    // Q^T rows the chunk starting at t0 reads: sources j < t0 + TC (<= RM)
+    auto zero_q = [&](int buf, int t0) {
+        float4 *q = reinterpret_cast<float4 *>(qt + buf * RM * TC);
+        for (int i = tid; i < (t0 + TC) * TC / 4; i += NT)
+            q[i] = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
+    };
+    zero_q(0, 0);
     __syncthreads();
 
     // ---- the path of every node (one lane per node), node first ----
@@ -399,14 +419,41 @@ __global__ __launch_bounds__(kTreeNT) void ssu_tree_kernel(
     }
     __syncthreads();
 
+    // this lane's MFMA A operand of the path product: x_{4s+qg}[row 16w+ln]
+    float xa[MX / 4];
+    {
+        const int rl = 16 * wave + ln;
+#pragma unroll
+        for (int s = 0; s < MX / 4; ++s) {
+            const int j = 4 * s + qg;
+            float v = 0.0f;
+            if (j < M) {
+                if constexpr (XB == 4)
+                    v = *reinterpret_cast<const float *>(xs + j * XP + rl * 4);
+                else
+                    v = cvt_raw1<IOT>(*reinterpret_cast<const uint16_t *>(xs + j * XP + rl * 2));
+            }
+            xa[s] = v;
+        }
+    }
+    // G value of this lane's path entry (entry tid%16 of chunk node tid/16) of
+    // the chunk starting at t0; entries past 16 are read in the loop below
+    auto load_g = [&](int t0) {
+        const int m = t0 + (tid >> 4), l = tid & 15;
+        float v = 0.0f;
+        if (m < M && l < n_len[m])
+            v = gbg[(int64_t)m * M + n_path[m * (m + 1) / 2 + l]];
+        return v;
+    };
+    float gcur = load_g(0);
+
     const int nchunks = (M + TC - 1) / TC;
-    constexpr int LPN = KS >= 16 ? 16 : KS;   // lanes per chunk node in the path sums
-    constexpr int EPN = NS / LPN;             // dstate elements per lane there
     for (int c = 0; c < nchunks; ++c) {
         const int t0 = c * TC;
         const int nt = min(TC, M - t0);
         const int mo = t0 + ln;                       // this lane's output node
         const int orow = rbase + 16 * wave + 4 * qg;  // and its first output row
+        float *q = qt + (c & 1) * RM * TC;
         // gate inputs of this lane's four outputs (raw bits; clamped indices)
         uint32_t zq[4] = {0u, 0u, 0u, 0u};
         if (z) {
@@ -414,8 +461,11 @@ __global__ __launch_bounds__(kTreeNT) void ssu_tree_kernel(
             for (int v = 0; v < 4; ++v)
                 zq[v] = ld_raw1<IOT>(z, ((bM + min(mo, M - 1)) * H + h) * Dm + min(orow + v, Dm - 1));
         }
-        if (c + 1 < nchunks)
+        float gnext = 0.0f;
+        if (c + 1 < nchunks) {
             load_c(t0 + TC);
+            gnext = load_g(t0 + TC);
+        }
 
         // S0 . C: 16 rows x 16 nodes per wave on the matrix cores, four
         // independent accumulators so that the MFMAs issue back to back
@@ -428,96 +478,80 @@ __global__ __launch_bounds__(kTreeNT) void ssu_tree_kernel(
 #pragma unroll
             for (int s0 = 0; s0 < KS; s0 += 4) {
                 float cv[4];
-                lds_row<BCT, 4>(cb + s0 * BB, cv);
+                ld_row_f32<BCT, 4>(cb + s0 * BB, cv);
 #pragma unroll
                 for (int e = 0; e < 4; ++e)
                     acc4[e] = __builtin_amdgcn_mfma_f32_16x16x4f32(sa[s0 + e], cv[e], acc4[e], 0, 0, 0);
             }
         }
 
-        // coefficients of the chunk's path entries: LPN lanes per node
-        for (int tt = tid / LPN; tt < TC; tt += NT / LPN) {
-            const int l = tid % LPN;
-            const int m = min(t0 + tt, M - 1);
-            const int nl = tt < nt ? n_len[m] : 0;
-            const uint8_t *pp = n_path + m * (m + 1) / 2;
-            float cv[EPN];
-            lds_row<BCT, EPN>(cs + tt * RB + l * EPN * BB, cv);
-            float wr = 1.0f;
-            // four entries at a time: their ids, then their records and B rows,
-            // then the arithmetic (the weight is a running product in registers)
-            for (int k0 = 0; k0 < nl; k0 += 4) {
-                int jj[4];
-#pragma unroll
-                for (int u = 0; u < 4; ++u)
-                    jj[u] = pp[min(k0 + u, nl - 1)];
-                float4 r[4];
-                float bv[4][EPN];
-#pragma unroll
-                for (int u = 0; u < 4; ++u) {
-                    r[u] = rec[jj[u]];
-                    lds_row<BCT, EPN>(bs + jj[u] * RB + l * EPN * BB, bv[u]);
-                }
-#pragma unroll
-                for (int u = 0; u < 4; ++u) {
-                    if (k0 + u < nl) {  // uniform over the node's lanes
-                        float d = 0.0f;
-#pragma unroll
-                        for (int e = 0; e < EPN; ++e)
-                            d = fmaf(bv[u][e], cv[e], d);
-                        d = row_group_sum<LPN>(d);
-                        if (l == 0)
-                            c_w[tt * M + k0 + u] = wr * r[u].y * d;
-                        wr *= r[u].x;
-                    }
-                }
+        // coefficients: the 16 lanes of chunk node tt take path entries
+        // l, l+16, ..; w of entry i is the product of the decays of entries
+        // 0 .. i-1 (a running product across the lanes, carried across blocks)
+        {
+            const int tt = tid >> 4, l = tid & 15;
+            const int m = t0 + tt;
+            const int len = tt < nt ? n_len[m] : 0;   // uniform over the node's 16 lanes
+            const uint8_t *pp = n_path + (tt < nt ? m * (m + 1) / 2 : 0);
+            float carry = 1.0f;
+            for (int i0 = 0; i0 < len; i0 += 16) {
+                const int i = i0 + l;
+                const bool v = i < len;
+                const int j = v ? pp[i] : m;
+                const float4 r = rec[j];
+                const float gv = i0 == 0 ? gcur : (v ? gbg[(int64_t)m * M + j] : 0.0f);
+                const float incl = row_prefix_prod16(v ? r.x : 1.0f);
+                const float excl = dpp_f32_fill<0x111>(1.0f, incl);  // row_shr:1
+                if (v)
+                    q[j * TC + tt] = carry * excl * r.y * gv;
+                carry *= __shfl(incl, (lane & ~15) | 15, 64);
             }
             if (l == 0 && tt < nt)
-                c_wS[tt] = wr;
+                c_wS[tt] = carry;
         }
+        if (c + 1 < nchunks)
+            zero_q((c + 1) & 1, t0 + TC);  // that buffer was last read by chunk c - 1
         __syncthreads();
         if (c + 1 < nchunks)
             store_c();  // every read of this chunk's C is done
 
         // outputs held in the accumulators: node mo, rows orow .. orow+3
-        if (ln < nt) {
+        {
             f32x4 acc = (acc4[0] + acc4[1]) + (acc4[2] + acc4[3]);
-            float y[4];
             const float wS = c_wS[ln];
 #pragma unroll
             for (int v = 0; v < 4; ++v)
-                y[v] = acc[v] * wS;
-            const int nl = n_len[mo];
-            const uint8_t *pp = n_path + mo * (mo + 1) / 2;
-            const float *cw = c_w + ln * M;
-            for (int k0 = 0; k0 < nl; k0 += 4) {
-                int jj[4];
-                float co[4], xv[4][4];
+                acc[v] *= wS;
+            // path terms: acc[row][node] += sum_j x_j[row] Q[node][j] over the
+            // chunk's sources j < t0 + TC, in groups of four k-steps whose Q^T
+            // reads are issued together (group indices are constants, so the
+            // x operands stay in registers)
 #pragma unroll
-                for (int u = 0; u < 4; ++u) {
-                    jj[u] = pp[min(k0 + u, nl - 1)];
-                    co[u] = cw[min(k0 + u, nl - 1)];
+            for (int gq = 0; gq < MX / 16; ++gq) {
+                if (gq <= c) {
+                    float qv[4];
+#pragma unroll
+                    for (int u = 0; u < 4; ++u)
+                        qv[u] = q[(16 * gq + 4 * u + qg) * TC + ln];
+#pragma unroll
+                    for (int u = 0; u < 4; ++u)
+                        acc = __builtin_amdgcn_mfma_f32_16x16x4f32(xa[4 * gq + u], qv[u], acc, 0, 0, 0);
                 }
-#pragma unroll
-                for (int u = 0; u < 4; ++u)
-                    lds_row<IOT, 4>(xs + jj[u] * XP + (orow - rbase) * XB, xv[u]);
-#pragma unroll
-                for (int u = 0; u < 4; ++u)
-#pragma unroll
-                    for (int v = 0; v < 4; ++v)
-                        y[v] = k0 + u < nl ? fmaf(co[u], xv[u][v], y[v]) : y[v];
             }
-            float xm[4];
-            lds_row<IOT, 4>(xs + mo * XP + (orow - rbase) * XB, xm);
+            if (ln < nt) {
+                float xm[4];
+                ld_row_f32<IOT, 4>(xs + mo * XP + (orow - rbase) * XB, xm);
 #pragma unroll
-            for (int v = 0; v < 4; ++v) {
-                float o = y[v] + dskip * xm[v];
-                if (z)
-                    o *= silu_f32(cvt_raw1<IOT>(zq[v]));
-                if (orow + v < Dm)
-                    st_elem<IOT>(out, ((bM + mo) * H + h) * Dm + orow + v, o);
+                for (int v = 0; v < 4; ++v) {
+                    float o = acc[v] + dskip * xm[v];
+                    if (z)
+                        o *= silu_f32(cvt_raw1<IOT>(zq[v]));
+                    if (orow + v < Dm)
+                        st_elem<IOT>(out, ((bM + mo) * H + h) * Dm + orow + v, o);
+                }
             }
         }
+        gcur = gnext;
         __syncthreads();
     }
 }
@@ -536,7 +570,8 @@ hipError_t launch_tree_cfg(const TreeParams &p, hipStream_t stream)
     sh.nrb = (d.dim + 63) / 64;
     sh.dt_softplus = d.dt_softplus;
     const int64_t blocks = (int64_t)d.batch * d.nheads * sh.nrb;
-    if (blocks > 0x7fffffff)
+    const int64_t gblocks = (int64_t)d.batch * d.ngroups * ((p.num_nodes + 15) / 16);
+    if (blocks > 0x7fffffff || gblocks > 0x7fffffff)
         return hipErrorInvalidConfiguration;
     constexpr int XB = (int)sizeof(IOT), BB = (int)sizeof(BCT);
     const TreeLds L = tree_lds(p.num_nodes, NS, XB, BB);
@@ -561,10 +596,15 @@ hipError_t launch_tree_cfg(const TreeParams &p, hipStream_t stream)
         }
     }
     (void)hipGetLastError();
+    hipLaunchKernelGGL((ssu_tree_gram_kernel<BCT, NS>), dim3((unsigned)gblocks), dim3(kTreeNT), 0,
+                       stream, d.B, d.C, d.idx, p.gram, p.st_B, p.num_nodes, d.ngroups);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess)
+        return e;
     hipLaunchKernelGGL(kern, dim3((unsigned)blocks), dim3(kTreeNT), (unsigned)L.total, stream,
-                       d.x, d.A, d.B, d.C, d.dt, d.dt_bias, d.D, d.z,
+                       d.x, d.A, d.C, d.dt, d.dt_bias, d.D, d.z,
                        static_cast<const ST *>(d.state), d.out, d.idx, p.parents, p.depths,
-                       p.st_dA, p.st_u, p.st_B, p.st_dt, sh);
+                       p.gram, p.st_dA, p.st_u, p.st_dt, sh);
     return hipGetLastError();
 }
 

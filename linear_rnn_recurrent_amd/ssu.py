@@ -22,7 +22,7 @@ _DT = {torch.float32: SSU_F32, torch.float16: SSU_F16, torch.bfloat16: SSU_BF16,
 
 EXPORTS = ("ssu_decode", "ssu_prefill", "ssu_replay", "ssu_tree_verify", "ssu_replay_layers",
            "ssu_state_clear_layers", "ssu_state_gather", "ssu_state_scatter", "ssu_state_pack",
-           "ssu_state_unpack", "ssu_gdn_decode", "ssu_gdn_workspace_bytes",
+           "ssu_state_unpack", "ssu_gdn_decode", "ssu_gdn_workspace_bytes", "ssu_tree_workspace_bytes",
            "ssu_pool_bytes_per_slot",
            "ssu_pool_alloc", "ssu_pool_free", "ssu_pool_info", "ssu_pool_state_ptr",
            "ssu_pool_state_bytes_per_slot", "ssu_pool_find_state", "ssu_pool_clear",
@@ -91,7 +91,7 @@ def load_library(path: Optional[str] = None):
                         _P, _P, _P, _P, _P],
         "ssu_replay": [D, _I32, _P, _P, _P, _P, _P, _P, _P, _I32, _P, _I32, _P],
         "ssu_tree_verify": [D, _I32, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _I32, _P, _P, _P,
-                            _P, _P, _P, _P, _P],
+                            _P, _P, _P, _P, _P, ctypes.c_int64, _P],
         "ssu_replay_layers": [D, _I32, _P, _I32, _P, _P, _I32, _P, _I32, _P],
         "ssu_state_clear_layers": [_P, _I32, _I32, _I32, ctypes.c_int64, ctypes.c_int64, _P],
         "ssu_state_gather": [_P, _I32, ctypes.c_int64, _P, ctypes.c_int64, _P, _I32,
@@ -121,6 +121,8 @@ def load_library(path: Optional[str] = None):
         f = getattr(lib, name)
         f.argtypes = args
         f.restype = ctypes.c_int32
+    lib.ssu_tree_workspace_bytes.argtypes = [D, _I32]
+    lib.ssu_tree_workspace_bytes.restype = ctypes.c_int64
     lib.ssu_gdn_workspace_bytes.argtypes = [ctypes.POINTER(ssu_gdn_dims)]
     lib.ssu_gdn_workspace_bytes.restype = ctypes.c_int64
     lib.ssu_last_error.argtypes = []
@@ -324,12 +326,14 @@ def ssu_replay(state, replay_dA, replay_u, replay_B, replay_dt, accepted_lengths
 
 def ssu_tree_verify(x, A, B, C, dt, state, out, parent_ids, *, depths=None, dt_bias=None,
                     D=None, z=None, dt_softplus=True, state_indices=None, replay_dA=None,
-                    replay_u=None, replay_B=None, replay_dt=None, stream=None):
+                    replay_u=None, replay_B=None, replay_dt=None, workspace=None, stream=None):
     """Every node of a draft tree per batch row, from the read-only committed state.
 
     x, z, out [batch, num_nodes, nheads, dim]; dt [batch, num_nodes, nheads];
     B, C [batch, num_nodes, ngroups, dstate]; parent_ids, depths [batch, num_nodes] int32.
     Replay stash (fp32, all four or none) in the ssu_prefill layouts with the node axis.
+    workspace: a uint8 GPU tensor of at least tree_workspace_bytes(...) bytes (allocated
+    here when None).
     """
     lib = load_library()
     _dense(x, "x", _FLOAT)
@@ -361,13 +365,23 @@ def ssu_tree_verify(x, A, B, C, dt, state, out, parent_ids, *, depths=None, dt_b
         _dense(replay_u, "replay_u", (torch.float32,), x.shape)
         _dense(replay_B, "replay_B", (torch.float32,), B.shape)
     d = _dims(batch, nheads, dim, dstate, ngroups, rows, stride, state.dtype, x.dtype, B.dtype)
+    if workspace is None:
+        need = max(int(lib.ssu_tree_workspace_bytes(ctypes.byref(d), num_nodes)), 16)
+        workspace = torch.empty(need, dtype=torch.uint8, device=x.device)
+    _dense(workspace, "workspace", (torch.uint8,))
     with torch.cuda.device(x.device):
         _check(lib.ssu_tree_verify(ctypes.byref(d), num_nodes, _ptr(x), _ptr(A), _ptr(B),
                                    _ptr(C), _ptr(dt), _ptr(dt_bias), _ptr(D), _ptr(z),
                                    _ptr(state), _ptr(out), 1 if dt_softplus else 0,
                                    _ptr(state_indices), _ptr(parent_ids), _ptr(depths),
-                                   *[_ptr(s) for s in stash], _stream(x.device, stream)))
+                                   *[_ptr(s) for s in stash], _ptr(workspace),
+                                   workspace.numel(), _stream(x.device, stream)))
     return out
+
+
+def tree_workspace_bytes(batch, ngroups, num_nodes):
+    """Bytes of the workspace ssu_tree_verify needs (no GPU needed)."""
+    return 4 * batch * ngroups * num_nodes * num_nodes
 
 
 def _device_table(structs, device):

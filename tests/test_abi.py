@@ -180,13 +180,13 @@ def test_replay_node_id_validation(lib):
     assert "'accepted_node_ids'" in err(lib) and "4-byte aligned" in err(lib)
 
 
-def tree(lib, d, num_nodes=8, stash=(None, None, None, None), **ptrs):
+def tree(lib, d, num_nodes=8, stash=(None, None, None, None), ws=FAKE, ws_bytes=1 << 30, **ptrs):
     p = dict(x=FAKE, A=FAKE, B=FAKE, C=FAKE, dt=FAKE, state=FAKE, out=FAKE, par=FAKE,
              dep=None, idx=None)
     p.update(ptrs)
     return lib.ssu_tree_verify(ctypes.byref(d), num_nodes, p["x"], p["A"], p["B"], p["C"],
                                p["dt"], None, None, None, p["state"], p["out"], 1, p["idx"],
-                               p["par"], p["dep"], *stash, None)
+                               p["par"], p["dep"], *stash, ws, ws_bytes, None)
 
 
 def test_tree_verify_validation(lib):
@@ -203,6 +203,14 @@ def test_tree_verify_validation(lib):
     assert tree(lib, dims(), stash=(FAKE, FAKE, FAKE + 4, FAKE)) == 1 and "'replay_B'" in err(lib)
     assert tree(lib, dims(batch=5)) == 1 and "pool_rows" in err(lib)
     assert tree(lib, dims(dstate=48)) == 2
+    assert tree(lib, dims(), ws=None) == 1 and "'workspace'" in err(lib)
+    assert tree(lib, dims(), ws=FAKE + 4) == 1 and "'workspace'" in err(lib)
+    d = dims()
+    need = lib.ssu_tree_workspace_bytes(ctypes.byref(d), 8)
+    assert need == 4 * d.batch * d.ngroups * 64 == S.tree_workspace_bytes(d.batch, d.ngroups, 8)
+    assert tree(lib, d, ws_bytes=need - 4) == 1 and "workspace_bytes" in err(lib)
+    assert lib.ssu_tree_workspace_bytes(ctypes.byref(d), 129) == -1
+    assert lib.ssu_tree_workspace_bytes(None, 8) == -1
 
 
 def spec_array(specs):
