@@ -71,6 +71,20 @@ constexpr int kTreeTC = 16;   // nodes per chunk (the N side of one 16x16 MFMA t
 constexpr int kTreeNT = 256;  // threads: four waves of 16 rows each
 
 typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+
+// With bf16 C (exact as a bf16 MFMA operand) S0 . C runs on the bf16 matrix
+// cores: S0 = hi + mid + lo, each a bf16 (round to nearest, the remainder
+// split again), so each product is that of fp32 S0 to within ~2^-24 of S0 and
+// the sums stay fp32; three v_mfma_f32_16x16x32_bf16 (16 cycles each) replace
+// eight v_mfma_f32_16x16x4_f32 (32 cycles each) per 32 dstate columns. A
+// 16-bit state needs fewer terms (bf16: hi only; fp16: hi + mid).
+template <typename ST, typename BCT, int NS>
+struct TreeSplit {
+    static constexpr bool on = __is_same(BCT, bf16_t) && NS % 32 == 0;
+    static constexpr int terms = sizeof(ST) == 4 ? 3 : (__is_same(ST, bf16_t) ? 1 : 2);
+    static constexpr int T = NS / 32;  // 16x16x32 steps over dstate
+};
 
 // Byte offsets of the LDS arrays for a tree of M nodes (host and device).
 struct TreeLds {
@@ -269,15 +283,35 @@ __global__ __launch_bounds__(kTreeNT) void ssu_tree_kernel(
     const float dskip = Dv ? Dv[h] : 0.0f;
 
     // ---- 1. prologue: every global load first ----
-    // MFMA A operand: lane (ln, qg) of wave w holds S0[row 16 w + ln][qg KS + s]
+    // MFMA A operand, fp32 form: lane (ln, qg) of wave w holds
+    // S0[row 16 w + ln][qg KS + s]; split-bf16 form: S0[row][32 t + 8 qg + e]
+    // as `terms` bf16 parts per element
+    using SP = TreeSplit<ST, BCT, NS>;
     const int arow = rbase + 16 * wave + ln;
-    float sa[KS];
+    float sa[SP::on ? 1 : KS];
+    bf16x8 sb[SP::on ? SP::terms * SP::T : 1];
     {
         const ST *sp = state + (int64_t)srow * sh.row_stride + (int64_t)h * Dm * NS +
-                       (int64_t)min(arow, Dm - 1) * NS + qg * KS;
+                       (int64_t)min(arow, Dm - 1) * NS;
+        if constexpr (SP::on) {
 #pragma unroll
-        for (int s = 0; s < KS; ++s)
-            sa[s] = ld_elem<ST>(sp, s);
+            for (int t = 0; t < SP::T; ++t) {
+#pragma unroll
+                for (int e = 0; e < 8; ++e) {
+                    float r = ld_elem<ST>(sp, 32 * t + 8 * qg + e);
+#pragma unroll
+                    for (int u = 0; u < SP::terms; ++u) {
+                        const __bf16 p = (__bf16)r;
+                        sb[u * SP::T + t][e] = p;
+                        r -= (float)p;
+                    }
+                }
+            }
+        } else {
+#pragma unroll
+            for (int s = 0; s < KS; ++s)
+                sa[s] = ld_elem<ST>(sp, qg * KS + s);
+        }
     }
     // per node: dt, parent id, hop bound
     float ndt[NPT];
@@ -473,7 +507,20 @@ __global__ __launch_bounds__(kTreeNT) void ssu_tree_kernel(
 #pragma unroll
         for (int a4 = 0; a4 < 4; ++a4)
             acc4[a4] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
-        {
+        if constexpr (SP::on) {
+            // B operand: C_{node ln}[32 t + 8 qg .. + 7], one 16-byte LDS read
+            const unsigned char *cb = cs + ln * RB + 16 * qg;
+            bf16x8 cv[SP::T];
+#pragma unroll
+            for (int t = 0; t < SP::T; ++t)
+                cv[t] = *reinterpret_cast<const bf16x8 *>(cb + 64 * t);
+#pragma unroll
+            for (int t = 0; t < SP::T; ++t)
+#pragma unroll
+                for (int u = 0; u < SP::terms; ++u)
+                    acc4[(u + t) & 3] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+                        sb[u * SP::T + t], cv[t], acc4[(u + t) & 3], 0, 0, 0);
+        } else {
             const unsigned char *cb = cs + ln * RB + qg * KS * BB;
 #pragma unroll
             for (int s0 = 0; s0 < KS; s0 += 4) {
