@@ -79,6 +79,14 @@ typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 // the sums stay fp32; three v_mfma_f32_16x16x32_bf16 (16 cycles each) replace
 // eight v_mfma_f32_16x16x4_f32 (32 cycles each) per 32 dstate columns. A
 // 16-bit state needs fewer terms (bf16: hi only; fp16: hi + mid).
+// With bf16 x (exact as an operand) the path product X . Q^T also runs on the
+// bf16 matrix cores, Q split into hi + lo bf16 terms (relative error ~2^-16
+// per coefficient, far below the bf16 rounding of the outputs).
+template <typename IOT>
+struct TreePathSplit {
+    static constexpr bool on = __is_same(IOT, bf16_t);
+};
+
 template <typename ST, typename BCT, int NS>
 struct TreeSplit {
     static constexpr bool on = __is_same(BCT, bf16_t) && NS % 32 == 0;
@@ -105,6 +113,9 @@ __host__ __device__ constexpr int tree_row_bytes(int NS, int bc_bytes) { return 
 __host__ __device__ constexpr int tree_x_pitch(int io_bytes) { return 64 * io_bytes + 16; }
 // source-node rows of the coefficient matrix: every chunk's range, padded
 __host__ __device__ constexpr int tree_q_rows(int M) { return (M + 15) & ~15; }
+// row pitch (elements) of Q in its split-bf16 form [term][node][source]: whole
+// 32-source MFMA steps plus a 16-byte pad against bank conflicts
+__host__ __device__ constexpr int tree_q_pitch(int M) { return ((M + 31) & ~31) + 8; }
 
 __host__ __device__ inline TreeLds tree_lds(int M, int NS, int io_bytes, int bc_bytes)
 {
@@ -116,7 +127,9 @@ __host__ __device__ inline TreeLds tree_lds(int M, int NS, int io_bytes, int bc_
     L.rec = tree_lds_take(o, M * 16);                     // node records
     L.path = tree_lds_take(o, M * (M + 1) / 2);           // path of node m at m(m+1)/2
     L.len = tree_lds_take(o, M * 4);                      // path lengths
-    L.qt = tree_lds_take(o, 2 * tree_q_rows(M) * kTreeTC * 4);  // Q^T [source][chunk node], x2
+    // Q of a chunk, double buffered: fp32 Q^T [source][chunk node] or the
+    // split-bf16 [2 terms][chunk node][source pitch] (the larger of the two)
+    L.qt = tree_lds_take(o, 2 * kTreeTC * tree_q_pitch(M) * 4);
     L.cws = tree_lds_take(o, kTreeTC * 4);                // weights of S0 of the chunk's nodes
     L.total = o;
     return L;
@@ -248,7 +261,10 @@ __global__ __launch_bounds__(kTreeNT) void ssu_tree_kernel(
     float4 *rec = reinterpret_cast<float4 *>(lds + L.rec);  // {exp(A dt'), dt', parent, bound}
     uint8_t *n_path = lds + L.path;                          // triangular path table
     int *n_len = reinterpret_cast<int *>(lds + L.len);
-    float *qt = reinterpret_cast<float *>(lds + L.qt);       // 2 x [RM][TC]
+    float *qt = reinterpret_cast<float *>(lds + L.qt);       // 2 x [RM][TC] (fp32 form)
+    constexpr bool PX = TreePathSplit<IOT>::on;
+    const int QP = tree_q_pitch(M);
+    uint16_t *qs = reinterpret_cast<uint16_t *>(lds + L.qt);  // 2 x [2][TC][QP] (split form)
     float *c_wS = reinterpret_cast<float *>(lds + L.cws);    // [TC]
 
     const int tid = threadIdx.x;
@@ -427,11 +443,19 @@ __global__ __launch_bounds__(kTreeNT) void ssu_tree_kernel(
         }
     }
     store_c();
-    // Q^T rows the chunk starting at t0 reads: sources j < t0 + TC (<= RM)
+    // the Q entries the chunk starting at t0 reads: sources j < t0 + TC (<= RM),
+    // in whole 32-source steps in the split form
     auto zero_q = [&](int buf, int t0) {
-        float4 *q = reinterpret_cast<float4 *>(qt + buf * RM * TC);
-        for (int i = tid; i < (t0 + TC) * TC / 4; i += NT)
-            q[i] = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
+        if constexpr (PX) {
+            const int nw = ((t0 + TC + 31) & ~31) / 2;  // u32 words per row
+            uint32_t *q = reinterpret_cast<uint32_t *>(qs + buf * 2 * TC * QP);
+            for (int i = tid; i < 2 * TC * nw; i += NT)
+                q[(i / nw) * (QP / 2) + i % nw] = 0u;
+        } else {
+            float4 *q = reinterpret_cast<float4 *>(qt + buf * RM * TC);
+            for (int i = tid; i < (t0 + TC) * TC / 4; i += NT)
+                q[i] = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
+        }
     };
     zero_q(0, 0);
     __syncthreads();
@@ -454,8 +478,20 @@ __global__ __launch_bounds__(kTreeNT) void ssu_tree_kernel(
     __syncthreads();
 
     // this lane's MFMA A operand of the path product: x_{4s+qg}[row 16w+ln]
-    float xa[MX / 4];
-    {
+    // (fp32 form) or x_{32t+8qg+e}[row 16w+ln] (bf16 form)
+    float xa[PX ? 1 : MX / 4];
+    bf16x8 xb[PX ? MX / 32 : 1];
+    if constexpr (PX) {
+        const int rl = 16 * wave + ln;
+#pragma unroll
+        for (int t = 0; t < MX / 32; ++t)
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+                const int j = 32 * t + 8 * qg + e;
+                const uint16_t w = j < M ? *reinterpret_cast<const uint16_t *>(xs + j * XP + rl * 2) : 0;
+                xb[t][e] = __builtin_bit_cast(__bf16, w);
+            }
+    } else {
         const int rl = 16 * wave + ln;
 #pragma unroll
         for (int s = 0; s < MX / 4; ++s) {
@@ -488,6 +524,7 @@ __global__ __launch_bounds__(kTreeNT) void ssu_tree_kernel(
         const int mo = t0 + ln;                       // this lane's output node
         const int orow = rbase + 16 * wave + 4 * qg;  // and its first output row
         float *q = qt + (c & 1) * RM * TC;
+        uint16_t *qc = qs + (c & 1) * 2 * TC * QP;
         // gate inputs of this lane's four outputs (raw bits; clamped indices)
         uint32_t zq[4] = {0u, 0u, 0u, 0u};
         if (z) {
@@ -549,8 +586,17 @@ __global__ __launch_bounds__(kTreeNT) void ssu_tree_kernel(
                 const float gv = i0 == 0 ? gcur : (v ? gbg[(int64_t)m * M + j] : 0.0f);
                 const float incl = row_prefix_prod16(v ? r.x : 1.0f);
                 const float excl = dpp_f32_fill<0x111>(1.0f, incl);  // row_shr:1
-                if (v)
-                    q[j * TC + tt] = carry * excl * r.y * gv;
+                if (v) {
+                    const float qv = carry * excl * r.y * gv;
+                    if constexpr (PX) {
+                        const __bf16 hi = (__bf16)qv;
+                        qc[tt * QP + j] = __builtin_bit_cast(uint16_t, hi);
+                        qc[(TC + tt) * QP + j] =
+                            __builtin_bit_cast(uint16_t, (__bf16)(qv - (float)hi));
+                    } else {
+                        q[j * TC + tt] = qv;
+                    }
+                }
                 carry *= __shfl(incl, (lane & ~15) | 15, 64);
             }
             if (l == 0 && tt < nt)
@@ -573,16 +619,30 @@ __global__ __launch_bounds__(kTreeNT) void ssu_tree_kernel(
             // chunk's sources j < t0 + TC, in groups of four k-steps whose Q^T
             // reads are issued together (group indices are constants, so the
             // x operands stay in registers)
+            if constexpr (PX) {
+                // B operand: Q[node ln][32 t + 8 qg .. + 7], hi and lo terms
+                const uint16_t *qr = qc + ln * QP + 8 * qg;
 #pragma unroll
-            for (int gq = 0; gq < MX / 16; ++gq) {
-                if (gq <= c) {
-                    float qv[4];
+                for (int t = 0; t < MX / 32; ++t) {
+                    if (32 * t < t0 + TC) {
+                        const bf16x8 qh = *reinterpret_cast<const bf16x8 *>(qr + 32 * t);
+                        const bf16x8 ql = *reinterpret_cast<const bf16x8 *>(qr + TC * QP + 32 * t);
+                        acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(xb[t], qh, acc, 0, 0, 0);
+                        acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(xb[t], ql, acc, 0, 0, 0);
+                    }
+                }
+            } else {
 #pragma unroll
-                    for (int u = 0; u < 4; ++u)
-                        qv[u] = q[(16 * gq + 4 * u + qg) * TC + ln];
+                for (int gq = 0; gq < MX / 16; ++gq) {
+                    if (gq <= c) {
+                        float qv[4];
 #pragma unroll
-                    for (int u = 0; u < 4; ++u)
-                        acc = __builtin_amdgcn_mfma_f32_16x16x4f32(xa[4 * gq + u], qv[u], acc, 0, 0, 0);
+                        for (int u = 0; u < 4; ++u)
+                            qv[u] = q[(16 * gq + 4 * u + qg) * TC + ln];
+#pragma unroll
+                        for (int u = 0; u < 4; ++u)
+                            acc = __builtin_amdgcn_mfma_f32_16x16x4f32(xa[4 * gq + u], qv[u], acc, 0, 0, 0);
+                    }
                 }
             }
             if (ln < nt) {
