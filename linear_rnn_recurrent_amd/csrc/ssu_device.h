@@ -93,6 +93,23 @@ __device__ __forceinline__ void st_elem(void *p, int64_t i, float v)
         static_cast<uint16_t *>(p)[i] = (uint16_t)f32_to_f16(v);
 }
 
+// Four consecutive elements at element offset i (base aligned to four
+// elements), rounded as st_elem rounds them, in one store.
+template <typename T>
+__device__ __forceinline__ void st_raw4(void *p, uint32_t i, const float (&v)[4])
+{
+    if constexpr (sizeof(T) == 4) {
+        *reinterpret_cast<float4 *>(static_cast<float *>(p) + i) = make_float4(v[0], v[1], v[2], v[3]);
+    } else {
+        uint32_t h[4];
+#pragma unroll
+        for (int k = 0; k < 4; ++k)
+            h[k] = __is_same(T, bf16_t) ? f32_to_bf16(v[k]) : f32_to_f16(v[k]);
+        *reinterpret_cast<u32x2 *>(static_cast<uint16_t *>(p) + i) =
+            u32x2{h[0] | (h[1] << 16), h[2] | (h[3] << 16)};
+    }
+}
+
 // N consecutive B/C elements (N a multiple of 4) of storage type T at element
 // offset i (a multiple of N; base 16-byte aligned), loaded as whole vectors
 // before any conversion so that the loads are all in flight together.

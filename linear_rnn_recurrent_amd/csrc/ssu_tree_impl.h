@@ -77,8 +77,10 @@ typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 // cores: S0 = hi + mid + lo, each a bf16 (round to nearest, the remainder
 // split again), so each product is that of fp32 S0 to within ~2^-24 of S0 and
 // the sums stay fp32; three v_mfma_f32_16x16x32_bf16 (16 cycles each) replace
-// eight v_mfma_f32_16x16x4_f32 (32 cycles each) per 32 dstate columns. A
-// 16-bit state needs fewer terms (bf16: hi only; fp16: hi + mid).
+// eight v_mfma_f32_16x16x4_f32 (32 cycles each) per 32 dstate columns. When
+// the outputs are 16-bit, hi + mid suffice for an fp32 state (~2^-17 of S0,
+// 2^6 below an fp16 output's own rounding). A 16-bit state needs fewer terms
+// (bf16: hi only; fp16: hi + mid, exact).
 // With bf16 x (exact as an operand) the path product X . Q^T also runs on the
 // bf16 matrix cores, Q split into hi + lo bf16 terms (relative error ~2^-16
 // per coefficient, far below the bf16 rounding of the outputs).
@@ -87,12 +89,22 @@ struct TreePathSplit {
     static constexpr bool on = __is_same(IOT, bf16_t);
 };
 
-template <typename ST, typename BCT, int NS>
+template <typename ST, typename IOT, typename BCT, int NS>
 struct TreeSplit {
     static constexpr bool on = __is_same(BCT, bf16_t) && NS % 32 == 0;
-    static constexpr int terms = sizeof(ST) == 4 ? 3 : (__is_same(ST, bf16_t) ? 1 : 2);
+    static constexpr int terms =
+        __is_same(ST, bf16_t) ? 1 : (sizeof(ST) == 4 && sizeof(IOT) == 4 ? 3 : 2);
     static constexpr int T = NS / 32;  // 16x16x32 steps over dstate
 };
+
+// Waves per SIMD the register budget is cut for: four (128 VGPRs) where the
+// operand registers (state slice, x of the path product, x staging) fit without
+// spilling, else what the compiler chooses.
+template <typename IOT, int NS>
+constexpr int tree_waves()
+{
+    return (TreePathSplit<IOT>::on ? NS <= 128 : NS * (int)sizeof(IOT) <= 128) ? 4 : 1;
+}
 
 // Byte offsets of the LDS arrays for a tree of M nodes (host and device).
 struct TreeLds {
@@ -122,17 +134,30 @@ __host__ __device__ inline TreeLds tree_lds(int M, int NS, int io_bytes, int bc_
     TreeLds L;
     int o = 0;
     const int rb = tree_row_bytes(NS, bc_bytes);
-    L.xs = tree_lds_take(o, M * tree_x_pitch(io_bytes));  // x [M][64 rows]
+    // x [M][64 rows] is staged here until every lane holds its share of it
+    // in registers; the same bytes then hold the chunk coefficients Q, double
+    // buffered: fp32 Q^T [source][chunk node] or the split-bf16 [2 terms]
+    // [chunk node][source pitch] (the larger of the two)
+    const int xs_bytes = M * tree_x_pitch(io_bytes);
+    const int q_bytes = 2 * kTreeTC * tree_q_pitch(M) * 4;
+    L.xs = L.qt = tree_lds_take(o, xs_bytes > q_bytes ? xs_bytes : q_bytes);
     L.cs = tree_lds_take(o, kTreeTC * rb);                // C of the current chunk [TC][NS]
     L.rec = tree_lds_take(o, M * 16);                     // node records
     L.path = tree_lds_take(o, M * (M + 1) / 2);           // path of node m at m(m+1)/2
     L.len = tree_lds_take(o, M * 4);                      // path lengths
-    // Q of a chunk, double buffered: fp32 Q^T [source][chunk node] or the
-    // split-bf16 [2 terms][chunk node][source pitch] (the larger of the two)
-    L.qt = tree_lds_take(o, 2 * kTreeTC * tree_q_pitch(M) * 4);
     L.cws = tree_lds_take(o, kTreeTC * 4);                // weights of S0 of the chunk's nodes
     L.total = o;
     return L;
+}
+
+// Triangular table slot of node m's path (m(m+1)/2, 32-bit).
+__device__ __forceinline__ uint32_t tri(int m) { return ((uint32_t)m * (uint32_t)(m + 1)) >> 1; }
+
+// fp32 at a 32-bit byte offset from a base (the offset zero-extends, so the
+// access takes a scalar base and one vector offset register).
+__device__ __forceinline__ float ld_f32_at(const float *base, uint32_t byte_off)
+{
+    return *reinterpret_cast<const float *>(reinterpret_cast<const unsigned char *>(base) + byte_off);
 }
 
 // n consecutive storage-dtype elements (16-bit or fp32) as fp32, from LDS or
@@ -229,7 +254,7 @@ __global__ __launch_bounds__(kTreeNT) void ssu_tree_gram_kernel(
 }
 
 template <typename ST, typename IOT, typename BCT, int NS>
-__global__ __launch_bounds__(kTreeNT) void ssu_tree_kernel(
+__global__ __launch_bounds__(kTreeNT) __attribute__((amdgpu_waves_per_eu(tree_waves<IOT, NS>()))) void ssu_tree_kernel(
     const void *__restrict__ x, const float *__restrict__ A, const void *__restrict__ Cm,
     const float *__restrict__ dt, const float *__restrict__ dt_bias, const float *__restrict__ Dv,
     const void *__restrict__ z, const ST *__restrict__ state, void *__restrict__ out,
@@ -294,6 +319,10 @@ __global__ __launch_bounds__(kTreeNT) void ssu_tree_kernel(
     const bool stash = st_dA != nullptr;
     const int g = h / sh.heads_per_group;
     const float *gbg = gram + ((int64_t)b * G + g) * M * M;  // G[m][j] of this (b, g)
+    // out and z of this (batch row, head): node m, row r at m H Dm + r
+    void *obase = static_cast<unsigned char *>(out) + (bM * H + h) * Dm * XB;
+    const void *zbase = z ? static_cast<const unsigned char *>(z) + (bM * H + h) * Dm * XB : nullptr;
+    const bool ovec = Dm % 4 == 0 && (reinterpret_cast<uintptr_t>(out) & (4 * XB - 1)) == 0;
     const float Ah = A[h];
     const float bias = dt_bias ? dt_bias[h] : 0.0f;
     const float dskip = Dv ? Dv[h] : 0.0f;
@@ -302,7 +331,7 @@ __global__ __launch_bounds__(kTreeNT) void ssu_tree_kernel(
     // MFMA A operand, fp32 form: lane (ln, qg) of wave w holds
     // S0[row 16 w + ln][qg KS + s]; split-bf16 form: S0[row][32 t + 8 qg + e]
     // as `terms` bf16 parts per element
-    using SP = TreeSplit<ST, BCT, NS>;
+    using SP = TreeSplit<ST, IOT, BCT, NS>;
     const int arow = rbase + 16 * wave + ln;
     float sa[SP::on ? 1 : KS];
     bf16x8 sb[SP::on ? SP::terms * SP::T : 1];
@@ -341,14 +370,14 @@ __global__ __launch_bounds__(kTreeNT) void ssu_tree_kernel(
     }
     // C of chunk c: 16-byte vectors of the storage dtype (nodes past M clamp to M-1)
     u32x4 rc[CV];
+    const unsigned char *cbase = static_cast<const unsigned char *>(Cm) + (bM * G + g) * NS * BB;
     auto load_c = [&](int t0) {
 #pragma unroll
         for (int k = 0; k < CV; ++k) {
             const int v = tid + NT * k;               // vector v: node v / (NS/BVE)
             const int m = min(t0 + v / (NS / BVE), M - 1);
             rc[k] = *reinterpret_cast<const u32x4 *>(
-                static_cast<const unsigned char *>(Cm) +
-                (((bM + m) * G + g) * NS + BVE * (v % (NS / BVE))) * BB);
+                cbase + (uint32_t)(m * (G * NS * BB) + 16 * (v % (NS / BVE))));
         }
     };
     auto store_c = [&]() {
@@ -443,26 +472,11 @@ __global__ __launch_bounds__(kTreeNT) void ssu_tree_kernel(
         }
     }
     store_c();
-    // the Q entries the chunk starting at t0 reads: sources j < t0 + TC (<= RM),
-    // in whole 32-source steps in the split form
-    auto zero_q = [&](int buf, int t0) {
-        if constexpr (PX) {
-            const int nw = ((t0 + TC + 31) & ~31) / 2;  // u32 words per row
-            uint32_t *q = reinterpret_cast<uint32_t *>(qs + buf * 2 * TC * QP);
-            for (int i = tid; i < 2 * TC * nw; i += NT)
-                q[(i / nw) * (QP / 2) + i % nw] = 0u;
-        } else {
-            float4 *q = reinterpret_cast<float4 *>(qt + buf * RM * TC);
-            for (int i = tid; i < (t0 + TC) * TC / 4; i += NT)
-                q[i] = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
-        }
-    };
-    zero_q(0, 0);
     __syncthreads();
 
     // ---- the path of every node (one lane per node), node first ----
     for (int m = tid; m < M; m += NT) {
-        uint8_t *pp = n_path + m * (m + 1) / 2;
+        uint8_t *pp = n_path + tri(m);
         const int cap = __float_as_int(rec[m].w);
         int j = m, hops = 0;
         while (true) {
@@ -475,8 +489,6 @@ __global__ __launch_bounds__(kTreeNT) void ssu_tree_kernel(
         }
         n_len[m] = hops + 1;
     }
-    __syncthreads();
-
     // this lane's MFMA A operand of the path product: x_{4s+qg}[row 16w+ln]
     // (fp32 form) or x_{32t+8qg+e}[row 16w+ln] (bf16 form)
     float xa[PX ? 1 : MX / 4];
@@ -506,16 +518,28 @@ __global__ __launch_bounds__(kTreeNT) void ssu_tree_kernel(
             xa[s] = v;
         }
     }
+    __syncthreads();  // x staging read by every lane; paths in place
+
     // G value of this lane's path entry (entry tid%16 of chunk node tid/16) of
     // the chunk starting at t0; entries past 16 are read in the loop below
     auto load_g = [&](int t0) {
         const int m = t0 + (tid >> 4), l = tid & 15;
         float v = 0.0f;
         if (m < M && l < n_len[m])
-            v = gbg[(int64_t)m * M + n_path[m * (m + 1) / 2 + l]];
+            v = ld_f32_at(gbg, (m * M + n_path[tri(m) + l]) * 4u);
         return v;
     };
     float gcur = load_g(0);
+    // both coefficient buffers (over the x staging) start at zero; from then
+    // on each chunk clears the entries that the chunk before it set
+    {
+        constexpr int QB = PX ? 2 * 2 * TC * 2 : 2 * TC * 4;  // bytes per unit of QP / RM
+        const int n16 = (PX ? QP : RM) * QB / 16;
+        u32x4 *q = reinterpret_cast<u32x4 *>(lds + L.qt);
+        for (int i = tid; i < n16; i += NT)
+            q[i] = u32x4{0u, 0u, 0u, 0u};
+    }
+    __syncthreads();
 
     const int nchunks = (M + TC - 1) / TC;
     for (int c = 0; c < nchunks; ++c) {
@@ -528,9 +552,11 @@ __global__ __launch_bounds__(kTreeNT) void ssu_tree_kernel(
         // gate inputs of this lane's four outputs (raw bits; clamped indices)
         uint32_t zq[4] = {0u, 0u, 0u, 0u};
         if (z) {
+            const int e = min(mo, M - 1) * (H * Dm);
 #pragma unroll
             for (int v = 0; v < 4; ++v)
-                zq[v] = ld_raw1<IOT>(z, ((bM + min(mo, M - 1)) * H + h) * Dm + min(orow + v, Dm - 1));
+                zq[v] = ld_raw1<IOT>(static_cast<const unsigned char *>(zbase) +
+                                         (uint32_t)((e + min(orow + v, Dm - 1)) * XB), 0);
         }
         float gnext = 0.0f;
         if (c + 1 < nchunks) {
@@ -540,9 +566,10 @@ __global__ __launch_bounds__(kTreeNT) void ssu_tree_kernel(
 
         // S0 . C: 16 rows x 16 nodes per wave on the matrix cores, four
         // independent accumulators so that the MFMAs issue back to back
-        f32x4 acc4[4];
+        constexpr int NACC = SP::on ? 2 : 4;  // a 16-cycle bf16 MFMA needs two in flight
+        f32x4 acc4[NACC];
 #pragma unroll
-        for (int a4 = 0; a4 < 4; ++a4)
+        for (int a4 = 0; a4 < NACC; ++a4)
             acc4[a4] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
         if constexpr (SP::on) {
             // B operand: C_{node ln}[32 t + 8 qg .. + 7], one 16-byte LDS read
@@ -555,8 +582,8 @@ __global__ __launch_bounds__(kTreeNT) void ssu_tree_kernel(
             for (int t = 0; t < SP::T; ++t)
 #pragma unroll
                 for (int u = 0; u < SP::terms; ++u)
-                    acc4[(u + t) & 3] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
-                        sb[u * SP::T + t], cv[t], acc4[(u + t) & 3], 0, 0, 0);
+                    acc4[(u + t) % NACC] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+                        sb[u * SP::T + t], cv[t], acc4[(u + t) % NACC], 0, 0, 0);
         } else {
             const unsigned char *cb = cs + ln * RB + qg * KS * BB;
 #pragma unroll
@@ -565,7 +592,8 @@ __global__ __launch_bounds__(kTreeNT) void ssu_tree_kernel(
                 ld_row_f32<BCT, 4>(cb + s0 * BB, cv);
 #pragma unroll
                 for (int e = 0; e < 4; ++e)
-                    acc4[e] = __builtin_amdgcn_mfma_f32_16x16x4f32(sa[s0 + e], cv[e], acc4[e], 0, 0, 0);
+                    acc4[e % NACC] =
+                        __builtin_amdgcn_mfma_f32_16x16x4f32(sa[s0 + e], cv[e], acc4[e % NACC], 0, 0, 0);
             }
         }
 
@@ -576,18 +604,19 @@ __global__ __launch_bounds__(kTreeNT) void ssu_tree_kernel(
             const int tt = tid >> 4, l = tid & 15;
             const int m = t0 + tt;
             const int len = tt < nt ? n_len[m] : 0;   // uniform over the node's 16 lanes
-            const uint8_t *pp = n_path + (tt < nt ? m * (m + 1) / 2 : 0);
+            const uint8_t *pp = n_path + (tt < nt ? tri(m) : 0u);
             float carry = 1.0f;
             for (int i0 = 0; i0 < len; i0 += 16) {
                 const int i = i0 + l;
                 const bool v = i < len;
                 const int j = v ? pp[i] : m;
                 const float4 r = rec[j];
-                const float gv = i0 == 0 ? gcur : (v ? gbg[(int64_t)m * M + j] : 0.0f);
+                const float gv = i0 == 0 ? gcur : (v ? ld_f32_at(gbg, (m * M + j) * 4u) : 0.0f);
                 const float incl = row_prefix_prod16(v ? r.x : 1.0f);
                 const float excl = dpp_f32_fill<0x111>(1.0f, incl);  // row_shr:1
                 if (v) {
-                    const float qv = carry * excl * r.y * gv;
+                    // entry 0 is the node itself: D x_m joins the path sum
+                    const float qv = carry * excl * r.y * gv + (i == 0 ? dskip : 0.0f);
                     if constexpr (PX) {
                         const __bf16 hi = (__bf16)qv;
                         qc[tt * QP + j] = __builtin_bit_cast(uint16_t, hi);
@@ -601,16 +630,34 @@ __global__ __launch_bounds__(kTreeNT) void ssu_tree_kernel(
             }
             if (l == 0 && tt < nt)
                 c_wS[tt] = carry;
+            // back to zero: the entries chunk c - 1 set in the other buffer
+            // (every lane read them before the last barrier; chunk c + 1
+            // writes there after the next one). Chunks before the last are full.
+            if (c > 0) {
+                const int mp = m - TC;
+                const int lenp = n_len[mp];
+                const uint8_t *ppp = n_path + tri(mp);
+                for (int i = l; i < lenp; i += 16) {
+                    const int j = ppp[i];
+                    if constexpr (PX) {
+                        uint16_t *qo = qs + ((c - 1) & 1) * 2 * TC * QP;
+                        qo[tt * QP + j] = 0;
+                        qo[(TC + tt) * QP + j] = 0;
+                    } else {
+                        qt[((c - 1) & 1) * RM * TC + j * TC + tt] = 0.0f;
+                    }
+                }
+            }
         }
-        if (c + 1 < nchunks)
-            zero_q((c + 1) & 1, t0 + TC);  // that buffer was last read by chunk c - 1
         __syncthreads();
         if (c + 1 < nchunks)
             store_c();  // every read of this chunk's C is done
 
         // outputs held in the accumulators: node mo, rows orow .. orow+3
         {
-            f32x4 acc = (acc4[0] + acc4[1]) + (acc4[2] + acc4[3]);
+            f32x4 acc = acc4[0] + acc4[1];
+            if constexpr (NACC == 4)
+                acc += acc4[2] + acc4[3];
             const float wS = c_wS[ln];
 #pragma unroll
             for (int v = 0; v < 4; ++v)
@@ -646,15 +693,22 @@ __global__ __launch_bounds__(kTreeNT) void ssu_tree_kernel(
                 }
             }
             if (ln < nt) {
-                float xm[4];
-                ld_row_f32<IOT, 4>(xs + mo * XP + (orow - rbase) * XB, xm);
+                float o[4];
 #pragma unroll
                 for (int v = 0; v < 4; ++v) {
-                    float o = acc[v] + dskip * xm[v];
+                    o[v] = acc[v];
                     if (z)
-                        o *= silu_f32(cvt_raw1<IOT>(zq[v]));
-                    if (orow + v < Dm)
-                        st_elem<IOT>(out, ((bM + mo) * H + h) * Dm + orow + v, o);
+                        o[v] *= silu_f32(cvt_raw1<IOT>(zq[v]));
+                }
+                unsigned char *op = static_cast<unsigned char *>(obase) + (uint32_t)((mo * (H * Dm) + orow) * XB);
+                if (ovec) {  // rows orow .. orow+3 are in range together
+                    if (orow < Dm)
+                        st_raw4<IOT>(op, 0, o);
+                } else {
+#pragma unroll
+                    for (int v = 0; v < 4; ++v)
+                        if (orow + v < Dm)
+                            st_elem<IOT>(op, v, o[v]);
                 }
             }
         }
