@@ -72,6 +72,8 @@ constexpr int kTreeNT = 256;  // threads: four waves of 16 rows each
 
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
 
 // With bf16 C (exact as a bf16 MFMA operand) S0 . C runs on the bf16 matrix
 // cores: S0 = hi + mid + lo, each a bf16 (round to nearest, the remainder
@@ -138,7 +140,7 @@ __host__ __device__ inline TreeLds tree_lds(int M, int NS, int io_bytes, int bc_
     // in registers; the same bytes then hold the chunk coefficients Q, double
     // buffered: fp32 Q^T [source][chunk node] or the split-bf16 [2 terms]
     // [chunk node][source pitch] (the larger of the two)
-    const int xs_bytes = M * tree_x_pitch(io_bytes);
+    const int xs_bytes = ((M + 31) & ~31) * tree_x_pitch(io_bytes);  // whole 32-node steps
     const int q_bytes = 2 * kTreeTC * tree_q_pitch(M) * 4;
     L.xs = L.qt = tree_lds_take(o, xs_bytes > q_bytes ? xs_bytes : q_bytes);
     L.cs = tree_lds_take(o, kTreeTC * rb);                // C of the current chunk [TC][NS]
@@ -323,6 +325,11 @@ __global__ __launch_bounds__(kTreeNT) __attribute__((amdgpu_waves_per_eu(tree_wa
     void *obase = static_cast<unsigned char *>(out) + (bM * H + h) * Dm * XB;
     const void *zbase = z ? static_cast<const unsigned char *>(z) + (bM * H + h) * Dm * XB : nullptr;
     const bool ovec = Dm % 4 == 0 && (reinterpret_cast<uintptr_t>(out) & (4 * XB - 1)) == 0;
+    // per-(batch row, head) bases; the offsets from them below are 32-bit
+    const int NSTR = H * Dm;                                  // elements between nodes
+    const float *dtb = dt + bM * H + h;                       // dt of node m at m H
+    const unsigned char *xbase = static_cast<const unsigned char *>(x) + (bM * H + h) * Dm * XB;
+    float *ubase = stash ? st_u + (bM * H + h) * Dm : nullptr;
     const float Ah = A[h];
     const float bias = dt_bias ? dt_bias[h] : 0.0f;
     const float dskip = Dv ? Dv[h] : 0.0f;
@@ -341,14 +348,22 @@ __global__ __launch_bounds__(kTreeNT) __attribute__((amdgpu_waves_per_eu(tree_wa
         if constexpr (SP::on) {
 #pragma unroll
             for (int t = 0; t < SP::T; ++t) {
+                float r[8];
 #pragma unroll
-                for (int e = 0; e < 8; ++e) {
-                    float r = ld_elem<ST>(sp, 32 * t + 8 * qg + e);
+                for (int e = 0; e < 8; ++e)
+                    r[e] = ld_elem<ST>(sp, 32 * t + 8 * qg + e);
+                // two elements per conversion (v_cvt_pk_bf16_f32, round to nearest)
 #pragma unroll
-                    for (int u = 0; u < SP::terms; ++u) {
-                        const __bf16 p = (__bf16)r;
-                        sb[u * SP::T + t][e] = p;
-                        r -= (float)p;
+                for (int u = 0; u < SP::terms; ++u) {
+#pragma unroll
+                    for (int e = 0; e < 8; e += 2) {
+                        const bf16x2 p = __builtin_convertvector((f32x2){r[e], r[e + 1]}, bf16x2);
+                        sb[u * SP::T + t][e] = p[0];
+                        sb[u * SP::T + t][e + 1] = p[1];
+                        if (u + 1 < SP::terms) {
+                            r[e] -= (float)p[0];
+                            r[e + 1] -= (float)p[1];
+                        }
                     }
                 }
             }
@@ -363,8 +378,8 @@ __global__ __launch_bounds__(kTreeNT) __attribute__((amdgpu_waves_per_eu(tree_wa
     int npar[NPT], ncap[NPT];
 #pragma unroll
     for (int k = 0; k < NPT; ++k) {
-        const int m = min(tid + NT * k, M - 1);
-        ndt[k] = dt[(bM + m) * H + h];
+        const uint32_t m = min(tid + NT * k, M - 1);
+        ndt[k] = dtb[m * H];
         npar[k] = parents[bM + m];
         ncap[k] = depths ? depths[bM + m] : m;
     }
@@ -402,9 +417,7 @@ __global__ __launch_bounds__(kTreeNT) __attribute__((amdgpu_waves_per_eu(tree_wa
         for (int k = 0; k < XVEC; ++k) {
             const int v = min(tid + NT * k, nvec - 1);
             const int r = min(rbase + XV * (v % VPN), Dm - XV);
-            xr[k] = *reinterpret_cast<const u32x4 *>(
-                static_cast<const unsigned char *>(x) +
-                ((((bM + v / VPN) * H + h) * Dm + r) * XB));
+            xr[k] = *reinterpret_cast<const u32x4 *>(xbase + (uint32_t)(((v / VPN) * NSTR + r) * XB));
         }
 #pragma unroll
         for (int k = 0; k < XVEC; ++k) {
@@ -429,10 +442,11 @@ __global__ __launch_bounds__(kTreeNT) __attribute__((amdgpu_waves_per_eu(tree_wa
                             f[2 * e + 1] = cvt_raw1<IOT>(w[e] >> 16);
                         }
                     }
-                    float *dst = st_u + ((bM + m) * H + h) * Dm + rbase + rl;
+                    unsigned char *dst = reinterpret_cast<unsigned char *>(ubase) +
+                                         (uint32_t)((m * NSTR + rbase + rl) * 4);
 #pragma unroll
                     for (int e = 0; e < XV; e += 4)
-                        *reinterpret_cast<float4 *>(dst + e) =
+                        *reinterpret_cast<float4 *>(dst + 4 * e) =
                             make_float4(f[e], f[e + 1], f[e + 2], f[e + 3]);
                 }
             }
@@ -466,11 +480,15 @@ __global__ __launch_bounds__(kTreeNT) __attribute__((amdgpu_waves_per_eu(tree_wa
             rec[m] = make_float4(expf(Ah * v), v, __int_as_float(p >= 0 && p < m ? p : -1),
                                  __int_as_float(ncap[k]));
             if (stash && rb == 0) {
-                st_dA[(bM + m) * H + h] = Ah * v;
-                st_dt[(bM + m) * H + h] = v;
+                const int64_t o = (bM + m) * H + h;
+                st_dA[o] = Ah * v;
+                st_dt[o] = v;
             }
         }
     }
+    // x rows of the nodes past M up to a whole 32-node step read as zeros
+    for (int i = tid; i < (((M + 31) & ~31) - M) * XP / 16; i += NT)
+        *reinterpret_cast<u32x4 *>(xs + M * XP + 16 * i) = u32x4{0u, 0u, 0u, 0u};
     store_c();
     __syncthreads();
 
@@ -493,29 +511,33 @@ __global__ __launch_bounds__(kTreeNT) __attribute__((amdgpu_waves_per_eu(tree_wa
     // (fp32 form) or x_{32t+8qg+e}[row 16w+ln] (bf16 form)
     float xa[PX ? 1 : MX / 4];
     bf16x8 xb[PX ? MX / 32 : 1];
-    if constexpr (PX) {
-        const int rl = 16 * wave + ln;
+    {
+        // this lane's row; the staging holds whole 32-node steps (zero past M)
+        const unsigned char *xl = xs + (16 * wave + ln) * XB;
+        if constexpr (PX) {
 #pragma unroll
-        for (int t = 0; t < MX / 32; ++t)
+            for (int t = 0; t < MX / 32; ++t) {
+                xb[t] = bf16x8{};
+                if (32 * t < M) {
 #pragma unroll
-            for (int e = 0; e < 8; ++e) {
-                const int j = 32 * t + 8 * qg + e;
-                const uint16_t w = j < M ? *reinterpret_cast<const uint16_t *>(xs + j * XP + rl * 2) : 0;
-                xb[t][e] = __builtin_bit_cast(__bf16, w);
+                    for (int e = 0; e < 8; ++e)
+                        xb[t][e] = __builtin_bit_cast(
+                            __bf16, *reinterpret_cast<const uint16_t *>(xl + (32 * t + 8 * qg + e) * XP));
+                }
             }
-    } else {
-        const int rl = 16 * wave + ln;
+        } else {
 #pragma unroll
-        for (int s = 0; s < MX / 4; ++s) {
-            const int j = 4 * s + qg;
-            float v = 0.0f;
-            if (j < M) {
-                if constexpr (XB == 4)
-                    v = *reinterpret_cast<const float *>(xs + j * XP + rl * 4);
-                else
-                    v = cvt_raw1<IOT>(*reinterpret_cast<const uint16_t *>(xs + j * XP + rl * 2));
+            for (int s = 0; s < MX / 4; ++s) {
+                float v = 0.0f;
+                if (4 * s < M) {
+                    const unsigned char *p = xl + (4 * s + qg) * XP;
+                    if constexpr (XB == 4)
+                        v = *reinterpret_cast<const float *>(p);
+                    else
+                        v = cvt_raw1<IOT>(*reinterpret_cast<const uint16_t *>(p));
+                }
+                xa[s] = v;
             }
-            xa[s] = v;
         }
     }
     __syncthreads();  // x staging read by every lane; paths in place
