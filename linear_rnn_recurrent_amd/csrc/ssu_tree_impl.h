@@ -99,18 +99,20 @@ struct TreeSplit {
     static constexpr int T = NS / 32;  // 16x16x32 steps over dstate
 };
 
-// Waves per SIMD the register budget is cut for: four (128 VGPRs) where the
-// operand registers (state slice, x of the path product, x staging) fit without
-// spilling, else what the compiler chooses.
-template <typename IOT, int NS>
+// Waves per SIMD the register budget is cut for (5: 96 VGPRs, 4: 128): the
+// most at which the operand registers (state slice, x of the path product,
+// C and Q reads) fit without spilling; dstate 256 is left to the compiler.
+template <typename IOT, typename BCT, int NS>
 constexpr int tree_waves()
 {
-    return (TreePathSplit<IOT>::on ? NS <= 128 : NS * (int)sizeof(IOT) <= 128) ? 4 : 1;
+    if (NS <= 16 || (TreePathSplit<IOT>::on && NS <= (__is_same(BCT, bf16_t) ? 128 : 64)))
+        return 5;
+    return NS <= 128 ? 4 : 1;
 }
 
 // Byte offsets of the LDS arrays for a tree of M nodes (host and device).
 struct TreeLds {
-    int xs, cs, rec, path, len, qt, cws, total;
+    int xs, cs, rec, pc, path, len, qt, cws, total;
 };
 
 __host__ __device__ inline int tree_lds_take(int &o, int bytes)
@@ -124,7 +126,9 @@ __host__ __device__ inline int tree_lds_take(int &o, int bytes)
 // the lanes of one instruction read together over the banks (C rows of
 // dstate elements; x rows of the block's 64 rows of dim).
 __host__ __device__ constexpr int tree_row_bytes(int NS, int bc_bytes) { return NS * bc_bytes + 16; }
-__host__ __device__ constexpr int tree_x_pitch(int io_bytes) { return 64 * io_bytes + 16; }
+// (16-bit x: an 8-byte pad, which already puts the four lane groups of the
+// path-operand reads, 8 nodes apart, on disjoint banks)
+__host__ __device__ constexpr int tree_x_pitch(int io_bytes) { return 64 * io_bytes + (io_bytes == 2 ? 8 : 16); }
 // source-node rows of the coefficient matrix: every chunk's range, padded
 __host__ __device__ constexpr int tree_q_rows(int M) { return (M + 15) & ~15; }
 // row pitch (elements) of Q in its split-bf16 form [term][node][source]: whole
@@ -144,9 +148,10 @@ __host__ __device__ inline TreeLds tree_lds(int M, int NS, int io_bytes, int bc_
     const int q_bytes = 2 * kTreeTC * tree_q_pitch(M) * 4;
     L.xs = L.qt = tree_lds_take(o, xs_bytes > q_bytes ? xs_bytes : q_bytes);
     L.cs = tree_lds_take(o, kTreeTC * rb);                // C of the current chunk [TC][NS]
-    L.rec = tree_lds_take(o, M * 16);                     // node records
+    L.rec = tree_lds_take(o, M * 8);                      // {exp(A dt'), dt'} per node
+    L.pc = tree_lds_take(o, M * 4);                       // {parent, hop bound} per node
     L.path = tree_lds_take(o, M * (M + 1) / 2);           // path of node m at m(m+1)/2
-    L.len = tree_lds_take(o, M * 4);                      // path lengths
+    L.len = tree_lds_take(o, M);                          // path lengths (<= 128)
     L.cws = tree_lds_take(o, kTreeTC * 4);                // weights of S0 of the chunk's nodes
     L.total = o;
     return L;
@@ -256,7 +261,7 @@ __global__ __launch_bounds__(kTreeNT) void ssu_tree_gram_kernel(
 }
 
 template <typename ST, typename IOT, typename BCT, int NS>
-__global__ __launch_bounds__(kTreeNT) __attribute__((amdgpu_waves_per_eu(tree_waves<IOT, NS>()))) void ssu_tree_kernel(
+__global__ __launch_bounds__(kTreeNT) __attribute__((amdgpu_waves_per_eu(tree_waves<IOT, BCT, NS>()))) void ssu_tree_kernel(
     const void *__restrict__ x, const float *__restrict__ A, const void *__restrict__ Cm,
     const float *__restrict__ dt, const float *__restrict__ dt_bias, const float *__restrict__ Dv,
     const void *__restrict__ z, const ST *__restrict__ state, void *__restrict__ out,
@@ -285,9 +290,10 @@ __global__ __launch_bounds__(kTreeNT) __attribute__((amdgpu_waves_per_eu(tree_wa
     const int RM = tree_q_rows(M);
     unsigned char *xs = lds + L.xs;
     unsigned char *cs = lds + L.cs;
-    float4 *rec = reinterpret_cast<float4 *>(lds + L.rec);  // {exp(A dt'), dt', parent, bound}
+    float2 *rec = reinterpret_cast<float2 *>(lds + L.rec);  // {exp(A dt'), dt'}
+    int *n_pc = reinterpret_cast<int *>(lds + L.pc);         // parent (low 16 bits), hop bound
     uint8_t *n_path = lds + L.path;                          // triangular path table
-    int *n_len = reinterpret_cast<int *>(lds + L.len);
+    uint8_t *n_len = lds + L.len;
     float *qt = reinterpret_cast<float *>(lds + L.qt);       // 2 x [RM][TC] (fp32 form)
     constexpr bool PX = TreePathSplit<IOT>::on;
     const int QP = tree_q_pitch(M);
@@ -428,7 +434,13 @@ __global__ __launch_bounds__(kTreeNT) __attribute__((amdgpu_waves_per_eu(tree_wa
                 u32x4 w = xr[k];
                 if (!valid)
                     w = u32x4{0u, 0u, 0u, 0u};
-                *reinterpret_cast<u32x4 *>(xs + m * XP + rl * XB) = w;
+                unsigned char *xw = xs + m * XP + rl * XB;  // 8-byte aligned at least
+                if constexpr (XP % 16 == 0) {
+                    *reinterpret_cast<u32x4 *>(xw) = w;
+                } else {
+                    reinterpret_cast<u32x2 *>(xw)[0] = u32x2{w[0], w[1]};
+                    reinterpret_cast<u32x2 *>(xw)[1] = u32x2{w[2], w[3]};
+                }
                 if (stash && valid) {
                     float f[XV];
                     if constexpr (XB == 4) {
@@ -467,8 +479,8 @@ __global__ __launch_bounds__(kTreeNT) __attribute__((amdgpu_waves_per_eu(tree_wa
                 *reinterpret_cast<uint16_t *>(xs + m * XP + rl * 2) = (uint16_t)w;
         }
     }
-    // node records {decay exp(A dt'), dt', parent id (-1 unless it precedes the
-    // node), hop bound}
+    // node records {decay exp(A dt'), dt'} and {parent id (-1 unless it
+    // precedes the node), hop bound}
 #pragma unroll
     for (int k = 0; k < NPT; ++k) {
         const int m = tid + NT * k;
@@ -477,8 +489,10 @@ __global__ __launch_bounds__(kTreeNT) __attribute__((amdgpu_waves_per_eu(tree_wa
             if (sh.dt_softplus)
                 v = softplus_f32(v);
             const int p = npar[k];
-            rec[m] = make_float4(expf(Ah * v), v, __int_as_float(p >= 0 && p < m ? p : -1),
-                                 __int_as_float(ncap[k]));
+            rec[m] = make_float2(expf(Ah * v), v);
+            // a walk never takes more than m hops, and a bound below 0 acts as 0
+            const int cap = max(0, min(ncap[k], m));
+            n_pc[m] = (int)(uint16_t)(p >= 0 && p < m ? p : -1) | (cap << 16);
             if (stash && rb == 0) {
                 const int64_t o = (bM + m) * H + h;
                 st_dA[o] = Ah * v;
@@ -487,19 +501,19 @@ __global__ __launch_bounds__(kTreeNT) __attribute__((amdgpu_waves_per_eu(tree_wa
         }
     }
     // x rows of the nodes past M up to a whole 32-node step read as zeros
-    for (int i = tid; i < (((M + 31) & ~31) - M) * XP / 16; i += NT)
-        *reinterpret_cast<u32x4 *>(xs + M * XP + 16 * i) = u32x4{0u, 0u, 0u, 0u};
+    for (int i = tid; i < (((M + 31) & ~31) - M) * XP / 8; i += NT)
+        *reinterpret_cast<u32x2 *>(xs + M * XP + 8 * i) = u32x2{0u, 0u};
     store_c();
     __syncthreads();
 
     // ---- the path of every node (one lane per node), node first ----
     for (int m = tid; m < M; m += NT) {
         uint8_t *pp = n_path + tri(m);
-        const int cap = __float_as_int(rec[m].w);
+        const int cap = n_pc[m] >> 16;
         int j = m, hops = 0;
         while (true) {
             pp[hops] = (uint8_t)j;
-            const int p = __float_as_int(rec[j].z);
+            const int p = (int16_t)n_pc[j];
             if (hops >= cap || p < 0)
                 break;
             j = p;
@@ -571,20 +585,6 @@ __global__ __launch_bounds__(kTreeNT) __attribute__((amdgpu_waves_per_eu(tree_wa
         const int orow = rbase + 16 * wave + 4 * qg;  // and its first output row
         float *q = qt + (c & 1) * RM * TC;
         uint16_t *qc = qs + (c & 1) * 2 * TC * QP;
-        // gate inputs of this lane's four outputs (raw bits; clamped indices)
-        uint32_t zq[4] = {0u, 0u, 0u, 0u};
-        if (z) {
-            const int e = min(mo, M - 1) * (H * Dm);
-#pragma unroll
-            for (int v = 0; v < 4; ++v)
-                zq[v] = ld_raw1<IOT>(static_cast<const unsigned char *>(zbase) +
-                                         (uint32_t)((e + min(orow + v, Dm - 1)) * XB), 0);
-        }
-        float gnext = 0.0f;
-        if (c + 1 < nchunks) {
-            load_c(t0 + TC);
-            gnext = load_g(t0 + TC);
-        }
 
         // S0 . C: 16 rows x 16 nodes per wave on the matrix cores, four
         // independent accumulators so that the MFMAs issue back to back
@@ -619,6 +619,13 @@ __global__ __launch_bounds__(kTreeNT) __attribute__((amdgpu_waves_per_eu(tree_wa
             }
         }
 
+        // next chunk's C and G values, in flight during the coefficients
+        float gnext = 0.0f;
+        if (c + 1 < nchunks) {
+            load_c(t0 + TC);
+            gnext = load_g(t0 + TC);
+        }
+
         // coefficients: the 16 lanes of chunk node tt take path entries
         // l, l+16, ..; w of entry i is the product of the decays of entries
         // 0 .. i-1 (a running product across the lanes, carried across blocks)
@@ -632,13 +639,14 @@ __global__ __launch_bounds__(kTreeNT) __attribute__((amdgpu_waves_per_eu(tree_wa
                 const int i = i0 + l;
                 const bool v = i < len;
                 const int j = v ? pp[i] : m;
-                const float4 r = rec[j];
+                const float2 r = rec[j];
                 const float gv = i0 == 0 ? gcur : (v ? ld_f32_at(gbg, (m * M + j) * 4u) : 0.0f);
                 const float incl = row_prefix_prod16(v ? r.x : 1.0f);
                 const float excl = dpp_f32_fill<0x111>(1.0f, incl);  // row_shr:1
                 if (v) {
-                    // entry 0 is the node itself: D x_m joins the path sum
-                    const float qv = carry * excl * r.y * gv + (i == 0 ? dskip : 0.0f);
+                    // entry 0 is the node itself (the only j == m): D x_m joins
+                    // the path sum
+                    const float qv = carry * excl * r.y * gv + (j == m ? dskip : 0.0f);
                     if constexpr (PX) {
                         const __bf16 hi = (__bf16)qv;
                         qc[tt * QP + j] = __builtin_bit_cast(uint16_t, hi);
@@ -677,6 +685,15 @@ __global__ __launch_bounds__(kTreeNT) __attribute__((amdgpu_waves_per_eu(tree_wa
 
         // outputs held in the accumulators: node mo, rows orow .. orow+3
         {
+            // gate inputs of this lane's four outputs (raw bits; clamped indices)
+            uint32_t zq[4] = {0u, 0u, 0u, 0u};
+            if (z) {
+                const int e = min(mo, M - 1) * (H * Dm);
+#pragma unroll
+                for (int v = 0; v < 4; ++v)
+                    zq[v] = ld_raw1<IOT>(static_cast<const unsigned char *>(zbase) +
+                                             (uint32_t)((e + min(orow + v, Dm - 1)) * XB), 0);
+            }
             f32x4 acc = acc4[0] + acc4[1];
             if constexpr (NACC == 4)
                 acc += acc4[2] + acc4[3];
