@@ -203,59 +203,99 @@ __device__ __forceinline__ void ld_row_f32(const unsigned char *p, float (&f)[N]
     }
 }
 
-// G[b,g][m][j] = B_j . C_m (fp32) for j <= m, on the matrix cores: one
-// workgroup per (b, g, block of 16 nodes m); wave w computes the 16 x 16 tiles
-// of source blocks jb = w, w+4, .. <= the node block (v_mfma_f32_16x16x4_f32,
-// lane group q summing the dstate slice [q NS/4, (q+1) NS/4)); and the stash
-// copy of B (fp32) of the block's nodes. Padded batch rows are skipped (their
-// stash stays untouched).
+// G[b,g][m][j] = B_j . C_m (fp32) for j <= m, on the matrix cores: the
+// 16 x 16 tiles (node block mb, source block jb <= mb) of every (b, g), one
+// tile per wave, four per workgroup. With 16-bit B and C the tile is
+// v_mfma_f32_16x16x32_{bf16,f16} over dstate (the products are exact, the
+// sums fp32), else v_mfma_f32_16x16x4_f32. The lane holding G[m][j..j+3]
+// writes it as one vector; entries above the diagonal of a diagonal tile are
+// written too (the verify kernel never reads them). Each workgroup also
+// copies its share of the rows of B to the fp32 stash. Padded batch rows are
+// skipped (their stash stays untouched).
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
+
 template <typename BCT, int NS>
 __global__ __launch_bounds__(kTreeNT) void ssu_tree_gram_kernel(
     const void *__restrict__ Bm, const void *__restrict__ Cm, const int32_t *__restrict__ idx,
     float *__restrict__ gram, float *__restrict__ st_B, int32_t M, int32_t G)
 {
-    constexpr int KS = NS / 4;
     constexpr int BB = (int)sizeof(BCT);
+    constexpr bool MF16 = BB == 2 && NS % 32 == 0;  // 16x16x32 on 16-bit operands
     const int tid = threadIdx.x;
     const int lane = tid & 63;
     const int wave = tid >> 6;
     const int qg = lane >> 4, ln = lane & 15;
     const int nmb = (M + 15) / 16;
-    const int bg = blockIdx.x / nmb;
-    const int mb = blockIdx.x - bg * nmb;
+    const int ntile = nmb * (nmb + 1) / 2;
+    const int nq = (ntile + 3) / 4;  // workgroups per (b, g)
+    const int bg = blockIdx.x / nq;
+    const int q = blockIdx.x - bg * nq;
     const int b = bg / G, g = bg - b * G;
     if (idx && idx[b] < 0)
         return;
-    const int m0 = 16 * mb;
-    auto row = [&](const void *base, int node) {  // this lane's dstate slice of a node's row
-        return static_cast<const unsigned char *>(base) +
-               ((((int64_t)b * M + min(node, M - 1)) * G + g) * NS + qg * KS) * BB;
-    };
-    float ca[KS];
-    ld_row_f32<BCT, KS>(row(Cm, m0 + ln), ca);
-    for (int jb = wave; jb <= mb; jb += 4) {
-        float bv[KS];
-        ld_row_f32<BCT, KS>(row(Bm, 16 * jb + ln), bv);
+    // the rows of (b, g): node n at n G NS elements
+    const unsigned char *brow = static_cast<const unsigned char *>(Bm) + ((int64_t)b * M * G + g) * NS * BB;
+    const unsigned char *crow = static_cast<const unsigned char *>(Cm) + ((int64_t)b * M * G + g) * NS * BB;
+    const uint32_t nstride = (uint32_t)G * NS * BB;
+    const int k = 4 * q + wave;  // tile k = mb (mb + 1) / 2 + jb
+    if (k < ntile) {
+        int mb = 0;
+        while ((mb + 1) * (mb + 2) / 2 <= k)
+            ++mb;
+        const int jb = k - mb * (mb + 1) / 2;
+        const uint32_t jn = min(16 * jb + ln, M - 1), mn = min(16 * mb + ln, M - 1);
         f32x4 acc = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+        if constexpr (MF16) {
+            // A: B_{16 jb + ln}[32 t + 8 qg ..], B: C_{16 mb + ln}[32 t + 8 qg ..]
+            u32x4 av[NS / 32], bv[NS / 32];
 #pragma unroll
-        for (int k = 0; k < KS; ++k)
-            acc = __builtin_amdgcn_mfma_f32_16x16x4f32(ca[k], bv[k], acc, 0, 0, 0);
-        // acc[v] = C_{m0 + 4 qg + v} . B_{16 jb + ln}
-        const int j = 16 * jb + ln;
+            for (int t = 0; t < NS / 32; ++t) {
+                av[t] = *reinterpret_cast<const u32x4 *>(brow + jn * nstride + (32 * t + 8 * qg) * BB);
+                bv[t] = *reinterpret_cast<const u32x4 *>(crow + mn * nstride + (32 * t + 8 * qg) * BB);
+            }
 #pragma unroll
-        for (int v = 0; v < 4; ++v) {
-            const int m = m0 + 4 * qg + v;
-            if (m < M && j <= m)
-                gram[((int64_t)bg * M + m) * M + j] = acc[v];
+            for (int t = 0; t < NS / 32; ++t) {
+                if constexpr (__is_same(BCT, bf16_t))
+                    acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, av[t]),
+                                                                  __builtin_bit_cast(bf16x8, bv[t]), acc, 0, 0, 0);
+                else
+                    acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(f16x8, av[t]),
+                                                                 __builtin_bit_cast(f16x8, bv[t]), acc, 0, 0, 0);
+            }
+        } else {
+            // lane group qg sums the dstate slice [qg NS/4, (qg+1) NS/4)
+            constexpr int KS = NS / 4;
+            float ca[KS], bw[KS];
+            ld_row_f32<BCT, KS>(crow + mn * nstride + qg * KS * BB, ca);
+            ld_row_f32<BCT, KS>(brow + jn * nstride + qg * KS * BB, bw);
+#pragma unroll
+            for (int s = 0; s < KS; ++s)
+                acc = __builtin_amdgcn_mfma_f32_16x16x4f32(bw[s], ca[s], acc, 0, 0, 0);
+        }
+        // acc[v] = B_{16 jb + 4 qg + v} . C_{16 mb + ln}
+        const int m = 16 * mb + ln, j0 = 16 * jb + 4 * qg;
+        if (m < M) {
+            float *gp = gram + ((int64_t)bg * M + m) * M + j0;
+            if (M % 4 == 0 && j0 < M && (reinterpret_cast<uintptr_t>(gram) & 15) == 0) {
+                *reinterpret_cast<float4 *>(gp) = make_float4(acc[0], acc[1], acc[2], acc[3]);
+            } else {
+#pragma unroll
+                for (int v = 0; v < 4; ++v)
+                    if (j0 + v < M)
+                        gp[v] = acc[v];
+            }
         }
     }
     if (st_B) {
-        for (int e = tid; e < 16 * NS; e += kTreeNT) {
-            const int r = m0 + e / NS;
-            if (r < M) {
-                const int64_t o = (((int64_t)b * M + r) * G + g) * NS + e % NS;
-                st_B[o] = cvt_raw1<BCT>(ld_raw1<BCT>(Bm, o));
-            }
+        // rows [q R, (q + 1) R) of B to the stash, 4 elements per thread and step
+        const int R = (M + nq - 1) / nq;
+        const int n0 = q * R, n1 = min(M, n0 + R);
+        for (int e = tid; e < (n1 - n0) * (NS / 4); e += kTreeNT) {
+            const int n = n0 + e / (NS / 4), c4 = 4 * (e % (NS / 4));
+            float f[4];
+            ld_row_f32<BCT, 4>(brow + (uint32_t)n * nstride + c4 * BB, f);
+            *reinterpret_cast<float4 *>(st_B + (((int64_t)b * M + n) * G + g) * NS + c4) =
+                make_float4(f[0], f[1], f[2], f[3]);
         }
     }
 }
@@ -770,7 +810,8 @@ hipError_t launch_tree_cfg(const TreeParams &p, hipStream_t stream)
     sh.nrb = (d.dim + 63) / 64;
     sh.dt_softplus = d.dt_softplus;
     const int64_t blocks = (int64_t)d.batch * d.nheads * sh.nrb;
-    const int64_t gblocks = (int64_t)d.batch * d.ngroups * ((p.num_nodes + 15) / 16);
+    const int nmb = (p.num_nodes + 15) / 16;
+    const int64_t gblocks = (int64_t)d.batch * d.ngroups * ((nmb * (nmb + 1) / 2 + 3) / 4);
     if (blocks > 0x7fffffff || gblocks > 0x7fffffff)
         return hipErrorInvalidConfiguration;
     constexpr int XB = (int)sizeof(IOT), BB = (int)sizeof(BCT);
