@@ -209,15 +209,14 @@ __device__ __forceinline__ void ld_row_f32(const unsigned char *p, float (&f)[N]
 // v_mfma_f32_16x16x32_{bf16,f16} over dstate (the products are exact, the
 // sums fp32), else v_mfma_f32_16x16x4_f32. The lane holding G[m][j..j+3]
 // writes it as one vector; entries above the diagonal of a diagonal tile are
-// written too (the verify kernel never reads them). Each workgroup also
-// copies its share of the rows of B to the fp32 stash. Padded batch rows are
-// skipped (their stash stays untouched).
+// written too (the verify kernel never reads them). Padded batch rows are
+// skipped.
 typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
 
 template <typename BCT, int NS>
 __global__ __launch_bounds__(kTreeNT) void ssu_tree_gram_kernel(
     const void *__restrict__ Bm, const void *__restrict__ Cm, const int32_t *__restrict__ idx,
-    float *__restrict__ gram, float *__restrict__ st_B, int32_t M, int32_t G)
+    float *__restrict__ gram, int32_t M, int32_t G)
 {
     constexpr int BB = (int)sizeof(BCT);
     constexpr bool MF16 = BB == 2 && NS % 32 == 0;  // 16x16x32 on 16-bit operands
@@ -286,18 +285,6 @@ __global__ __launch_bounds__(kTreeNT) void ssu_tree_gram_kernel(
             }
         }
     }
-    if (st_B) {
-        // rows [q R, (q + 1) R) of B to the stash, 4 elements per thread and step
-        const int R = (M + nq - 1) / nq;
-        const int n0 = q * R, n1 = min(M, n0 + R);
-        for (int e = tid; e < (n1 - n0) * (NS / 4); e += kTreeNT) {
-            const int n = n0 + e / (NS / 4), c4 = 4 * (e % (NS / 4));
-            float f[4];
-            ld_row_f32<BCT, 4>(brow + (uint32_t)n * nstride + c4 * BB, f);
-            *reinterpret_cast<float4 *>(st_B + (((int64_t)b * M + n) * G + g) * NS + c4) =
-                make_float4(f[0], f[1], f[2], f[3]);
-        }
-    }
 }
 
 template <typename ST, typename IOT, typename BCT, int NS>
@@ -306,8 +293,8 @@ __global__ __launch_bounds__(kTreeNT) __attribute__((amdgpu_waves_per_eu(tree_wa
     const float *__restrict__ dt, const float *__restrict__ dt_bias, const float *__restrict__ Dv,
     const void *__restrict__ z, const ST *__restrict__ state, void *__restrict__ out,
     const int32_t *__restrict__ idx, const int32_t *__restrict__ parents,
-    const int32_t *__restrict__ depths, const float *__restrict__ gram,
-    float *__restrict__ st_dA, float *__restrict__ st_u, float *__restrict__ st_dt,
+    const int32_t *__restrict__ depths, const float *__restrict__ gram, const void *__restrict__ Bm,
+    float *__restrict__ st_dA, float *__restrict__ st_u, float *__restrict__ st_B, float *__restrict__ st_dt,
     const TreeShape sh)
 {
     constexpr int NT = kTreeNT;
@@ -538,6 +525,20 @@ __global__ __launch_bounds__(kTreeNT) __attribute__((amdgpu_waves_per_eu(tree_wa
                 st_dA[o] = Ah * v;
                 st_dt[o] = v;
             }
+        }
+    }
+    // B of every node to the fp32 stash: the workgroups of row block 0 of
+    // the group's heads take equal shares of the nodes
+    if (st_B && rb == 0) {
+        const int hpg = sh.heads_per_group;
+        const int R = (M + hpg - 1) / hpg, n0 = (h - g * hpg) * R, n1 = min(M, n0 + R);
+        const unsigned char *brow = static_cast<const unsigned char *>(Bm) + (bM * G + g) * NS * BB;
+        float *sbrow = st_B + (bM * G + g) * NS;
+        for (int e = tid; e < (n1 - n0) * (NS / 4); e += NT) {
+            const int n = n0 + e / (NS / 4), c4 = 4 * (e % (NS / 4));
+            float f[4];
+            ld_row_f32<BCT, 4>(brow + (uint32_t)((n * G * NS + c4) * BB), f);
+            *reinterpret_cast<float4 *>(sbrow + (uint32_t)(n * G * NS + c4)) = make_float4(f[0], f[1], f[2], f[3]);
         }
     }
     // x rows of the nodes past M up to a whole 32-node step read as zeros
@@ -838,14 +839,14 @@ hipError_t launch_tree_cfg(const TreeParams &p, hipStream_t stream)
     }
     (void)hipGetLastError();
     hipLaunchKernelGGL((ssu_tree_gram_kernel<BCT, NS>), dim3((unsigned)gblocks), dim3(kTreeNT), 0,
-                       stream, d.B, d.C, d.idx, p.gram, p.st_B, p.num_nodes, d.ngroups);
+                       stream, d.B, d.C, d.idx, p.gram, p.num_nodes, d.ngroups);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess)
         return e;
     hipLaunchKernelGGL(kern, dim3((unsigned)blocks), dim3(kTreeNT), (unsigned)L.total, stream,
                        d.x, d.A, d.C, d.dt, d.dt_bias, d.D, d.z,
                        static_cast<const ST *>(d.state), d.out, d.idx, p.parents, p.depths,
-                       p.gram, p.st_dA, p.st_u, p.st_dt, sh);
+                       p.gram, d.B, p.st_dA, p.st_u, p.st_B, p.st_dt, sh);
     return hipGetLastError();
 }
 
