@@ -599,12 +599,13 @@ __global__ __launch_bounds__(kTreeNT) __attribute__((amdgpu_waves_per_eu(tree_wa
 
     // G value of this lane's path entry (entry tid%16 of chunk node tid/16) of
     // the chunk starting at t0; entries past 16 are read in the loop below
+    // (issued on every lane, at a clamped entry, so that no branch hides the
+    // load from the wait counting: a wait for it then leaves the later
+    // loads in flight; lanes past the path never use the value)
     auto load_g = [&](int t0) {
-        const int m = t0 + (tid >> 4), l = tid & 15;
-        float v = 0.0f;
-        if (m < M && l < n_len[m])
-            v = ld_f32_at(gbg, (m * M + n_path[tri(m) + l]) * 4u);
-        return v;
+        const int m = min(t0 + (tid >> 4), M - 1), l = tid & 15;
+        const int j = n_path[tri(m) + min(l, (int)n_len[m] - 1)];
+        return ld_f32_at(gbg, (m * M + j) * 4u);
     };
     float gcur = load_g(0);
     // both coefficient buffers (over the x staging) start at zero; from then
@@ -661,11 +662,11 @@ __global__ __launch_bounds__(kTreeNT) __attribute__((amdgpu_waves_per_eu(tree_wa
         }
 
         // next chunk's C and G values, in flight during the coefficients
-        float gnext = 0.0f;
-        if (c + 1 < nchunks) {
-            load_c(t0 + TC);
-            gnext = load_g(t0 + TC);
-        }
+        // (unconditional: past the last chunk they read clamped nodes). G
+        // goes first: the wait for C before it is stored to LDS then also
+        // covers G, and the end-of-chunk hand-over of G waits for nothing
+        const float gnext = load_g(t0 + TC);
+        load_c(t0 + TC);
 
         // coefficients: the 16 lanes of chunk node tt take path entries
         // l, l+16, ..; w of entry i is the product of the decays of entries
