@@ -67,6 +67,7 @@ struct TreeShape {
     int32_t dt_softplus;
 };
 
+constexpr int kXcds = 8;     // accelerator dies, each with its own L2
 constexpr int kTreeTC = 16;   // nodes per chunk (the N side of one 16x16 MFMA tile)
 constexpr int kTreeNT = 256;  // threads: four waves of 16 rows each
 
@@ -227,8 +228,12 @@ __global__ __launch_bounds__(kTreeNT) void ssu_tree_gram_kernel(
     const int nmb = (M + 15) / 16;
     const int ntile = nmb * (nmb + 1) / 2;
     const int nq = (ntile + 3) / 4;  // workgroups per (b, g)
-    const int bg = blockIdx.x / nq;
-    const int q = blockIdx.x - bg * nq;
+    // (the workgroups of one (b, g) on one XCD, as in the verify kernel)
+    int wg = blockIdx.x;
+    if (gridDim.x % kXcds == 0)
+        wg = (wg % kXcds) * (gridDim.x / kXcds) + wg / kXcds;
+    const int bg = wg / nq;
+    const int q = wg - bg * nq;
     const int b = bg / G, g = bg - b * G;
     if (idx && idx[b] < 0)
         return;
@@ -334,8 +339,14 @@ __global__ __launch_bounds__(kTreeNT) __attribute__((amdgpu_waves_per_eu(tree_wa
     const int ln = lane & 15;     // MFMA A row / B and D column (node of the chunk)
     const int H = sh.nheads, Dm = sh.dim, G = sh.ngroups;
     const int per_b = H * sh.nrb;
-    const int b = blockIdx.x / per_b;
-    const int rem = blockIdx.x - b * per_b;
+    // workgroup i runs on XCD i % 8: the workgroups of one batch row (which
+    // share its C, B and G) are given consecutive slots of one XCD, so that
+    // its L2 serves them (identity when the grid is not a multiple of 8)
+    int wg = blockIdx.x;
+    if (gridDim.x % kXcds == 0)
+        wg = (wg % kXcds) * (gridDim.x / kXcds) + wg / kXcds;
+    const int b = wg / per_b;
+    const int rem = wg - b * per_b;
     const int h = rem % H;
     const int rb = rem / H;
     const int64_t bM = (int64_t)b * M;
