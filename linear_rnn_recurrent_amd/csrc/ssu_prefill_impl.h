@@ -475,8 +475,16 @@ __global__ __launch_bounds__(64 * NW) void ssu_prefill_kernel(
     }
 }
 
-template <typename ST, typename IOT, typename BCT, int NS, int NW>
-hipError_t launch_prefill_cfg(const PrefillParams &p, hipStream_t stream)
+}  // namespace
+}  // namespace ssu
+
+// the matrix-core prefill (bf16 operands), dispatched to from launch_prefill_bc
+#include "ssu_prefill_mm.h"
+
+namespace ssu {
+namespace {
+
+inline PrefillShape prefill_shape(const PrefillParams &p)
 {
     const DecodeParams &d = p.d;
     PrefillShape sh;
@@ -491,6 +499,14 @@ hipError_t launch_prefill_cfg(const PrefillParams &p, hipStream_t stream)
     sh.dt_softplus = d.dt_softplus;
     sh.sort_by_length = (p.ctx != nullptr && d.batch <= 256) ? 1 : 0;
     sh.pass = p.cu_count;
+    return sh;
+}
+
+template <typename ST, typename IOT, typename BCT, int NS, int NW>
+hipError_t launch_prefill_cfg(const PrefillParams &p, hipStream_t stream)
+{
+    const DecodeParams &d = p.d;
+    const PrefillShape sh = prefill_shape(p);
     const int64_t blocks = (int64_t)d.batch * d.nheads * sh.nrb;
     if (blocks > 0x7fffffff)
         return hipErrorInvalidConfiguration;
@@ -505,6 +521,18 @@ hipError_t launch_prefill_cfg(const PrefillParams &p, hipStream_t stream)
 template <typename ST, typename IOT, typename BCT>
 hipError_t launch_prefill_bc(const PrefillParams &p, hipStream_t stream)
 {
+    if constexpr (__is_same(IOT, bf16_t) && __is_same(BCT, bf16_t)) {
+        if (prefill_mm_fits(p)) {
+            const PrefillShape sh = prefill_shape(p);
+            switch (p.d.dstate) {
+            case 32: return launch_prefill_mm<ST, 32>(p, sh, stream);
+            case 64: return launch_prefill_mm<ST, 64>(p, sh, stream);
+            case 128: return launch_prefill_mm<ST, 128>(p, sh, stream);
+            case 256: return launch_prefill_mm<ST, 256>(p, sh, stream);
+            default: break;
+            }
+        }
+    }
     // Eight waves per workgroup when every CU gets at most one workgroup: a lone
     // wave issues well below its SIMD's VALU rate, so two per SIMD finish the
     // sequence sooner. With more workgroups the larger footprint would keep

@@ -1,0 +1,562 @@
+// Prefill on the matrix cores: the same operation as ssu_prefill_kernel
+// (TensorRT-Edge-LLM, "Selective State Update" page,
+// invokeSelectiveStateUpdatePrefill: the decode step applied to tokens
+// t < L_b in order, outputs beyond L_b zero, optional replay stash with the
+// committed state read-only), evaluated a chunk of 32 tokens at a time in
+// closed form. Used for bf16 x/z/out with bf16 B/C (both exact as bf16
+// matrix-core operands) and dstate a multiple of 32.
+//
+// Within a chunk that starts from state S0 (a_k = A dt'_k, Lc[t] = sum of a_k
+// over k <= t, both within the chunk):
+//   y_t   = e^{Lc[t]} (S0 C_t) + sum_{j<=t} e^{Lc[t]-Lc[j]} dt'_j (B_j . C_t) x_j + D x_t
+//   S_end = e^{Lc[last]} S0 + sum_j e^{Lc[last]-Lc[j]} dt'_j x_j B_j^T
+// which is the token-by-token recurrence regrouped (the tree verify's closed
+// form on a chain, plus the state the chain ends in). Four products per chunk
+// and wave (16 rows of dim), all v_mfma_f32_16x16x32_bf16:
+//   Y^T  = C . S^T            (inter-chunk term; S as bf16 hi + lo)
+//   G^T  = B . C^T            (the B_j . C_t dots, lower triangle)
+//   Y^T += Q . X^T            (Q[t][j] = e^{Lc[t]-Lc[j]} dt'_j G[t][j], D on
+//                              the diagonal; Q as bf16 hi + lo)
+//   S^T  = e^{Lc[last]} S^T + B^T . X'^T   (X'[r][j] = w_j x_j[r], w_j the
+//                              suffix weight; X' as three bf16 terms, so the
+//                              carried fp32 state keeps fp32 accuracy)
+// The state never leaves registers: each lane holds S[r][16 nt + 4 qg + v],
+// the accumulator layout of the last product, and the inter-chunk product
+// takes it as its B operand directly by ordering the dstate index of the
+// contraction as that layout does (the C operand follows the same order).
+// Likewise the token index of Q . X^T is ordered as the G^T accumulator
+// holds it, so Q is formed in registers.
+#pragma once
+
+#include "ssu_device.h"
+#include "ssu_internal.h"
+
+namespace ssu {
+namespace {
+
+typedef float pm_f32x4 __attribute__((ext_vector_type(4)));
+typedef __bf16 pm_bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 pm_bf16x2 __attribute__((ext_vector_type(2)));
+typedef float pm_f32x2 __attribute__((ext_vector_type(2)));
+
+constexpr int kPmTT = 32;   // tokens per chunk (two 16-token MFMA tiles)
+constexpr int kPmNT = 256;  // threads: four waves of 16 rows
+
+// LDS layout (bytes) of one workgroup
+struct PmLds {
+    int cs, bs, bt, xt, zs, ys, lc, sf, dp, tot, sb, total;
+};
+__host__ __device__ constexpr int pm_row_pitch(int NS) { return NS * 2 + 16; }   // C, B rows
+__host__ __device__ constexpr int pm_t_pitch() { return kPmTT * 2 + 8; }          // B^T, x^T rows
+__host__ __device__ constexpr int pm_y_pitch() { return 64 * 4 + 16; }            // fp32 outputs
+__host__ __device__ constexpr int pm_z_pitch() { return 64 * 2 + 16; }            // z rows
+__host__ __device__ inline PmLds pm_lds(int NS)
+{
+    PmLds L;
+    int o = 0;
+    auto take = [&o](int bytes) { const int r = o; o += (bytes + 15) & ~15; return r; };
+    L.cs = take(kPmTT * pm_row_pitch(NS));   // C of the chunk [t][n]
+    L.bs = take(kPmTT * pm_row_pitch(NS));   // B of the chunk [j][n]
+    L.bt = take(NS * pm_t_pitch());          // B^T [n][j]
+    L.xt = take(64 * pm_t_pitch());          // x^T [row][j]
+    L.zs = take(kPmTT * pm_z_pitch());       // z [t][row]
+    L.ys = take(kPmTT * pm_y_pitch());       // outputs before the gate [t][row], fp32
+    L.lc = take(kPmTT * 4);                  // Lc[t] log2(e) (base-2 exponent)
+    L.sf = take(kPmTT * 4);                  // w_j = e^{Lc[last]-Lc[j]} dt'_j
+    L.dp = take(kPmTT * 4);                  // dt'_j
+    L.tot = take(16);                        // e^{Lc[last]}
+    L.sb = take(16);                         // the batch row of this workgroup
+    L.total = o;
+    return L;
+}
+
+// An 8-element operand from two runs of 4 bf16 in LDS: at p and at p + 32
+// bytes (16 elements on)
+__device__ __forceinline__ pm_bf16x8 pm_op(const unsigned char *p)
+{
+    const u32x2 lo = *reinterpret_cast<const u32x2 *>(p);
+    const u32x2 hi = *reinterpret_cast<const u32x2 *>(p + 32);
+    return __builtin_bit_cast(pm_bf16x8, u32x4{lo[0], lo[1], hi[0], hi[1]});
+}
+
+// fp32 values as `terms` bf16 parts (round to nearest, the remainder split again)
+template <int TERMS>
+__device__ __forceinline__ void pm_split(const float (&f)[8], pm_bf16x8 (&o)[TERMS])
+{
+    float r[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e)
+        r[e] = f[e];
+#pragma unroll
+    for (int u = 0; u < TERMS; ++u) {
+#pragma unroll
+        for (int e = 0; e < 8; e += 2) {
+            const pm_bf16x2 p = __builtin_convertvector((pm_f32x2){r[e], r[e + 1]}, pm_bf16x2);
+            o[u][e] = p[0];
+            o[u][e + 1] = p[1];
+            if (u + 1 < TERMS) {
+                r[e] -= (float)p[0];
+                r[e + 1] -= (float)p[1];
+            }
+        }
+    }
+}
+
+template <typename ST, int NS>
+__global__ __launch_bounds__(kPmNT) __attribute__((amdgpu_waves_per_eu(NS <= 128 ? 3 : 1))) void ssu_prefill_mm_kernel(
+    const void *__restrict__ x, const float *__restrict__ A, const void *__restrict__ Bm,
+    const void *__restrict__ Cm, const float *__restrict__ dt, const float *__restrict__ dt_bias,
+    const float *__restrict__ Dv, const void *__restrict__ z, ST *__restrict__ state,
+    void *__restrict__ out, const int32_t *__restrict__ ctx, const int32_t *__restrict__ idx,
+    float *__restrict__ st_dA, float *__restrict__ st_u, float *__restrict__ st_B,
+    float *__restrict__ st_dt, const PrefillShape sh)
+{
+    constexpr int TT = kPmTT;
+    constexpr int NT = kPmNT;
+    constexpr int KN = NS / 32;          // k-steps over dstate
+    constexpr int NT16 = NS / 16;        // dstate tiles of the state
+    constexpr int PC = pm_row_pitch(NS), PT = pm_t_pitch(), PY = pm_y_pitch(), PZ = pm_z_pitch();
+    constexpr int NCB = NS / 8;                      // 16-byte column blocks of a B (C) row
+    constexpr int NVP = (16 * NCB + NT - 1) / NT;    // token pairs x column blocks per thread
+    static_assert(NS % 32 == 0, "dstate in whole 32-column steps");
+
+    extern __shared__ __attribute__((aligned(16))) unsigned char lds[];
+    const PmLds L = pm_lds(NS);
+    unsigned char *Cs = lds + L.cs, *Bs = lds + L.bs, *Bt = lds + L.bt, *Xt = lds + L.xt;
+    unsigned char *Zs = lds + L.zs;
+    float *Ys = reinterpret_cast<float *>(lds + L.ys);
+    float *lcs = reinterpret_cast<float *>(lds + L.lc);
+    float *sfs = reinterpret_cast<float *>(lds + L.sf);
+    float *dps = reinterpret_cast<float *>(lds + L.dp);
+    float *tot = reinterpret_cast<float *>(lds + L.tot);
+    int *sorted_b = reinterpret_cast<int *>(lds + L.sb);
+
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int qg = lane >> 4, ln = lane & 15;
+    const int T = sh.seq_len, H = sh.nheads, Dm = sh.dim, G = sh.ngroups;
+
+    // work item: as ssu_prefill_kernel (longest rows first, snake over passes)
+    int u = blockIdx.x;
+    if (sh.sort_by_length && sh.pass > 0) {
+        const int pass = u / sh.pass, pos = u - pass * sh.pass;
+        const int base = pass * sh.pass;
+        const int width = min(sh.pass, (int)gridDim.x - base);
+        u = base + ((pass & 1) ? width - 1 - pos : pos);
+    }
+    const int per_b = H * sh.nrb;
+    const int qb = u / per_b;
+    const int rem = u - qb * per_b;
+    const int h = rem % H;
+    const int rb = rem / H;
+    int b = qb;
+    if (sh.sort_by_length) {
+        if (tid == 0)
+            *sorted_b = qb;
+        __syncthreads();
+        for (int c = tid; c < sh.batch; c += NT) {
+            const int lc = clamp_len(ctx[c], T);
+            int rank = 0;
+            for (int c2 = 0; c2 < sh.batch; ++c2) {
+                const int l2 = clamp_len(ctx[c2], T);
+                rank += (l2 > lc) || (l2 == lc && c2 < c);
+            }
+            if (rank == qb)
+                *sorted_b = c;
+        }
+        __syncthreads();
+        b = __builtin_amdgcn_readfirstlane(*sorted_b);
+    }
+
+    const int srow = idx ? idx[b] : b;
+    const int Lb = ctx ? clamp_len(ctx[b], T) : T;
+    const int64_t bT = (int64_t)b * T;
+    const int rbase = rb * 64;
+    const int NSTR = H * Dm;  // elements between tokens of x, z, out, st_u
+
+    if (srow < 0) {  // padding row: outputs zero, state and stash untouched
+        for (int i = tid; i < T * 64; i += NT) {
+            const int r = rbase + (i & 63);
+            if (r < Dm)
+                st_elem<bf16_t>(out, ((bT + (i >> 6)) * H + h) * Dm + r, 0.0f);
+        }
+        return;
+    }
+
+    const bool stash = st_dA != nullptr;
+    const int g = h / sh.heads_per_group;
+    const float Ah = A[h];
+    const float bias = dt_bias ? dt_bias[h] : 0.0f;
+    const float dskip = Dv ? Dv[h] : 0.0f;
+    const bool writes_B = stash && rb == 0 && (h % sh.heads_per_group) == 0;
+    // per-row bases (elements); offsets from them are 32-bit
+    const unsigned char *xrow = static_cast<const unsigned char *>(x) + (bT * H + h) * Dm * 2;
+    const unsigned char *zrow = z ? static_cast<const unsigned char *>(z) + (bT * H + h) * Dm * 2 : nullptr;
+    unsigned char *orow = static_cast<unsigned char *>(out) + (bT * H + h) * Dm * 2;
+    const unsigned char *brow = static_cast<const unsigned char *>(Bm) + (bT * G + g) * NS * 2;
+    const unsigned char *crow = static_cast<const unsigned char *>(Cm) + (bT * G + g) * NS * 2;
+    const float *dtrow = dt + bT * H + h;
+
+    // ---- the state: lane (ln, qg) of wave w holds S[r][16 nt + 4 qg + v] ----
+    const int rl = 16 * wave + ln;  // row within the block
+    const int r = rbase + rl;
+    const bool rv = r < Dm;
+    ST *srowp = state + (int64_t)srow * sh.row_stride + (int64_t)h * Dm * NS + (int64_t)min(r, Dm - 1) * NS;
+    pm_f32x4 S[NT16];
+#pragma unroll
+    for (int nt = 0; nt < NT16; ++nt) {
+#pragma unroll
+        for (int v = 0; v < 4; ++v)
+            S[nt][v] = rv ? ld_elem<ST>(srowp, 16 * nt + 4 * qg + v) : 0.0f;
+    }
+
+    // ---- chunk staging: global -> registers (prefetch) -> LDS ----
+    // B and C: item v = (token pair p = v % 16, column block cb = v / 16), two
+    // 16-byte loads (tokens 2p, 2p+1); B^T takes the pair as one 32-bit word
+    // per column. x: threads < 128 take (token pair tid % 16, rows
+    // 8 (tid / 16) ..+7) and x^T the pair as one word per row. z (and the
+    // outputs): token tid / 8, rows 8 (tid % 8) ..+7.
+    u32x4 rB[NVP][2], rC[NVP][2], rX[2], rZ;
+    float rDt = 0.0f;
+    const int xtok = tid >> 3, xr8 = 8 * (tid & 7);  // z / output mapping
+    const bool xrv = rbase + xr8 < Dm;               // Dm is a multiple of 8
+    const int xp = tid & 15, xb8 = 8 * ((tid >> 4) & 7);  // x mapping (threads < 128)
+    const bool xbv = rbase + xb8 < Dm;
+    auto load_chunk = [&](int t0, int nv) {
+#pragma unroll
+        for (int k = 0; k < NVP; ++k) {
+            const int v = min(tid + NT * k, 16 * NCB - 1);
+            const int p = v & 15, col = 8 * (v >> 4);
+#pragma unroll
+            for (int q = 0; q < 2; ++q) {
+                const int tok = min(2 * p + q, nv - 1);
+                const uint32_t o = (uint32_t)((((t0 + tok) * G) * NS + col) * 2);
+                rB[k][q] = *reinterpret_cast<const u32x4 *>(brow + o);
+                rC[k][q] = *reinterpret_cast<const u32x4 *>(crow + o);
+            }
+        }
+#pragma unroll
+        for (int q = 0; q < 2; ++q) {
+            const int tok = min(2 * xp + q, nv - 1);
+            rX[q] = *reinterpret_cast<const u32x4 *>(
+                xrow + (uint32_t)(((t0 + tok) * NSTR + min(rbase + xb8, Dm - 8)) * 2));
+        }
+        if (zrow)
+            rZ = *reinterpret_cast<const u32x4 *>(
+                zrow + (uint32_t)(((t0 + min(xtok, nv - 1)) * NSTR + min(rbase + xr8, Dm - 8)) * 2));
+        if (tid < TT)
+            rDt = dtrow[(uint32_t)(min(t0 + tid, t0 + nv - 1) * H)];
+    };
+    // 16-bit element i of a 16-byte register group
+    auto h16 = [](const u32x4 &w, int i) { return (w[i >> 1] >> (16 * (i & 1))) & 0xffffu; };
+    auto store_chunk = [&](int t0, int nv) {
+#pragma unroll
+        for (int k = 0; k < NVP; ++k) {
+            const int v = tid + NT * k;
+            if (v < 16 * NCB) {
+                const int p = v & 15, col = 8 * (v >> 4);
+#pragma unroll
+                for (int q = 0; q < 2; ++q) {
+                    *reinterpret_cast<u32x4 *>(Bs + (2 * p + q) * PC + col * 2) = rB[k][q];
+                    *reinterpret_cast<u32x4 *>(Cs + (2 * p + q) * PC + col * 2) = rC[k][q];
+                }
+#pragma unroll
+                for (int i = 0; i < 8; ++i)
+                    *reinterpret_cast<uint32_t *>(Bt + (col + i) * PT + 4 * p) =
+                        h16(rB[k][0], i) | (h16(rB[k][1], i) << 16);
+                if (writes_B) {
+#pragma unroll
+                    for (int q = 0; q < 2; ++q) {
+                        if (2 * p + q < nv) {
+                            float *sb = st_B + ((bT + t0 + 2 * p + q) * G + g) * NS + col;
+#pragma unroll
+                            for (int i = 0; i < 8; i += 4)
+                                *reinterpret_cast<float4 *>(sb + i) =
+                                    make_float4(bf16_to_f32(h16(rB[k][q], i)), bf16_to_f32(h16(rB[k][q], i + 1)),
+                                                bf16_to_f32(h16(rB[k][q], i + 2)), bf16_to_f32(h16(rB[k][q], i + 3)));
+                        }
+                    }
+                }
+            }
+        }
+        if (tid < 128) {
+            u32x4 w[2];
+#pragma unroll
+            for (int q = 0; q < 2; ++q) {
+                const bool live = 2 * xp + q < nv && xbv;
+                w[q] = live ? rX[q] : u32x4{0u, 0u, 0u, 0u};
+                if (stash && live) {
+                    float *su = reinterpret_cast<float *>(reinterpret_cast<unsigned char *>(st_u) +
+                                                          ((bT + t0 + 2 * xp + q) * H + h) * Dm * 4) + rbase + xb8;
+#pragma unroll
+                    for (int i = 0; i < 8; i += 4)
+                        *reinterpret_cast<float4 *>(su + i) =
+                            make_float4(bf16_to_f32(h16(w[q], i)), bf16_to_f32(h16(w[q], i + 1)),
+                                        bf16_to_f32(h16(w[q], i + 2)), bf16_to_f32(h16(w[q], i + 3)));
+                }
+            }
+#pragma unroll
+            for (int i = 0; i < 8; ++i)
+                *reinterpret_cast<uint32_t *>(Xt + (xb8 + i) * PT + 4 * xp) = h16(w[0], i) | (h16(w[1], i) << 16);
+        }
+        if (zrow)
+            *reinterpret_cast<u32x4 *>(Zs + xtok * PZ + xr8 * 2) = rZ;
+        if (wave == 0) {
+            // lanes < TT: one token each (a = 0, dt' = 0 past the chunk's end);
+            // Lc by an inclusive prefix scan, the suffix sums by a second scan
+            // (not as differences of prefix sums: no cancellation)
+            float v = rDt + bias;
+            if (sh.dt_softplus)
+                v = softplus_f32(v);
+            const bool live = lane < nv;
+            const float dtp = live ? v : 0.0f;
+            const float a = (live && lane < TT) ? Ah * v : 0.0f;
+            float pre = a, suf = a;
+#pragma unroll
+            for (int d = 1; d < TT; d <<= 1) {
+                const float o1 = __shfl_up(pre, d, 64);
+                const float o2 = __shfl_down(suf, d, 64);
+                if ((lane & (TT - 1)) >= d)
+                    pre += o1;
+                if ((lane & (TT - 1)) + d < TT)
+                    suf += o2;
+            }
+            // suf includes a_j itself: the weight of x_j in the chunk's end state
+            // takes the decays after j only
+            if (lane < TT) {
+                lcs[lane] = pre * 1.4426950408889634f;
+                sfs[lane] = expf(suf - a) * dtp;
+                dps[lane] = dtp;
+                if (stash && rb == 0 && live) {
+                    st_dA[(bT + t0 + lane) * H + h] = a;
+                    st_dt[(bT + t0 + lane) * H + h] = v;
+                }
+            }
+            const float total = __shfl(pre, TT - 1, 64);
+            if (lane == 0)
+                tot[0] = expf(total);
+        }
+    };
+
+    const int nchunks = (Lb + TT - 1) / TT;
+    if (nchunks > 0) {
+        load_chunk(0, min(TT, Lb));
+        store_chunk(0, min(TT, Lb));
+    }
+    __syncthreads();
+
+    for (int c = 0; c < nchunks; ++c) {
+        const int t0 = c * TT;
+        const int nv = min(TT, Lb - t0);
+        if (c + 1 < nchunks)
+            load_chunk(t0 + TT, min(TT, Lb - t0 - TT));
+
+        // ---- Y^T = C . S^T and G^T = B . C^T over dstate ----
+        pm_f32x4 ay[2] = {pm_f32x4{0.0f, 0.0f, 0.0f, 0.0f}, pm_f32x4{0.0f, 0.0f, 0.0f, 0.0f}};
+        pm_f32x4 ag[3] = {pm_f32x4{0.0f, 0.0f, 0.0f, 0.0f}, pm_f32x4{0.0f, 0.0f, 0.0f, 0.0f},
+                          pm_f32x4{0.0f, 0.0f, 0.0f, 0.0f}};
+#pragma unroll
+        for (int kk = 0; kk < KN; ++kk) {
+            // dstate order of step kk for lane group qg: 32kk+4qg+e (e<4), 32kk+16+4qg+e-4
+            pm_bf16x8 cop[2], bop[2];
+#pragma unroll
+            for (int t = 0; t < 2; ++t) {
+                cop[t] = pm_op(Cs + (16 * t + ln) * PC + (32 * kk + 4 * qg) * 2);
+                bop[t] = pm_op(Bs + (16 * t + ln) * PC + (32 * kk + 4 * qg) * 2);
+            }
+            float sv[8];
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                sv[e] = S[2 * kk][e];
+                sv[4 + e] = S[2 * kk + 1][e];
+            }
+            pm_bf16x8 sp[2];
+            pm_split<2>(sv, sp);
+#pragma unroll
+            for (int t = 0; t < 2; ++t)
+#pragma unroll
+                for (int uu = 0; uu < 2; ++uu)
+                    ay[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(cop[t], sp[uu], ay[t], 0, 0, 0);
+            ag[0] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(bop[0], cop[0], ag[0], 0, 0, 0);
+            ag[1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(bop[0], cop[1], ag[1], 0, 0, 0);
+            ag[2] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(bop[1], cop[1], ag[2], 0, 0, 0);
+        }
+
+        // inter-chunk term decays to token t: lanes hold tokens 16t + 4qg + v
+        // (the outputs are bf16: the hardware exp2 is accurate enough here; the
+        // state's own weights use expf)
+#pragma unroll
+        for (int t = 0; t < 2; ++t) {
+            const float4 l4 = *reinterpret_cast<const float4 *>(lcs + 16 * t + 4 * qg);
+            ay[t][0] *= __builtin_amdgcn_exp2f(l4.x);
+            ay[t][1] *= __builtin_amdgcn_exp2f(l4.y);
+            ay[t][2] *= __builtin_amdgcn_exp2f(l4.z);
+            ay[t][3] *= __builtin_amdgcn_exp2f(l4.w);
+        }
+
+        // ---- Q in registers: lane (t = 16tt + ln, qg) element e holds source
+        // j = 4qg + e (e < 4) or 16 + 4qg + e - 4, as the G^T accumulators do ----
+        const float4 lj0 = *reinterpret_cast<const float4 *>(lcs + 4 * qg);
+        const float4 lj1 = *reinterpret_cast<const float4 *>(lcs + 16 + 4 * qg);
+        const float4 dj0 = *reinterpret_cast<const float4 *>(dps + 4 * qg);
+        const float4 dj1 = *reinterpret_cast<const float4 *>(dps + 16 + 4 * qg);
+        const float lj[8] = {lj0.x, lj0.y, lj0.z, lj0.w, lj1.x, lj1.y, lj1.z, lj1.w};
+        const float dj[8] = {dj0.x, dj0.y, dj0.z, dj0.w, dj1.x, dj1.y, dj1.z, dj1.w};
+        // x^T operand in the same source order: lane (row rl, qg)
+        const pm_bf16x8 xop = pm_op(Xt + rl * PT + (4 * qg) * 2);
+#pragma unroll
+        for (int t = 0; t < 2; ++t) {
+            const int tq = 16 * t + ln;  // this lane's token as a Q row
+            const float lt = lcs[tq];
+            float qv[8];
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+                const int j = e < 4 ? 4 * qg + e : 12 + 4 * qg + e;
+                const float gv = e < 4 ? ag[t][e] : (t == 1 ? ag[2][e - 4] : 0.0f);
+                float q = 0.0f;
+                if (j <= tq && tq < nv)
+                    q = __builtin_amdgcn_exp2f(lt - lj[e]) * dj[e] * gv + (j == tq ? dskip : 0.0f);
+                qv[e] = q;
+            }
+            pm_bf16x8 qp[2];
+            pm_split<2>(qv, qp);
+#pragma unroll
+            for (int uu = 0; uu < 2; ++uu)
+                ay[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qp[uu], xop, ay[t], 0, 0, 0);
+        }
+
+        // outputs before the gate: Ys[t][row]
+#pragma unroll
+        for (int t = 0; t < 2; ++t)
+#pragma unroll
+            for (int v = 0; v < 4; ++v)
+                Ys[(16 * t + 4 * qg + v) * (PY / 4) + rl] = ay[t][v];
+
+        // ---- S^T = e^{Lc[last]} S^T + B^T . X'^T ----
+        {
+            const float4 w0 = *reinterpret_cast<const float4 *>(sfs + 4 * qg);
+            const float4 w1 = *reinterpret_cast<const float4 *>(sfs + 16 + 4 * qg);
+            const float wj[8] = {w0.x, w0.y, w0.z, w0.w, w1.x, w1.y, w1.z, w1.w};
+            float xw[8];
+#pragma unroll
+            for (int e = 0; e < 8; ++e)
+                xw[e] = wj[e] * (float)xop[e];
+            pm_bf16x8 xp[3];
+            pm_split<3>(xw, xp);
+            const float ws = tot[0];
+#pragma unroll
+            for (int nt = 0; nt < NT16; ++nt) {
+                const pm_bf16x8 bt = pm_op(Bt + (16 * nt + ln) * PT + (4 * qg) * 2);
+#pragma unroll
+                for (int v = 0; v < 4; ++v)
+                    S[nt][v] *= ws;
+#pragma unroll
+                for (int uu = 0; uu < 3; ++uu)
+                    S[nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(bt, xp[uu], S[nt], 0, 0, 0);
+            }
+        }
+        __syncthreads();
+
+        // ---- gate and store the chunk's outputs: 8 rows of one token per thread ----
+        if (xtok < nv && xrv) {
+            const float4 y0 = *reinterpret_cast<const float4 *>(Ys + xtok * (PY / 4) + xr8);
+            const float4 y1 = *reinterpret_cast<const float4 *>(Ys + xtok * (PY / 4) + xr8 + 4);
+            float y[8] = {y0.x, y0.y, y0.z, y0.w, y1.x, y1.y, y1.z, y1.w};
+            if (zrow) {
+                const u32x4 zw = *reinterpret_cast<const u32x4 *>(Zs + xtok * PZ + xr8 * 2);
+#pragma unroll
+                for (int i = 0; i < 8; ++i) {
+                    const float zi = bf16_to_f32((zw[i >> 1] >> (16 * (i & 1))) & 0xffffu);
+                    y[i] *= zi * __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(-1.4426950408889634f * zi));
+                }
+            }
+            u32x4 ow;  // round to nearest even, two values per conversion
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+                ow[i] = __builtin_bit_cast(uint32_t, __builtin_convertvector((pm_f32x2){y[2 * i], y[2 * i + 1]}, pm_bf16x2));
+            *reinterpret_cast<u32x4 *>(orow + (uint32_t)(((t0 + xtok) * NSTR + rbase + xr8) * 2)) = ow;
+        }
+        if (c + 1 < nchunks)
+            store_chunk(t0 + TT, min(TT, Lb - t0 - TT));
+        __syncthreads();
+    }
+
+    // ---- tokens beyond the context: zero outputs and zero stash ----
+    for (int i = tid; i < (T - Lb) * 64; i += NT) {
+        const int rr = rbase + (i & 63);
+        if (rr < Dm) {
+            const int64_t o = ((bT + Lb + (i >> 6)) * H + h) * Dm + rr;
+            st_elem<bf16_t>(out, o, 0.0f);
+            if (stash)
+                st_u[o] = 0.0f;
+        }
+    }
+    if (stash && rb == 0) {
+        for (int t = Lb + tid; t < T; t += NT) {
+            st_dA[(bT + t) * H + h] = 0.0f;
+            st_dt[(bT + t) * H + h] = 0.0f;
+        }
+    }
+    if (writes_B) {
+        for (int i = tid; i < (T - Lb) * NS; i += NT)
+            st_B[((bT + Lb + i / NS) * G + g) * NS + (i % NS)] = 0.0f;
+    }
+
+    // ---- the final state (without the stash the pool row is updated) ----
+    if (!stash && Lb > 0 && rv) {
+        ST *sp = state + (int64_t)srow * sh.row_stride + (int64_t)h * Dm * NS + (int64_t)r * NS;
+#pragma unroll
+        for (int nt = 0; nt < NT16; ++nt)
+#pragma unroll
+            for (int v = 0; v < 4; ++v)
+                st_elem<ST>(sp, 16 * nt + 4 * qg + v, S[nt][v]);
+    }
+}
+
+template <typename ST, int NS>
+hipError_t launch_prefill_mm(const PrefillParams &p, const PrefillShape &sh, hipStream_t stream)
+{
+    const DecodeParams &d = p.d;
+    const int64_t blocks = (int64_t)d.batch * d.nheads * sh.nrb;
+    if (blocks > 0x7fffffff)
+        return hipErrorInvalidConfiguration;
+    const int lds = pm_lds(NS).total;
+    auto kern = ssu_prefill_mm_kernel<ST, NS>;
+    if (lds > 64 * 1024) {
+        // above 64 KiB of dynamic LDS the kernel must be allowed it, once per device
+        static int allowed[64] = {0};
+        int dev = 0;
+        hipError_t e = hipGetDevice(&dev);
+        if (e != hipSuccess)
+            return e;
+        if (dev < 0 || dev >= 64 || !allowed[dev]) {
+            e = hipFuncSetAttribute(reinterpret_cast<const void *>(kern),
+                                    hipFuncAttributeMaxDynamicSharedMemorySize, lds);
+            if (e != hipSuccess)
+                return e;
+            if (dev >= 0 && dev < 64)
+                allowed[dev] = 1;
+        }
+    }
+    (void)hipGetLastError();
+    hipLaunchKernelGGL(kern, dim3((unsigned)blocks), dim3(kPmNT), (unsigned)lds, stream, d.x, d.A,
+                       d.B, d.C, d.dt, d.dt_bias, d.D, d.z, static_cast<ST *>(d.state), d.out, p.ctx,
+                       d.idx, p.st_dA, p.st_u, p.st_B, p.st_dt, sh);
+    return hipGetLastError();
+}
+
+// The matrix-core prefill takes bf16 x/z/out and B/C (exact operands), dstate a
+// multiple of 32, dim a multiple of 8 and 16-byte aligned x, z, out and x
+// stash (whole 8-row vectors); everything else runs on ssu_prefill_kernel.
+inline bool prefill_mm_fits(const PrefillParams &p)
+{
+    const DecodeParams &d = p.d;
+    auto al16 = [](const void *q) { return (reinterpret_cast<uintptr_t>(q) & 15) == 0; };
+    return d.io_dtype == kBF16 && d.bc_dtype == kBF16 && d.dstate % 32 == 0 && d.dim % 8 == 0 &&
+           al16(d.x) && al16(d.out) && (d.z == nullptr || al16(d.z)) &&
+           (p.st_u == nullptr || al16(p.st_u)) && p.waves_per_wg == 0;
+}
+
+}  // namespace
+}  // namespace ssu
