@@ -33,6 +33,25 @@ __device__ __forceinline__ float row_prefix_prod16(float v)
     return v;
 }
 
+// Inclusive prefix and suffix sums along each row of 16 lanes (row shifts
+// with zero fill, Hillis-Steele).
+__device__ __forceinline__ float row_prefix_sum16(float v)
+{
+    v += dpp_f32_fill<0x111>(0.0f, v);  // row_shr:1
+    v += dpp_f32_fill<0x112>(0.0f, v);  // row_shr:2
+    v += dpp_f32_fill<0x114>(0.0f, v);  // row_shr:4
+    v += dpp_f32_fill<0x118>(0.0f, v);  // row_shr:8
+    return v;
+}
+__device__ __forceinline__ float row_suffix_sum16(float v)
+{
+    v += dpp_f32_fill<0x101>(0.0f, v);  // row_shl:1
+    v += dpp_f32_fill<0x102>(0.0f, v);  // row_shl:2
+    v += dpp_f32_fill<0x104>(0.0f, v);  // row_shl:4
+    v += dpp_f32_fill<0x108>(0.0f, v);  // row_shl:8
+    return v;
+}
+
 // Sum over aligned groups of W lanes (W = 4, 8 or 16): quad permutations, then
 // the half-row and row mirrors; every lane of a group gets the group's sum.
 template <int W>

@@ -29,6 +29,7 @@
 #pragma once
 
 #include "ssu_device.h"
+#include "ssu_dpp.h"
 #include "ssu_internal.h"
 
 namespace ssu {
@@ -307,21 +308,22 @@ __global__ __launch_bounds__(kPmNT) __attribute__((amdgpu_waves_per_eu(NS <= 128
             // Lc by an inclusive prefix scan, the suffix sums by a second scan
             // (not as differences of prefix sums: no cancellation)
             float v = rDt + bias;
-            if (sh.dt_softplus)
-                v = softplus_f32(v);
+            if (sh.dt_softplus)  // log(1 + e^v) on the hardware exp2 / log2 (~2 ulp)
+                v = v > 20.0f ? v
+                              : __builtin_amdgcn_logf(1.0f + __builtin_amdgcn_exp2f(v * 1.4426950408889634f)) *
+                                    0.6931471805599453f;
             const bool live = lane < nv;
             const float dtp = live ? v : 0.0f;
             const float a = (live && lane < TT) ? Ah * v : 0.0f;
-            float pre = a, suf = a;
-#pragma unroll
-            for (int d = 1; d < TT; d <<= 1) {
-                const float o1 = __shfl_up(pre, d, 64);
-                const float o2 = __shfl_down(suf, d, 64);
-                if ((lane & (TT - 1)) >= d)
-                    pre += o1;
-                if ((lane & (TT - 1)) + d < TT)
-                    suf += o2;
-            }
+            // inclusive prefix and suffix sums over lanes 0 .. 31 (two rows of
+            // 16: row sums by DPP, then the other row's total added)
+            float pre = row_prefix_sum16(a), suf = row_suffix_sum16(a);
+            const float p15 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, pre), 15));
+            const float s16 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, suf), 16));
+            if (lane >= 16)
+                pre += p15;
+            if (lane < 16)
+                suf += s16;
             // suf includes a_j itself: the weight of x_j in the chunk's end state
             // takes the decays after j only
             if (lane < TT) {
@@ -333,7 +335,7 @@ __global__ __launch_bounds__(kPmNT) __attribute__((amdgpu_waves_per_eu(NS <= 128
                     st_dt[(bT + t0 + lane) * H + h] = v;
                 }
             }
-            const float total = __shfl(pre, TT - 1, 64);
+            const float total = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, pre), TT - 1));
             if (lane == 0)
                 tot[0] = expf(total);
         }
