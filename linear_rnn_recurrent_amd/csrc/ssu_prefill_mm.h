@@ -42,6 +42,7 @@ typedef float pm_f32x2 __attribute__((ext_vector_type(2)));
 
 constexpr int kPmTT = 32;   // tokens per chunk (two 16-token MFMA tiles)
 constexpr int kPmNT = 256;  // threads: four waves of 16 rows
+constexpr int kPmScanWave = 3;  // the wave that forms a chunk's decays (it stages no x)
 
 // LDS layout (bytes) of one workgroup
 struct PmLds {
@@ -246,8 +247,8 @@ __global__ __launch_bounds__(kPmNT) __attribute__((amdgpu_waves_per_eu(NS <= 128
         if (zrow)
             rZ = *reinterpret_cast<const u32x4 *>(
                 zrow + (uint32_t)(((t0 + min(xtok, nv - 1)) * NSTR + min(rbase + xr8, Dm - 8)) * 2));
-        if (tid < TT)
-            rDt = dtrow[(uint32_t)(min(t0 + tid, t0 + nv - 1) * H)];
+        if (wave == kPmScanWave && lane < TT)
+            rDt = dtrow[(uint32_t)(min(t0 + lane, t0 + nv - 1) * H)];
     };
     // 16-bit element i of a 16-byte register group
     auto h16 = [](const u32x4 &w, int i) { return (w[i >> 1] >> (16 * (i & 1))) & 0xffffu; };
@@ -303,15 +304,13 @@ __global__ __launch_bounds__(kPmNT) __attribute__((amdgpu_waves_per_eu(NS <= 128
         }
         if (zrow)
             *reinterpret_cast<u32x4 *>(Zs + xtok * PZ + xr8 * 2) = rZ;
-        if (wave == 0) {
-            // lanes < TT: one token each (a = 0, dt' = 0 past the chunk's end);
+        if (wave == kPmScanWave) {
+            // (the wave with the least staging work) lanes < TT: one token each (a = 0, dt' = 0 past the chunk's end);
             // Lc by an inclusive prefix scan, the suffix sums by a second scan
             // (not as differences of prefix sums: no cancellation)
             float v = rDt + bias;
-            if (sh.dt_softplus)  // log(1 + e^v) on the hardware exp2 / log2 (~2 ulp)
-                v = v > 20.0f ? v
-                              : __builtin_amdgcn_logf(1.0f + __builtin_amdgcn_exp2f(v * 1.4426950408889634f)) *
-                                    0.6931471805599453f;
+            if (sh.dt_softplus)  // as every other kernel computes it: the same dt' bits
+                v = softplus_f32(v);
             const bool live = lane < nv;
             const float dtp = live ? v : 0.0f;
             const float a = (live && lane < TT) ? Ah * v : 0.0f;
