@@ -138,8 +138,9 @@ def test_prefill_equals_repeated_decode():
                                 pool_rows=6, seed=21, bc_std=128 ** -0.5, ctx=("none",))
     st_p, out_p, _ = run_prefill(w)
     st_d, out_d = _decode_steps(w, 20)
-    # prefill runs the rescaled form of the recurrence (two FMAs per element),
-    # decode the direct one: equal up to each side's fp32 rounding
+    # prefill evaluates 32-token chunks in closed form on the matrix cores (bf16
+    # operands; the rescaled recurrence otherwise), decode the direct recurrence:
+    # equal up to each side's fp32 rounding
     assert_close(st_p.cpu(), f64(st_d), 2 * TOL_F32, "state: prefill vs repeated decode")
     assert_close(out_p.cpu(), f64(out_d), TOL_LOW, "out: prefill vs repeated decode")
 
@@ -153,7 +154,7 @@ def test_stash_then_replay_equals_prefill_with_accepted_context():
                state_indices=gpu(w["state_indices"]))
     st_k, _, _ = run_prefill(w, context_lengths=accepted)
     # rows with nothing accepted are bit-identical; the rest agree to rounding
-    # (replay runs the direct recurrence, prefill the rescaled one)
+    # (replay runs the direct recurrence, prefill the chunked closed form)
     idx = w["state_indices"].numpy()
     assert_bitwise(st_s[idx[0]], st_k[idx[0]], "row with accepted = 0")
     assert_close(st_s.cpu(), f64(st_k), 2 * TOL_F32, "stash + replay(k) vs prefill(contextLengths = k)")
