@@ -199,6 +199,12 @@ __global__ __launch_bounds__(kPmNT) __attribute__((amdgpu_waves_per_eu(NS <= 128
     const unsigned char *brow = static_cast<const unsigned char *>(Bm) + (bT * G + g) * NS * 2;
     const unsigned char *crow = static_cast<const unsigned char *>(Cm) + (bT * G + g) * NS * 2;
     const float *dtrow = dt + bT * H + h;
+    // stash bases of this (batch row, head / group): token t at t H (dA, dt),
+    // t NSTR (x, from the block's first row), t G NS (B)
+    float *sArow = stash ? st_dA + bT * H + h : nullptr;
+    float *sDrow = stash ? st_dt + bT * H + h : nullptr;
+    float *sUrow = stash ? st_u + (bT * H + h) * Dm + rbase : nullptr;
+    float *sBrow = writes_B ? st_B + (bT * G + g) * NS : nullptr;
 
     // ---- the state: lane (ln, qg) of wave w holds S[r][16 nt + 4 qg + v] ----
     const int rl = 16 * wave + ln;  // row within the block
@@ -250,8 +256,13 @@ __global__ __launch_bounds__(kPmNT) __attribute__((amdgpu_waves_per_eu(NS <= 128
         if (wave == kPmScanWave && lane < TT)
             rDt = dtrow[(uint32_t)(min(t0 + lane, t0 + nv - 1) * H)];
     };
-    // 16-bit element i of a 16-byte register group
+    // 16-bit element i of a 16-byte register group; the elements i of two
+    // groups as one word (one v_perm_b32: bytes of the low or high halves)
     auto h16 = [](const u32x4 &w, int i) { return (w[i >> 1] >> (16 * (i & 1))) & 0xffffu; };
+    auto pair16 = [](const u32x4 &w0, const u32x4 &w1, int i) {
+        // selector bytes 0-3 pick from w0's word, 4-7 from w1's (perm takes (hi, lo))
+        return __builtin_amdgcn_perm(w1[i >> 1], w0[i >> 1], (i & 1) ? 0x07060302u : 0x05040100u);
+    };
     auto store_chunk = [&](int t0, int nv) {
 #pragma unroll
         for (int k = 0; k < NVP; ++k) {
@@ -265,13 +276,12 @@ __global__ __launch_bounds__(kPmNT) __attribute__((amdgpu_waves_per_eu(NS <= 128
                 }
 #pragma unroll
                 for (int i = 0; i < 8; ++i)
-                    *reinterpret_cast<uint32_t *>(Bt + (col + i) * PT + 4 * p) =
-                        h16(rB[k][0], i) | (h16(rB[k][1], i) << 16);
+                    *reinterpret_cast<uint32_t *>(Bt + (col + i) * PT + 4 * p) = pair16(rB[k][0], rB[k][1], i);
                 if (writes_B) {
 #pragma unroll
                     for (int q = 0; q < 2; ++q) {
                         if (2 * p + q < nv) {
-                            float *sb = st_B + ((bT + t0 + 2 * p + q) * G + g) * NS + col;
+                            float *sb = sBrow + (uint32_t)((t0 + 2 * p + q) * G * NS + col);
 #pragma unroll
                             for (int i = 0; i < 8; i += 4)
                                 *reinterpret_cast<float4 *>(sb + i) =
@@ -289,8 +299,7 @@ __global__ __launch_bounds__(kPmNT) __attribute__((amdgpu_waves_per_eu(NS <= 128
                 const bool live = 2 * xp + q < nv && xbv;
                 w[q] = live ? rX[q] : u32x4{0u, 0u, 0u, 0u};
                 if (stash && live) {
-                    float *su = reinterpret_cast<float *>(reinterpret_cast<unsigned char *>(st_u) +
-                                                          ((bT + t0 + 2 * xp + q) * H + h) * Dm * 4) + rbase + xb8;
+                    float *su = sUrow + (uint32_t)((t0 + 2 * xp + q) * NSTR + xb8);
 #pragma unroll
                     for (int i = 0; i < 8; i += 4)
                         *reinterpret_cast<float4 *>(su + i) =
@@ -300,7 +309,7 @@ __global__ __launch_bounds__(kPmNT) __attribute__((amdgpu_waves_per_eu(NS <= 128
             }
 #pragma unroll
             for (int i = 0; i < 8; ++i)
-                *reinterpret_cast<uint32_t *>(Xt + (xb8 + i) * PT + 4 * xp) = h16(w[0], i) | (h16(w[1], i) << 16);
+                *reinterpret_cast<uint32_t *>(Xt + (xb8 + i) * PT + 4 * xp) = pair16(w[0], w[1], i);
         }
         if (zrow)
             *reinterpret_cast<u32x4 *>(Zs + xtok * PZ + xr8 * 2) = rZ;
@@ -330,8 +339,8 @@ __global__ __launch_bounds__(kPmNT) __attribute__((amdgpu_waves_per_eu(NS <= 128
                 sfs[lane] = expf(suf - a) * dtp;
                 dps[lane] = dtp;
                 if (stash && rb == 0 && live) {
-                    st_dA[(bT + t0 + lane) * H + h] = a;
-                    st_dt[(bT + t0 + lane) * H + h] = v;
+                    sArow[(uint32_t)((t0 + lane) * H)] = a;
+                    sDrow[(uint32_t)((t0 + lane) * H)] = v;
                 }
             }
             const float total = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, pre), TT - 1));
@@ -414,10 +423,12 @@ __global__ __launch_bounds__(kPmNT) __attribute__((amdgpu_waves_per_eu(NS <= 128
 #pragma unroll
             for (int e = 0; e < 8; ++e) {
                 const int j = e < 4 ? 4 * qg + e : 12 + 4 * qg + e;
-                const float gv = e < 4 ? ag[t][e] : (t == 1 ? ag[2][e - 4] : 0.0f);
                 float q = 0.0f;
-                if (j <= tq && tq < nv)
-                    q = __builtin_amdgcn_exp2f(lt - lj[e]) * dj[e] * gv + (j == tq ? dskip : 0.0f);
+                if (t == 1 || e < 4) {  // sources 16.. lie past every token of tile 0
+                    const float gv = e < 4 ? ag[t][e] : ag[2][e - 4];
+                    if (j <= tq && tq < nv)
+                        q = __builtin_amdgcn_exp2f(lt - lj[e]) * dj[e] * gv + (j == tq ? dskip : 0.0f);
+                }
                 qv[e] = q;
             }
             pm_bf16x8 qp[2];
