@@ -367,8 +367,16 @@ struct SV<bf16_t> {
 
 __device__ __forceinline__ float softplus_f32(float v)
 {
-    // log(1 + e^v); above 20 the correction e^-v is below fp32 resolution of v
-    return v > 20.0f ? v : log1pf(expf(v));
+    // log(1 + e^v), a few ulp, on the hardware exp2 / log2 / rcp. Above 20 the
+    // correction e^-v is below the fp32 resolution of v. log1p(e) as
+    // log(u) e / (u - 1) with u = 1 + e (the rounding of u cancels: Goldberg's
+    // method); below 2^-24 (u == 1) log1p(e) is e itself.
+    const float e = __builtin_amdgcn_exp2f(v * 1.4426950408889634f);
+    const float u = 1.0f + e;
+    const float l = u == 1.0f ? e
+                              : __builtin_amdgcn_logf(u) * 0.6931471805599453f * e *
+                                    __builtin_amdgcn_rcpf(u - 1.0f);
+    return v > 20.0f ? v : l;
 }
 
 __device__ __forceinline__ float silu_f32(float z) { return z / (1.0f + expf(-z)); }

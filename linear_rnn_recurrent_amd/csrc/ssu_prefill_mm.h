@@ -46,7 +46,7 @@ constexpr int kPmScanWave = 3;  // the wave that forms a chunk's decays (it stag
 
 // LDS layout (bytes) of one workgroup
 struct PmLds {
-    int cs, bs, bt, xt, zs, ys, lc, sf, dp, tot, sb, total;
+    int cs, bs, bt, xt, zs, ys, lc, rq, sf, dp, tot, sb, total;
 };
 __host__ __device__ constexpr int pm_row_pitch(int NS) { return NS * 2 + 16; }   // C, B rows
 __host__ __device__ constexpr int pm_t_pitch() { return kPmTT * 2 + 8; }          // B^T, x^T rows
@@ -64,6 +64,7 @@ __host__ __device__ inline PmLds pm_lds(int NS)
     L.zs = take(kPmTT * pm_z_pitch());       // z [t][row]
     L.ys = take(kPmTT * pm_y_pitch());       // outputs before the gate [t][row], fp32
     L.lc = take(kPmTT * 4);                  // Lc[t] log2(e) (base-2 exponent)
+    L.rq = take(kPmTT * 4);                  // 2^(Lc[j0]-Lc[j]) log2(e), j0 = j's quad start
     L.sf = take(kPmTT * 4);                  // w_j = e^{Lc[last]-Lc[j]} dt'_j
     L.dp = take(kPmTT * 4);                  // dt'_j
     L.tot = take(16);                        // e^{Lc[last]}
@@ -128,6 +129,7 @@ __global__ __launch_bounds__(kPmNT) __attribute__((amdgpu_waves_per_eu(NS <= 128
     unsigned char *Zs = lds + L.zs;
     float *Ys = reinterpret_cast<float *>(lds + L.ys);
     float *lcs = reinterpret_cast<float *>(lds + L.lc);
+    float *rqs = reinterpret_cast<float *>(lds + L.rq);
     float *sfs = reinterpret_cast<float *>(lds + L.sf);
     float *dps = reinterpret_cast<float *>(lds + L.dp);
     float *tot = reinterpret_cast<float *>(lds + L.tot);
@@ -334,8 +336,11 @@ __global__ __launch_bounds__(kPmNT) __attribute__((amdgpu_waves_per_eu(NS <= 128
                 suf += s16;
             // suf includes a_j itself: the weight of x_j in the chunk's end state
             // takes the decays after j only
+            const float l2 = pre * 1.4426950408889634f;
+            const float l2q = dpp_f32<0x00>(l2);  // quad_perm [0,0,0,0]: the quad's first token
             if (lane < TT) {
-                lcs[lane] = pre * 1.4426950408889634f;
+                lcs[lane] = l2;
+                rqs[lane] = __builtin_amdgcn_exp2f(l2q - l2);
                 sfs[lane] = expf(suf - a) * dtp;
                 dps[lane] = dtp;
                 if (stash && rb == 0 && live) {
@@ -411,7 +416,10 @@ __global__ __launch_bounds__(kPmNT) __attribute__((amdgpu_waves_per_eu(NS <= 128
         const float4 lj1 = *reinterpret_cast<const float4 *>(lcs + 16 + 4 * qg);
         const float4 dj0 = *reinterpret_cast<const float4 *>(dps + 4 * qg);
         const float4 dj1 = *reinterpret_cast<const float4 *>(dps + 16 + 4 * qg);
-        const float lj[8] = {lj0.x, lj0.y, lj0.z, lj0.w, lj1.x, lj1.y, lj1.z, lj1.w};
+        const float4 rq0 = *reinterpret_cast<const float4 *>(rqs + 4 * qg);
+        const float4 rq1 = *reinterpret_cast<const float4 *>(rqs + 16 + 4 * qg);
+        // 2^(Lc[t]-Lc[j]) as 2^(Lc[t]-Lc[j0]) 2^(Lc[j0]-Lc[j]): one exp2 per quad
+        const float rj[8] = {rq0.x, rq0.y, rq0.z, rq0.w, rq1.x, rq1.y, rq1.z, rq1.w};
         const float dj[8] = {dj0.x, dj0.y, dj0.z, dj0.w, dj1.x, dj1.y, dj1.z, dj1.w};
         // x^T operand in the same source order: lane (row rl, qg)
         const pm_bf16x8 xop = pm_op(Xt + rl * PT + (4 * qg) * 2);
@@ -419,6 +427,8 @@ __global__ __launch_bounds__(kPmNT) __attribute__((amdgpu_waves_per_eu(NS <= 128
         for (int t = 0; t < 2; ++t) {
             const int tq = 16 * t + ln;  // this lane's token as a Q row
             const float lt = lcs[tq];
+            const float eq0 = __builtin_amdgcn_exp2f(lt - lj0.x);
+            const float eq1 = t == 1 ? __builtin_amdgcn_exp2f(lt - lj1.x) : 0.0f;
             float qv[8];
 #pragma unroll
             for (int e = 0; e < 8; ++e) {
@@ -427,7 +437,7 @@ __global__ __launch_bounds__(kPmNT) __attribute__((amdgpu_waves_per_eu(NS <= 128
                 if (t == 1 || e < 4) {  // sources 16.. lie past every token of tile 0
                     const float gv = e < 4 ? ag[t][e] : ag[2][e - 4];
                     if (j <= tq && tq < nv)
-                        q = __builtin_amdgcn_exp2f(lt - lj[e]) * dj[e] * gv + (j == tq ? dskip : 0.0f);
+                        q = (e < 4 ? eq0 : eq1) * rj[e] * dj[e] * gv + (j == tq ? dskip : 0.0f);
                 }
                 qv[e] = q;
             }
