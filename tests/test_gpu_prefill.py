@@ -102,6 +102,19 @@ def test_row_blocks_and_ragged_dim(dim):
     check_prefill(w, stash=True)
 
 
+@pytest.mark.parametrize("state_dtype", ["f32", "bf16"])
+def test_chunk_boundaries(state_dtype):
+    # bf16 operands take the 32-token chunked closed form: lengths at, around and
+    # across chunk ends, a one-token tail, strong decays (A dt' ~ -8 per token) and
+    # weak ones in the same batch, the stash with the same lengths
+    w = inputs.prefill_workload(batch=8, seq_len=97, nheads=4, dim=64, dstate=128, ngroups=2,
+                                pool_rows=9, seed=31, state_dtype=state_dtype, bc_std=128 ** -0.5,
+                                ctx=[32, 33, 31, 64, 65, 96, 97, 1])
+    w.tensors["dt"][:, :, :2] = w["dt"][:, :, :2].abs() + 2.0
+    check_prefill(w)
+    check_prefill(w, stash=True)
+
+
 def test_large_batch_without_length_sort():
     w = inputs.prefill_workload(batch=300, seq_len=6, nheads=2, dim=64, dstate=16, ngroups=1,
                                 pool_rows=320, seed=8, bc_std=0.25, ctx=("uniform", 0, 6))
