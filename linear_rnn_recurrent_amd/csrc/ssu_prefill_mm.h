@@ -42,7 +42,7 @@ typedef float pm_f32x2 __attribute__((ext_vector_type(2)));
 
 constexpr int kPmTT = 32;   // tokens per chunk (two 16-token MFMA tiles)
 constexpr int kPmNT = 256;  // threads: four waves of 16 rows
-constexpr int kPmScanWave = 3;  // the wave that forms a chunk's decays (it stages no x)
+constexpr int kPmSeg = 16;  // chunks whose decay tables are formed together
 
 // LDS layout (bytes) of one workgroup
 struct PmLds {
@@ -63,11 +63,12 @@ __host__ __device__ inline PmLds pm_lds(int NS)
     L.xt = take(64 * pm_t_pitch());          // x^T [row][j]
     L.zs = take(kPmTT * pm_z_pitch());       // z [t][row]
     L.ys = take(kPmTT * pm_y_pitch());       // outputs before the gate [t][row], fp32
-    L.lc = take(kPmTT * 4);                  // Lc[t] log2(e) (base-2 exponent)
-    L.rq = take(kPmTT * 4);                  // 2^(Lc[j0]-Lc[j]) log2(e), j0 = j's quad start
-    L.sf = take(kPmTT * 4);                  // w_j = e^{Lc[last]-Lc[j]} dt'_j
-    L.dp = take(kPmTT * 4);                  // dt'_j
-    L.tot = take(16);                        // e^{Lc[last]}
+    // decay tables of kPmSeg chunks, [chunk][token]
+    L.lc = take(kPmSeg * kPmTT * 4);         // Lc[t] log2(e) (base-2 exponent)
+    L.rq = take(kPmSeg * kPmTT * 4);         // 2^(Lc[j0]-Lc[j]) log2(e), j0 = j's quad start
+    L.sf = take(kPmSeg * kPmTT * 4);         // w_j = e^{Lc[last]-Lc[j]} dt'_j
+    L.dp = take(kPmSeg * kPmTT * 4);         // dt'_j
+    L.tot = take(kPmSeg * 4);                // e^{Lc[last]}
     L.sb = take(16);                         // the batch row of this workgroup
     L.total = o;
     return L;
@@ -128,11 +129,11 @@ __global__ __launch_bounds__(kPmNT) __attribute__((amdgpu_waves_per_eu(NS <= 128
     unsigned char *Cs = lds + L.cs, *Bs = lds + L.bs, *Bt = lds + L.bt, *Xt = lds + L.xt;
     unsigned char *Zs = lds + L.zs;
     float *Ys = reinterpret_cast<float *>(lds + L.ys);
-    float *lcs = reinterpret_cast<float *>(lds + L.lc);
-    float *rqs = reinterpret_cast<float *>(lds + L.rq);
-    float *sfs = reinterpret_cast<float *>(lds + L.sf);
-    float *dps = reinterpret_cast<float *>(lds + L.dp);
-    float *tot = reinterpret_cast<float *>(lds + L.tot);
+    float *const lcs_all = reinterpret_cast<float *>(lds + L.lc);
+    float *const rqs_all = reinterpret_cast<float *>(lds + L.rq);
+    float *const sfs_all = reinterpret_cast<float *>(lds + L.sf);
+    float *const dps_all = reinterpret_cast<float *>(lds + L.dp);
+    float *const tot_all = reinterpret_cast<float *>(lds + L.tot);
     int *sorted_b = reinterpret_cast<int *>(lds + L.sb);
 
     const int tid = threadIdx.x;
@@ -214,12 +215,6 @@ __global__ __launch_bounds__(kPmNT) __attribute__((amdgpu_waves_per_eu(NS <= 128
     const bool rv = r < Dm;
     ST *srowp = state + (int64_t)srow * sh.row_stride + (int64_t)h * Dm * NS + (int64_t)min(r, Dm - 1) * NS;
     pm_f32x4 S[NT16];
-#pragma unroll
-    for (int nt = 0; nt < NT16; ++nt) {
-#pragma unroll
-        for (int v = 0; v < 4; ++v)
-            S[nt][v] = rv ? ld_elem<ST>(srowp, 16 * nt + 4 * qg + v) : 0.0f;
-    }
 
     // ---- chunk staging: global -> registers (prefetch) -> LDS ----
     // B and C: item v = (token pair p = v % 16, column block cb = v / 16), two
@@ -228,7 +223,6 @@ __global__ __launch_bounds__(kPmNT) __attribute__((amdgpu_waves_per_eu(NS <= 128
     // 8 (tid / 16) ..+7) and x^T the pair as one word per row. z (and the
     // outputs): token tid / 8, rows 8 (tid % 8) ..+7.
     u32x4 rB[NVP][2], rC[NVP][2], rX[2], rZ;
-    float rDt = 0.0f;
     const int xtok = tid >> 3, xr8 = 8 * (tid & 7);  // z / output mapping
     const bool xrv = rbase + xr8 < Dm;               // Dm is a multiple of 8
     const int xp = tid & 15, xb8 = 8 * ((tid >> 4) & 7);  // x mapping (threads < 128)
@@ -252,11 +246,10 @@ __global__ __launch_bounds__(kPmNT) __attribute__((amdgpu_waves_per_eu(NS <= 128
             rX[q] = *reinterpret_cast<const u32x4 *>(
                 xrow + (uint32_t)(((t0 + tok) * NSTR + min(rbase + xb8, Dm - 8)) * 2));
         }
-        if (zrow)
-            rZ = *reinterpret_cast<const u32x4 *>(
-                zrow + (uint32_t)(((t0 + min(xtok, nv - 1)) * NSTR + min(rbase + xr8, Dm - 8)) * 2));
-        if (wave == kPmScanWave && lane < TT)
-            rDt = dtrow[(uint32_t)(min(t0 + lane, t0 + nv - 1) * H)];
+        // (without z the same words of x: a load on every path, never waited for
+        // out of turn)
+        rZ = *reinterpret_cast<const u32x4 *>(
+            (zrow ? zrow : xrow) + (uint32_t)(((t0 + min(xtok, nv - 1)) * NSTR + min(rbase + xr8, Dm - 8)) * 2));
     };
     // 16-bit element i of a 16-byte register group; the elements i of two
     // groups as one word (one v_perm_b32: bytes of the low or high halves)
@@ -313,50 +306,83 @@ __global__ __launch_bounds__(kPmNT) __attribute__((amdgpu_waves_per_eu(NS <= 128
             for (int i = 0; i < 8; ++i)
                 *reinterpret_cast<uint32_t *>(Xt + (xb8 + i) * PT + 4 * xp) = pair16(w[0], w[1], i);
         }
-        if (zrow)
-            *reinterpret_cast<u32x4 *>(Zs + xtok * PZ + xr8 * 2) = rZ;
-        if (wave == kPmScanWave) {
-            // (the wave with the least staging work) lanes < TT: one token each (a = 0, dt' = 0 past the chunk's end);
-            // Lc by an inclusive prefix scan, the suffix sums by a second scan
-            // (not as differences of prefix sums: no cancellation)
-            float v = rDt + bias;
+        *reinterpret_cast<u32x4 *>(Zs + xtok * PZ + xr8 * 2) = rZ;
+    };
+
+    // ---- decay tables of chunks c0 .. c0 + kPmSeg - 1, all four waves: wave w
+    // takes chunk pairs w, w + 4 (lanes 0-31 the first chunk, 32-63 the
+    // second), one token per lane (a = 0, dt' = 0 past the context); Lc by an
+    // inclusive prefix scan, the suffix sums by a second scan (not as
+    // differences of prefix sums: no cancellation) ----
+    auto fill_tables = [&](int c0) {
+        constexpr int NPASS = kPmSeg / 8;
+        float rdt[NPASS];
+#pragma unroll
+        for (int k = 0; k < NPASS; ++k) {
+            const int t = (c0 + 2 * (wave + 4 * k)) * TT + lane;
+            rdt[k] = dtrow[(uint32_t)(min(t, Lb - 1) * H)];
+        }
+#pragma unroll
+        for (int k = 0; k < NPASS; ++k) {
+            const int cl = 2 * (wave + 4 * k) + (lane >> 5);  // chunk within the tables
+            const int t = (c0 + 2 * (wave + 4 * k)) * TT + lane;
+            float v = rdt[k] + bias;
             if (sh.dt_softplus)  // as every other kernel computes it: the same dt' bits
                 v = softplus_f32(v);
-            const bool live = lane < nv;
+            const bool live = t < Lb;
             const float dtp = live ? v : 0.0f;
-            const float a = (live && lane < TT) ? Ah * v : 0.0f;
-            // inclusive prefix and suffix sums over lanes 0 .. 31 (two rows of
-            // 16: row sums by DPP, then the other row's total added)
+            const float a = live ? Ah * v : 0.0f;
+            // inclusive prefix and suffix sums within each 32-lane half (two
+            // rows of 16: row sums by DPP, then the other row's total added)
             float pre = row_prefix_sum16(a), suf = row_suffix_sum16(a);
             const float p15 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, pre), 15));
+            const float p47 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, pre), 47));
             const float s16 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, suf), 16));
-            if (lane >= 16)
+            const float s48 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, suf), 48));
+            const int row = lane >> 4;
+            if (row == 1)
                 pre += p15;
-            if (lane < 16)
+            else if (row == 3)
+                pre += p47;
+            if (row == 0)
                 suf += s16;
+            else if (row == 2)
+                suf += s48;
             // suf includes a_j itself: the weight of x_j in the chunk's end state
             // takes the decays after j only
             const float l2 = pre * 1.4426950408889634f;
             const float l2q = dpp_f32<0x00>(l2);  // quad_perm [0,0,0,0]: the quad's first token
-            if (lane < TT) {
-                lcs[lane] = l2;
-                rqs[lane] = __builtin_amdgcn_exp2f(l2q - l2);
-                sfs[lane] = expf(suf - a) * dtp;
-                dps[lane] = dtp;
-                if (stash && rb == 0 && live) {
-                    sArow[(uint32_t)((t0 + lane) * H)] = a;
-                    sDrow[(uint32_t)((t0 + lane) * H)] = v;
-                }
+            const int o = cl * TT + (lane & 31);
+            lcs_all[o] = l2;
+            rqs_all[o] = __builtin_amdgcn_exp2f(l2q - l2);
+            sfs_all[o] = expf(suf - a) * dtp;
+            dps_all[o] = dtp;
+            if (stash && rb == 0 && live) {
+                sArow[(uint32_t)(t * H)] = a;
+                sDrow[(uint32_t)(t * H)] = v;
             }
-            const float total = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, pre), TT - 1));
-            if (lane == 0)
-                tot[0] = expf(total);
+            if ((lane & 31) == 31)  // the chunk's total decay
+                tot_all[cl] = expf(pre);
         }
     };
 
+    // Every load is consumed on every path: the state and the first chunk
+    // before the loop, each prefetch by the same iteration's store_chunk (the
+    // last iteration loads its own chunk again and stores nothing live). No
+    // load is then outstanding at the loop head on any path, and the chunk's
+    // matrix products do not wait for the prefetch.
     const int nchunks = (Lb + TT - 1) / TT;
     if (nchunks > 0) {
+#pragma unroll
+        for (int nt = 0; nt < NT16; ++nt) {
+            float f[4];  // four consecutive dstate entries (the row pointer is clamped)
+            cvt_raw4<ST>(ld_raw4<ST>(srowp, 16 * nt + 4 * qg), f);
+#pragma unroll
+            for (int v = 0; v < 4; ++v)
+                S[nt][v] = rv ? f[v] : 0.0f;
+        }
         load_chunk(0, min(TT, Lb));
+        fill_tables(0);
         store_chunk(0, min(TT, Lb));
     }
     __syncthreads();
@@ -364,8 +390,18 @@ __global__ __launch_bounds__(kPmNT) __attribute__((amdgpu_waves_per_eu(NS <= 128
     for (int c = 0; c < nchunks; ++c) {
         const int t0 = c * TT;
         const int nv = min(TT, Lb - t0);
-        if (c + 1 < nchunks)
-            load_chunk(t0 + TT, min(TT, Lb - t0 - TT));
+        const int tn = min(t0 + TT, (nchunks - 1) * TT);  // the next chunk, or this one again
+        const int cs = c % kPmSeg;
+        if (cs == 0 && c > 0) {  // the next kPmSeg chunks' tables (their readers are past the barrier)
+            fill_tables(c);
+            __syncthreads();
+        }
+        load_chunk(tn, min(TT, Lb - tn));
+        // the prefetch stays here, a whole chunk of work ahead of its use (the
+        // scheduler would otherwise sink it towards store_chunk to save registers)
+        __builtin_amdgcn_sched_barrier(0);
+        const float *lcs = lcs_all + cs * TT, *rqs = rqs_all + cs * TT;
+        const float *sfs = sfs_all + cs * TT, *dps = dps_all + cs * TT;
 
         // ---- Y^T = C . S^T and G^T = B . C^T over dstate ----
         pm_f32x4 ay[2] = {pm_f32x4{0.0f, 0.0f, 0.0f, 0.0f}, pm_f32x4{0.0f, 0.0f, 0.0f, 0.0f}};
@@ -466,7 +502,7 @@ __global__ __launch_bounds__(kPmNT) __attribute__((amdgpu_waves_per_eu(NS <= 128
                 xw[e] = wj[e] * (float)xop[e];
             pm_bf16x8 xp[3];
             pm_split<3>(xw, xp);
-            const float ws = tot[0];
+            const float ws = tot_all[cs];
 #pragma unroll
             for (int nt = 0; nt < NT16; ++nt) {
                 const pm_bf16x8 bt = pm_op(Bt + (16 * nt + ln) * PT + (4 * qg) * 2);
@@ -499,8 +535,7 @@ __global__ __launch_bounds__(kPmNT) __attribute__((amdgpu_waves_per_eu(NS <= 128
                 ow[i] = __builtin_bit_cast(uint32_t, __builtin_convertvector((pm_f32x2){y[2 * i], y[2 * i + 1]}, pm_bf16x2));
             *reinterpret_cast<u32x4 *>(orow + (uint32_t)(((t0 + xtok) * NSTR + rbase + xr8) * 2)) = ow;
         }
-        if (c + 1 < nchunks)
-            store_chunk(t0 + TT, min(TT, Lb - t0 - TT));
+        store_chunk(t0 + TT, min(TT, Lb - t0 - TT));  // nothing live past the last chunk
         __syncthreads();
     }
 
