@@ -40,50 +40,65 @@ __global__ __launch_bounds__(256) void ssu_segments_kernel(const SegBatch sb)
 }
 
 // invokeMambaStateClear ("Selective State Update" page): zero row `slot` (or
-// every row, slot -1) of the recurrent (blockIdx.z == 0) and conv (== 1) state
-// of layer blockIdx.y, whose pointers come from a device array of
-// MambaStateLayerInfo-like entries. Any alignment: bytes up to the first
-// 16-byte boundary, then 16-byte stores, then the tail bytes.
+// every row, slot -1) of the recurrent and conv state of every layer, whose
+// pointers come from a device array of MambaStateLayerInfo-like entries. A
+// one-dimensional grid of (layer, piece) workgroups, the recurrent pieces of a
+// layer first and then its conv pieces, so that no workgroup is launched
+// without bytes to clear. A layer's pieces interleave in 4 KiB blocks (piece p
+// takes blocks p, p + np, ..), so the workgroups of a layer sweep its range
+// together instead of each writing a separate stretch: fewer write fronts
+// open in the memory at once. Any alignment: the bytes before the first
+// 16-byte boundary and after the last one go to piece 0.
+constexpr uint64_t kClearPiece = 16 * 1024;
+
 __global__ __launch_bounds__(256) void ssu_clear_layers_kernel(const ssu_state_layer *layers,
                                                                int rows, int slot,
                                                                int64_t rec_row_bytes,
-                                                               int64_t conv_row_bytes)
+                                                               int64_t conv_row_bytes,
+                                                               uint32_t nrec, uint32_t nconv)
 {
-    const ssu_state_layer ly = layers[blockIdx.y];
-    uint8_t *base = static_cast<uint8_t *>(blockIdx.z ? ly.conv_state : ly.recurrent_state);
-    const uint64_t rb = (uint64_t)(blockIdx.z ? conv_row_bytes : rec_row_bytes);
+    const uint32_t per = nrec + nconv;
+    const uint32_t l = blockIdx.x / per;
+    const uint32_t k = blockIdx.x - l * per;
+    const bool conv = k >= nrec;
+    const uint64_t piece = conv ? k - nrec : k;
+    uint8_t *base = static_cast<uint8_t *>(conv ? layers[l].conv_state : layers[l].recurrent_state);
+    const uint64_t rb = (uint64_t)(conv ? conv_row_bytes : rec_row_bytes);
     if (base == nullptr || rb == 0)
         return;
     uint8_t *d = base + (slot >= 0 ? (uint64_t)slot * rb : 0);
     const uint64_t n = slot >= 0 ? rb : (uint64_t)rows * rb;
     const uint64_t mis = (uint64_t)((16 - ((uintptr_t)d & 15)) & 15);
     const uint64_t head = mis < n ? mis : n;
-    const uint64_t body = (n - head) / 16;
-    const uint64_t first = (uint64_t)blockIdx.x * blockDim.x + threadIdx.x;
-    const uint64_t step = (uint64_t)gridDim.x * blockDim.x;
-    if (first < head)
-        d[first] = 0;
-    // four 16-byte stores per thread per pass, a workgroup's lanes side by side
-    u32x4 *d4 = reinterpret_cast<u32x4 *>(d + head);
-    const uint64_t b0 = (uint64_t)blockIdx.x * blockDim.x * 4 + threadIdx.x;
-    const uint64_t bstep = (uint64_t)gridDim.x * blockDim.x * 4;
-    for (uint64_t i = b0; i < body; i += bstep) {
-#pragma unroll
-        for (int k = 0; k < 4; ++k)
-            if (i + (uint64_t)k * blockDim.x < body)
-                __builtin_nontemporal_store(u32x4{0u, 0u, 0u, 0u}, &d4[i + (uint64_t)k * blockDim.x]);
+    const uint64_t body = (n - head) / 16;  // 16-byte vectors
+    constexpr uint64_t kVec = kClearPiece / 16;
+    const int tid = threadIdx.x;
+    if (piece == 0) {
+        if ((uint64_t)tid < head)
+            d[tid] = 0;
+        const uint64_t tail = n - head - body * 16;
+        if ((uint64_t)tid < tail)
+            d[head + body * 16 + tid] = 0;
     }
-    for (uint64_t i = head + body * 16 + first; i < n; i += step)
-        d[i] = 0;
+    const uint64_t np = conv ? nconv : nrec;
+    u32x4 *d4 = reinterpret_cast<u32x4 *>(d + head);
+#pragma unroll
+    for (int j = 0; j < (int)(kVec / 256); ++j) {
+        const uint64_t i = ((uint64_t)j * np + piece) * 256 + tid;
+        if (i < body)
+            __builtin_nontemporal_store(u32x4{0u, 0u, 0u, 0u}, &d4[i]);
+    }
 }
 
 // Row moves between a pool and working rows (invokeMambaStateGather /
 // invokeMambaStateScatter, "Selective State Update" page; the activateStep /
 // scatterActive packing of the "Class DeltaNetStatePool" page): workgroup
-// (x, y, z) moves bytes [x * kRowChunk, (x+1) * kRowChunk) of row y of move set
-// z. Streaming 16-byte non-temporal loads and stores when both rows are
-// 16-byte aligned, bytes otherwise.
-constexpr int64_t kRowChunk = 64 * 1024;
+// (x, y, z) moves piece x of row y of move set z. When both rows are 16-byte
+// aligned the row's pieces interleave in 4 KiB blocks (piece x takes blocks
+// x, x + np, ..), each lane issuing its four streaming 16-byte loads before
+// its four stores, so the workgroups of a row sweep it together; otherwise
+// piece x is the byte range [x * kRowPiece, (x+1) * kRowPiece), copied bytewise.
+constexpr int64_t kRowPiece = 16 * 1024;
 
 struct RowMoves {
     RowMove m[2];
@@ -102,38 +117,39 @@ __global__ __launch_bounds__(256) void ssu_row_moves_kernel(const RowMoves rm)
     if (d < 0)
         return;
     const int s = mv.src ? (mv.src_idx ? mv.src_idx[b] : b) : -1;
-    const uint64_t lo = (uint64_t)blockIdx.x * kRowChunk;
     const uint64_t n = (uint64_t)rm.row_bytes;
-    if (lo >= n)
-        return;
-    const uint64_t len = n - lo < (uint64_t)kRowChunk ? n - lo : (uint64_t)kRowChunk;
-    uint8_t *dp = static_cast<uint8_t *>(mv.dst) + (uint64_t)d * mv.dst_stride + lo;
-    const uint8_t *sp =
-        s >= 0 ? static_cast<const uint8_t *>(mv.src) + (uint64_t)s * mv.src_stride + lo : nullptr;
+    const uint64_t x = blockIdx.x, np = gridDim.x;
+    const int tid = threadIdx.x;
+    uint8_t *dp = static_cast<uint8_t *>(mv.dst) + (uint64_t)d * mv.dst_stride;
+    const uint8_t *sp = s >= 0 ? static_cast<const uint8_t *>(mv.src) + (uint64_t)s * mv.src_stride : nullptr;
     const bool aligned = (((uintptr_t)dp | (sp ? (uintptr_t)sp : 0)) & 15) == 0;
-    uint64_t done = 0;
     if (aligned) {
-        const uint64_t nv = len / 16;
+        constexpr int kIt = (int)(kRowPiece / 16 / 256);  // 16-byte vectors per lane
+        const uint64_t nv = n / 16;
         u32x4 *d4 = reinterpret_cast<u32x4 *>(dp);
         const u32x4 *s4 = reinterpret_cast<const u32x4 *>(sp);
-        for (uint64_t i = threadIdx.x; i < nv; i += 4 * blockDim.x) {
-            u32x4 v[4];
+        u32x4 v[kIt];
 #pragma unroll
-            for (int k = 0; k < 4; ++k) {
-                const uint64_t j = i + (uint64_t)k * blockDim.x;
-                v[k] = (s4 && j < nv) ? __builtin_nontemporal_load(&s4[j]) : u32x4{0u, 0u, 0u, 0u};
-            }
-#pragma unroll
-            for (int k = 0; k < 4; ++k) {
-                const uint64_t j = i + (uint64_t)k * blockDim.x;
-                if (j < nv)
-                    __builtin_nontemporal_store(v[k], &d4[j]);
-            }
+        for (int k = 0; k < kIt; ++k) {
+            const uint64_t j = ((uint64_t)k * np + x) * 256 + tid;
+            v[k] = (s4 && j < nv) ? __builtin_nontemporal_load(&s4[j]) : u32x4{0u, 0u, 0u, 0u};
         }
-        done = nv * 16;
+#pragma unroll
+        for (int k = 0; k < kIt; ++k) {
+            const uint64_t j = ((uint64_t)k * np + x) * 256 + tid;
+            if (j < nv)
+                __builtin_nontemporal_store(v[k], &d4[j]);
+        }
+        if (x == 0 && (uint64_t)tid < n - nv * 16)  // tail bytes
+            dp[nv * 16 + tid] = sp ? sp[nv * 16 + tid] : (uint8_t)0;
+        return;
     }
-    for (uint64_t i = done + threadIdx.x; i < len; i += blockDim.x)
-        dp[i] = sp ? sp[i] : (uint8_t)0;
+    const uint64_t lo = x * (uint64_t)kRowPiece;
+    if (lo >= n)
+        return;
+    const uint64_t len = n - lo < (uint64_t)kRowPiece ? n - lo : (uint64_t)kRowPiece;
+    for (uint64_t i = tid; i < len; i += blockDim.x)
+        dp[lo + i] = sp ? sp[lo + i] : (uint8_t)0;
 }
 
 }  // namespace
@@ -153,7 +169,7 @@ hipError_t launch_row_moves(const RowMove *moves, int n, int64_t row_bytes, hipS
         return hipSuccess;
     if (rows > 65535)
         return hipErrorInvalidConfiguration;
-    const uint64_t chunks = ((uint64_t)row_bytes + kRowChunk - 1) / kRowChunk;
+    const uint64_t chunks = ((uint64_t)row_bytes + kRowPiece - 1) / kRowPiece;
     if (chunks > 0x7fffffffull)
         return hipErrorInvalidConfiguration;
     (void)hipGetLastError();
@@ -167,17 +183,20 @@ hipError_t launch_clear_layers(const ssu_state_layer *layers, int num_layers, in
 {
     if (num_layers == 0 || rows == 0)
         return hipSuccess;
-    if (num_layers > 65535)
-        return hipErrorInvalidConfiguration;
-    const uint64_t rb = (uint64_t)(rec_row_bytes > conv_row_bytes ? rec_row_bytes : conv_row_bytes);
-    const uint64_t maxb = slot >= 0 ? rb : (uint64_t)rows * rb;
-    if (maxb == 0)
+    // pieces per layer of each kind (every layer has the same row sizes)
+    auto pieces = [&](int64_t row_bytes) -> uint64_t {
+        const uint64_t n = slot >= 0 ? (uint64_t)row_bytes : (uint64_t)rows * (uint64_t)row_bytes;
+        return (n + kClearPiece - 1) / kClearPiece;
+    };
+    const uint64_t nrec = pieces(rec_row_bytes), nconv = pieces(conv_row_bytes);
+    const uint64_t blocks = (uint64_t)num_layers * (nrec + nconv);
+    if (blocks == 0)
         return hipSuccess;
-    uint64_t blocks = (maxb / 16 + 1023) / 1024;  // 256 threads x 4 vectors each
-    blocks = blocks < 1 ? 1 : (blocks > 2048 ? 2048 : blocks);
+    if (blocks > 0x7fffffffull)
+        return hipErrorInvalidConfiguration;
     (void)hipGetLastError();
-    hipLaunchKernelGGL(ssu_clear_layers_kernel, dim3((unsigned)blocks, (unsigned)num_layers, 2),
-                       dim3(256), 0, stream, layers, rows, slot, rec_row_bytes, conv_row_bytes);
+    hipLaunchKernelGGL(ssu_clear_layers_kernel, dim3((unsigned)blocks), dim3(256), 0, stream, layers,
+                       rows, slot, rec_row_bytes, conv_row_bytes, (uint32_t)nrec, (uint32_t)nconv);
     return hipGetLastError();
 }
 
