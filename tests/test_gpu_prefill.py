@@ -115,6 +115,16 @@ def test_chunk_boundaries(state_dtype):
     check_prefill(w, stash=True)
 
 
+@pytest.mark.parametrize("stash", [False, True])
+def test_long_sequences_past_sixteen_chunks(stash):
+    # bf16 operands: the decay tables cover 16 chunks (512 tokens) and are formed
+    # again every 16 chunks; lengths across the 512- and 1024-token seams, one
+    # just past a seam, one a single token
+    w = inputs.prefill_workload(batch=4, seq_len=1100, nheads=2, dim=64, dstate=128, ngroups=1,
+                                pool_rows=6, seed=41, bc_std=128 ** -0.5, ctx=[1100, 513, 1025, 1])
+    check_prefill(w, stash=stash)
+
+
 def test_large_batch_without_length_sort():
     w = inputs.prefill_workload(batch=300, seq_len=6, nheads=2, dim=64, dstate=16, ngroups=1,
                                 pool_rows=320, seed=8, bc_std=0.25, ctx=("uniform", 0, 6))
