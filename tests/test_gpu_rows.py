@@ -56,6 +56,30 @@ def test_gather_strided_views():
     assert torch.all(act_buf[:, 96:] == 0)      # nothing written past a row
 
 
+@pytest.mark.parametrize("row_floats,stride_floats", [(10, 12), (4101, 4104)])
+def test_gather_aligned_rows_with_tail(row_floats, stride_floats):
+    # 16-byte aligned rows whose length is not a multiple of 16 bytes: whole
+    # vectors in interleaved pieces, the tail bytes by the first piece; the
+    # second case spans two pieces
+    padded = _pool((7, stride_floats), seed=4)
+    pool = padded[:, :row_floats]
+    act_buf = torch.full((4, stride_floats + 4), -3.0).cuda()
+    act = act_buf[:, :row_floats]
+    idx = torch.tensor([5, -1, 0, 6], dtype=torch.int32)
+    src = padded.cuda()[:, :row_floats]                 # row stride stride_floats
+    ssu_state_gather(src, act, idx.cuda())
+    want = oracle.gather(pool.contiguous().numpy(), idx.numpy())
+    np.testing.assert_array_equal(act.cpu().numpy(), want)
+    assert torch.all(act_buf[:, row_floats:] == -3.0)   # nothing written past a row
+    res_buf = padded.clone().cuda()
+    ssu_state_scatter(act, res_buf[:, :row_floats], idx.cuda())
+    ref = padded.clone()
+    ref_np = ref[:, :row_floats].numpy().copy()
+    oracle.scatter(act.cpu().numpy(), ref_np, idx.numpy())
+    ref[:, :row_floats] = torch.from_numpy(ref_np)
+    assert_bitwise(res_buf, ref, "scatter")
+
+
 def _pack_case(rows, homes, bystanders, dtype=torch.float32, seed=3, width=(2, 64, 128)):
     pool = _pool((rows,) + width, dtype, seed)
     h = torch.tensor(homes, dtype=torch.int32).cuda()
