@@ -46,7 +46,7 @@ constexpr int kPmSeg = 16;  // chunks whose decay tables are formed together
 
 // LDS layout (bytes) of one workgroup
 struct PmLds {
-    int cs, bs, bt, xt, zs, ys, lc, rq, sf, dp, tot, sb, total;
+    int cs, bs, bt, xt, zs, ys, lc, rd, sf, tot, sb, total;
 };
 __host__ __device__ constexpr int pm_row_pitch(int NS) { return NS * 2 + 16; }   // C, B rows
 __host__ __device__ constexpr int pm_t_pitch() { return kPmTT * 2 + 8; }          // B^T, x^T rows
@@ -65,9 +65,8 @@ __host__ __device__ inline PmLds pm_lds(int NS)
     L.ys = take(kPmTT * pm_y_pitch());       // outputs before the gate [t][row], fp32
     // decay tables of kPmSeg chunks, [chunk][token]
     L.lc = take(kPmSeg * kPmTT * 4);         // Lc[t] log2(e) (base-2 exponent)
-    L.rq = take(kPmSeg * kPmTT * 4);         // 2^(Lc[j0]-Lc[j]) log2(e), j0 = j's quad start
+    L.rd = take(kPmSeg * kPmTT * 4);         // 2^((Lc[j0]-Lc[j]) log2(e)) dt'_j, j0 = j's quad start
     L.sf = take(kPmSeg * kPmTT * 4);         // w_j = e^{Lc[last]-Lc[j]} dt'_j
-    L.dp = take(kPmSeg * kPmTT * 4);         // dt'_j
     L.tot = take(kPmSeg * 4);                // e^{Lc[last]}
     L.sb = take(16);                         // the batch row of this workgroup
     L.total = o;
@@ -130,9 +129,8 @@ __global__ __launch_bounds__(kPmNT) __attribute__((amdgpu_waves_per_eu(NS <= 128
     unsigned char *Zs = lds + L.zs;
     float *Ys = reinterpret_cast<float *>(lds + L.ys);
     float *const lcs_all = reinterpret_cast<float *>(lds + L.lc);
-    float *const rqs_all = reinterpret_cast<float *>(lds + L.rq);
+    float *const rds_all = reinterpret_cast<float *>(lds + L.rd);
     float *const sfs_all = reinterpret_cast<float *>(lds + L.sf);
-    float *const dps_all = reinterpret_cast<float *>(lds + L.dp);
     float *const tot_all = reinterpret_cast<float *>(lds + L.tot);
     int *sorted_b = reinterpret_cast<int *>(lds + L.sb);
 
@@ -354,9 +352,8 @@ __global__ __launch_bounds__(kPmNT) __attribute__((amdgpu_waves_per_eu(NS <= 128
             const float l2q = dpp_f32<0x00>(l2);  // quad_perm [0,0,0,0]: the quad's first token
             const int o = cl * TT + (lane & 31);
             lcs_all[o] = l2;
-            rqs_all[o] = __builtin_amdgcn_exp2f(l2q - l2);
+            rds_all[o] = __builtin_amdgcn_exp2f(l2q - l2) * dtp;
             sfs_all[o] = expf(suf - a) * dtp;
-            dps_all[o] = dtp;
             if (stash && rb == 0 && live) {
                 sArow[(uint32_t)(t * H)] = a;
                 sDrow[(uint32_t)(t * H)] = v;
@@ -400,8 +397,8 @@ __global__ __launch_bounds__(kPmNT) __attribute__((amdgpu_waves_per_eu(NS <= 128
         // the prefetch stays here, a whole chunk of work ahead of its use (the
         // scheduler would otherwise sink it towards store_chunk to save registers)
         __builtin_amdgcn_sched_barrier(0);
-        const float *lcs = lcs_all + cs * TT, *rqs = rqs_all + cs * TT;
-        const float *sfs = sfs_all + cs * TT, *dps = dps_all + cs * TT;
+        const float *lcs = lcs_all + cs * TT, *rds = rds_all + cs * TT;
+        const float *sfs = sfs_all + cs * TT;
 
         // ---- Y^T = C . S^T and G^T = B . C^T over dstate ----
         pm_f32x4 ay[2] = {pm_f32x4{0.0f, 0.0f, 0.0f, 0.0f}, pm_f32x4{0.0f, 0.0f, 0.0f, 0.0f}};
@@ -450,13 +447,10 @@ __global__ __launch_bounds__(kPmNT) __attribute__((amdgpu_waves_per_eu(NS <= 128
         // j = 4qg + e (e < 4) or 16 + 4qg + e - 4, as the G^T accumulators do ----
         const float4 lj0 = *reinterpret_cast<const float4 *>(lcs + 4 * qg);
         const float4 lj1 = *reinterpret_cast<const float4 *>(lcs + 16 + 4 * qg);
-        const float4 dj0 = *reinterpret_cast<const float4 *>(dps + 4 * qg);
-        const float4 dj1 = *reinterpret_cast<const float4 *>(dps + 16 + 4 * qg);
-        const float4 rq0 = *reinterpret_cast<const float4 *>(rqs + 4 * qg);
-        const float4 rq1 = *reinterpret_cast<const float4 *>(rqs + 16 + 4 * qg);
-        // 2^(Lc[t]-Lc[j]) as 2^(Lc[t]-Lc[j0]) 2^(Lc[j0]-Lc[j]): one exp2 per quad
-        const float rj[8] = {rq0.x, rq0.y, rq0.z, rq0.w, rq1.x, rq1.y, rq1.z, rq1.w};
-        const float dj[8] = {dj0.x, dj0.y, dj0.z, dj0.w, dj1.x, dj1.y, dj1.z, dj1.w};
+        const float4 rd0 = *reinterpret_cast<const float4 *>(rds + 4 * qg);
+        const float4 rd1 = *reinterpret_cast<const float4 *>(rds + 16 + 4 * qg);
+        // 2^(Lc[t]-Lc[j]) dt'_j as 2^(Lc[t]-Lc[j0]) (2^(Lc[j0]-Lc[j]) dt'_j): one exp2 per quad
+        const float rd[8] = {rd0.x, rd0.y, rd0.z, rd0.w, rd1.x, rd1.y, rd1.z, rd1.w};
         // x^T operand in the same source order: lane (row rl, qg)
         const pm_bf16x8 xop = pm_op(Xt + rl * PT + (4 * qg) * 2);
 #pragma unroll
@@ -472,8 +466,10 @@ __global__ __launch_bounds__(kPmNT) __attribute__((amdgpu_waves_per_eu(NS <= 128
                 float q = 0.0f;
                 if (t == 1 || e < 4) {  // sources 16.. lie past every token of tile 0
                     const float gv = e < 4 ? ag[t][e] : ag[2][e - 4];
-                    if (j <= tq && tq < nv)
-                        q = (e < 4 ? eq0 : eq1) * rj[e] * dj[e] * gv + (j == tq ? dskip : 0.0f);
+                    // (rows t past the chunk's end are formed too but never stored;
+                    // their sources past the end have dt' = 0)
+                    if (j <= tq)
+                        q = (e < 4 ? eq0 : eq1) * rd[e] * gv + (j == tq ? dskip : 0.0f);
                 }
                 qv[e] = q;
             }
