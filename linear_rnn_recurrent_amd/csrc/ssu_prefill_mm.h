@@ -15,8 +15,8 @@
 // and wave (16 rows of dim), all v_mfma_f32_16x16x32_bf16:
 //   Y^T  = C . S^T            (inter-chunk term; S as bf16 hi + lo)
 //   G^T  = B . C^T            (the B_j . C_t dots, lower triangle)
-//   Y^T += Q . X^T            (Q[t][j] = e^{Lc[t]-Lc[j]} dt'_j G[t][j], D on
-//                              the diagonal; Q as bf16 hi + lo)
+//   Y^T += Q . X^T            (Q[t][j] = e^{Lc[t]-Lc[j]} dt'_j G[t][j]; Q as
+//                              bf16 hi + lo; D x_t added in fp32 after it)
 //   S^T  = e^{Lc[last]} S^T + B^T . X'^T   (X'[r][j] = w_j x_j[r], w_j the
 //                              suffix weight; X' as three bf16 terms, so the
 //                              carried fp32 state keeps fp32 accuracy)
@@ -469,7 +469,7 @@ __global__ __launch_bounds__(kPmNT) __attribute__((amdgpu_waves_per_eu(NS <= 128
                     // (rows t past the chunk's end are formed too but never stored;
                     // their sources past the end have dt' = 0)
                     if (j <= tq)
-                        q = (e < 4 ? eq0 : eq1) * rd[e] * gv + (j == tq ? dskip : 0.0f);
+                        q = (e < 4 ? eq0 : eq1) * rd[e] * gv;
                 }
                 qv[e] = q;
             }
@@ -478,6 +478,17 @@ __global__ __launch_bounds__(kPmNT) __attribute__((amdgpu_waves_per_eu(NS <= 128
 #pragma unroll
             for (int uu = 0; uu < 2; ++uu)
                 ay[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qp[uu], xop, ay[t], 0, 0, 0);
+        }
+        // D x_t in fp32: the x^T operand holds x of tokens 4qg + v (elements
+        // 0-3) and 16 + 4qg + v (4-7) of row rl, the tokens of ay[0][v], ay[1][v]
+        float xf[8];
+#pragma unroll
+        for (int e = 0; e < 8; ++e)
+            xf[e] = (float)xop[e];
+#pragma unroll
+        for (int v = 0; v < 4; ++v) {
+            ay[0][v] = fmaf(dskip, xf[v], ay[0][v]);
+            ay[1][v] = fmaf(dskip, xf[4 + v], ay[1][v]);
         }
 
         // outputs before the gate: Ys[t][row]
@@ -495,7 +506,7 @@ __global__ __launch_bounds__(kPmNT) __attribute__((amdgpu_waves_per_eu(NS <= 128
             float xw[8];
 #pragma unroll
             for (int e = 0; e < 8; ++e)
-                xw[e] = wj[e] * (float)xop[e];
+                xw[e] = wj[e] * xf[e];
             pm_bf16x8 xp[3];
             pm_split<3>(xw, xp);
             const float ws = tot_all[cs];
