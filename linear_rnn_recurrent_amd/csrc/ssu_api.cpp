@@ -1,6 +1,7 @@
 // C ABI of libssu: host-side argument checks, dispatch to the kernel
 // launchers, and the recurrent-state pool. No entry point reads device memory
 // on the host, synchronises, or allocates, except ssu_pool_alloc/ssu_pool_free.
+#include <atomic>
 #include <math.h>
 #include <stdarg.h>
 #include <stdio.h>
@@ -114,17 +115,20 @@ size_t io_bytes(int32_t dt) { return dt == SSU_F32 ? 4 : 2; }
 // query; no device work, no synchronisation). 0 if the query fails.
 int32_t current_cu_count()
 {
-    static int32_t cache[64] = {0};
+    static std::atomic<int32_t> cache[64];  // zero-initialised; benign races between host threads
     int dev = 0;
     if (hipGetDevice(&dev) != hipSuccess || dev < 0)
         return 0;
-    if (dev < 64 && cache[dev] > 0)
-        return cache[dev];
+    if (dev < 64) {
+        const int32_t c = cache[dev].load(std::memory_order_relaxed);
+        if (c > 0)
+            return c;
+    }
     int n = 0;
     if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
         return 0;
     if (dev < 64)
-        cache[dev] = n;
+        cache[dev].store(n, std::memory_order_relaxed);
     return n;
 }
 

@@ -28,6 +28,7 @@
 // holds it, so Q is formed in registers.
 #pragma once
 
+#include <atomic>
 #include "ssu_device.h"
 #include "ssu_dpp.h"
 #include "ssu_internal.h"
@@ -589,18 +590,18 @@ hipError_t launch_prefill_mm(const PrefillParams &p, const PrefillShape &sh, hip
     auto kern = ssu_prefill_mm_kernel<ST, NS>;
     if (lds > 64 * 1024) {
         // above 64 KiB of dynamic LDS the kernel must be allowed it, once per device
-        static int allowed[64] = {0};
+        static std::atomic<int> allowed[64];  // zero-initialised; benign races between host threads
         int dev = 0;
         hipError_t e = hipGetDevice(&dev);
         if (e != hipSuccess)
             return e;
-        if (dev < 0 || dev >= 64 || !allowed[dev]) {
+        if (dev < 0 || dev >= 64 || !allowed[dev].load(std::memory_order_relaxed)) {
             e = hipFuncSetAttribute(reinterpret_cast<const void *>(kern),
                                     hipFuncAttributeMaxDynamicSharedMemorySize, lds);
             if (e != hipSuccess)
                 return e;
             if (dev >= 0 && dev < 64)
-                allowed[dev] = 1;
+                allowed[dev].store(1, std::memory_order_relaxed);
         }
     }
     (void)hipGetLastError();

@@ -54,6 +54,7 @@
 //      registers of step 1; then D x, gate, store.
 #pragma once
 
+#include <atomic>
 #include "ssu_device.h"
 #include "ssu_dpp.h"
 #include "ssu_internal.h"
@@ -834,19 +835,19 @@ hipError_t launch_tree_cfg(const TreeParams &p, hipStream_t stream)
         // Above 64 KiB of dynamic LDS the kernel must be allowed it first, once
         // per device: raise the limit to the largest tree this kernel can get,
         // so that later launches (under stream capture too) need no call.
-        static int allowed[64] = {0};
+        static std::atomic<int> allowed[64];  // zero-initialised; benign races between host threads
         int dev = 0;
         hipError_t e = hipGetDevice(&dev);
         if (e != hipSuccess)
             return e;
-        if (dev < 0 || dev >= 64 || allowed[dev] < L.total) {
+        if (dev < 0 || dev >= 64 || allowed[dev].load(std::memory_order_relaxed) < L.total) {
             const int most = tree_lds(SSU_MAX_TREE_NODES, NS, XB, BB).total;
             e = hipFuncSetAttribute(reinterpret_cast<const void *>(kern),
                                     hipFuncAttributeMaxDynamicSharedMemorySize, most);
             if (e != hipSuccess)
                 return e;
             if (dev >= 0 && dev < 64)
-                allowed[dev] = most;
+                allowed[dev].store(most, std::memory_order_relaxed);
         }
     }
     (void)hipGetLastError();
