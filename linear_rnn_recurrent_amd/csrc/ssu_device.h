@@ -12,6 +12,19 @@ enum : int { kF32 = 0, kF16 = 1, kBF16 = 2 };
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 
+// A buffer pointer read from a device-side table is generic to the compiler,
+// so accesses through it become flat instructions (which also count against
+// the LDS/scalar wait counter). Re-deriving it from a kernel-argument pointer
+// by its byte distance gives the same address as a global-memory pointer:
+// valid for every buffer the library accepts (device or host-mapped memory,
+// never LDS or scratch).
+template <typename T>
+__device__ __forceinline__ T *table_ptr(const void *anchor, const void *p)
+{
+    const char *a = static_cast<const char *>(anchor);
+    return reinterpret_cast<T *>(const_cast<char *>(a + (reinterpret_cast<uintptr_t>(p) - reinterpret_cast<uintptr_t>(a))));
+}
+
 // Storage tag for a bf16 state element (no arithmetic is done on it).
 struct bf16_t {
     uint16_t bits;

@@ -62,10 +62,11 @@ __global__ __launch_bounds__(256) void ssu_clear_layers_kernel(const ssu_state_l
     const uint32_t k = blockIdx.x - l * per;
     const bool conv = k >= nrec;
     const uint64_t piece = conv ? k - nrec : k;
-    uint8_t *base = static_cast<uint8_t *>(conv ? layers[l].conv_state : layers[l].recurrent_state);
+    const void *raw = conv ? layers[l].conv_state : layers[l].recurrent_state;
     const uint64_t rb = (uint64_t)(conv ? conv_row_bytes : rec_row_bytes);
-    if (base == nullptr || rb == 0)
+    if (raw == nullptr || rb == 0)  // (tested before re-deriving: a derived pointer is never null to the compiler)
         return;
+    uint8_t *base = table_ptr<uint8_t>(layers, raw);
     uint8_t *d = base + (slot >= 0 ? (uint64_t)slot * rb : 0);
     const uint64_t n = slot >= 0 ? rb : (uint64_t)rows * rb;
     const uint64_t mis = (uint64_t)((16 - ((uintptr_t)d & 15)) & 15);

@@ -44,11 +44,11 @@ __global__ __launch_bounds__(256) void ssu_replay_kernel(
 {
     if (layers) {  // batched over layers: this workgroup's layer is blockIdx.y
         const ssu_replay_layer &ly = layers[blockIdx.y];
-        state = static_cast<ST *>(ly.state);
-        sdA = ly.replay_dA;
-        su = ly.replay_u;
-        sB = ly.replay_B;
-        sdt = ly.replay_dt;
+        state = table_ptr<ST>(layers, ly.state);
+        sdA = table_ptr<const float>(layers, ly.replay_dA);
+        su = table_ptr<const float>(layers, ly.replay_u);
+        sB = table_ptr<const float>(layers, ly.replay_B);
+        sdt = table_ptr<const float>(layers, ly.replay_dt);
     }
     constexpr int VEC = SV<ST>::VEC;
     constexpr int LPR = NS / VEC;
