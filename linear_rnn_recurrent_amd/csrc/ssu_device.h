@@ -14,15 +14,14 @@ typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 
 // A buffer pointer read from a device-side table is generic to the compiler,
 // so accesses through it become flat instructions (which also count against
-// the LDS/scalar wait counter). Re-deriving it from a kernel-argument pointer
-// by its byte distance gives the same address as a global-memory pointer:
-// valid for every buffer the library accepts (device or host-mapped memory,
-// never LDS or scratch).
+// the LDS/scalar wait counter). Converting its address to a global-memory
+// pointer lets them compile to global instructions: valid for every buffer the
+// library accepts (device or host-mapped memory, never LDS or scratch), whose
+// global and generic addresses are the same.
 template <typename T>
-__device__ __forceinline__ T *table_ptr(const void *anchor, const void *p)
+__device__ __forceinline__ T *table_ptr(const void *p)
 {
-    const char *a = static_cast<const char *>(anchor);
-    return reinterpret_cast<T *>(const_cast<char *>(a + (reinterpret_cast<uintptr_t>(p) - reinterpret_cast<uintptr_t>(a))));
+    return (T *)(__attribute__((address_space(1))) T *)reinterpret_cast<uintptr_t>(p);
 }
 
 // Storage tag for a bf16 state element (no arithmetic is done on it).

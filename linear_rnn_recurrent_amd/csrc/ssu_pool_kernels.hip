@@ -64,9 +64,9 @@ __global__ __launch_bounds__(256) void ssu_clear_layers_kernel(const ssu_state_l
     const uint64_t piece = conv ? k - nrec : k;
     const void *raw = conv ? layers[l].conv_state : layers[l].recurrent_state;
     const uint64_t rb = (uint64_t)(conv ? conv_row_bytes : rec_row_bytes);
-    if (raw == nullptr || rb == 0)  // (tested before re-deriving: a derived pointer is never null to the compiler)
+    if (raw == nullptr || rb == 0)
         return;
-    uint8_t *base = table_ptr<uint8_t>(layers, raw);
+    uint8_t *base = table_ptr<uint8_t>(raw);
     uint8_t *d = base + (slot >= 0 ? (uint64_t)slot * rb : 0);
     const uint64_t n = slot >= 0 ? rb : (uint64_t)rows * rb;
     const uint64_t mis = (uint64_t)((16 - ((uintptr_t)d & 15)) & 15);

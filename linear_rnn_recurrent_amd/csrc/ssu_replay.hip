@@ -44,11 +44,11 @@ __global__ __launch_bounds__(256) void ssu_replay_kernel(
 {
     if (layers) {  // batched over layers: this workgroup's layer is blockIdx.y
         const ssu_replay_layer &ly = layers[blockIdx.y];
-        state = table_ptr<ST>(layers, ly.state);
-        sdA = table_ptr<const float>(layers, ly.replay_dA);
-        su = table_ptr<const float>(layers, ly.replay_u);
-        sB = table_ptr<const float>(layers, ly.replay_B);
-        sdt = table_ptr<const float>(layers, ly.replay_dt);
+        state = table_ptr<ST>(ly.state);
+        sdA = table_ptr<const float>(ly.replay_dA);
+        su = table_ptr<const float>(ly.replay_u);
+        sB = table_ptr<const float>(ly.replay_B);
+        sdt = table_ptr<const float>(ly.replay_dt);
     }
     constexpr int VEC = SV<ST>::VEC;
     constexpr int LPR = NS / VEC;
