@@ -28,7 +28,9 @@
 // holds it, so Q is formed in registers.
 #pragma once
 
+#include <algorithm>
 #include <atomic>
+#include <type_traits>
 #include "ssu_device.h"
 #include "ssu_dpp.h"
 #include "ssu_internal.h"
@@ -47,7 +49,7 @@ constexpr int kPmSeg = 16;  // chunks whose decay tables are formed together
 
 // LDS layout (bytes) of one workgroup
 struct PmLds {
-    int cs, bs, bt, xt, zs, ys, lc, rd, sf, tot, sb, total;
+    int cs, bs, bt, xt, zs, ys, lc, rd, sf, tot, big, sb, total;
 };
 __host__ __device__ constexpr int pm_row_pitch(int NS) { return NS * 2 + 16; }   // C, B rows
 __host__ __device__ constexpr int pm_t_pitch() { return kPmTT * 2 + 8; }          // B^T, x^T rows
@@ -67,8 +69,10 @@ __host__ __device__ inline PmLds pm_lds(int NS)
     // decay tables of kPmSeg chunks, [chunk][token]
     L.lc = take(kPmSeg * kPmTT * 4);         // Lc[t] log2(e) (base-2 exponent)
     L.rd = take(kPmSeg * kPmTT * 4);         // 2^((Lc[j0]-Lc[j]) log2(e)) dt'_j, j0 = j's quad start
+                                             // (dt'_j alone in a chunk marked in `big`)
     L.sf = take(kPmSeg * kPmTT * 4);         // w_j = e^{Lc[last]-Lc[j]} dt'_j
     L.tot = take(kPmSeg * 4);                // e^{Lc[last]}
+    L.big = take(kPmSeg * 4);                // 1: a quad of the chunk spans more than 2^64 of decay
     L.sb = take(16);                         // the batch row of this workgroup
     L.total = o;
     return L;
@@ -133,6 +137,7 @@ __global__ __launch_bounds__(kPmNT) __attribute__((amdgpu_waves_per_eu(NS <= 128
     float *const rds_all = reinterpret_cast<float *>(lds + L.rd);
     float *const sfs_all = reinterpret_cast<float *>(lds + L.sf);
     float *const tot_all = reinterpret_cast<float *>(lds + L.tot);
+    int *const big_all = reinterpret_cast<int *>(lds + L.big);
     int *sorted_b = reinterpret_cast<int *>(lds + L.sb);
 
     const int tid = threadIdx.x;
@@ -347,14 +352,26 @@ __global__ __launch_bounds__(kPmNT) __attribute__((amdgpu_waves_per_eu(NS <= 128
                 suf += s16;
             else if (row == 2)
                 suf += s48;
-            // suf includes a_j itself: the weight of x_j in the chunk's end state
-            // takes the decays after j only
+            // suf includes a_j itself; the weight of x_j in the chunk's end state
+            // takes the decays after j only: the next token's suffix sum (taken
+            // as it is, not as suf - a_j, which loses the small sum after an
+            // extreme decay to cancellation)
+            float after = __shfl_down(suf, 1, 64);
+            if ((lane & 31) == 31)
+                after = 0.0f;
             const float l2 = pre * 1.4426950408889634f;
             const float l2q = dpp_f32<0x00>(l2);  // quad_perm [0,0,0,0]: the quad's first token
+            // Q's per-quad factoring 2^(Lc[t]-Lc[j0]) * 2^(Lc[j0]-Lc[j]) overflows
+            // (inf * 0) once a quad's decays span more than ~2^127; chunks with a
+            // span above 2^64 form every Q entry from its own exponent instead
+            const uint64_t wide = __ballot(!(fabsf(l2q - l2) <= 64.0f));
+            const bool big = ((lane & 32) ? (wide >> 32) : (wide & 0xffffffffull)) != 0;
             const int o = cl * TT + (lane & 31);
             lcs_all[o] = l2;
-            rds_all[o] = __builtin_amdgcn_exp2f(l2q - l2) * dtp;
-            sfs_all[o] = expf(suf - a) * dtp;
+            rds_all[o] = big ? dtp : __builtin_amdgcn_exp2f(l2q - l2) * dtp;
+            sfs_all[o] = expf(after) * dtp;
+            if ((lane & 31) == 0)
+                big_all[cl] = big ? 1 : 0;
             if (stash && rb == 0 && live) {
                 sArow[(uint32_t)(t * H)] = a;
                 sDrow[(uint32_t)(t * H)] = v;
@@ -452,14 +469,15 @@ __global__ __launch_bounds__(kPmNT) __attribute__((amdgpu_waves_per_eu(NS <= 128
         const float4 rd1 = *reinterpret_cast<const float4 *>(rds + 16 + 4 * qg);
         // 2^(Lc[t]-Lc[j]) dt'_j as 2^(Lc[t]-Lc[j0]) (2^(Lc[j0]-Lc[j]) dt'_j): one exp2 per quad
         const float rd[8] = {rd0.x, rd0.y, rd0.z, rd0.w, rd1.x, rd1.y, rd1.z, rd1.w};
+        const float lj[8] = {lj0.x, lj0.y, lj0.z, lj0.w, lj1.x, lj1.y, lj1.z, lj1.w};
         // x^T operand in the same source order: lane (row rl, qg)
         const pm_bf16x8 xop = pm_op(Xt + rl * PT + (4 * qg) * 2);
-#pragma unroll
-        for (int t = 0; t < 2; ++t) {
+        // Q of token tile t: per quad, or (chunks with extreme decays) per entry
+        auto q_tile = [&](auto per_entry, int t) {
             const int tq = 16 * t + ln;  // this lane's token as a Q row
             const float lt = lcs[tq];
-            const float eq0 = __builtin_amdgcn_exp2f(lt - lj0.x);
-            const float eq1 = t == 1 ? __builtin_amdgcn_exp2f(lt - lj1.x) : 0.0f;
+            const float eq0 = per_entry ? 0.0f : __builtin_amdgcn_exp2f(lt - lj0.x);
+            const float eq1 = (per_entry || t == 0) ? 0.0f : __builtin_amdgcn_exp2f(lt - lj1.x);
             float qv[8];
 #pragma unroll
             for (int e = 0; e < 8; ++e) {
@@ -469,8 +487,10 @@ __global__ __launch_bounds__(kPmNT) __attribute__((amdgpu_waves_per_eu(NS <= 128
                     const float gv = e < 4 ? ag[t][e] : ag[2][e - 4];
                     // (rows t past the chunk's end are formed too but never stored;
                     // their sources past the end have dt' = 0)
-                    if (j <= tq)
-                        q = (e < 4 ? eq0 : eq1) * rd[e] * gv;
+                    if (j <= tq) {
+                        const float f = per_entry ? __builtin_amdgcn_exp2f(lt - lj[e]) : (e < 4 ? eq0 : eq1);
+                        q = f * rd[e] * gv;
+                    }
                 }
                 qv[e] = q;
             }
@@ -479,6 +499,15 @@ __global__ __launch_bounds__(kPmNT) __attribute__((amdgpu_waves_per_eu(NS <= 128
 #pragma unroll
             for (int uu = 0; uu < 2; ++uu)
                 ay[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qp[uu], xop, ay[t], 0, 0, 0);
+        };
+        if (__builtin_amdgcn_readfirstlane(big_all[cs]) != 0) {
+#pragma unroll
+            for (int t = 0; t < 2; ++t)
+                q_tile(std::true_type{}, t);
+        } else {
+#pragma unroll
+            for (int t = 0; t < 2; ++t)
+                q_tile(std::false_type{}, t);
         }
         // D x_t in fp32: the x^T operand holds x of tokens 4qg + v (elements
         // 0-3) and 16 + 4qg + v (4-7) of row rl, the tokens of ay[0][v], ay[1][v]
@@ -614,11 +643,16 @@ hipError_t launch_prefill_mm(const PrefillParams &p, const PrefillShape &sh, hip
 // The matrix-core prefill takes bf16 x/z/out and B/C (exact operands), dstate a
 // multiple of 32, dim a multiple of 8 and 16-byte aligned x, z, out and x
 // stash (whole 8-row vectors); everything else runs on ssu_prefill_kernel.
+// Offsets within one batch row's tokens are formed in 32 bits: a row's x, z,
+// out, B and C (and the fp32 x and B stash) must span under 2^31 bytes, with a
+// factor of two to spare.
 inline bool prefill_mm_fits(const PrefillParams &p)
 {
     const DecodeParams &d = p.d;
     auto al16 = [](const void *q) { return (reinterpret_cast<uintptr_t>(q) & 15) == 0; };
-    return d.io_dtype == kBF16 && d.bc_dtype == kBF16 && d.dstate % 32 == 0 && d.dim % 8 == 0 &&
+    const int64_t per_token = std::max((int64_t)d.nheads * d.dim, (int64_t)d.ngroups * d.dstate);
+    const bool offsets_fit = (int64_t)p.seq_len * per_token * 4 < ((int64_t)1 << 31);
+    return offsets_fit && d.io_dtype == kBF16 && d.bc_dtype == kBF16 && d.dstate % 32 == 0 && d.dim % 8 == 0 &&
            al16(d.x) && al16(d.out) && (d.z == nullptr || al16(d.z)) &&
            (p.st_u == nullptr || al16(p.st_u)) && p.waves_per_wg == 0;
 }

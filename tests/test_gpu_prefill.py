@@ -67,6 +67,20 @@ def test_config2_stash_mode_full_size():
     check_prefill(inputs.config(2), stash=True)
 
 
+@pytest.mark.parametrize("stash", [False, True])
+@pytest.mark.parametrize("io", ["f32", "f16"])
+def test_config2_shape_on_the_valu_kernel(io, stash):
+    # config 2's shape and recipe with fp32 or fp16 x/z/B/C: the rescaled VALU
+    # recurrence over up to 512 tokens, where the running product of decays
+    # (sum of A dt' near -100 at full length) leaves [1e-30, 1e30] and the
+    # state is renormalised at a chunk start
+    w = inputs.prefill_workload(batch=8, seq_len=512, nheads=80, dim=64, dstate=128,
+                                ngroups=1, pool_rows=64, seed=2, state_dtype="f32",
+                                io_dtype=io, bc_dtype=io, bc_std=1.0 / np.sqrt(128),
+                                ctx=("uniform", 64, 512), zero_state=True)
+    check_prefill(w, stash=stash)
+
+
 @pytest.mark.parametrize("dstate", [16, 32, 64, 128, 256])
 @pytest.mark.parametrize("state_dtype", ["f32", "f16", "bf16"])
 def test_dstate_and_state_dtype_matrix(dstate, state_dtype):
