@@ -30,8 +30,13 @@ shorter than the binding's per-call host time).
 Prints one JSON line: value = algorithmic GB/s (bytes the method must move,
 each element counted once, divided by the average launch time measured with
 HIP events on the launch stream), plus token*head updates/s, the roofline
-object of the timed kernel and the fp64 oracle's throughput on the host
-(cpu_baseline, a reported baseline and not a target).
+object of the timed kernel (HBM for every configuration; prefill and tree
+verify also report their rate on the bf16 matrix cores they run on), the
+flushed protocol (--flushed launches timed one by one, each after a 1 GiB
+scratch write that evicts the last-level cache: median, p10, p90) with a
+device-to-device copy rate as context, and the fp64 oracle's throughput on
+the host (cpu_baseline: all threads and one thread, CPU model; a reported
+baseline, not a target).
 """
 import argparse
 import hashlib
@@ -44,7 +49,10 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0            # MI355X HBM3E, 8 TB/s
-MFMA_F32_PEAK_TFLOPS = 157.3                     # dense fp32 matrix-core peak
+MFMA_BF16_PEAK_TFLOPS = 2500.0   # dense bf16 matrix-core peak (the instruction the
+                                 # prefill and tree kernels issue)
+MFMA_F32_PEAK_TFLOPS = 157.3     # dense fp32 matrix-core peak (context only)
+FLUSH_BYTES = 1 << 30            # scratch written before each individually timed launch
 
 
 def metric_name():
@@ -131,6 +139,15 @@ def prefill_mm_fmas(T, L, chunk=32):
             pairs = nv * (nv + 1) // 2
             f += h * (2 * nv * d * n + pairs * d) + g * pairs * n
     return f
+
+
+def prefill_method_flops(T, L):
+    """Flops of the method itself, 5 per state element and token (decay multiply,
+    the B dt' x FMA and the C dot FMA), over the live rows' tokens."""
+    b, t, h, d = T["x"].shape
+    n = T["B"].shape[3]
+    idx = T["state_indices"].cpu().tolist() if T["state_indices"] is not None else list(range(b))
+    return 5 * h * d * n * sum(int(Lb) for r, Lb in enumerate(L) if idx[r] >= 0)
 
 
 def tree_lane_ops(T):
@@ -270,17 +287,79 @@ def cpu_baseline(kind, w, seconds, bytes_per_call, units_per_call):
         else:
             sample = f"{reps} of the {inputs_mod.STACK_LAYERS} layers per call"
             scale = reps / inputs_mod.STACK_LAYERS
-    calls, t0 = 0, time.perf_counter()
-    while True:
-        call()
-        calls += 1
-        el = time.perf_counter() - t0
-        if el >= seconds:
-            break
+    def timed(limit):
+        calls, t0 = 0, time.perf_counter()
+        while True:
+            call()
+            calls += 1
+            el = time.perf_counter() - t0
+            if el >= limit:
+                return calls, el
+
+    threads = oracle.num_threads()
+    calls, el = timed(seconds)
     gbs = bytes_per_call * scale * calls / el / 1e9
-    return {"value": round(gbs, 4), "unit": "GB/s", "cores": oracle.num_threads(), "kind": "oracle",
+    # the same sample on one thread (a single call at least)
+    oracle.set_num_threads(1)
+    try:
+        calls1, el1 = timed(seconds / 3)
+    finally:
+        oracle.set_num_threads(threads)
+    return {"value": round(gbs, 4), "unit": "GB/s", "cores": threads, "kind": "oracle",
             "sample": f"{sample}, {calls} call(s) in {el:.1f} s (fp64, OpenMP)",
-            "token_head_updates_per_s": units_per_call * scale * calls / el}
+            "cpu_model": cpu_model(),
+            "token_head_updates_per_s": units_per_call * scale * calls / el,
+            "single_thread": {"value": round(bytes_per_call * scale * calls1 / el1 / 1e9, 4),
+                              "unit": "GB/s", "calls": calls1, "seconds": round(el1, 2)}}
+
+
+def cpu_model():
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+def flushed_launches(step, first, n, warm, dev):
+    """Per-launch times (us) of n steps, each preceded by a write of FLUSH_BYTES
+    of scratch outside its event pair, so that no step finds its data in the
+    last-level cache; warm untimed flushed steps first."""
+    import torch
+    scratch = torch.empty(FLUSH_BYTES // 4, dtype=torch.float32, device=dev)
+    evs = []
+    for i in range(warm + n):
+        scratch.fill_(float(i))
+        a = torch.cuda.Event(enable_timing=True)
+        b = torch.cuda.Event(enable_timing=True)
+        a.record()
+        step(first + i)
+        b.record()
+        if i >= warm:
+            evs.append((a, b))
+    torch.cuda.synchronize()
+    del scratch
+    return sorted(a.elapsed_time(b) * 1e3 for a, b in evs)
+
+
+def copy_bandwidth(dev, nbytes=1 << 30, reps=10):
+    """Device-to-device copy rate (bytes read + written per second): the
+    achievable streaming rate on this machine, as context for the HBM peak."""
+    import torch
+    src = torch.ones(nbytes // 4, dtype=torch.float32, device=dev)
+    dst = torch.empty_like(src)
+    dst.copy_(src)
+    torch.cuda.synchronize()
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    a.record()
+    for _ in range(reps):
+        dst.copy_(src)
+    b.record()
+    torch.cuda.synchronize()
+    return 2 * nbytes * reps / (a.elapsed_time(b) * 1e-3) / 1e9
 
 
 def main():
@@ -295,6 +374,9 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-graph", action="store_true",
                     help="launch the timed steps one by one from Python instead of one HIP graph")
+    ap.add_argument("--flushed", type=int, default=100,
+                    help="after the graph-timed steps, time this many launches one by one, each "
+                         "after a 1 GiB scratch write (median, p10, p90); 0 skips it")
     ap.add_argument("--copy-mib", type=int, default=0,
                     help="after the timed steps, one plain device copy of this many MiB "
                          "(a known-size kernel for scaling memory-traffic counters)")
@@ -340,6 +422,7 @@ def main():
             reps.append(r)
         return reps
 
+    matrix = None
     if args.config in (1, 3):
         kind = "decode"
         B = T["x"].shape[0]
@@ -368,9 +451,9 @@ def main():
         L = T["context_lengths"].clamp(0, T["x"].shape[1]).cpu().tolist()
         nbytes = prefill_bytes(T, L)
         units = sum(L) * T["x"].shape[2]
-        reps = replicas(["x", "z", "B", "C", "dt", "state"], 2)
+        reps = replicas(["x", "z", "B", "C", "dt", "state"], 4)
         outs = [torch.empty_like(T["x"]) for _ in reps]
-        rot = "steps alternate 2 replicas of the pool and of every input and output"
+        rot = "steps rotate 4 replicas of the pool and of every input and output"
 
         def step(i):
             R = reps[i % len(reps)]
@@ -380,8 +463,10 @@ def main():
         src = source_hash("ssu_prefill_impl.h", "ssu_prefill_mm.h", "ssu_rowblock.h", "ssu_device.h",
                           "ssu_dpp.h")
         kkey = "prefill_config2"
-        lane_ops = prefill_mm_fmas(T, L)
-        bound, peak, unit = "mfma", MFMA_F32_PEAK_TFLOPS, "TFLOP/s"
+        matrix = {"flops_per_step": prefill_method_flops(T, L),
+                  "flops": "the method's own: 5 per state element and token",
+                  "closed_form_fmas_per_step": prefill_mm_fmas(T, L)}
+        bound, peak, unit = "hbm", HBM_PEAK_GBS, "GB/s"
     elif args.config == 5:
         kind = "tree"
         b, m, h, d = T["x"].shape
@@ -406,8 +491,12 @@ def main():
                             workspace=tws, **R["S"])
         src = source_hash("ssu_tree_impl.h", "ssu_dpp.h", "ssu_device.h")
         kkey = "tree_config5"
-        lane_ops = tree_lane_ops(T)
-        bound, peak, unit = "mfma", MFMA_F32_PEAK_TFLOPS, "TFLOP/s"
+        fmas = tree_lane_ops(T)
+        matrix = {"flops_per_step": 2 * fmas,
+                  "flops": "the closed form's: S0.C per node and one B.C dot and x term per "
+                           "path entry",
+                  "closed_form_fmas_per_step": fmas}
+        bound, peak, unit = "hbm", HBM_PEAK_GBS, "GB/s"
     elif args.config == 6:
         kind = "replay_layers"
         nl = inputs.STACK_LAYERS
@@ -551,10 +640,7 @@ def main():
 
     ms = total_ms / args.steps
     gbs = nbytes / (ms * 1e-3) / 1e9
-    if bound == "hbm":
-        achieved = gbs
-    else:  # tree verify and prefill: the fp32 flops of the closed forms they evaluate
-        achieved = 2.0 * lane_ops / (ms * 1e-3) / 1e12
+    achieved = gbs
     traffic = measured_traffic(kkey, src)
     rec = {
         "metric": metric_name(),
@@ -580,6 +666,30 @@ def main():
         "wall_s_timed": round(wall, 3),
         "prewarm": {"ms": args.prewarm_ms, "launches": n_pre},
     }
+    if matrix is not None:
+        # the matrix cores these kernels run on: bf16 MFMA (fp32 operands are split
+        # into bf16 terms); neither this roof nor HBM binds them
+        tf = matrix["flops_per_step"] / (ms * 1e-3) / 1e12
+        cf = 2.0 * matrix["closed_form_fmas_per_step"] / (ms * 1e-3) / 1e12
+        rec["roofline_matrix_cores"] = {
+            "dtype": "bf16", "flops": matrix["flops"], "achieved": round(tf, 3),
+            "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
+            "frac": round(tf / MFMA_BF16_PEAK_TFLOPS, 4),
+            "closed_form_fp32_equivalent": {"achieved": round(cf, 3),
+                                            "peak_fp32_mfma": MFMA_F32_PEAK_TFLOPS,
+                                            "frac": round(cf / MFMA_F32_PEAK_TFLOPS, 4)}}
+    if args.flushed > 0:
+        print(f"[bench] {args.flushed} launches, each after a {FLUSH_BYTES >> 30} GiB scratch write",
+              file=sys.stderr, flush=True)
+        us = flushed_launches(step, args.warmup + args.steps, args.flushed, 10, dev)
+        pick = lambda q: us[min(len(us) - 1, int(round(q * (len(us) - 1))))]
+        med = pick(0.5)
+        rec["flushed"] = {"launches": len(us), "flush_bytes": FLUSH_BYTES,
+                          "median_us": round(med, 2), "p10_us": round(pick(0.1), 2),
+                          "p90_us": round(pick(0.9), 2),
+                          "median_gbs": round(nbytes / (med * 1e-6) / 1e9, 1),
+                          "median_hbm_frac": round(nbytes / (med * 1e-6) / 1e9 / HBM_PEAK_GBS, 4)}
+        rec["d2d_copy_gbs"] = round(copy_bandwidth(dev), 1)
     if args.copy_mib > 0:
         cal_src = torch.ones(args.copy_mib << 18, dtype=torch.float32, device=dev)
         cal_dst = torch.empty_like(cal_src)

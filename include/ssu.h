@@ -14,9 +14,10 @@
  *   [PAD]  FlashInfer, "flashinfer.gdn_fused_decode_step" page, parameters
  *          ssm_state (paged pool, padded row stride) and state_indices
  *          (negative index = padding row; index >= rows is a caller bug).
- *   [RSM]  TensorRT-Edge-LLM, "Recurrent State Manager" page: constructor,
- *          clear, clearSlot, capture, restore, copySlotFrom, bytesPerSlot,
- *          stateBytesPerSlot, findState.
+ *   [RSM]  TensorRT-Edge-LLM, "Recurrent State Manager" page: constructor
+ *          (specs, slotCount, name, stream), spec, specs, clear, clearSlot,
+ *          capture, restore, copySlotFrom, bytesPerSlot, stateBytesPerSlot,
+ *          findState.
  *   [DNP]  Smile, "Class DeltaNetStatePool" page: activateStep, scatterActive
  *          (pack a cohort's home rows into working slots [0, B) and back).
  *   [GDN]  FlashInfer, "flashinfer.gdn_fused_decode_step" page: the fused
@@ -358,19 +359,50 @@ typedef struct ssu_state_spec {
  * Fails with SSU_EINVAL on an invalid spec list (see ssu_pool_alloc). */
 ssu_status ssu_pool_bytes_per_slot(const ssu_state_spec *specs, int32_t n_specs, size_t *out);
 
-/* Allocate one zeroed slab per spec on the current device; the zeroing runs on
- * `stream` [RSM constructor]. SSU_EINVAL if a spec has non-positive volume, a
- * negative layer, a bad rank or dtype, or repeats a {kind, layer} pair.
- * slot_count == 0 or n_specs == 0 gives a valid pool that owns no memory.
- * The pool keeps its own copy of the specs. Free with ssu_pool_free. */
+/* Bytes of a caller slab that holds slot_count slots of every spec for
+ * ssu_pool_alloc: the states' slabs in spec order, each starting at a
+ * 256-byte boundary (sizing against a byte budget before any allocation, as
+ * [RSM bytesPerSlot] does for one slot). No HIP call. */
+ssu_status ssu_pool_slab_bytes(const ssu_state_spec *specs, int32_t n_specs, int32_t slot_count,
+                               size_t *out);
+
+/* Create a pool of slot_count zeroed slots of every spec on the current
+ * device; the zeroing runs on `stream` [RSM constructor: specs, slotCount,
+ * name, stream].
+ *   name: NULL or a string copied into the pool, the prefix of its states in
+ *         diagnostics ([RSM] "prefix for the slab tensor names");
+ *   base: NULL -> the pool allocates one slab per spec (hipMalloc) and frees
+ *         them in ssu_pool_free. Non-NULL -> a caller-owned device buffer of
+ *         base_bytes >= ssu_pool_slab_bytes(specs, n_specs, slot_count)
+ *         bytes, 256-byte aligned: the states are laid out in it as that call
+ *         describes, the pool allocates nothing and ssu_pool_free leaves the
+ *         buffer alone (the caller keeps it alive while the pool is used).
+ * SSU_EINVAL if a spec has non-positive volume, a negative layer, a bad rank
+ * or dtype, or repeats a {kind, layer} pair, or if the caller slab is
+ * misaligned or too small (nothing is written then). slot_count == 0 or
+ * n_specs == 0 gives a valid pool that uses no memory. The pool keeps its own
+ * copy of the specs. Free with ssu_pool_free. */
 ssu_status ssu_pool_alloc(const ssu_state_spec *specs, int32_t n_specs, int32_t slot_count,
-                          hipStream_t stream, ssu_pool **out);
-/* Release the slabs (after synchronising the device). NULL is a no-op. */
+                          const char *name, void *base, size_t base_bytes, hipStream_t stream,
+                          ssu_pool **out);
+/* Release the pool. Slabs the pool allocated are freed after synchronising
+ * the device; a caller slab is left untouched (no HIP call). NULL is a no-op. */
 ssu_status ssu_pool_free(ssu_pool *pool);
 /* Geometry queries [RSM slotCount, numStates, state, stateBytesPerSlot, findState]. */
 ssu_status ssu_pool_info(const ssu_pool *pool, int32_t *num_states, int32_t *slot_count);
 ssu_status ssu_pool_state_ptr(const ssu_pool *pool, int32_t state_idx, void **dev_ptr);
 ssu_status ssu_pool_state_bytes_per_slot(const ssu_pool *pool, int32_t state_idx, size_t *out);
+/* The spec state state_idx was created from [RSM spec]. */
+ssu_status ssu_pool_spec(const ssu_pool *pool, int32_t state_idx, ssu_state_spec *out);
+/* Every spec in pool order [RSM specs]: the first min(capacity, numStates)
+ * are written to out (NULL allowed when capacity is 0); *n_specs = numStates. */
+ssu_status ssu_pool_specs(const ssu_pool *pool, ssu_state_spec *out, int32_t capacity,
+                          int32_t *n_specs);
+/* The pool's name ("" when created without one); the string is owned by the
+ * pool and lives until ssu_pool_free. */
+ssu_status ssu_pool_name(const ssu_pool *pool, const char **name);
+/* *owns = 1 if the pool allocated its slabs, 0 if they lie in a caller slab. */
+ssu_status ssu_pool_owns_memory(const ssu_pool *pool, int32_t *owns);
 /* *state_idx = index of the state with this {kind, layer}, or -1 if none. */
 ssu_status ssu_pool_find_state(const ssu_pool *pool, int32_t kind, int32_t layer,
                                int32_t *state_idx);

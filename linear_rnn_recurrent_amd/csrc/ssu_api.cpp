@@ -156,7 +156,7 @@ extern "C" {
 
 const char *ssu_last_error(void) { return g_last_error.c_str(); }
 
-int32_t ssu_version(void) { return 10100; }
+int32_t ssu_version(void) { return 10200; }
 
 ssu_status ssu_decode(const ssu_dims *dims, const void *x, const float *A, const void *B,
                       const void *C, const float *dt, const float *dt_bias, const float *D,
@@ -748,9 +748,13 @@ struct ssu_pool {
     std::vector<size_t> bytes_per_slot;  // per state
     std::vector<void *> slabs;           // per state, slot_count * bytes_per_slot[i] bytes
     int32_t slot_count = 0;
+    bool owns = true;                    // false: the slabs lie in a caller slab
+    std::string name;                    // prefix of the state names in diagnostics
 };
 
 namespace {
+
+constexpr size_t kSlabAlign = 256;  // every state's slab starts at this alignment
 
 ssu_status check_specs(const ssu_state_spec *specs, int32_t n, const char *fn,
                        std::vector<size_t> *per_state)
@@ -786,7 +790,34 @@ ssu_status check_specs(const ssu_state_spec *specs, int32_t n, const char *fn,
     return SSU_OK;
 }
 
+// Byte offset of every state's slab inside one slab holding all of them (each
+// aligned to kSlabAlign), and the total; false if the sizes overflow.
+bool slab_layout(const std::vector<size_t> &per, int32_t slot_count, std::vector<size_t> *offs,
+                 size_t *total)
+{
+    size_t o = 0;
+    offs->clear();
+    for (size_t b : per) {
+        if (slot_count > 0 && b > (SIZE_MAX / 4) / (size_t)slot_count)
+            return false;
+        offs->push_back(o);
+        const size_t bytes = b * (size_t)slot_count;
+        const size_t padded = (bytes + kSlabAlign - 1) / kSlabAlign * kSlabAlign;
+        if (padded > SIZE_MAX / 4 - o)
+            return false;
+        o += padded;
+    }
+    *total = o;
+    return true;
+}
+
 bool slot_ok(const ssu_pool *p, int32_t slot) { return slot >= 0 && slot < p->slot_count; }
+
+// "pool 'name'" (or "pool") for diagnostics
+std::string label(const ssu_pool *p)
+{
+    return p->name.empty() ? std::string("pool") : "pool '" + p->name + "'";
+}
 
 }  // namespace
 
@@ -808,44 +839,83 @@ ssu_status ssu_pool_bytes_per_slot(const ssu_state_spec *specs, int32_t n_specs,
     return ok();
 }
 
+ssu_status ssu_pool_slab_bytes(const ssu_state_spec *specs, int32_t n_specs, int32_t slot_count,
+                               size_t *out)
+{
+    const char *fn = "ssu_pool_slab_bytes";
+    if (!out)
+        return fail(SSU_EINVAL, "%s: out is NULL", fn);
+    if (slot_count < 0)
+        return fail(SSU_EINVAL, "%s: slot_count %d < 0", fn, slot_count);
+    std::vector<size_t> per, offs;
+    const ssu_status st = check_specs(specs, n_specs, fn, &per);
+    if (st != SSU_OK)
+        return st;
+    size_t total = 0;
+    if (!slab_layout(per, slot_count, &offs, &total))
+        return fail(SSU_EINVAL, "%s: slab size overflows", fn);
+    *out = total;
+    return ok();
+}
+
 ssu_status ssu_pool_alloc(const ssu_state_spec *specs, int32_t n_specs, int32_t slot_count,
-                          hipStream_t stream, ssu_pool **out)
+                          const char *name, void *base, size_t base_bytes, hipStream_t stream,
+                          ssu_pool **out)
 {
     const char *fn = "ssu_pool_alloc";
     if (!out)
         return fail(SSU_EINVAL, "%s: out is NULL", fn);
     *out = nullptr;
+    const std::string nm = name ? name : "";
+    const std::string lb = nm.empty() ? std::string("pool") : "pool '" + nm + "'";
     if (slot_count < 0)
-        return fail(SSU_EINVAL, "%s: slot_count %d < 0", fn, slot_count);
-    std::vector<size_t> per;
+        return fail(SSU_EINVAL, "%s (%s): slot_count %d < 0", fn, lb.c_str(), slot_count);
+    std::vector<size_t> per, offs;
     ssu_status st = check_specs(specs, n_specs, fn, &per);
     if (st != SSU_OK)
         return st;
+    size_t need = 0;
+    if (!slab_layout(per, slot_count, &offs, &need))
+        return fail(SSU_EINVAL, "%s (%s): slab size overflows", fn, lb.c_str());
+    if (base) {
+        if ((reinterpret_cast<uintptr_t>(base) & (kSlabAlign - 1)) != 0)
+            return fail(SSU_EINVAL, "%s (%s): caller slab is not %zu-byte aligned", fn, lb.c_str(),
+                        kSlabAlign);
+        if (base_bytes < need)
+            return fail(SSU_EINVAL, "%s (%s): caller slab holds %zu bytes, the states need %zu", fn,
+                        lb.c_str(), base_bytes, need);
+    }
     ssu_pool *p = new (std::nothrow) ssu_pool();
     if (!p)
-        return fail(SSU_ENOMEM, "%s: host allocation failed", fn);
+        return fail(SSU_ENOMEM, "%s (%s): host allocation failed", fn, lb.c_str());
     p->specs.assign(specs, specs + n_specs);
     p->bytes_per_slot = per;
     p->slot_count = slot_count;
     p->slabs.assign(n_specs, nullptr);
+    p->owns = base == nullptr;
+    p->name = nm;
     if (slot_count > 0) {
         std::vector<ssu::Segment> segs;
         for (int32_t i = 0; i < n_specs; ++i) {
             const size_t bytes = per[i] * (size_t)slot_count;
-            const hipError_t e = hipMalloc(&p->slabs[i], bytes);
-            if (e != hipSuccess) {
-                p->slabs[i] = nullptr;
-                ssu_pool_free(p);
-                return fail(e == hipErrorOutOfMemory ? SSU_ENOMEM : SSU_EHIP,
-                            "%s: hipMalloc of %zu bytes for state %d: %s", fn, bytes, i,
-                            hipGetErrorString(e));
+            if (base) {
+                p->slabs[i] = static_cast<uint8_t *>(base) + offs[i];
+            } else {
+                const hipError_t e = hipMalloc(&p->slabs[i], bytes);
+                if (e != hipSuccess) {
+                    p->slabs[i] = nullptr;
+                    ssu_pool_free(p);
+                    return fail(e == hipErrorOutOfMemory ? SSU_ENOMEM : SSU_EHIP,
+                                "%s (%s): hipMalloc of %zu bytes for state %d: %s", fn,
+                                lb.c_str(), bytes, i, hipGetErrorString(e));
+                }
             }
             segs.push_back({p->slabs[i], nullptr, (uint64_t)bytes});
         }
         const hipError_t e = ssu::launch_segments(segs.data(), (int)segs.size(), stream);
         if (e != hipSuccess) {
             ssu_pool_free(p);
-            return hip_status(e, "ssu_pool_alloc zero fill");
+            return fail(SSU_EHIP, "%s (%s): zero fill: %s", fn, lb.c_str(), hipGetErrorString(e));
         }
     }
     *out = p;
@@ -856,6 +926,10 @@ ssu_status ssu_pool_free(ssu_pool *pool)
 {
     if (!pool)
         return ok();
+    if (!pool->owns) {  // a caller slab: nothing to release or wait for
+        delete pool;
+        return ok();
+    }
     bool any = false;
     for (void *s : pool->slabs)
         any = any || s;
@@ -906,6 +980,48 @@ ssu_status ssu_pool_state_bytes_per_slot(const ssu_pool *pool, int32_t state_idx
     return ok();
 }
 
+ssu_status ssu_pool_spec(const ssu_pool *pool, int32_t state_idx, ssu_state_spec *out)
+{
+    if (!pool || !out)
+        return fail(SSU_EINVAL, "ssu_pool_spec: NULL argument");
+    if (state_idx < 0 || state_idx >= (int32_t)pool->specs.size())
+        return fail(SSU_EINVAL, "ssu_pool_spec (%s): state %d outside [0, %zu)",
+                    label(pool).c_str(), state_idx, pool->specs.size());
+    *out = pool->specs[state_idx];
+    return ok();
+}
+
+ssu_status ssu_pool_specs(const ssu_pool *pool, ssu_state_spec *out, int32_t capacity,
+                          int32_t *n_specs)
+{
+    if (!pool || !n_specs)
+        return fail(SSU_EINVAL, "ssu_pool_specs: NULL argument");
+    if (capacity < 0 || (capacity > 0 && !out))
+        return fail(SSU_EINVAL, "ssu_pool_specs (%s): capacity %d with %s buffer",
+                    label(pool).c_str(), capacity, out ? "a" : "no");
+    const int32_t n = (int32_t)pool->specs.size();
+    for (int32_t i = 0; i < n && i < capacity; ++i)
+        out[i] = pool->specs[i];
+    *n_specs = n;
+    return ok();
+}
+
+ssu_status ssu_pool_name(const ssu_pool *pool, const char **name)
+{
+    if (!pool || !name)
+        return fail(SSU_EINVAL, "ssu_pool_name: NULL argument");
+    *name = pool->name.c_str();
+    return ok();
+}
+
+ssu_status ssu_pool_owns_memory(const ssu_pool *pool, int32_t *owns)
+{
+    if (!pool || !owns)
+        return fail(SSU_EINVAL, "ssu_pool_owns_memory: NULL argument");
+    *owns = pool->owns ? 1 : 0;
+    return ok();
+}
+
 ssu_status ssu_pool_find_state(const ssu_pool *pool, int32_t kind, int32_t layer,
                                int32_t *state_idx)
 {
@@ -924,7 +1040,8 @@ ssu_status ssu_pool_clear_slot(ssu_pool *pool, int32_t slot, hipStream_t stream)
     if (!pool)
         return fail(SSU_EINVAL, "%s: pool is NULL", fn);
     if (slot < -1 || slot >= pool->slot_count || (slot == -1 && pool->slot_count < 0))
-        return fail(SSU_EINVAL, "%s: slot %d outside [-1, %d)", fn, slot, pool->slot_count);
+        return fail(SSU_EINVAL, "%s (%s): slot %d outside [-1, %d)", fn,
+                    label(pool).c_str(), slot, pool->slot_count);
     if (pool->slot_count == 0)
         return ok();
     std::vector<ssu::Segment> segs;
@@ -953,16 +1070,19 @@ ssu_status ssu_pool_capture(const ssu_pool *pool, int32_t slot, void *const *dst
     if (!pool)
         return fail(SSU_EINVAL, "%s: pool is NULL", fn);
     if (!slot_ok(pool, slot))
-        return fail(SSU_EINVAL, "%s: slot %d outside [0, %d)", fn, slot, pool->slot_count);
+        return fail(SSU_EINVAL, "%s (%s): slot %d outside [0, %d)", fn,
+                    label(pool).c_str(), slot, pool->slot_count);
     if (n != (int32_t)pool->specs.size())
-        return fail(SSU_EINVAL, "%s: %d buffers given for %zu states", fn, n, pool->specs.size());
+        return fail(SSU_EINVAL, "%s (%s): %d buffers given for %zu states", fn,
+                    label(pool).c_str(), n, pool->specs.size());
     if (n > 0 && (!dst || !dst_bytes))
         return fail(SSU_EINVAL, "%s: dst or dst_bytes is NULL", fn);
     for (int32_t i = 0; i < n; ++i) {
         if (!dst[i])
-            return fail(SSU_EINVAL, "%s: dst[%d] is NULL", fn, i);
+            return fail(SSU_EINVAL, "%s (%s): dst[%d] is NULL", fn, label(pool).c_str(), i);
         if (dst_bytes[i] != pool->bytes_per_slot[i])
-            return fail(SSU_EINVAL, "%s: dst_bytes[%d] = %zu, state holds %zu bytes per slot", fn,
+            return fail(SSU_EINVAL, "%s (%s): dst_bytes[%d] = %zu, state holds %zu bytes per slot", fn,
+                        label(pool).c_str(),
                         i, dst_bytes[i], pool->bytes_per_slot[i]);
     }
     std::vector<ssu::Segment> segs;
@@ -981,17 +1101,20 @@ ssu_status ssu_pool_restore(ssu_pool *pool, int32_t slot, const void *const *src
     if (!pool)
         return fail(SSU_EINVAL, "%s: pool is NULL", fn);
     if (!slot_ok(pool, slot))
-        return fail(SSU_EINVAL, "%s: slot %d outside [0, %d)", fn, slot, pool->slot_count);
+        return fail(SSU_EINVAL, "%s (%s): slot %d outside [0, %d)", fn,
+                    label(pool).c_str(), slot, pool->slot_count);
     if (n_saved < 0 || n_saved > (int32_t)pool->specs.size())
-        return fail(SSU_EINVAL, "%s: n_saved %d outside [0, %zu]", fn, n_saved,
+        return fail(SSU_EINVAL, "%s (%s): n_saved %d outside [0, %zu]", fn,
+                    label(pool).c_str(), n_saved,
                     pool->specs.size());
     if (n_saved > 0 && (!src || !src_bytes))
         return fail(SSU_EINVAL, "%s: src or src_bytes is NULL", fn);
     for (int32_t i = 0; i < n_saved; ++i) {  // validate everything before any write
         if (!src[i])
-            return fail(SSU_EINVAL, "%s: src[%d] is NULL", fn, i);
+            return fail(SSU_EINVAL, "%s (%s): src[%d] is NULL", fn, label(pool).c_str(), i);
         if (src_bytes[i] != pool->bytes_per_slot[i])
-            return fail(SSU_EINVAL, "%s: src_bytes[%d] = %zu, state holds %zu bytes per slot", fn,
+            return fail(SSU_EINVAL, "%s (%s): src_bytes[%d] = %zu, state holds %zu bytes per slot", fn,
+                        label(pool).c_str(),
                         i, src_bytes[i], pool->bytes_per_slot[i]);
     }
     std::vector<ssu::Segment> segs;
@@ -1011,7 +1134,8 @@ ssu_status ssu_pool_copy_slot_from(ssu_pool *pool, const ssu_pool *source, int32
     if (!pool || !source)
         return fail(SSU_EINVAL, "%s: pool is NULL", fn);
     if (pool->specs.size() != source->specs.size())
-        return fail(SSU_EINVAL, "%s: pools hold %zu and %zu states", fn, pool->specs.size(),
+        return fail(SSU_EINVAL, "%s (%s): pools hold %zu and %zu states", fn,
+                    label(pool).c_str(), pool->specs.size(),
                     source->specs.size());
     for (size_t i = 0; i < pool->specs.size(); ++i) {
         const ssu_state_spec &a = pool->specs[i], &b = source->specs[i];
@@ -1020,13 +1144,16 @@ ssu_status ssu_pool_copy_slot_from(ssu_pool *pool, const ssu_pool *source, int32
         for (int k = 0; same && k < a.rank; ++k)
             same = a.shape[k] == b.shape[k];
         if (!same)
-            return fail(SSU_EINVAL, "%s: state %zu differs between the pools", fn, i);
+            return fail(SSU_EINVAL, "%s (%s): state %zu differs between the pools", fn,
+                        label(pool).c_str(), i);
     }
     if (!slot_ok(pool, dst_slot))
-        return fail(SSU_EINVAL, "%s: destination slot %d outside [0, %d)", fn, dst_slot,
+        return fail(SSU_EINVAL, "%s (%s): destination slot %d outside [0, %d)", fn,
+                    label(pool).c_str(), dst_slot,
                     pool->slot_count);
     if (!slot_ok(source, src_slot))
-        return fail(SSU_EINVAL, "%s: source slot %d outside [0, %d)", fn, src_slot,
+        return fail(SSU_EINVAL, "%s (%s): source slot %d outside [0, %d)", fn,
+                    label(source).c_str(), src_slot,
                     source->slot_count);
     std::vector<ssu::Segment> segs;
     for (size_t i = 0; i < pool->specs.size(); ++i) {

@@ -23,7 +23,8 @@ _DT = {torch.float32: SSU_F32, torch.float16: SSU_F16, torch.bfloat16: SSU_BF16,
 EXPORTS = ("ssu_decode", "ssu_prefill", "ssu_replay", "ssu_tree_verify", "ssu_replay_layers",
            "ssu_state_clear_layers", "ssu_state_gather", "ssu_state_scatter", "ssu_state_pack",
            "ssu_state_unpack", "ssu_gdn_decode", "ssu_gdn_workspace_bytes", "ssu_tree_workspace_bytes",
-           "ssu_pool_bytes_per_slot",
+           "ssu_pool_bytes_per_slot", "ssu_pool_slab_bytes", "ssu_pool_spec", "ssu_pool_specs",
+           "ssu_pool_name", "ssu_pool_owns_memory",
            "ssu_pool_alloc", "ssu_pool_free", "ssu_pool_info", "ssu_pool_state_ptr",
            "ssu_pool_state_bytes_per_slot", "ssu_pool_find_state", "ssu_pool_clear",
            "ssu_pool_clear_slot", "ssu_pool_capture", "ssu_pool_restore",
@@ -103,7 +104,13 @@ def load_library(path: Optional[str] = None):
                            ctypes.c_float, _P, _P, _P, _P, ctypes.c_int64, _P],
         "ssu_state_unpack": [_P, _I32, ctypes.c_int64, ctypes.c_int64, _P, _I32, _P, _I32, _P, _P],
         "ssu_pool_bytes_per_slot": [S, _I32, ctypes.POINTER(ctypes.c_size_t)],
-        "ssu_pool_alloc": [S, _I32, _I32, _P, ctypes.POINTER(_P)],
+        "ssu_pool_slab_bytes": [S, _I32, _I32, ctypes.POINTER(ctypes.c_size_t)],
+        "ssu_pool_alloc": [S, _I32, _I32, ctypes.c_char_p, _P, ctypes.c_size_t, _P,
+                           ctypes.POINTER(_P)],
+        "ssu_pool_spec": [_P, _I32, S],
+        "ssu_pool_specs": [_P, S, _I32, ctypes.POINTER(_I32)],
+        "ssu_pool_name": [_P, ctypes.POINTER(ctypes.c_char_p)],
+        "ssu_pool_owns_memory": [_P, ctypes.POINTER(_I32)],
         "ssu_pool_free": [_P],
         "ssu_pool_info": [_P, ctypes.POINTER(_I32), ctypes.POINTER(_I32)],
         "ssu_pool_state_ptr": [_P, _I32, ctypes.POINTER(_P)],
@@ -651,44 +658,95 @@ class DeviceArray:
 
 
 class SsuPool:
-    """Owning handle of an ssu_pool: one zeroed [slot_count] + shape slab per spec.
+    """Handle of an ssu_pool: one zeroed [slot_count] + shape slab per spec.
 
     specs: sequence of (kind, layer, shape, dtype) with dtype a torch dtype
-    (float32, float16, bfloat16 or uint8).
+    (float32, float16, bfloat16 or uint8). name: the pool's name in the
+    library's diagnostics. base: None (the library allocates the slabs) or a
+    uint8 GPU tensor of at least slab_bytes(specs, slot_count) bytes, 256-byte
+    aligned, in which the states are laid out (the pool then owns no memory and
+    keeps a reference to the tensor).
     """
 
-    def __init__(self, specs: Sequence, slot_count: int, *, stream=None, device=None):
+    def __init__(self, specs: Sequence, slot_count: int, *, name=None, base=None, stream=None,
+                 device=None):
         self._lib = load_library()
+        if base is not None:
+            _dense(base, "base", (torch.uint8,))
+            device = base.device if device is None else device
         self.device = (torch.device("cuda", torch.cuda.current_device()) if device is None
                        else torch.device(device))
-        arr = (ssu_state_spec * max(len(specs), 1))()
-        self.specs = []
-        for i, (kind, layer, shape, dtype) in enumerate(specs):
-            shape = tuple(int(s) for s in shape)
-            _need(1 <= len(shape) <= 4, "spec shape must have 1..4 entries")
-            arr[i].kind, arr[i].layer, arr[i].rank = kind, layer, len(shape)
-            arr[i].dtype = _DT[dtype]
-            for k, s in enumerate(shape):
-                arr[i].shape[k] = s
-            self.specs.append((kind, layer, shape, dtype))
+        arr = self._spec_array(specs)
+        self.specs = [(kind, layer, tuple(int(v) for v in shape), dtype)
+                      for (kind, layer, shape, dtype) in specs]
+        self._base = base
         self._h = ctypes.c_void_p()
         with torch.cuda.device(self.device):
             _check(self._lib.ssu_pool_alloc(arr, len(specs), slot_count,
+                                            None if name is None else name.encode(),
+                                            _ptr(base) if base is not None else None,
+                                            0 if base is None else base.numel(),
                                             _stream(self.device, stream), ctypes.byref(self._h)))
         self.slot_count = slot_count
 
     @staticmethod
-    def bytes_per_slot(specs):
-        lib = load_library()
+    def _spec_array(specs):
         arr = (ssu_state_spec * max(len(specs), 1))()
         for i, (kind, layer, shape, dtype) in enumerate(specs):
+            shape = tuple(int(v) for v in shape)
+            _need(1 <= len(shape) <= 4, "spec shape must have 1..4 entries")
             arr[i].kind, arr[i].layer, arr[i].rank = kind, layer, len(shape)
             arr[i].dtype = _DT.get(dtype, 99)
-            for k, s in enumerate(shape):
-                arr[i].shape[k] = s
+            for k, v in enumerate(shape):
+                arr[i].shape[k] = v
+        return arr
+
+    @staticmethod
+    def bytes_per_slot(specs):
+        lib = load_library()
         out = ctypes.c_size_t()
-        _check(lib.ssu_pool_bytes_per_slot(arr, len(specs), ctypes.byref(out)))
+        _check(lib.ssu_pool_bytes_per_slot(SsuPool._spec_array(specs), len(specs),
+                                           ctypes.byref(out)))
         return out.value
+
+    @staticmethod
+    def slab_bytes(specs, slot_count):
+        """Bytes a caller slab (`base`) must hold for these specs and slots."""
+        lib = load_library()
+        out = ctypes.c_size_t()
+        _check(lib.ssu_pool_slab_bytes(SsuPool._spec_array(specs), len(specs), slot_count,
+                                       ctypes.byref(out)))
+        return out.value
+
+    @property
+    def name(self):
+        p = ctypes.c_char_p()
+        _check(self._lib.ssu_pool_name(self._h, ctypes.byref(p)))
+        return p.value.decode()
+
+    @property
+    def owns_memory(self):
+        o = ctypes.c_int32()
+        _check(self._lib.ssu_pool_owns_memory(self._h, ctypes.byref(o)))
+        return bool(o.value)
+
+    def spec(self, i):
+        """(kind, layer, shape, dtype) of state i, as the library holds it."""
+        sp = ssu_state_spec()
+        _check(self._lib.ssu_pool_spec(self._h, i, ctypes.byref(sp)))
+        return self._spec_tuple(sp)
+
+    def specs_from_library(self):
+        n = ctypes.c_int32()
+        _check(self._lib.ssu_pool_specs(self._h, None, 0, ctypes.byref(n)))
+        arr = (ssu_state_spec * max(n.value, 1))()
+        _check(self._lib.ssu_pool_specs(self._h, arr, n.value, ctypes.byref(n)))
+        return [self._spec_tuple(arr[i]) for i in range(n.value)]
+
+    @staticmethod
+    def _spec_tuple(sp):
+        dt = {v: k for k, v in _DT.items()}[sp.dtype]
+        return (sp.kind, sp.layer, tuple(int(sp.shape[k]) for k in range(sp.rank)), dt)
 
     def close(self):
         if getattr(self, "_h", None) and self._h.value:

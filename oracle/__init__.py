@@ -56,6 +56,8 @@ def _lib():
         lib.oracle_gdn_decode.restype = None
         lib.oracle_num_threads.argtypes = []
         lib.oracle_num_threads.restype = ctypes.c_int32
+        lib.oracle_set_num_threads.argtypes = [ctypes.c_int32]
+        lib.oracle_set_num_threads.restype = None
         _LIB = lib
     return _LIB
 
@@ -284,3 +286,8 @@ def tree(x, A, B, C, dt, state, out, parent_ids, *, depths=None, dt_bias=None, D
 def num_threads():
     """OpenMP threads the oracle's loops run on."""
     return int(_lib().oracle_num_threads())
+
+
+def set_num_threads(n):
+    """Thread count of the oracle's OpenMP loops in this thread's later calls."""
+    _lib().oracle_set_num_threads(int(n))

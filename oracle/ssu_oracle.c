@@ -343,3 +343,15 @@ int32_t oracle_num_threads(void)
     return 1;
 #endif
 }
+
+/* Sets the thread count of the OpenMP loops above (for a single-thread timing
+ * beside the parallel one); 0 or less keeps the current count. */
+void oracle_set_num_threads(int32_t n)
+{
+#ifdef _OPENMP
+    if (n > 0)
+        omp_set_num_threads((int)n);
+#else
+    (void)n;
+#endif
+}

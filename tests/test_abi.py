@@ -64,7 +64,7 @@ def test_struct_layout_matches_header(tmp_path):
 
 
 def test_version(lib):
-    assert lib.ssu_version() == 10100
+    assert lib.ssu_version() == 10200
 
 
 # ---------------------------------------------------------------------------
@@ -242,7 +242,8 @@ def test_pool_rejects_bad_specs(lib, specs, needle):
     assert lib.ssu_pool_bytes_per_slot(spec_array(specs), len(specs), ctypes.byref(out)) == 1
     assert needle in err(lib)
     h = ctypes.c_void_p(123)
-    assert lib.ssu_pool_alloc(spec_array(specs), len(specs), 4, None, ctypes.byref(h)) == 1
+    assert lib.ssu_pool_alloc(spec_array(specs), len(specs), 4, None, None, 0, None,
+                              ctypes.byref(h)) == 1
     assert h.value is None
 
 
@@ -257,7 +258,7 @@ def test_empty_pool_needs_no_device(lib):
     """slot_count == 0 allocates nothing, so the whole lifecycle runs on the host."""
     specs = [(0, 0, (80, 64, 128), 0), (1, 0, (128, 3), 2)]
     h = ctypes.c_void_p()
-    assert lib.ssu_pool_alloc(spec_array(specs), 2, 0, None, ctypes.byref(h)) == 0
+    assert lib.ssu_pool_alloc(spec_array(specs), 2, 0, b"rsm", None, 0, None, ctypes.byref(h)) == 0
     n, sc = ctypes.c_int32(), ctypes.c_int32()
     assert lib.ssu_pool_info(h, ctypes.byref(n), ctypes.byref(sc)) == 0
     assert (n.value, sc.value) == (2, 0)
@@ -275,16 +276,79 @@ def test_empty_pool_needs_no_device(lib):
     ptrs = (ctypes.c_void_p * 2)(FAKE, FAKE)
     sizes = (ctypes.c_size_t * 2)(80 * 64 * 128 * 4, 768)
     assert lib.ssu_pool_capture(h, 0, ptrs, sizes, 2, None) == 1 and "slot" in err(lib)
+    assert "pool 'rsm'" in err(lib)  # the pool's name prefixes its diagnostics
     assert lib.ssu_pool_restore(h, 0, ptrs, sizes, 2, None) == 1 and "slot" in err(lib)
     assert lib.ssu_pool_free(h) == 0
     assert lib.ssu_pool_free(None) == 0
+
+
+def test_pool_slab_bytes_aligns_every_state(lib):
+    # 1000 and 7 bytes per slot: 3 slots -> 3000 (3072 aligned) + 21 (256 aligned)
+    specs = [(0, 0, (250,), 0), (1, 0, (7,), 3)]
+    out = ctypes.c_size_t()
+    assert lib.ssu_pool_slab_bytes(spec_array(specs), 2, 3, ctypes.byref(out)) == 0
+    assert out.value == 3072 + 256
+    assert lib.ssu_pool_slab_bytes(spec_array(specs), 2, 0, ctypes.byref(out)) == 0
+    assert out.value == 0
+    assert lib.ssu_pool_slab_bytes(spec_array(specs), 2, -1, ctypes.byref(out)) == 1
+    assert lib.ssu_pool_slab_bytes(spec_array([(0, 0, (0,), 0)]), 1, 3, ctypes.byref(out)) == 1
+
+
+def test_pool_caller_slab_checks_before_any_device_call(lib):
+    specs = [(0, 0, (250,), 0), (1, 0, (7,), 3)]
+    h = ctypes.c_void_p(123)
+    # misaligned, then too small: rejected on the host, no pool returned
+    assert lib.ssu_pool_alloc(spec_array(specs), 2, 3, b"p", FAKE + 16, 4096, None,
+                              ctypes.byref(h)) == 1
+    assert "aligned" in err(lib) and "pool 'p'" in err(lib) and h.value is None
+    assert lib.ssu_pool_alloc(spec_array(specs), 2, 3, b"p", FAKE, 3327, None,
+                              ctypes.byref(h)) == 1
+    assert "3328" in err(lib) and h.value is None
+    # zero slots in a caller slab: a valid pool that uses and owns no memory
+    assert lib.ssu_pool_alloc(spec_array(specs), 2, 0, b"p", FAKE, 0, None, ctypes.byref(h)) == 0
+    owns = ctypes.c_int32(7)
+    assert lib.ssu_pool_owns_memory(h, ctypes.byref(owns)) == 0 and owns.value == 0
+    assert lib.ssu_pool_free(h) == 0
+
+
+def test_pool_spec_getters_and_name(lib):
+    specs = [(0, 3, (80, 64, 128), 0), (1, 3, (128, 3), 2), (0, 4, (5,), 3)]
+    h = ctypes.c_void_p()
+    assert lib.ssu_pool_alloc(spec_array(specs), 3, 0, b"layers-3-4", None, 0, None,
+                              ctypes.byref(h)) == 0
+    name = ctypes.c_char_p()
+    assert lib.ssu_pool_name(h, ctypes.byref(name)) == 0 and name.value == b"layers-3-4"
+    owns = ctypes.c_int32()
+    assert lib.ssu_pool_owns_memory(h, ctypes.byref(owns)) == 0 and owns.value == 1
+    sp = S.ssu_state_spec()
+    for i, (kind, layer, shape, dt) in enumerate(specs):
+        assert lib.ssu_pool_spec(h, i, ctypes.byref(sp)) == 0
+        assert (sp.kind, sp.layer, sp.rank, sp.dtype) == (kind, layer, len(shape), dt)
+        assert tuple(sp.shape[:sp.rank]) == shape
+    assert lib.ssu_pool_spec(h, 3, ctypes.byref(sp)) == 1 and "layers-3-4" in err(lib)
+    assert lib.ssu_pool_spec(h, -1, ctypes.byref(sp)) == 1
+    n = ctypes.c_int32()
+    assert lib.ssu_pool_specs(h, None, 0, ctypes.byref(n)) == 0 and n.value == 3
+    arr = (S.ssu_state_spec * 2)()
+    assert lib.ssu_pool_specs(h, arr, 2, ctypes.byref(n)) == 0 and n.value == 3
+    assert [(a.kind, a.layer) for a in arr] == [(0, 3), (1, 3)]
+    assert lib.ssu_pool_specs(h, None, 2, ctypes.byref(n)) == 1
+    assert lib.ssu_pool_free(h) == 0
+    # unnamed pool: empty name, "pool" in diagnostics
+    assert lib.ssu_pool_alloc(spec_array(specs), 3, 0, None, None, 0, None, ctypes.byref(h)) == 0
+    assert lib.ssu_pool_name(h, ctypes.byref(name)) == 0 and name.value == b""
+    assert lib.ssu_pool_free(h) == 0
 
 
 def test_null_pool_arguments(lib):
     assert lib.ssu_pool_clear(None, None) == 1
     assert lib.ssu_pool_clear_slot(None, 0, None) == 1
     assert lib.ssu_pool_info(None, None, None) == 1
-    assert lib.ssu_pool_alloc(spec_array([]), 0, 0, None, None) == 1
+    assert lib.ssu_pool_alloc(spec_array([]), 0, 0, None, None, 0, None, None) == 1
+    assert lib.ssu_pool_spec(None, 0, None) == 1
+    assert lib.ssu_pool_specs(None, None, 0, None) == 1
+    assert lib.ssu_pool_name(None, None) == 1
+    assert lib.ssu_pool_owns_memory(None, None) == 1
     assert lib.ssu_pool_copy_slot_from(None, None, 0, 0, None) == 1
 
 

@@ -137,3 +137,59 @@ def test_pool_state_is_zero_copy_torch_view_when_supported():
     cap = pool.capture(1)[0]
     assert torch.all(cap == 2.5)
     assert torch.count_nonzero(pool.capture(0)[0]) == 0
+
+
+def test_pool_in_a_caller_slab():
+    # the states laid out in a torch-allocated slab: zeroed there, nothing
+    # written outside it, nothing freed by the pool, every operation as usual
+    need = SsuPool.slab_bytes(SPECS, 4)
+    assert need == 131072 + 2304 + 256  # 4 slots of 32768, 576 and 7 bytes, 256-aligned
+    slab = torch.full((need + 512,), 0xAB, dtype=torch.uint8, device="cuda")
+    assert slab.data_ptr() % 256 == 0
+    base = slab[256:256 + need]
+    pool = SsuPool(SPECS, 4, name="caller-slab", base=base)
+    assert not pool.owns_memory and pool.name == "caller-slab"
+    assert pool.specs_from_library() == pool.specs and pool.spec(1) == SPECS[1]
+    offs = [0, 131072, 131072 + 2304]
+    for i, o in enumerate(offs):
+        assert pool.state(i).data_ptr() == base.data_ptr() + o
+    torch.cuda.synchronize()
+    assert all(torch.count_nonzero(t) == 0 for slot in snapshot(pool) for t in slot)
+    assert torch.all(slab[:256] == 0xAB) and torch.all(slab[256 + need:] == 0xAB)
+    before = fill(pool, 11)
+    pool.clear_slot(1)
+    after = snapshot(pool)
+    assert all(torch.count_nonzero(t) == 0 for t in after[1])
+    assert same(after[0], before[0]) and same(after[2], before[2]) and same(after[3], before[3])
+    with pytest.raises(SsuError, match="caller-slab"):
+        pool.capture(4)
+    pool.close()
+    torch.cuda.synchronize()
+    # the slab outlives the pool with the pool's last contents in place
+    slot3 = slab[256 + 3 * 32768:256 + 4 * 32768].view(torch.float32).reshape(4, 32, 64)
+    assert torch.equal(slot3, before[3][0][0])
+    with pytest.raises(SsuError, match="aligned"):
+        SsuPool(SPECS, 4, base=slab[16:16 + need])
+    with pytest.raises(SsuError, match=str(need)):
+        SsuPool(SPECS, 4, base=slab[256:256 + need - 1])
+
+
+def test_decode_runs_on_a_pool_in_a_caller_slab():
+    specs = [(0, 0, (4, 32, 64), torch.float32)]
+    slab = torch.empty(SsuPool.slab_bytes(specs, 6), dtype=torch.uint8, device="cuda")
+    pool = SsuPool(specs, 6, base=slab)
+    w = inputs.decode_workload(batch=3, nheads=4, dim=32, dstate=64, ngroups=1, pool_rows=6,
+                               seed=8, io_dtype="bf16", bc_dtype="bf16", indices=[1, 5, -1])
+    for s in range(6):
+        pool.restore([gpu(w["state"][s:s + 1])], s)
+    T = {k: gpu(v) for k, v in w.tensors.items()}
+    out = torch.full_like(T["x"], float("nan"))
+    # the slab itself, viewed as the [slots, H, dim, dstate] state, is the decode's state
+    ssu_decode(T["x"], T["A"], T["B"], T["C"], T["dt"], slab.view(torch.float32).view(6, 4, 32, 64),
+               out, dt_bias=T["dt_bias"], D=T["D"], z=T["z"], state_indices=T["state_indices"])
+    st_ref, out_ref = oracle_decode(w)
+    got = torch.cat([pool.capture(s)[0] for s in range(6)]).cpu()
+    assert_close(got, st_ref, TOL_F32, "pool state")
+    assert_close(out.cpu(), out_ref, TOL_LOW, "out")
+    assert_bitwise(got[[0, 2, 3, 4]], w["state"][[0, 2, 3, 4]], "rows not addressed")
+    assert_bitwise(out[2].cpu(), torch.zeros_like(out[2].cpu()), "padding row output")
