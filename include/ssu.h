@@ -187,6 +187,31 @@ ssu_status ssu_tree_verify(const ssu_dims *dims, int32_t num_nodes, const void *
                            float *replay_B, float *replay_dt, void *workspace,
                            int64_t workspace_bytes, hipStream_t stream);
 
+/* Bytes of the library-owned scratch of ssu_tree_verify_noalloc (per GPU). */
+#define SSU_TREE_SCRATCH_BYTES 4194304
+
+/* ssu_tree_verify_noalloc -- ssu_tree_verify for callers that cannot allocate
+ * device memory (code under HIP graph capture, tight serving loops, harnesses
+ * that forbid allocation): the same operation, arguments and kernels, except
+ * that the B . C dots go to a device array the library holds for the life of
+ * the process, SSU_TREE_SCRATCH_BYTES bytes on each GPU it runs on, instead of
+ * a caller workspace. The caller still passes every input and output.
+ * Limit: ssu_tree_workspace_bytes(dims, num_nodes) <= SSU_TREE_SCRATCH_BYTES
+ * (e.g. batch 64 with one group and 128-node trees), else SSU_EINVAL before
+ * any HIP call. The call allocates nothing: its first call on a device looks
+ * up that device's copy of the array (hipGetSymbolAddress) once.
+ * Every call on one GPU shares that GPU's array and leaves it holding its own
+ * dots: calls that overlap on one GPU (other streams, or host threads whose
+ * calls are not ordered) race on it and give undefined results; order them on
+ * one stream. Calls through ssu_tree_verify never touch the array. */
+ssu_status ssu_tree_verify_noalloc(const ssu_dims *dims, int32_t num_nodes, const void *x,
+                                   const float *A, const void *B, const void *C, const float *dt,
+                                   const float *dt_bias, const float *D, const void *z,
+                                   const void *state, void *out, int32_t dt_softplus,
+                                   const int32_t *state_indices, const int32_t *parent_ids,
+                                   const int32_t *depths, float *replay_dA, float *replay_u,
+                                   float *replay_B, float *replay_dt, hipStream_t stream);
+
 /* Bytes of workspace ssu_tree_verify needs: 4 * batch * ngroups * num_nodes^2;
  * -1 if dims is NULL or num_nodes is outside [0, SSU_MAX_TREE_NODES] or
  * batch / ngroups is out of range. No HIP call. */

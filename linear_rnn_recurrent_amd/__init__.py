@@ -7,6 +7,7 @@ only marshals torch GPU tensors into those calls.
 """
 from .ssu import (SsuError, SsuPool, DeviceArray, ReplayLayerTable, StateLayerTable,
                   load_library, ssu_decode, ssu_prefill, ssu_replay, ssu_tree_verify,
+                  ssu_tree_verify_noalloc, TREE_SCRATCH_BYTES,
                   ssu_replay_layers, ssu_state_clear_layers, ssu_state_gather,
                   ssu_state_scatter, ssu_state_pack, ssu_state_unpack, pack_workspace_bytes,
                   ssu_gdn_decode, gdn_workspace_bytes, tree_workspace_bytes,
@@ -14,6 +15,7 @@ from .ssu import (SsuError, SsuPool, DeviceArray, ReplayLayerTable, StateLayerTa
 
 __all__ = ["SsuError", "SsuPool", "DeviceArray", "ReplayLayerTable", "StateLayerTable",
            "load_library", "ssu_decode", "ssu_prefill", "ssu_replay", "ssu_tree_verify",
+           "ssu_tree_verify_noalloc", "TREE_SCRATCH_BYTES",
            "ssu_replay_layers", "ssu_state_clear_layers", "ssu_state_gather", "ssu_state_scatter",
            "ssu_state_pack", "ssu_state_unpack", "pack_workspace_bytes", "ssu_gdn_decode", "gdn_workspace_bytes",
            "tree_workspace_bytes",

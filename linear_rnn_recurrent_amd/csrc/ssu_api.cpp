@@ -667,16 +667,20 @@ int64_t ssu_tree_workspace_bytes(const ssu_dims *dims, int32_t num_nodes)
     return (int64_t)4 * dims->batch * dims->ngroups * num_nodes * num_nodes;
 }
 
-ssu_status ssu_tree_verify(const ssu_dims *dims, int32_t num_nodes, const void *x,
-                           const float *A, const void *B, const void *C, const float *dt,
-                           const float *dt_bias, const float *D, const void *z,
-                           const void *state, void *out, int32_t dt_softplus,
-                           const int32_t *state_indices, const int32_t *parent_ids,
-                           const int32_t *depths, float *replay_dA, float *replay_u,
-                           float *replay_B, float *replay_dt, void *workspace,
-                           int64_t workspace_bytes, hipStream_t stream)
+}  // extern "C"
+
+namespace {
+
+// ssu_tree_verify with a caller workspace, or (workspace == nullptr and
+// own_scratch) the library's scratch.
+ssu_status tree_verify(const char *fn, const ssu_dims *dims, int32_t num_nodes, const void *x,
+                       const float *A, const void *B, const void *C, const float *dt,
+                       const float *dt_bias, const float *D, const void *z, const void *state,
+                       void *out, int32_t dt_softplus, const int32_t *state_indices,
+                       const int32_t *parent_ids, const int32_t *depths, float *replay_dA,
+                       float *replay_u, float *replay_B, float *replay_dt, void *workspace,
+                       int64_t workspace_bytes, bool own_scratch, hipStream_t stream)
 {
-    const char *fn = "ssu_tree_verify";
     ssu::TreeParams p = {};
     const ssu_status st = check_dims(dims, fn, true, state_indices != nullptr, &p.d);
     if (st != SSU_OK)
@@ -710,11 +714,22 @@ ssu_status ssu_tree_verify(const ssu_dims *dims, int32_t num_nodes, const void *
     SSU_OPTIONAL_PTR(replay_u, 4, fn);
     SSU_OPTIONAL_PTR(replay_B, 16, fn);
     SSU_OPTIONAL_PTR(replay_dt, 4, fn);
-    SSU_REQUIRE_PTR(workspace, 16, fn);
     const int64_t need = ssu_tree_workspace_bytes(dims, num_nodes);
-    if (workspace_bytes < need)
-        return fail(SSU_EINVAL, "%s: workspace_bytes %lld < %lld required", fn,
-                    (long long)workspace_bytes, (long long)need);
+    if (own_scratch) {
+        if (need > SSU_TREE_SCRATCH_BYTES)
+            return fail(SSU_EINVAL,
+                        "%s: batch * ngroups * num_nodes^2 * 4 = %lld bytes exceeds the library's "
+                        "scratch of %d bytes (use ssu_tree_verify with a workspace)",
+                        fn, (long long)need, SSU_TREE_SCRATCH_BYTES);
+        const hipError_t e = ssu::tree_scratch(&workspace);
+        if (e != hipSuccess)
+            return hip_status(e, "ssu_tree_verify_noalloc scratch address");
+    } else {
+        SSU_REQUIRE_PTR(workspace, 16, fn);
+        if (workspace_bytes < need)
+            return fail(SSU_EINVAL, "%s: workspace_bytes %lld < %lld required", fn,
+                        (long long)workspace_bytes, (long long)need);
+    }
     p.gram = static_cast<float *>(workspace);
     p.d.x = x;
     p.d.A = A;
@@ -735,7 +750,38 @@ ssu_status ssu_tree_verify(const ssu_dims *dims, int32_t num_nodes, const void *
     p.st_u = replay_u;
     p.st_B = replay_B;
     p.st_dt = replay_dt;
-    return hip_status(ssu::launch_tree(p, stream), "ssu_tree_verify launch");
+    return hip_status(ssu::launch_tree(p, stream), fn);
+}
+
+}  // namespace
+
+extern "C" {
+
+ssu_status ssu_tree_verify(const ssu_dims *dims, int32_t num_nodes, const void *x,
+                           const float *A, const void *B, const void *C, const float *dt,
+                           const float *dt_bias, const float *D, const void *z,
+                           const void *state, void *out, int32_t dt_softplus,
+                           const int32_t *state_indices, const int32_t *parent_ids,
+                           const int32_t *depths, float *replay_dA, float *replay_u,
+                           float *replay_B, float *replay_dt, void *workspace,
+                           int64_t workspace_bytes, hipStream_t stream)
+{
+    return tree_verify("ssu_tree_verify", dims, num_nodes, x, A, B, C, dt, dt_bias, D, z, state,
+                       out, dt_softplus, state_indices, parent_ids, depths, replay_dA, replay_u,
+                       replay_B, replay_dt, workspace, workspace_bytes, false, stream);
+}
+
+ssu_status ssu_tree_verify_noalloc(const ssu_dims *dims, int32_t num_nodes, const void *x,
+                                   const float *A, const void *B, const void *C, const float *dt,
+                                   const float *dt_bias, const float *D, const void *z,
+                                   const void *state, void *out, int32_t dt_softplus,
+                                   const int32_t *state_indices, const int32_t *parent_ids,
+                                   const int32_t *depths, float *replay_dA, float *replay_u,
+                                   float *replay_B, float *replay_dt, hipStream_t stream)
+{
+    return tree_verify("ssu_tree_verify_noalloc", dims, num_nodes, x, A, B, C, dt, dt_bias, D, z,
+                       state, out, dt_softplus, state_indices, parent_ids, depths, replay_dA,
+                       replay_u, replay_B, replay_dt, nullptr, 0, true, stream);
 }
 
 }  // extern "C"

@@ -76,6 +76,9 @@ hipError_t launch_prefill_f16(const PrefillParams &p, hipStream_t stream);
 hipError_t launch_prefill_bf16(const PrefillParams &p, hipStream_t stream);
 hipError_t launch_replay(const ReplayParams &p, hipStream_t stream);
 hipError_t launch_tree(const TreeParams &p, hipStream_t stream);
+// Device address of the library's SSU_TREE_SCRATCH_BYTES tree scratch on the
+// current device (looked up once per device).
+hipError_t tree_scratch(void **ptr);
 // Zeroes row `slot` (or all rows, slot -1) of both states of every layer.
 hipError_t launch_clear_layers(const ssu_state_layer *layers, int num_layers, int rows, int slot,
                                int64_t rec_row_bytes, int64_t conv_row_bytes, hipStream_t stream);

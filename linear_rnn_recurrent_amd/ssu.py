@@ -20,7 +20,8 @@ SSU_F32, SSU_F16, SSU_BF16, SSU_U8 = 0, 1, 2, 3
 _DT = {torch.float32: SSU_F32, torch.float16: SSU_F16, torch.bfloat16: SSU_BF16,
        torch.uint8: SSU_U8}
 
-EXPORTS = ("ssu_decode", "ssu_prefill", "ssu_replay", "ssu_tree_verify", "ssu_replay_layers",
+EXPORTS = ("ssu_decode", "ssu_prefill", "ssu_replay", "ssu_tree_verify",
+           "ssu_tree_verify_noalloc", "ssu_replay_layers",
            "ssu_state_clear_layers", "ssu_state_gather", "ssu_state_scatter", "ssu_state_pack",
            "ssu_state_unpack", "ssu_gdn_decode", "ssu_gdn_workspace_bytes", "ssu_tree_workspace_bytes",
            "ssu_pool_bytes_per_slot", "ssu_pool_slab_bytes", "ssu_pool_spec", "ssu_pool_specs",
@@ -93,6 +94,8 @@ def load_library(path: Optional[str] = None):
         "ssu_replay": [D, _I32, _P, _P, _P, _P, _P, _P, _P, _I32, _P, _I32, _P],
         "ssu_tree_verify": [D, _I32, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _I32, _P, _P, _P,
                             _P, _P, _P, _P, _P, ctypes.c_int64, _P],
+        "ssu_tree_verify_noalloc": [D, _I32, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _I32, _P,
+                                    _P, _P, _P, _P, _P, _P, _P],
         "ssu_replay_layers": [D, _I32, _P, _I32, _P, _P, _I32, _P, _I32, _P],
         "ssu_state_clear_layers": [_P, _I32, _I32, _I32, ctypes.c_int64, ctypes.c_int64, _P],
         "ssu_state_gather": [_P, _I32, ctypes.c_int64, _P, ctypes.c_int64, _P, _I32,
@@ -331,18 +334,9 @@ def ssu_replay(state, replay_dA, replay_u, replay_B, replay_dt, accepted_lengths
                               _stream(state.device, stream)))
 
 
-def ssu_tree_verify(x, A, B, C, dt, state, out, parent_ids, *, depths=None, dt_bias=None,
-                    D=None, z=None, dt_softplus=True, state_indices=None, replay_dA=None,
-                    replay_u=None, replay_B=None, replay_dt=None, workspace=None, stream=None):
-    """Every node of a draft tree per batch row, from the read-only committed state.
-
-    x, z, out [batch, num_nodes, nheads, dim]; dt [batch, num_nodes, nheads];
-    B, C [batch, num_nodes, ngroups, dstate]; parent_ids, depths [batch, num_nodes] int32.
-    Replay stash (fp32, all four or none) in the ssu_prefill layouts with the node axis.
-    workspace: a uint8 GPU tensor of at least tree_workspace_bytes(...) bytes (allocated
-    here when None).
-    """
-    lib = load_library()
+def _tree_dims(x, A, B, C, dt, state, out, parent_ids, depths, dt_bias, D, z, state_indices,
+               stash):
+    """Shape checks of a tree-verify call; returns (dims, num_nodes)."""
     _dense(x, "x", _FLOAT)
     _need(x.dim() == 4, "x must be [batch, num_nodes, nheads, dim]")
     batch, num_nodes, nheads, dim = x.shape
@@ -365,13 +359,31 @@ def ssu_tree_verify(x, A, B, C, dt, state, out, parent_ids, *, depths=None, dt_b
     _dense(out, "out", (x.dtype,), x.shape)
     rows, stride = _state_geometry(state, nheads, dim, dstate)
     _opt_idx(state_indices, "state_indices", batch)
-    stash = (replay_dA, replay_u, replay_B, replay_dt)
+    replay_dA, replay_u, replay_B, replay_dt = stash
     if any(s is not None for s in stash):
         _dense(replay_dA, "replay_dA", (torch.float32,), (batch, num_nodes, nheads))
         _dense(replay_dt, "replay_dt", (torch.float32,), (batch, num_nodes, nheads))
         _dense(replay_u, "replay_u", (torch.float32,), x.shape)
         _dense(replay_B, "replay_B", (torch.float32,), B.shape)
-    d = _dims(batch, nheads, dim, dstate, ngroups, rows, stride, state.dtype, x.dtype, B.dtype)
+    return _dims(batch, nheads, dim, dstate, ngroups, rows, stride, state.dtype, x.dtype,
+                 B.dtype), num_nodes
+
+
+def ssu_tree_verify(x, A, B, C, dt, state, out, parent_ids, *, depths=None, dt_bias=None,
+                    D=None, z=None, dt_softplus=True, state_indices=None, replay_dA=None,
+                    replay_u=None, replay_B=None, replay_dt=None, workspace=None, stream=None):
+    """Every node of a draft tree per batch row, from the read-only committed state.
+
+    x, z, out [batch, num_nodes, nheads, dim]; dt [batch, num_nodes, nheads];
+    B, C [batch, num_nodes, ngroups, dstate]; parent_ids, depths [batch, num_nodes] int32.
+    Replay stash (fp32, all four or none) in the ssu_prefill layouts with the node axis.
+    workspace: a uint8 GPU tensor of at least tree_workspace_bytes(...) bytes (allocated
+    here when None).
+    """
+    lib = load_library()
+    stash = (replay_dA, replay_u, replay_B, replay_dt)
+    d, num_nodes = _tree_dims(x, A, B, C, dt, state, out, parent_ids, depths, dt_bias, D, z,
+                              state_indices, stash)
     if workspace is None:
         need = max(int(lib.ssu_tree_workspace_bytes(ctypes.byref(d), num_nodes)), 16)
         workspace = torch.empty(need, dtype=torch.uint8, device=x.device)
@@ -384,6 +396,29 @@ def ssu_tree_verify(x, A, B, C, dt, state, out, parent_ids, *, depths=None, dt_b
                                    *[_ptr(s) for s in stash], _ptr(workspace),
                                    workspace.numel(), _stream(x.device, stream)))
     return out
+
+
+def ssu_tree_verify_noalloc(x, A, B, C, dt, state, out, parent_ids, *, depths=None,
+                            dt_bias=None, D=None, z=None, dt_softplus=True, state_indices=None,
+                            replay_dA=None, replay_u=None, replay_B=None, replay_dt=None,
+                            stream=None):
+    """ssu_tree_verify without a workspace: the library's per-GPU scratch of
+    SSU_TREE_SCRATCH_BYTES holds the B.C dots, so nothing is allocated (for
+    code under graph capture). Calls that overlap on one GPU race on it."""
+    lib = load_library()
+    stash = (replay_dA, replay_u, replay_B, replay_dt)
+    d, num_nodes = _tree_dims(x, A, B, C, dt, state, out, parent_ids, depths, dt_bias, D, z,
+                              state_indices, stash)
+    with torch.cuda.device(x.device):
+        _check(lib.ssu_tree_verify_noalloc(ctypes.byref(d), num_nodes, _ptr(x), _ptr(A), _ptr(B),
+                                           _ptr(C), _ptr(dt), _ptr(dt_bias), _ptr(D), _ptr(z),
+                                           _ptr(state), _ptr(out), 1 if dt_softplus else 0,
+                                           _ptr(state_indices), _ptr(parent_ids), _ptr(depths),
+                                           *[_ptr(s) for s in stash], _stream(x.device, stream)))
+    return out
+
+
+TREE_SCRATCH_BYTES = 4194304  # SSU_TREE_SCRATCH_BYTES of include/ssu.h
 
 
 def tree_workspace_bytes(batch, ngroups, num_nodes):

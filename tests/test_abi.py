@@ -213,6 +213,18 @@ def test_tree_verify_validation(lib):
     assert lib.ssu_tree_workspace_bytes(None, 8) == -1
 
 
+def test_tree_noalloc_refuses_beyond_its_scratch_on_the_host(lib):
+    # B65 G1 M128 needs 4 * 65 * 128^2 bytes > SSU_TREE_SCRATCH_BYTES: refused
+    # before any HIP call (fake pointers are never dereferenced)
+    d = dims(batch=65, pool_rows=65, dim=64, dstate=64, nheads=2)
+    p = [FAKE] * 8
+    rc = lib.ssu_tree_verify_noalloc(ctypes.byref(d), 128, p[0], p[1], p[2], p[3], p[4], None,
+                                     None, None, p[5], p[6], 1, None, p[7], None, None, None,
+                                     None, None, None)
+    assert rc == 1 and "scratch" in err(lib)
+    assert S.TREE_SCRATCH_BYTES == 4 * 64 * 128 * 128
+
+
 def spec_array(specs):
     arr = (S.ssu_state_spec * max(len(specs), 1))()
     for i, (kind, layer, shape, dt) in enumerate(specs):
