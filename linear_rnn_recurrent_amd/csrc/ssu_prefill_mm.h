@@ -51,7 +51,12 @@ constexpr int kPmSeg = 16;  // chunks whose decay tables are formed together
 struct PmLds {
     int cs, bs, bt, xt, zs, ys, lc, rd, sf, tot, big, sb, total;
 };
-__host__ __device__ constexpr int pm_row_pitch(int NS) { return NS * 2 + 16; }   // C, B rows
+// C, B rows: a pitch of 16 bytes past whole 128-byte lines keeps the 16-byte
+// row stores aligned; rows 8-15 of each 16 swap the 8-byte halves of every
+// 16-byte block (pm_swz), so that the 16 rows an operand read touches at once
+// fall in 16 different 8-byte bank pairs of the 32 4-byte LDS banks.
+__host__ __device__ constexpr int pm_row_pitch(int NS) { return NS * 2 + 16; }
+__device__ __forceinline__ int pm_swz(int row) { return ((row >> 3) & 1) * 8; }
 __host__ __device__ constexpr int pm_t_pitch() { return kPmTT * 2 + 8; }          // B^T, x^T rows
 __host__ __device__ constexpr int pm_y_pitch() { return 64 * 4 + 16; }            // fp32 outputs
 __host__ __device__ constexpr int pm_z_pitch() { return 64 * 2 + 16; }            // z rows
@@ -270,8 +275,13 @@ __global__ __launch_bounds__(kPmNT) __attribute__((amdgpu_waves_per_eu(NS <= 128
                 const int p = v & 15, col = 8 * (v >> 4);
 #pragma unroll
                 for (int q = 0; q < 2; ++q) {
-                    *reinterpret_cast<u32x4 *>(Bs + (2 * p + q) * PC + col * 2) = rB[k][q];
-                    *reinterpret_cast<u32x4 *>(Cs + (2 * p + q) * PC + col * 2) = rC[k][q];
+                    const int row = 2 * p + q;
+                    const u32x4 b = rB[k][q], c = rC[k][q];
+                    const bool sw = pm_swz(row) != 0;  // the block's 8-byte halves swapped
+                    *reinterpret_cast<u32x4 *>(Bs + row * PC + col * 2) =
+                        sw ? u32x4{b[2], b[3], b[0], b[1]} : b;
+                    *reinterpret_cast<u32x4 *>(Cs + row * PC + col * 2) =
+                        sw ? u32x4{c[2], c[3], c[0], c[1]} : c;
                 }
 #pragma unroll
                 for (int i = 0; i < 8; ++i)
@@ -428,8 +438,9 @@ __global__ __launch_bounds__(kPmNT) __attribute__((amdgpu_waves_per_eu(NS <= 128
             pm_bf16x8 cop[2], bop[2];
 #pragma unroll
             for (int t = 0; t < 2; ++t) {
-                cop[t] = pm_op(Cs + (16 * t + ln) * PC + (32 * kk + 4 * qg) * 2);
-                bop[t] = pm_op(Bs + (16 * t + ln) * PC + (32 * kk + 4 * qg) * 2);
+                const int o = (16 * t + ln) * PC + (((32 * kk + 4 * qg) * 2) ^ pm_swz(ln));
+                cop[t] = pm_op(Cs + o);
+                bop[t] = pm_op(Bs + o);
             }
             float sv[8];
 #pragma unroll
