@@ -30,6 +30,11 @@
  * Parity pins: tests/test_oracle_gdn_pins.py (closed forms, the delta rule's
  * write-at-key property, conv shift, padding) and brute force against the
  * pure-Python oracle/ref_tiny.py.
+ *
+ * Parity unpinned as to the page: it prints no formula and no worked value for
+ * this step, so the pins above fix the oracle to the readings listed here (the
+ * gate parameterisation, the norm eps, the conv tap order, the q/k/v split and
+ * the head map), not to anything the page states.
  */
 #include <math.h>
 #include <stdint.h>
