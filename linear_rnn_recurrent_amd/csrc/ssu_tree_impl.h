@@ -480,28 +480,9 @@ __global__ __launch_bounds__(kTreeNT) __attribute__((amdgpu_waves_per_eu(tree_wa
                     reinterpret_cast<u32x2 *>(xw)[0] = u32x2{w[0], w[1]};
                     reinterpret_cast<u32x2 *>(xw)[1] = u32x2{w[2], w[3]};
                 }
-                if (stash && valid) {
-                    float f[XV];
-                    if constexpr (XB == 4) {
-#pragma unroll
-                        for (int e = 0; e < 4; ++e)
-                            f[e] = __uint_as_float(w[e]);
-                    } else {
-#pragma unroll
-                        for (int e = 0; e < 4; ++e) {
-                            f[2 * e] = cvt_raw1<IOT>(w[e] & 0xffffu);
-                            f[2 * e + 1] = cvt_raw1<IOT>(w[e] >> 16);
-                        }
-                    }
-                    unsigned char *dst = reinterpret_cast<unsigned char *>(ubase) +
-                                         (uint32_t)((m * NSTR + rbase + rl) * 4);
-#pragma unroll
-                    for (int e = 0; e < XV; e += 4)
-                        *reinterpret_cast<float4 *>(dst + 4 * e) =
-                            make_float4(f[e], f[e + 1], f[e + 2], f[e + 3]);
-                }
             }
         }
+        // (the fp32 x stash of this path is written after the chunk loop)
     } else {
         for (int e = tid; e < M * 64; e += NT) {
             const int m = e >> 6, rl = e & 63, r = rbase + rl;
@@ -807,6 +788,41 @@ __global__ __launch_bounds__(kTreeNT) __attribute__((amdgpu_waves_per_eu(tree_wa
         }
         gcur = gnext;
         __syncthreads();
+    }
+
+    // ---- the fp32 x stash (16-byte x vectors): written last, from a second
+    // read of x, with non-temporal stores. Every workgroup starts together and
+    // streams its state and x in the prologue; stash stores there (twice the
+    // bytes of x) lengthened that memory-bound phase, while here they overlap
+    // other workgroups' chunk loops, which move little data ----
+    if (stash && xvec) {
+        constexpr int VPN = 64 / XV;  // vectors per node
+        for (int v = tid; v < M * VPN; v += NT) {
+            const int m = v / VPN, rl = XV * (v % VPN);
+            if (rbase + rl < Dm) {
+                const uint32_t o = (uint32_t)(m * NSTR + rbase + rl);
+                const u32x4 w = *reinterpret_cast<const u32x4 *>(xbase + o * XB);
+                float f[XV];
+                if constexpr (XB == 4) {
+#pragma unroll
+                    for (int e = 0; e < 4; ++e)
+                        f[e] = __uint_as_float(w[e]);
+                } else {
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) {
+                        f[2 * e] = cvt_raw1<IOT>(w[e] & 0xffffu);
+                        f[2 * e + 1] = cvt_raw1<IOT>(w[e] >> 16);
+                    }
+                }
+                float *dst = ubase + o;
+#pragma unroll
+                for (int e = 0; e < XV; e += 4)
+                    __builtin_nontemporal_store(
+                        u32x4{__float_as_uint(f[e]), __float_as_uint(f[e + 1]),
+                              __float_as_uint(f[e + 2]), __float_as_uint(f[e + 3])},
+                        reinterpret_cast<u32x4 *>(dst + e));
+            }
+        }
     }
 }
 
