@@ -292,10 +292,10 @@ __global__ __launch_bounds__(kPmNT) __attribute__((amdgpu_waves_per_eu(NS <= 128
                         if (2 * p + q < nv) {
                             float *sb = sBrow + (uint32_t)((t0 + 2 * p + q) * G * NS + col);
 #pragma unroll
-                            for (int i = 0; i < 8; i += 4)
-                                *reinterpret_cast<float4 *>(sb + i) =
-                                    make_float4(bf16_to_f32(h16(rB[k][q], i)), bf16_to_f32(h16(rB[k][q], i + 1)),
-                                                bf16_to_f32(h16(rB[k][q], i + 2)), bf16_to_f32(h16(rB[k][q], i + 3)));
+                            for (int i = 0; i < 8; i += 4)  // (bf16 -> fp32: the bits shifted up)
+                                __builtin_nontemporal_store(u32x4{h16(rB[k][q], i) << 16, h16(rB[k][q], i + 1) << 16,
+                                                                  h16(rB[k][q], i + 2) << 16, h16(rB[k][q], i + 3) << 16},
+                                                            reinterpret_cast<u32x4 *>(sb + i));
                         }
                     }
                 }
@@ -311,9 +311,9 @@ __global__ __launch_bounds__(kPmNT) __attribute__((amdgpu_waves_per_eu(NS <= 128
                     float *su = sUrow + (uint32_t)((t0 + 2 * xp + q) * NSTR + xb8);
 #pragma unroll
                     for (int i = 0; i < 8; i += 4)
-                        *reinterpret_cast<float4 *>(su + i) =
-                            make_float4(bf16_to_f32(h16(w[q], i)), bf16_to_f32(h16(w[q], i + 1)),
-                                        bf16_to_f32(h16(w[q], i + 2)), bf16_to_f32(h16(w[q], i + 3)));
+                        __builtin_nontemporal_store(u32x4{h16(w[q], i) << 16, h16(w[q], i + 1) << 16,
+                                                          h16(w[q], i + 2) << 16, h16(w[q], i + 3) << 16},
+                                                    reinterpret_cast<u32x4 *>(su + i));
                 }
             }
 #pragma unroll
@@ -587,14 +587,21 @@ __global__ __launch_bounds__(kPmNT) __attribute__((amdgpu_waves_per_eu(NS <= 128
         __syncthreads();
     }
 
-    // ---- tokens beyond the context: zero outputs and zero stash ----
-    for (int i = tid; i < (T - Lb) * 64; i += NT) {
-        const int rr = rbase + (i & 63);
-        if (rr < Dm) {
-            const int64_t o = ((bT + Lb + (i >> 6)) * H + h) * Dm + rr;
-            st_elem<bf16_t>(out, o, 0.0f);
-            if (stash)
-                st_u[o] = 0.0f;
+    // ---- tokens beyond the context: zero outputs and zero stash, in 16-byte
+    // stores (dim is a multiple of 8 and out, the x stash 16-byte aligned) ----
+    {
+        const u32x4 zero = u32x4{0u, 0u, 0u, 0u};
+        for (int i = tid; i < (T - Lb) * 8; i += NT) {  // 8 bf16 outputs per store
+            const int rr = rbase + 8 * (i & 7);
+            if (rr < Dm)
+                *reinterpret_cast<u32x4 *>(orow + (uint32_t)(((Lb + (i >> 3)) * NSTR + rr) * 2)) = zero;
+        }
+        if (stash) {
+            for (int i = tid; i < (T - Lb) * 16; i += NT) {  // 4 fp32 stash values per store
+                const int rr = 4 * (i & 15);
+                if (rbase + rr < Dm)
+                    __builtin_nontemporal_store(zero, reinterpret_cast<u32x4 *>(sUrow + (uint32_t)((Lb + (i >> 4)) * NSTR + rr)));
+            }
         }
     }
     if (stash && rb == 0) {
@@ -603,9 +610,10 @@ __global__ __launch_bounds__(kPmNT) __attribute__((amdgpu_waves_per_eu(NS <= 128
             st_dt[(bT + t) * H + h] = 0.0f;
         }
     }
-    if (writes_B) {
-        for (int i = tid; i < (T - Lb) * NS; i += NT)
-            st_B[((bT + Lb + i / NS) * G + g) * NS + (i % NS)] = 0.0f;
+    if (writes_B) {  // B rows are 16-byte aligned (dstate a multiple of 32)
+        for (int i = tid; i < (T - Lb) * (NS / 4); i += NT)
+            __builtin_nontemporal_store(u32x4{0u, 0u, 0u, 0u},
+                                        reinterpret_cast<u32x4 *>(sBrow + (uint32_t)((Lb + i / (NS / 4)) * G * NS + 4 * (i % (NS / 4)))));
     }
 
     // ---- the final state (without the stash the pool row is updated) ----
