@@ -478,7 +478,7 @@ __global__ __launch_bounds__(64 * NW) void ssu_prefill_kernel(
 }  // namespace
 }  // namespace ssu
 
-// the matrix-core prefill (bf16 operands), dispatched to from launch_prefill_bc
+// the matrix-core prefill (bf16 or fp16 operands), dispatched to from launch_prefill_bc
 #include "ssu_prefill_mm.h"
 
 namespace ssu {
@@ -521,14 +521,14 @@ hipError_t launch_prefill_cfg(const PrefillParams &p, hipStream_t stream)
 template <typename ST, typename IOT, typename BCT>
 hipError_t launch_prefill_bc(const PrefillParams &p, hipStream_t stream)
 {
-    if constexpr (__is_same(IOT, bf16_t) && __is_same(BCT, bf16_t)) {
+    if constexpr (__is_same(IOT, BCT) && (__is_same(IOT, bf16_t) || __is_same(IOT, _Float16))) {
         if (prefill_mm_fits(p)) {
             const PrefillShape sh = prefill_shape(p);
             switch (p.d.dstate) {
-            case 32: return launch_prefill_mm<ST, 32>(p, sh, stream);
-            case 64: return launch_prefill_mm<ST, 64>(p, sh, stream);
-            case 128: return launch_prefill_mm<ST, 128>(p, sh, stream);
-            case 256: return launch_prefill_mm<ST, 256>(p, sh, stream);
+            case 32: return launch_prefill_mm<ST, IOT, BCT, 32>(p, sh, stream);
+            case 64: return launch_prefill_mm<ST, IOT, BCT, 64>(p, sh, stream);
+            case 128: return launch_prefill_mm<ST, IOT, BCT, 128>(p, sh, stream);
+            case 256: return launch_prefill_mm<ST, IOT, BCT, 256>(p, sh, stream);
             default: break;
             }
         }

@@ -3,8 +3,8 @@
 // invokeSelectiveStateUpdatePrefill: the decode step applied to tokens
 // t < L_b in order, outputs beyond L_b zero, optional replay stash with the
 // committed state read-only), evaluated a chunk of 32 tokens at a time in
-// closed form. Used for bf16 x/z/out with bf16 B/C (both exact as bf16
-// matrix-core operands) and dstate a multiple of 32.
+// closed form. Used for x/z/out and B/C both bf16 or both fp16 (exact as
+// 16-bit matrix-core operands) and dstate a multiple of 32.
 //
 // Within a chunk that starts from state S0 (a_k = A dt'_k, Lc[t] = sum of a_k
 // over k <= t, both within the chunk):
@@ -20,6 +20,11 @@
 //   S^T  = e^{Lc[last]} S^T + B^T . X'^T   (X'[r][j] = w_j x_j[r], w_j the
 //                              suffix weight; X' as three bf16 terms, so the
 //                              carried fp32 state keeps fp32 accuracy)
+// With fp16 B/C the products that take B or C run on v_mfma_f32_16x16x32_f16
+// (B . C^T as it is; C . S^T and B^T . X'^T with S and X' scaled per row by a
+// power of two that puts the row's largest magnitude in [2^14, 2^15), then cut
+// into two fp16 parts, the scale undone on the fp32 result), and fp16 x enters
+// Q . X^T as two exact bf16 parts (x = hi + lo).
 // The state never leaves registers: each lane holds S[r][16 nt + 4 qg + v],
 // the accumulator layout of the last product, and the inter-chunk product
 // takes it as its B operand directly by ordering the dstate index of the
@@ -41,6 +46,8 @@ namespace {
 typedef float pm_f32x4 __attribute__((ext_vector_type(4)));
 typedef __bf16 pm_bf16x8 __attribute__((ext_vector_type(8)));
 typedef __bf16 pm_bf16x2 __attribute__((ext_vector_type(2)));
+typedef _Float16 pm_f16x8 __attribute__((ext_vector_type(8)));
+typedef _Float16 pm_f16x2 __attribute__((ext_vector_type(2)));
 typedef float pm_f32x2 __attribute__((ext_vector_type(2)));
 
 constexpr int kPmTT = 32;   // tokens per chunk (two 16-token MFMA tiles)
@@ -85,11 +92,93 @@ __host__ __device__ inline PmLds pm_lds(int NS)
 
 // An 8-element operand from two runs of 4 bf16 in LDS: at p and at p + 32
 // bytes (16 elements on)
-__device__ __forceinline__ pm_bf16x8 pm_op(const unsigned char *p)
+__device__ __forceinline__ u32x4 pm_op(const unsigned char *p)
 {
     const u32x2 lo = *reinterpret_cast<const u32x2 *>(p);
     const u32x2 hi = *reinterpret_cast<const u32x2 *>(p + 32);
-    return __builtin_bit_cast(pm_bf16x8, u32x4{lo[0], lo[1], hi[0], hi[1]});
+    return u32x4{lo[0], lo[1], hi[0], hi[1]};
+}
+
+// D += A B on the matrix cores for 16-bit operands of type T (bf16_t or
+// _Float16), eight per lane given as their bits
+template <typename T>
+__device__ __forceinline__ pm_f32x4 pm_mfma(const u32x4 &a, const u32x4 &b, const pm_f32x4 &c)
+{
+    if constexpr (__is_same(T, _Float16))
+        return __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(pm_f16x8, a),
+                                                      __builtin_bit_cast(pm_f16x8, b), c, 0, 0, 0);
+    else
+        return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(pm_bf16x8, a),
+                                                       __builtin_bit_cast(pm_bf16x8, b), c, 0, 0, 0);
+}
+
+// a 16-bit value of type T (its bits) as fp32, and eight of them
+template <typename T>
+__device__ __forceinline__ float pm_to_f32(uint32_t h)
+{
+    if constexpr (__is_same(T, _Float16))
+        return f16_to_f32(h);
+    else
+        return bf16_to_f32(h);
+}
+template <typename T>
+__device__ __forceinline__ void pm_to_f32x8(const u32x4 &w, float (&f)[8])
+{
+    if constexpr (__is_same(T, _Float16)) {
+        const pm_f16x8 v = __builtin_bit_cast(pm_f16x8, w);
+#pragma unroll
+        for (int e = 0; e < 8; ++e)
+            f[e] = (float)v[e];
+    } else {
+        const pm_bf16x8 v = __builtin_bit_cast(pm_bf16x8, w);
+#pragma unroll
+        for (int e = 0; e < 8; ++e)
+            f[e] = (float)v[e];
+    }
+}
+
+// two fp32 values rounded to nearest-even in type T, packed into one word
+template <typename T>
+__device__ __forceinline__ uint32_t pm_pack2(float a, float b)
+{
+    if constexpr (__is_same(T, _Float16))
+        return __builtin_bit_cast(uint32_t, __builtin_convertvector((pm_f32x2){a, b}, pm_f16x2));
+    else
+        return __builtin_bit_cast(uint32_t, __builtin_convertvector((pm_f32x2){a, b}, pm_bf16x2));
+}
+
+// The largest of m over the four lanes ln + 16 q of a wave (the lanes that
+// hold one row's values in the accumulator and operand layouts used here)
+__device__ __forceinline__ float pm_row_max(float m)
+{
+    const auto a = __builtin_amdgcn_permlane32_swap(__float_as_uint(m), __float_as_uint(m), false, false);
+    m = fmaxf(__uint_as_float(a[0]), __uint_as_float(a[1]));
+    const auto b = __builtin_amdgcn_permlane16_swap(__float_as_uint(m), __float_as_uint(m), false, false);
+    return fmaxf(__uint_as_float(b[0]), __uint_as_float(b[1]));
+}
+
+// The power of two 2^k that puts a row's largest magnitude m in [2^14, 2^15)
+// (k clamped to the normal range; m = 0 gives 2^15), and its inverse
+__device__ __forceinline__ void pm_row_scale(float m, float &sc, float &inv)
+{
+    const int k = min(max(15 - __builtin_amdgcn_frexp_expf(m), -113), 126);
+    sc = __builtin_amdgcn_ldexpf(1.0f, k);
+    inv = __builtin_amdgcn_ldexpf(1.0f, -k);
+}
+
+// sc f (|sc f| < 2^15) as two fp16 parts: the nearest fp16, then the nearest
+// fp16 to the remainder (exact in fp32); relative error 2^-22, or 2^-25 absolute
+// where the remainder falls below fp16's normal range
+__device__ __forceinline__ void pm_split_f16(const float (&f)[8], float sc, u32x4 (&o)[2])
+{
+#pragma unroll
+    for (int e = 0; e < 8; e += 2) {
+        const float a = f[e] * sc, b = f[e + 1] * sc;
+        const pm_f16x2 p = __builtin_convertvector((pm_f32x2){a, b}, pm_f16x2);
+        const pm_f16x2 q = __builtin_convertvector((pm_f32x2){a - (float)p[0], b - (float)p[1]}, pm_f16x2);
+        o[0][e >> 1] = __builtin_bit_cast(uint32_t, p);
+        o[1][e >> 1] = __builtin_bit_cast(uint32_t, q);
+    }
 }
 
 // fp32 values as `terms` bf16 parts (round to nearest, the remainder split again)
@@ -115,7 +204,8 @@ __device__ __forceinline__ void pm_split(const float (&f)[8], pm_bf16x8 (&o)[TER
     }
 }
 
-template <typename ST, int NS>
+// IOT: x/z/out type, BCT: B/C type (bf16_t or _Float16)
+template <typename ST, typename IOT, typename BCT, int NS>
 __global__ __launch_bounds__(kPmNT) __attribute__((amdgpu_waves_per_eu(NS <= 128 ? 3 : 1))) void ssu_prefill_mm_kernel(
     const void *__restrict__ x, const float *__restrict__ A, const void *__restrict__ Bm,
     const void *__restrict__ Cm, const float *__restrict__ dt, const float *__restrict__ dt_bias,
@@ -132,6 +222,8 @@ __global__ __launch_bounds__(kPmNT) __attribute__((amdgpu_waves_per_eu(NS <= 128
     constexpr int NCB = NS / 8;                      // 16-byte column blocks of a B (C) row
     constexpr int NVP = (16 * NCB + NT - 1) / NT;    // token pairs x column blocks per thread
     static_assert(NS % 32 == 0, "dstate in whole 32-column steps");
+    constexpr bool BCH = __is_same(BCT, _Float16);  // fp16 B/C: scaled fp16 parts of S and X'
+    constexpr bool IOH = __is_same(IOT, _Float16);  // fp16 x: two bf16 parts in Q . X^T
 
     extern __shared__ __attribute__((aligned(16))) unsigned char lds[];
     const PmLds L = pm_lds(NS);
@@ -193,7 +285,7 @@ __global__ __launch_bounds__(kPmNT) __attribute__((amdgpu_waves_per_eu(NS <= 128
         for (int i = tid; i < T * 64; i += NT) {
             const int r = rbase + (i & 63);
             if (r < Dm)
-                st_elem<bf16_t>(out, ((bT + (i >> 6)) * H + h) * Dm + r, 0.0f);
+                st_elem<IOT>(out, ((bT + (i >> 6)) * H + h) * Dm + r, 0.0f);
         }
         return;
     }
@@ -263,6 +355,9 @@ __global__ __launch_bounds__(kPmNT) __attribute__((amdgpu_waves_per_eu(NS <= 128
     // 16-bit element i of a 16-byte register group; the elements i of two
     // groups as one word (one v_perm_b32: bytes of the low or high halves)
     auto h16 = [](const u32x4 &w, int i) { return (w[i >> 1] >> (16 * (i & 1))) & 0xffffu; };
+    // the same element as fp32 bits, for the stash (bf16: the bits shifted up)
+    auto c32 = [&](const u32x4 &w, int i) { return __float_as_uint(pm_to_f32<BCT>(h16(w, i))); };
+    auto x32 = [&](const u32x4 &w, int i) { return __float_as_uint(pm_to_f32<IOT>(h16(w, i))); };
     auto pair16 = [](const u32x4 &w0, const u32x4 &w1, int i) {
         // selector bytes 0-3 pick from w0's word, 4-7 from w1's (perm takes (hi, lo))
         return __builtin_amdgcn_perm(w1[i >> 1], w0[i >> 1], (i & 1) ? 0x07060302u : 0x05040100u);
@@ -292,9 +387,9 @@ __global__ __launch_bounds__(kPmNT) __attribute__((amdgpu_waves_per_eu(NS <= 128
                         if (2 * p + q < nv) {
                             float *sb = sBrow + (uint32_t)((t0 + 2 * p + q) * G * NS + col);
 #pragma unroll
-                            for (int i = 0; i < 8; i += 4)  // (bf16 -> fp32: the bits shifted up)
-                                __builtin_nontemporal_store(u32x4{h16(rB[k][q], i) << 16, h16(rB[k][q], i + 1) << 16,
-                                                                  h16(rB[k][q], i + 2) << 16, h16(rB[k][q], i + 3) << 16},
+                            for (int i = 0; i < 8; i += 4)
+                                __builtin_nontemporal_store(u32x4{c32(rB[k][q], i), c32(rB[k][q], i + 1),
+                                                                  c32(rB[k][q], i + 2), c32(rB[k][q], i + 3)},
                                                             reinterpret_cast<u32x4 *>(sb + i));
                         }
                     }
@@ -311,8 +406,8 @@ __global__ __launch_bounds__(kPmNT) __attribute__((amdgpu_waves_per_eu(NS <= 128
                     float *su = sUrow + (uint32_t)((t0 + 2 * xp + q) * NSTR + xb8);
 #pragma unroll
                     for (int i = 0; i < 8; i += 4)
-                        __builtin_nontemporal_store(u32x4{h16(w[q], i) << 16, h16(w[q], i + 1) << 16,
-                                                          h16(w[q], i + 2) << 16, h16(w[q], i + 3) << 16},
+                        __builtin_nontemporal_store(u32x4{x32(w[q], i), x32(w[q], i + 1),
+                                                          x32(w[q], i + 2), x32(w[q], i + 3)},
                                                     reinterpret_cast<u32x4 *>(su + i));
                 }
             }
@@ -432,10 +527,21 @@ __global__ __launch_bounds__(kPmNT) __attribute__((amdgpu_waves_per_eu(NS <= 128
         pm_f32x4 ay[2] = {pm_f32x4{0.0f, 0.0f, 0.0f, 0.0f}, pm_f32x4{0.0f, 0.0f, 0.0f, 0.0f}};
         pm_f32x4 ag[3] = {pm_f32x4{0.0f, 0.0f, 0.0f, 0.0f}, pm_f32x4{0.0f, 0.0f, 0.0f, 0.0f},
                           pm_f32x4{0.0f, 0.0f, 0.0f, 0.0f}};
+        // fp16 B/C: S enters C . S^T scaled per row (this lane's row rl)
+        float ssc = 1.0f, sinv = 1.0f;
+        if constexpr (BCH) {
+            float m = 0.0f;
+#pragma unroll
+            for (int nt = 0; nt < NT16; ++nt)
+#pragma unroll
+                for (int v = 0; v < 4; ++v)
+                    m = fmaxf(m, fabsf(S[nt][v]));
+            pm_row_scale(pm_row_max(m), ssc, sinv);
+        }
 #pragma unroll
         for (int kk = 0; kk < KN; ++kk) {
             // dstate order of step kk for lane group qg: 32kk+4qg+e (e<4), 32kk+16+4qg+e-4
-            pm_bf16x8 cop[2], bop[2];
+            u32x4 cop[2], bop[2];
 #pragma unroll
             for (int t = 0; t < 2; ++t) {
                 const int o = (16 * t + ln) * PC + (((32 * kk + 4 * qg) * 2) ^ pm_swz(ln));
@@ -448,28 +554,35 @@ __global__ __launch_bounds__(kPmNT) __attribute__((amdgpu_waves_per_eu(NS <= 128
                 sv[e] = S[2 * kk][e];
                 sv[4 + e] = S[2 * kk + 1][e];
             }
-            pm_bf16x8 sp[2];
-            pm_split<2>(sv, sp);
+            u32x4 sp[2];
+            if constexpr (BCH) {
+                pm_split_f16(sv, ssc, sp);
+            } else {
+                pm_bf16x8 sb[2];
+                pm_split<2>(sv, sb);
+                sp[0] = __builtin_bit_cast(u32x4, sb[0]);
+                sp[1] = __builtin_bit_cast(u32x4, sb[1]);
+            }
 #pragma unroll
             for (int t = 0; t < 2; ++t)
 #pragma unroll
                 for (int uu = 0; uu < 2; ++uu)
-                    ay[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(cop[t], sp[uu], ay[t], 0, 0, 0);
-            ag[0] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(bop[0], cop[0], ag[0], 0, 0, 0);
-            ag[1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(bop[0], cop[1], ag[1], 0, 0, 0);
-            ag[2] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(bop[1], cop[1], ag[2], 0, 0, 0);
+                    ay[t] = pm_mfma<BCT>(cop[t], sp[uu], ay[t]);
+            ag[0] = pm_mfma<BCT>(bop[0], cop[0], ag[0]);
+            ag[1] = pm_mfma<BCT>(bop[0], cop[1], ag[1]);
+            ag[2] = pm_mfma<BCT>(bop[1], cop[1], ag[2]);
         }
 
         // inter-chunk term decays to token t: lanes hold tokens 16t + 4qg + v
-        // (the outputs are bf16: the hardware exp2 is accurate enough here; the
-        // state's own weights use expf)
+        // (the outputs are 16-bit: the hardware exp2 is accurate enough here; the
+        // state's own weights use expf); with fp16 B/C the row scale is undone
 #pragma unroll
         for (int t = 0; t < 2; ++t) {
             const float4 l4 = *reinterpret_cast<const float4 *>(lcs + 16 * t + 4 * qg);
-            ay[t][0] *= __builtin_amdgcn_exp2f(l4.x);
-            ay[t][1] *= __builtin_amdgcn_exp2f(l4.y);
-            ay[t][2] *= __builtin_amdgcn_exp2f(l4.z);
-            ay[t][3] *= __builtin_amdgcn_exp2f(l4.w);
+            ay[t][0] *= __builtin_amdgcn_exp2f(l4.x) * sinv;
+            ay[t][1] *= __builtin_amdgcn_exp2f(l4.y) * sinv;
+            ay[t][2] *= __builtin_amdgcn_exp2f(l4.z) * sinv;
+            ay[t][3] *= __builtin_amdgcn_exp2f(l4.w) * sinv;
         }
 
         // ---- Q in registers: lane (t = 16tt + ln, qg) element e holds source
@@ -481,8 +594,20 @@ __global__ __launch_bounds__(kPmNT) __attribute__((amdgpu_waves_per_eu(NS <= 128
         // 2^(Lc[t]-Lc[j]) dt'_j as 2^(Lc[t]-Lc[j0]) (2^(Lc[j0]-Lc[j]) dt'_j): one exp2 per quad
         const float rd[8] = {rd0.x, rd0.y, rd0.z, rd0.w, rd1.x, rd1.y, rd1.z, rd1.w};
         const float lj[8] = {lj0.x, lj0.y, lj0.z, lj0.w, lj1.x, lj1.y, lj1.z, lj1.w};
-        // x^T operand in the same source order: lane (row rl, qg)
-        const pm_bf16x8 xop = pm_op(Xt + rl * PT + (4 * qg) * 2);
+        // x^T operand in the same source order: lane (row rl, qg); fp16 x as
+        // two exact bf16 parts
+        const u32x4 xop = pm_op(Xt + rl * PT + (4 * qg) * 2);
+        u32x4 xq[2];
+        if constexpr (IOH) {
+            float xs[8];
+            pm_to_f32x8<IOT>(xop, xs);
+            pm_bf16x8 xb[2];
+            pm_split<2>(xs, xb);
+            xq[0] = __builtin_bit_cast(u32x4, xb[0]);
+            xq[1] = __builtin_bit_cast(u32x4, xb[1]);
+        } else {
+            xq[0] = xop;
+        }
         // Q of token tile t: per quad, or (chunks with extreme decays) per entry
         auto q_tile = [&](auto per_entry, int t) {
             const int tq = 16 * t + ln;  // this lane's token as a Q row
@@ -509,7 +634,9 @@ __global__ __launch_bounds__(kPmNT) __attribute__((amdgpu_waves_per_eu(NS <= 128
             pm_split<2>(qv, qp);
 #pragma unroll
             for (int uu = 0; uu < 2; ++uu)
-                ay[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qp[uu], xop, ay[t], 0, 0, 0);
+                ay[t] = pm_mfma<bf16_t>(__builtin_bit_cast(u32x4, qp[uu]), xq[0], ay[t]);
+            if constexpr (IOH)  // (the lo x lo part, 2^-18 of the product, is left out)
+                ay[t] = pm_mfma<bf16_t>(__builtin_bit_cast(u32x4, qp[0]), xq[1], ay[t]);
         };
         if (__builtin_amdgcn_readfirstlane(big_all[cs]) != 0) {
 #pragma unroll
@@ -523,9 +650,16 @@ __global__ __launch_bounds__(kPmNT) __attribute__((amdgpu_waves_per_eu(NS <= 128
         // D x_t in fp32: the x^T operand holds x of tokens 4qg + v (elements
         // 0-3) and 16 + 4qg + v (4-7) of row rl, the tokens of ay[0][v], ay[1][v]
         float xf[8];
+        if constexpr (IOH) {  // x = hi + lo exactly (fewer registers than converting x again)
+            float xh[8], xl[8];
+            pm_to_f32x8<bf16_t>(xq[0], xh);
+            pm_to_f32x8<bf16_t>(xq[1], xl);
 #pragma unroll
-        for (int e = 0; e < 8; ++e)
-            xf[e] = (float)xop[e];
+            for (int e = 0; e < 8; ++e)
+                xf[e] = xh[e] + xl[e];
+        } else {
+            pm_to_f32x8<IOT>(xop, xf);
+        }
 #pragma unroll
         for (int v = 0; v < 4; ++v) {
             ay[0][v] = fmaf(dskip, xf[v], ay[0][v]);
@@ -548,18 +682,40 @@ __global__ __launch_bounds__(kPmNT) __attribute__((amdgpu_waves_per_eu(NS <= 128
 #pragma unroll
             for (int e = 0; e < 8; ++e)
                 xw[e] = wj[e] * xf[e];
-            pm_bf16x8 xp[3];
-            pm_split<3>(xw, xp);
             const float ws = tot_all[cs];
+            if constexpr (BCH) {
+                // X' scaled per row into two fp16 parts; the product, unscaled,
+                // is added to the decayed state
+                float m = 0.0f;
 #pragma unroll
-            for (int nt = 0; nt < NT16; ++nt) {
-                const pm_bf16x8 bt = pm_op(Bt + (16 * nt + ln) * PT + (4 * qg) * 2);
+                for (int e = 0; e < 8; ++e)
+                    m = fmaxf(m, fabsf(xw[e]));
+                float xsc, xinv;
+                pm_row_scale(pm_row_max(m), xsc, xinv);
+                u32x4 xh[2];
+                pm_split_f16(xw, xsc, xh);
 #pragma unroll
-                for (int v = 0; v < 4; ++v)
-                    S[nt][v] *= ws;
+                for (int nt = 0; nt < NT16; ++nt) {
+                    const u32x4 bt = pm_op(Bt + (16 * nt + ln) * PT + (4 * qg) * 2);
+                    pm_f32x4 pr = pm_mfma<_Float16>(bt, xh[0], pm_f32x4{0.0f, 0.0f, 0.0f, 0.0f});
+                    pr = pm_mfma<_Float16>(bt, xh[1], pr);
 #pragma unroll
-                for (int uu = 0; uu < 3; ++uu)
-                    S[nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(bt, xp[uu], S[nt], 0, 0, 0);
+                    for (int v = 0; v < 4; ++v)
+                        S[nt][v] = fmaf(pr[v], xinv, S[nt][v] * ws);
+                }
+            } else {
+                pm_bf16x8 xp[3];
+                pm_split<3>(xw, xp);
+#pragma unroll
+                for (int nt = 0; nt < NT16; ++nt) {
+                    const u32x4 bt = pm_op(Bt + (16 * nt + ln) * PT + (4 * qg) * 2);
+#pragma unroll
+                    for (int v = 0; v < 4; ++v)
+                        S[nt][v] *= ws;
+#pragma unroll
+                    for (int uu = 0; uu < 3; ++uu)
+                        S[nt] = pm_mfma<bf16_t>(bt, __builtin_bit_cast(u32x4, xp[uu]), S[nt]);
+                }
             }
         }
         __syncthreads();
@@ -573,25 +729,26 @@ __global__ __launch_bounds__(kPmNT) __attribute__((amdgpu_waves_per_eu(NS <= 128
                 const u32x4 zw = *reinterpret_cast<const u32x4 *>(Zs + xtok * PZ + xr8 * 2);
 #pragma unroll
                 for (int i = 0; i < 8; ++i) {
-                    const float zi = bf16_to_f32((zw[i >> 1] >> (16 * (i & 1))) & 0xffffu);
+                    const float zi = pm_to_f32<IOT>((zw[i >> 1] >> (16 * (i & 1))) & 0xffffu);
                     y[i] *= zi * __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(-1.4426950408889634f * zi));
                 }
             }
             u32x4 ow;  // round to nearest even, two values per conversion
 #pragma unroll
             for (int i = 0; i < 4; ++i)
-                ow[i] = __builtin_bit_cast(uint32_t, __builtin_convertvector((pm_f32x2){y[2 * i], y[2 * i + 1]}, pm_bf16x2));
+                ow[i] = pm_pack2<IOT>(y[2 * i], y[2 * i + 1]);
             *reinterpret_cast<u32x4 *>(orow + (uint32_t)(((t0 + xtok) * NSTR + rbase + xr8) * 2)) = ow;
         }
         store_chunk(t0 + TT, min(TT, Lb - t0 - TT));  // nothing live past the last chunk
         __syncthreads();
     }
 
-    // ---- tokens beyond the context: zero outputs and zero stash, in 16-byte
+    // ---- tokens beyond the context: zero outputs and zero stash (+0.0 is all
+    // zero bits in every type), in 16-byte
     // stores (dim is a multiple of 8 and out, the x stash 16-byte aligned) ----
     {
         const u32x4 zero = u32x4{0u, 0u, 0u, 0u};
-        for (int i = tid; i < (T - Lb) * 8; i += NT) {  // 8 bf16 outputs per store
+        for (int i = tid; i < (T - Lb) * 8; i += NT) {  // 8 16-bit outputs per store
             const int rr = rbase + 8 * (i & 7);
             if (rr < Dm)
                 *reinterpret_cast<u32x4 *>(orow + (uint32_t)(((Lb + (i >> 3)) * NSTR + rr) * 2)) = zero;
@@ -627,7 +784,7 @@ __global__ __launch_bounds__(kPmNT) __attribute__((amdgpu_waves_per_eu(NS <= 128
     }
 }
 
-template <typename ST, int NS>
+template <typename ST, typename IOT, typename BCT, int NS>
 hipError_t launch_prefill_mm(const PrefillParams &p, const PrefillShape &sh, hipStream_t stream)
 {
     const DecodeParams &d = p.d;
@@ -635,7 +792,7 @@ hipError_t launch_prefill_mm(const PrefillParams &p, const PrefillShape &sh, hip
     if (blocks > 0x7fffffff)
         return hipErrorInvalidConfiguration;
     const int lds = pm_lds(NS).total;
-    auto kern = ssu_prefill_mm_kernel<ST, NS>;
+    auto kern = ssu_prefill_mm_kernel<ST, IOT, BCT, NS>;
     if (lds > 64 * 1024) {
         // above 64 KiB of dynamic LDS the kernel must be allowed it, once per device
         static std::atomic<int> allowed[64];  // zero-initialised; benign races between host threads
@@ -659,8 +816,8 @@ hipError_t launch_prefill_mm(const PrefillParams &p, const PrefillShape &sh, hip
     return hipGetLastError();
 }
 
-// The matrix-core prefill takes bf16 x/z/out and B/C (exact operands), dstate a
-// multiple of 32, dim a multiple of 8 and 16-byte aligned x, z, out and x
+// The matrix-core prefill takes x/z/out and B/C both bf16 or both fp16 (exact
+// operands), dstate a multiple of 32, dim a multiple of 8 and 16-byte aligned x, z, out and x
 // stash (whole 8-row vectors); everything else runs on ssu_prefill_kernel.
 // Offsets within one batch row's tokens are formed in 32 bits: a row's x, z,
 // out, B and C (and the fp32 x and B stash) must span under 2^31 bytes, with a
@@ -671,7 +828,8 @@ inline bool prefill_mm_fits(const PrefillParams &p)
     auto al16 = [](const void *q) { return (reinterpret_cast<uintptr_t>(q) & 15) == 0; };
     const int64_t per_token = std::max((int64_t)d.nheads * d.dim, (int64_t)d.ngroups * d.dstate);
     const bool offsets_fit = (int64_t)p.seq_len * per_token * 4 < ((int64_t)1 << 31);
-    return offsets_fit && d.io_dtype == kBF16 && d.bc_dtype == kBF16 && d.dstate % 32 == 0 && d.dim % 8 == 0 &&
+    const bool types = (d.io_dtype == kBF16 || d.io_dtype == kF16) && d.bc_dtype == d.io_dtype;
+    return offsets_fit && types && d.dstate % 32 == 0 && d.dim % 8 == 0 &&
            al16(d.x) && al16(d.out) && (d.z == nullptr || al16(d.z)) &&
            (p.st_u == nullptr || al16(p.st_u)) && p.waves_per_wg == 0;
 }

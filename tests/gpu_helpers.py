@@ -26,10 +26,13 @@ def gpu(t):
     return None if t is None else t.cuda()
 
 
-def assert_close(got, ref, tol, what):
+def assert_close(got, ref, tol, what, scale=None):
+    """max|got - ref| <= tol * (1 + scale) elementwise; scale defaults to |ref|
+    (a caller may pass the magnitude of each value's terms instead, which bounds
+    the rounding of a sum whose terms cancel)."""
     got = f64(got) if isinstance(got, torch.Tensor) else got
     err = np.abs(got - ref)
-    bound = tol * (1.0 + np.abs(ref))
+    bound = tol * (1.0 + (np.abs(ref) if scale is None else scale))
     bad = ~(err <= bound)
     if bad.any():
         i = np.unravel_index(np.argmax(np.where(bad, err / bound, 0)), err.shape)
@@ -45,6 +48,19 @@ def assert_bitwise(a, b, what):
     vb = b.contiguous().view(torch.uint8)
     if not torch.equal(va, vb):
         raise AssertionError(f"{what}: not bitwise identical")
+
+
+def misaligned(t):
+    """The values of a 16-bit tensor on the GPU, 2 bytes past a 16-byte boundary.
+
+    The matrix-core prefill reads x with 16-byte vector loads and is chosen only
+    for 16-byte aligned x; this routes a 16-bit prefill to the VALU kernel."""
+    assert t.element_size() == 2
+    buf = torch.empty(t.numel() + 8, dtype=t.dtype, device="cuda")
+    v = buf[1:1 + t.numel()].view(t.shape)
+    v.copy_(t)
+    assert v.data_ptr() % 16 == 2
+    return v
 
 
 def run_decode(w, state=None, out=None, **over):
@@ -102,6 +118,23 @@ def oracle_prefill(w, stash=False, **over):
                    context_lengths=a["context_lengths"], state_indices=a["state_indices"],
                    stash=S)
     return st, out, S
+
+
+def oracle_prefill_magnitude(w):
+    """The oracle's prefill of |state|, |x|, |B|, |C|, |D| and |z| with the same
+    decays and dt': every state entry and output as the sum of the magnitudes of
+    its terms (silu(|z|) >= |silu(z)|), the scale of fp32 rounding in any order
+    of evaluation where the terms cancel."""
+    a = {k: f64(v) for k, v in w.tensors.items()}
+    for k in ("state", "x", "B", "C", "D", "z"):
+        if a.get(k) is not None:
+            a[k] = np.abs(a[k])
+    st = a["state"].copy()
+    out = np.zeros(a["x"].shape)
+    oracle.prefill(a["x"], a["A"], a["B"], a["C"], a["dt"], st, out, dt_bias=a["dt_bias"],
+                   D=a["D"], z=a["z"], dt_softplus=w.dt_softplus,
+                   context_lengths=a["context_lengths"], state_indices=a["state_indices"])
+    return st, out
 
 
 def run_replay(w, **over):

@@ -9,7 +9,7 @@ import torch
 from linear_rnn_recurrent_amd import inputs
 from gpu_helpers import (TOL_F32, assert_bitwise, assert_close, f64, oracle_decode, oracle_replay,
                          oracle_tree, run_decode, run_replay, run_tree, tol_for)
-from test_gpu_prefill import check_prefill
+from test_gpu_prefill import check_prefill, valu_kernel
 
 pytestmark = pytest.mark.gpu
 
@@ -41,11 +41,15 @@ def test_prefill_at_the_largest_dim(io):
 
 
 def test_prefill_at_the_largest_dstate_on_both_kernels():
-    for io in ("bf16", "f16"):
+    # bf16 and fp16 on the matrix cores; fp16 with x off 16-byte alignment and
+    # fp32 on the VALU kernel
+    for io in ("bf16", "f16", "f32"):
         w = inputs.prefill_workload(batch=2, seq_len=70, nheads=2, dim=64, dstate=256, ngroups=1,
                                     pool_rows=2, seed=73, io_dtype=io, bc_dtype=io,
                                     bc_std=256 ** -0.5, ctx=[70, 38])
         check_prefill(w)
+        if io == "f16":
+            check_prefill(w, **valu_kernel(w))
 
 
 @pytest.mark.parametrize("io", ["bf16", "f32"])

@@ -25,7 +25,7 @@ from linear_rnn_recurrent_amd import inputs, ssu_prefill, ssu_replay
 from gpu_helpers import (TOL_F32, assert_close, f64, gpu, oracle_decode, oracle_prefill,
                          oracle_replay, oracle_tree, run_decode, run_prefill, run_replay,
                          run_tree, tol_for)
-from test_gpu_prefill import check_prefill
+from test_gpu_prefill import check_prefill, valu_kernel
 
 pytestmark = pytest.mark.gpu
 
@@ -89,24 +89,26 @@ def check_collapsed_head_out(w, out, head=0):
                      f"collapsed outputs of row {b}")
 
 
-@pytest.mark.parametrize("io,bc", [("bf16", "bf16"), ("f32", "f32"), ("f16", "f16"),
-                                   ("f32", "bf16")])
-def test_prefill_decay_regimes(io, bc):
-    # bf16/bf16: the matrix-core kernel; the rest: the rescaled VALU recurrence
+@pytest.mark.parametrize("io,bc,kernel", [("bf16", "bf16", "mm"), ("f16", "f16", "mm"),
+                                          ("f32", "f32", "valu"), ("f16", "f16", "valu"),
+                                          ("f32", "bf16", "valu")])
+def test_prefill_decay_regimes(io, bc, kernel):
+    # bf16/bf16 and fp16/fp16: the matrix-core kernel, or (fp16 x off 16-byte
+    # alignment) the rescaled VALU recurrence, which also takes the other types
     w = strong_prefill_workload(io, bc)
-    st, out, _ = check_prefill(w)
+    st, out, _ = check_prefill(w, **(valu_kernel(w) if kernel == "valu" else {}))
     check_collapsed_head_state(w, st.cpu())
     check_collapsed_head_out(w, out.cpu())
 
 
-@pytest.mark.parametrize("io", ["bf16", "f32"])
+@pytest.mark.parametrize("io", ["bf16", "f16", "f32"])
 def test_prefill_decay_regimes_fp16_state_and_stash(io):
     w = strong_prefill_workload(io, io, state_dtype="f16", seed=62)
     check_prefill(w)
     check_prefill(w, stash=True)
 
 
-@pytest.mark.parametrize("io", ["bf16", "f32"])
+@pytest.mark.parametrize("io", ["bf16", "f16", "f32"])
 def test_prefill_stash_then_replay_in_the_collapse(io):
     # the stash of an extreme-decay prefill replayed over the whole context
     # equals the plain prefill (the replay applies exp(dA) = 0 directly)

@@ -1,10 +1,11 @@
 """Which prefill kernel a call takes, decided on the host and checked on the CPU.
 
-The matrix-core prefill (bf16 x/z/out and B/C, dstate a multiple of 32, dim a
-multiple of 8, 16-byte aligned x/out/z/x stash) forms its offsets inside one
-batch row in 32 bits, so a row whose tokens span 2^31 bytes or more (with a
-factor of two to spare: seq_len * max(nheads * dim, ngroups * dstate) * 4 must
-stay below 2^31) goes to the VALU kernel, whose offsets are 64-bit. The host
+The matrix-core prefill (x/z/out and B/C both bf16 or both fp16, dstate a
+multiple of 32, dim a multiple of 8, 16-byte aligned x/out/z/x stash) forms its
+offsets inside one batch row in 32 bits, so a row whose tokens span 2^31 bytes
+or more (with a factor of two to spare: seq_len * max(nheads * dim, ngroups *
+dstate) * 4 must stay below 2^31) goes to the VALU kernel, whose offsets are
+64-bit. The host
 predicate is compiled for the host alone (no device code, no GPU) and run here on
 the boundary cases; no out-of-bounds case ever runs on a GPU.
 """
@@ -24,7 +25,11 @@ CASES = [
     ("at the bound", dict(nheads=64, dim=64, seq_len=(1 << 29) // 4096), 0),
     ("B/C rows set the bound", dict(ngroups=64, dstate=256, nheads=64, dim=8, seq_len=(1 << 29) // 16384), 0),
     ("B/C rows just below", dict(ngroups=64, dstate=256, nheads=64, dim=8, seq_len=(1 << 29) // 16384 - 1), 1),
-    ("fp16 x/z/out", dict(io="kF16"), 0),
+    ("fp16 x/z/out and B/C", dict(io="kF16", bc="kF16"), 1),
+    ("fp16 x/z/out, bf16 B/C", dict(io="kF16"), 0),
+    ("bf16 x/z/out, fp16 B/C", dict(bc="kF16"), 0),
+    ("fp16 at dstate 16", dict(io="kF16", bc="kF16", dstate=16), 0),
+    ("fp16 x not 16-byte aligned", dict(io="kF16", bc="kF16", x_off=2), 0),
     ("fp32 B/C", dict(bc="kF32"), 0),
     ("dstate 16", dict(dstate=16), 0),
     ("dim 100", dict(dim=100), 0),
