@@ -20,11 +20,11 @@
 //   S^T  = e^{Lc[last]} S^T + B^T . X'^T   (X'[r][j] = w_j x_j[r], w_j the
 //                              suffix weight; X' as three bf16 terms, so the
 //                              carried fp32 state keeps fp32 accuracy)
-// With fp16 B/C the products that take B or C run on v_mfma_f32_16x16x32_f16
-// (B . C^T as it is; C . S^T and B^T . X'^T with S and X' scaled per row by a
-// power of two that puts the row's largest magnitude in [2^14, 2^15), then cut
-// into two fp16 parts, the scale undone on the fp32 result), and fp16 x enters
-// Q . X^T as two exact bf16 parts (x = hi + lo).
+// With fp16 operands every product runs on v_mfma_f32_16x16x32_f16: B . C^T
+// as it is; C . S^T, B^T . X'^T and Q . X^T with S and X' scaled per row, Q per
+// 16-token tile, by the power of two that puts the largest magnitude in
+// [2^14, 2^15), then cut into two fp16 parts, the scale undone on the fp32
+// result.
 // The state never leaves registers: each lane holds S[r][16 nt + 4 qg + v],
 // the accumulator layout of the last product, and the inter-chunk product
 // takes it as its B operand directly by ordering the dstate index of the
@@ -157,6 +157,16 @@ __device__ __forceinline__ float pm_row_max(float m)
     return fmaxf(__uint_as_float(b[0]), __uint_as_float(b[1]));
 }
 
+// The largest of m over the 64 lanes of a wave
+__device__ __forceinline__ float pm_wave_max(float m)
+{
+    m = pm_row_max(m);                   // the four rows of 16
+    m = fmaxf(m, dpp_f32<0xB1>(m));      // quad_perm [1,0,3,2]
+    m = fmaxf(m, dpp_f32<0x4E>(m));      // quad_perm [2,3,0,1]
+    m = fmaxf(m, dpp_f32<0x141>(m));     // row_half_mirror
+    return fmaxf(m, dpp_f32<0x140>(m));  // row_mirror
+}
+
 // The power of two 2^k that puts a row's largest magnitude m in [2^14, 2^15)
 // (k clamped to the normal range; m = 0 gives 2^15), and its inverse
 __device__ __forceinline__ void pm_row_scale(float m, float &sc, float &inv)
@@ -223,7 +233,7 @@ __global__ __launch_bounds__(kPmNT) __attribute__((amdgpu_waves_per_eu(NS <= 128
     constexpr int NVP = (16 * NCB + NT - 1) / NT;    // token pairs x column blocks per thread
     static_assert(NS % 32 == 0, "dstate in whole 32-column steps");
     constexpr bool BCH = __is_same(BCT, _Float16);  // fp16 B/C: scaled fp16 parts of S and X'
-    constexpr bool IOH = __is_same(IOT, _Float16);  // fp16 x: two bf16 parts in Q . X^T
+    constexpr bool IOH = __is_same(IOT, _Float16);  // fp16 x: Q . X^T on fp16, Q in scaled parts
 
     extern __shared__ __attribute__((aligned(16))) unsigned char lds[];
     const PmLds L = pm_lds(NS);
@@ -594,20 +604,8 @@ __global__ __launch_bounds__(kPmNT) __attribute__((amdgpu_waves_per_eu(NS <= 128
         // 2^(Lc[t]-Lc[j]) dt'_j as 2^(Lc[t]-Lc[j0]) (2^(Lc[j0]-Lc[j]) dt'_j): one exp2 per quad
         const float rd[8] = {rd0.x, rd0.y, rd0.z, rd0.w, rd1.x, rd1.y, rd1.z, rd1.w};
         const float lj[8] = {lj0.x, lj0.y, lj0.z, lj0.w, lj1.x, lj1.y, lj1.z, lj1.w};
-        // x^T operand in the same source order: lane (row rl, qg); fp16 x as
-        // two exact bf16 parts
+        // x^T operand in the same source order: lane (row rl, qg)
         const u32x4 xop = pm_op(Xt + rl * PT + (4 * qg) * 2);
-        u32x4 xq[2];
-        if constexpr (IOH) {
-            float xs[8];
-            pm_to_f32x8<IOT>(xop, xs);
-            pm_bf16x8 xb[2];
-            pm_split<2>(xs, xb);
-            xq[0] = __builtin_bit_cast(u32x4, xb[0]);
-            xq[1] = __builtin_bit_cast(u32x4, xb[1]);
-        } else {
-            xq[0] = xop;
-        }
         // Q of token tile t: per quad, or (chunks with extreme decays) per entry
         auto q_tile = [&](auto per_entry, int t) {
             const int tq = 16 * t + ln;  // this lane's token as a Q row
@@ -630,13 +628,29 @@ __global__ __launch_bounds__(kPmNT) __attribute__((amdgpu_waves_per_eu(NS <= 128
                 }
                 qv[e] = q;
             }
-            pm_bf16x8 qp[2];
-            pm_split<2>(qv, qp);
+            if constexpr (IOH) {
+                // fp16 x as it is; Q scaled per tile into two fp16 parts, the
+                // product unscaled into the output
+                float m = 0.0f;
 #pragma unroll
-            for (int uu = 0; uu < 2; ++uu)
-                ay[t] = pm_mfma<bf16_t>(__builtin_bit_cast(u32x4, qp[uu]), xq[0], ay[t]);
-            if constexpr (IOH)  // (the lo x lo part, 2^-18 of the product, is left out)
-                ay[t] = pm_mfma<bf16_t>(__builtin_bit_cast(u32x4, qp[0]), xq[1], ay[t]);
+                for (int e = 0; e < 8; ++e)
+                    m = fmaxf(m, fabsf(qv[e]));
+                float qsc, qinv;
+                pm_row_scale(pm_wave_max(m), qsc, qinv);
+                u32x4 qh[2];
+                pm_split_f16(qv, qsc, qh);
+                pm_f32x4 pq = pm_mfma<_Float16>(qh[0], xop, pm_f32x4{0.0f, 0.0f, 0.0f, 0.0f});
+                pq = pm_mfma<_Float16>(qh[1], xop, pq);
+#pragma unroll
+                for (int v = 0; v < 4; ++v)
+                    ay[t][v] = fmaf(pq[v], qinv, ay[t][v]);
+            } else {
+                pm_bf16x8 qp[2];
+                pm_split<2>(qv, qp);
+#pragma unroll
+                for (int uu = 0; uu < 2; ++uu)
+                    ay[t] = pm_mfma<bf16_t>(__builtin_bit_cast(u32x4, qp[uu]), xop, ay[t]);
+            }
         };
         if (__builtin_amdgcn_readfirstlane(big_all[cs]) != 0) {
 #pragma unroll
@@ -650,16 +664,7 @@ __global__ __launch_bounds__(kPmNT) __attribute__((amdgpu_waves_per_eu(NS <= 128
         // D x_t in fp32: the x^T operand holds x of tokens 4qg + v (elements
         // 0-3) and 16 + 4qg + v (4-7) of row rl, the tokens of ay[0][v], ay[1][v]
         float xf[8];
-        if constexpr (IOH) {  // x = hi + lo exactly (fewer registers than converting x again)
-            float xh[8], xl[8];
-            pm_to_f32x8<bf16_t>(xq[0], xh);
-            pm_to_f32x8<bf16_t>(xq[1], xl);
-#pragma unroll
-            for (int e = 0; e < 8; ++e)
-                xf[e] = xh[e] + xl[e];
-        } else {
-            pm_to_f32x8<IOT>(xop, xf);
-        }
+        pm_to_f32x8<IOT>(xop, xf);
 #pragma unroll
         for (int v = 0; v < 4; ++v) {
             ay[0][v] = fmaf(dskip, xf[v], ay[0][v]);
