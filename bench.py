@@ -11,6 +11,8 @@ last-level cache cannot serve them.
     python bench.py [--steps K] [--warmup W] [--config {1,2,3,4,5,6,7,8,9}]
 
 --config 2/3/4/5 time prefill / padded decode / MTP replay / tree verify
+(prefill: --operands f16 or f32 for fp16 or fp32 x/z/B/C instead of bf16,
+--stash with the replay stash)
 (16 requests with 128-node draft trees, replay stash on) instead; 6 and 7 the
 layer-batched calls over a 64-layer stack: the MTP replay of config 4 for every
 layer in one launch, and the clear of one resident slot (recurrent and conv
@@ -73,15 +75,20 @@ def decode_bytes(T, live):
     return live * per_live + b * h * d * s_x + 12 * h + 4 * b
 
 
-def prefill_bytes(T, L):
+def prefill_bytes(T, L, stash=False):
+    """Algorithmic bytes of one prefill launch. With the replay stash the state is
+    only read, and the fp32 stash (A dt', dt', x, B) is written for every token
+    position (zero past the context)."""
     b, t, h, d = T["x"].shape
     g, n = T["B"].shape[2], T["B"].shape[3]
     s_s, s_x = esize(T["state"]), esize(T["x"])
     per_tok = h * d * (2 * s_x + (s_x if T["z"] is not None else 0)) + 2 * g * n * esize(T["B"]) + 4 * h
     total = 0
     for Lb in L:
-        total += h * d * n * 2 * s_s + int(Lb) * per_tok
+        total += h * d * n * (1 if stash else 2) * s_s + int(Lb) * per_tok
         total += (t - int(Lb)) * h * d * s_x
+        if stash:
+            total += t * (8 * h + 4 * h * d + 4 * g * n)
     return total + 12 * h + 8 * b
 
 
@@ -196,7 +203,7 @@ def measured_traffic(kernel_key, src_hash):
     return rec.get("bytes_per_launch")
 
 
-def cpu_baseline(kind, w, seconds, bytes_per_call, units_per_call):
+def cpu_baseline(kind, w, seconds, bytes_per_call, units_per_call, stash=False):
     """The fp64 oracle, as it stands, on a bounded sample of the same workload."""
     import numpy as np
     import oracle
@@ -220,12 +227,16 @@ def cpu_baseline(kind, w, seconds, bytes_per_call, units_per_call):
     elif kind == "prefill":
         st = a["state"].copy()
         out = np.zeros(a["x"].shape)
+        b, t, h, d = a["x"].shape
+        S = ({"dA": np.zeros((b, t, h)), "dt": np.zeros((b, t, h)), "u": np.zeros((b, t, h, d)),
+              "B": np.zeros(a["B"].shape)} if stash else None)
 
         def call():
             oracle.prefill(a["x"], a["A"], a["B"], a["C"], a["dt"], st, out, dt_bias=a["dt_bias"],
                            D=a["D"], z=a["z"], dt_softplus=w.dt_softplus,
-                           context_lengths=a["context_lengths"], state_indices=a["state_indices"])
-        sample = "the full prefill batch of this workload"
+                           context_lengths=a["context_lengths"], state_indices=a["state_indices"],
+                           stash=S)
+        sample = "the full prefill batch of this workload" + (", replay stash on" if stash else "")
     elif kind == "tree":
         out = np.zeros(a["x"].shape)
         b, m, h, d = a["x"].shape
@@ -377,10 +388,16 @@ def main():
     ap.add_argument("--flushed", type=int, default=100,
                     help="after the graph-timed steps, time this many launches one by one, each "
                          "after a 1 GiB scratch write (median, p10, p90); 0 skips it")
+    ap.add_argument("--operands", choices=["bf16", "f16", "f32"], default="bf16",
+                    help="config 2: the dtype of x/z/B/C/out (bf16 as the workload states; fp16 "
+                         "also runs on the matrix cores, fp32 on the VALU kernel)")
+    ap.add_argument("--stash", action="store_true", help="config 2: prefill with the replay stash")
     ap.add_argument("--copy-mib", type=int, default=0,
                     help="after the timed steps, one plain device copy of this many MiB "
                          "(a known-size kernel for scaling memory-traffic counters)")
     args = ap.parse_args()
+    if args.config != 2 and (args.operands != "bf16" or args.stash):
+        ap.error("--operands and --stash apply to --config 2 (prefill) only")
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
         print("bench.py measures one GPU: the selective state update needs no collective, "
@@ -408,6 +425,14 @@ def main():
         w, name = inputs.gdn_config(), inputs.GDN_NAME
     else:
         w, name = inputs.config(args.config), inputs.CONFIG_NAMES[args.config]
+    if args.operands != "bf16":  # config 2 with the same values in another dtype
+        dt_ = {"f16": torch.float16, "f32": torch.float32}[args.operands]
+        for k in ("x", "z", "B", "C"):
+            if w.tensors[k] is not None:
+                w.tensors[k] = w.tensors[k].to(dt_)
+        name += f"; {args.operands} x/z/B/C/out"
+    if args.stash:
+        name += "; replay stash on (state read-only)"
     T = {k: (None if v is None else v.to(dev)) for k, v in w.tensors.items()}
     stream = torch.cuda.current_stream(dev)
 
@@ -449,23 +474,34 @@ def main():
     elif args.config == 2:
         kind = "prefill"
         L = T["context_lengths"].clamp(0, T["x"].shape[1]).cpu().tolist()
-        nbytes = prefill_bytes(T, L)
+        nbytes = prefill_bytes(T, L, args.stash)
         units = sum(L) * T["x"].shape[2]
         reps = replicas(["x", "z", "B", "C", "dt", "state"], 4)
         outs = [torch.empty_like(T["x"]) for _ in reps]
         rot = "steps rotate 4 replicas of the pool and of every input and output"
+        stashes = [{}] * len(reps)
+        if args.stash:
+            b_, t_, h_, d_ = T["x"].shape
+            stashes = [{"replay_dA": torch.empty((b_, t_, h_), device=dev),
+                        "replay_dt": torch.empty((b_, t_, h_), device=dev),
+                        "replay_u": torch.empty((b_, t_, h_, d_), device=dev),
+                        "replay_B": torch.empty(tuple(T["B"].shape), device=dev)} for _ in reps]
 
         def step(i):
             R = reps[i % len(reps)]
             ssu_prefill(R["x"], R["A"], R["B"], R["C"], R["dt"], R["state"], outs[i % len(reps)],
                         dt_bias=R["dt_bias"], D=R["D"], z=R["z"], dt_softplus=w.dt_softplus,
-                        context_lengths=R["context_lengths"], state_indices=R["state_indices"])
+                        context_lengths=R["context_lengths"], state_indices=R["state_indices"],
+                        **stashes[i % len(reps)])
         src = source_hash("ssu_prefill_impl.h", "ssu_prefill_mm.h", "ssu_rowblock.h", "ssu_device.h",
                           "ssu_dpp.h")
         kkey = "prefill_config2"
-        matrix = {"flops_per_step": prefill_method_flops(T, L),
-                  "flops": "the method's own: 5 per state element and token",
-                  "closed_form_fmas_per_step": prefill_mm_fmas(T, L)}
+        if args.operands != "bf16" or args.stash:  # no counters are kept for these variants
+            kkey += f"_{args.operands}" + ("_stash" if args.stash else "")
+        if args.operands != "f32":
+            matrix = {"flops_per_step": prefill_method_flops(T, L),
+                      "flops": "the method's own: 5 per state element and token",
+                      "closed_form_fmas_per_step": prefill_mm_fmas(T, L), "dtype": args.operands}
         bound, peak, unit = "hbm", HBM_PEAK_GBS, "GB/s"
     elif args.config == 5:
         kind = "tree"
@@ -672,7 +708,7 @@ def main():
         tf = matrix["flops_per_step"] / (ms * 1e-3) / 1e12
         cf = 2.0 * matrix["closed_form_fmas_per_step"] / (ms * 1e-3) / 1e12
         rec["roofline_matrix_cores"] = {
-            "dtype": "bf16", "flops": matrix["flops"], "achieved": round(tf, 3),
+            "dtype": matrix.get("dtype", "bf16"), "flops": matrix["flops"], "achieved": round(tf, 3),
             "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
             "frac": round(tf / MFMA_BF16_PEAK_TFLOPS, 4),
             "closed_form_fp32_equivalent": {"achieved": round(cf, 3),
@@ -701,7 +737,7 @@ def main():
     if not args.no_cpu_baseline:
         print(f"[bench] timing the fp64 oracle for about {args.cpu_seconds:.0f} s",
               file=sys.stderr, flush=True)
-        rec["cpu_baseline"] = cpu_baseline(kind, w, args.cpu_seconds, nbytes, units)
+        rec["cpu_baseline"] = cpu_baseline(kind, w, args.cpu_seconds, nbytes, units, args.stash)
     print(json.dumps(rec), flush=True)
 
 
