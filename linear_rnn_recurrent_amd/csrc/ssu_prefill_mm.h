@@ -391,41 +391,57 @@ __global__ __launch_bounds__(kPmNT) __attribute__((amdgpu_waves_per_eu(NS <= 128
 #pragma unroll
                 for (int i = 0; i < 8; ++i)
                     *reinterpret_cast<uint32_t *>(Bt + (col + i) * PT + 4 * p) = pair16(rB[k][0], rB[k][1], i);
-                if (writes_B) {
-#pragma unroll
-                    for (int q = 0; q < 2; ++q) {
-                        if (2 * p + q < nv) {
-                            float *sb = sBrow + (uint32_t)((t0 + 2 * p + q) * G * NS + col);
-#pragma unroll
-                            for (int i = 0; i < 8; i += 4)
-                                __builtin_nontemporal_store(u32x4{c32(rB[k][q], i), c32(rB[k][q], i + 1),
-                                                                  c32(rB[k][q], i + 2), c32(rB[k][q], i + 3)},
-                                                            reinterpret_cast<u32x4 *>(sb + i));
-                        }
-                    }
-                }
             }
         }
         if (tid < 128) {
             u32x4 w[2];
 #pragma unroll
-            for (int q = 0; q < 2; ++q) {
-                const bool live = 2 * xp + q < nv && xbv;
-                w[q] = live ? rX[q] : u32x4{0u, 0u, 0u, 0u};
-                if (stash && live) {
-                    float *su = sUrow + (uint32_t)((t0 + 2 * xp + q) * NSTR + xb8);
-#pragma unroll
-                    for (int i = 0; i < 8; i += 4)
-                        __builtin_nontemporal_store(u32x4{x32(w[q], i), x32(w[q], i + 1),
-                                                          x32(w[q], i + 2), x32(w[q], i + 3)},
-                                                    reinterpret_cast<u32x4 *>(su + i));
-                }
-            }
+            for (int q = 0; q < 2; ++q)
+                w[q] = 2 * xp + q < nv && xbv ? rX[q] : u32x4{0u, 0u, 0u, 0u};
 #pragma unroll
             for (int i = 0; i < 8; ++i)
                 *reinterpret_cast<uint32_t *>(Xt + (xb8 + i) * PT + 4 * xp) = pair16(w[0], w[1], i);
         }
         *reinterpret_cast<u32x4 *>(Zs + xtok * PZ + xr8 * 2) = rZ;
+    };
+    // The stash stores of the staged chunk (B and x as fp32), issued after every
+    // prefetched register has been read: loads and stores share one in-order
+    // memory counter, so a store issued before the last use of a prefetched
+    // register would be waited for there (a write round trip per chunk); here
+    // the next such wait is a chunk later.
+    auto stash_chunk = [&](int t0, int nv) {
+        __builtin_amdgcn_sched_barrier(0);
+        if (writes_B) {
+#pragma unroll
+            for (int k = 0; k < NVP; ++k) {
+                const int v = tid + NT * k;
+                const int p = v & 15, col = 8 * (v >> 4);
+#pragma unroll
+                for (int q = 0; q < 2; ++q) {
+                    if (v < 16 * NCB && 2 * p + q < nv) {
+                        float *sb = sBrow + (uint32_t)((t0 + 2 * p + q) * G * NS + col);
+#pragma unroll
+                        for (int i = 0; i < 8; i += 4)
+                            __builtin_nontemporal_store(u32x4{c32(rB[k][q], i), c32(rB[k][q], i + 1),
+                                                              c32(rB[k][q], i + 2), c32(rB[k][q], i + 3)},
+                                                        reinterpret_cast<u32x4 *>(sb + i));
+                    }
+                }
+            }
+        }
+        if (stash && tid < 128) {
+#pragma unroll
+            for (int q = 0; q < 2; ++q) {
+                if (2 * xp + q < nv && xbv) {
+                    float *su = sUrow + (uint32_t)((t0 + 2 * xp + q) * NSTR + xb8);
+#pragma unroll
+                    for (int i = 0; i < 8; i += 4)
+                        __builtin_nontemporal_store(u32x4{x32(rX[q], i), x32(rX[q], i + 1),
+                                                          x32(rX[q], i + 2), x32(rX[q], i + 3)},
+                                                    reinterpret_cast<u32x4 *>(su + i));
+                }
+            }
+        }
     };
 
     // ---- decay tables of chunks c0 .. c0 + kPmSeg - 1, all four waves: wave w
@@ -514,6 +530,7 @@ __global__ __launch_bounds__(kPmNT) __attribute__((amdgpu_waves_per_eu(NS <= 128
         load_chunk(0, min(TT, Lb));
         fill_tables(0);
         store_chunk(0, min(TT, Lb));
+        stash_chunk(0, min(TT, Lb));
     }
     __syncthreads();
 
@@ -725,8 +742,11 @@ __global__ __launch_bounds__(kPmNT) __attribute__((amdgpu_waves_per_eu(NS <= 128
         }
         __syncthreads();
 
-        // ---- gate and store the chunk's outputs: 8 rows of one token per thread ----
-        if (xtok < nv && xrv) {
+        // ---- gate the chunk's outputs: 8 rows of one token per thread (stored
+        // below, once the next chunk is staged) ----
+        const bool olive = xtok < nv && xrv;
+        u32x4 ow = u32x4{0u, 0u, 0u, 0u};
+        if (olive) {
             const float4 y0 = *reinterpret_cast<const float4 *>(Ys + xtok * (PY / 4) + xr8);
             const float4 y1 = *reinterpret_cast<const float4 *>(Ys + xtok * (PY / 4) + xr8 + 4);
             float y[8] = {y0.x, y0.y, y0.z, y0.w, y1.x, y1.y, y1.z, y1.w};
@@ -738,13 +758,19 @@ __global__ __launch_bounds__(kPmNT) __attribute__((amdgpu_waves_per_eu(NS <= 128
                     y[i] *= zi * __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(-1.4426950408889634f * zi));
                 }
             }
-            u32x4 ow;  // round to nearest even, two values per conversion
 #pragma unroll
-            for (int i = 0; i < 4; ++i)
+            for (int i = 0; i < 4; ++i)  // round to nearest even, two values per conversion
                 ow[i] = pm_pack2<IOT>(y[2 * i], y[2 * i + 1]);
-            *reinterpret_cast<u32x4 *>(orow + (uint32_t)(((t0 + xtok) * NSTR + rbase + xr8) * 2)) = ow;
         }
+        // the next chunk into LDS (z over this chunk's z: read above, in the same
+        // thread), then every global store of this iteration: loads and stores
+        // share one in-order memory counter, so a store issued before the last
+        // use of a prefetched register would be waited for there
         store_chunk(t0 + TT, min(TT, Lb - t0 - TT));  // nothing live past the last chunk
+        __builtin_amdgcn_sched_barrier(0);
+        if (olive)
+            *reinterpret_cast<u32x4 *>(orow + (uint32_t)(((t0 + xtok) * NSTR + rbase + xr8) * 2)) = ow;
+        stash_chunk(t0 + TT, min(TT, Lb - t0 - TT));
         __syncthreads();
     }
 
