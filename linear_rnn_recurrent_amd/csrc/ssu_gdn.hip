@@ -20,12 +20,14 @@
 //    a few useful bytes), one round of loads per thread.
 // 2. gdn_stream: the state, all but a few percent of the bytes. Every wave is
 //    independent (no barrier, no LDS): it owns a few rows of one value head's
-//    D x D fp32 state, 8 (or 16) lanes per row with the columns interleaved
-//    in 16-byte chunks so that every non-temporal vector load or store covers
-//    whole cache lines; it issues its state loads first, then reads its q/k
-//    slices, v values and the b/a partial sums from the workspace (cache
-//    hits), forms its head's gates, and per row applies decay, prediction,
-//    delta update and output (row dots summed over the row's lanes with DPP).
+//    D x D fp32 state, 16 lanes per row (8 below D = 128; at D = 128 its 16 KiB
+//    of state per workgroup measured faster than 32 or 8) with the columns
+//    interleaved in 16-byte chunks so that every non-temporal vector load or
+//    store covers whole cache lines; it issues its state loads first, then
+//    reads its q/k slices, v values and the b/a partial sums from the
+//    workspace (cache hits), forms its head's gates, and per row applies decay,
+//    prediction, delta update and output (row dots summed over the row's lanes
+//    with DPP).
 // Splitting the step in two lets the state stream run as many small,
 // barrier-free waves that the dispatcher overlaps freely; in one launch each
 // workgroup had to finish its latency-bound setup before streaming, and the
@@ -264,14 +266,14 @@ __global__ __launch_bounds__(kGdnNT) void gdn_prep_kernel(
 // ---------------------------------------------------------------------------
 // gdn_stream
 // ---------------------------------------------------------------------------
-// A state row (D fp32) is spread over LPR lanes (8; 16 at D = 256), EPL = D /
+// A state row (D fp32) is spread over LPR lanes (16 at D >= 128, else 8), EPL = D /
 // LPR floats each, as NV = EPL / 4 16-byte vectors: lane l's vector v holds
 // columns 4 LPR v + 4 l .. + 3, so each vector access of a row's LPR lanes
 // covers 16 LPR >= 128 consecutive bytes (whole cache lines). One wave
 // instruction serves RPI = 64 / LPR rows; a wave runs PW such passes.
 template <int D>
 struct StreamCfg {
-    static constexpr int LPR = D == 256 ? 16 : 8;
+    static constexpr int LPR = D >= 128 ? 16 : 8;
     static constexpr int EPL = D / LPR;
     static constexpr int NV = EPL / 4;
     static constexpr int RPI = 64 / LPR;
