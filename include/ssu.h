@@ -119,7 +119,12 @@ ssu_status ssu_decode(const ssu_dims *dims, const void *x, const float *A, const
  *   replay_u  [batch, seq_len, nheads, dim]     = x  (unscaled, fp32)
  *   replay_B  [batch, seq_len, ngroups, dstate] = B  (fp32)
  * and zeros for t >= L_b; outputs are produced as without the stash.
- * Padding rows: out[b,:] = +0.0, state and stash rows untouched. */
+ * Padding rows: out[b,:] = +0.0, state and stash rows untouched.
+ * Numerics: fp32 state arithmetic either way. With x/z/out and B/C both bf16 or
+ * both fp16, dstate a multiple of 32, dim a multiple of 8 and x, z, out and
+ * replay_u 16-byte aligned, the tokens are evaluated 32 at a time in closed form
+ * on the matrix cores; otherwise one at a time. Both agree with the token-by-token
+ * recurrence to fp32 rounding, not bitwise; dt' and the stash are bit-identical. */
 ssu_status ssu_prefill(const ssu_dims *dims, int32_t seq_len, const void *x, const float *A,
                        const void *B, const void *C, const float *dt, const float *dt_bias,
                        const float *D, const void *z, void *state, void *out,
