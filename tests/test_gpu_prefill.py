@@ -241,21 +241,25 @@ def _decode_steps(w, steps):
     return st, torch.stack(outs, 1)
 
 
-def test_prefill_equals_repeated_decode():
+@pytest.mark.parametrize("io", ["bf16", "f16"])
+def test_prefill_equals_repeated_decode(io):
     w = inputs.prefill_workload(batch=4, seq_len=20, nheads=8, dim=64, dstate=128, ngroups=2,
-                                pool_rows=6, seed=21, bc_std=128 ** -0.5, ctx=("none",))
+                                pool_rows=6, seed=21, bc_std=128 ** -0.5, ctx=("none",),
+                                io_dtype=io, bc_dtype=io)
     st_p, out_p, _ = run_prefill(w)
     st_d, out_d = _decode_steps(w, 20)
-    # prefill evaluates 32-token chunks in closed form on the matrix cores (bf16
-    # operands; the rescaled recurrence otherwise), decode the direct recurrence:
+    # prefill evaluates 32-token chunks in closed form on the matrix cores (bf16 or
+    # fp16 operands; the rescaled recurrence otherwise), decode the direct recurrence:
     # equal up to each side's fp32 rounding
     assert_close(st_p.cpu(), f64(st_d), 2 * TOL_F32, "state: prefill vs repeated decode")
     assert_close(out_p.cpu(), f64(out_d), TOL_LOW, "out: prefill vs repeated decode")
 
 
-def test_stash_then_replay_equals_prefill_with_accepted_context():
+@pytest.mark.parametrize("io", ["bf16", "f16"])
+def test_stash_then_replay_equals_prefill_with_accepted_context(io):
     w = inputs.prefill_workload(batch=5, seq_len=6, nheads=8, dim=64, dstate=128, ngroups=1,
-                                pool_rows=7, seed=22, bc_std=128 ** -0.5, ctx=("none",))
+                                pool_rows=7, seed=22, bc_std=128 ** -0.5, ctx=("none",),
+                                io_dtype=io, bc_dtype=io)
     st_s, out_s, S = run_prefill(w, stash=True)
     accepted = torch.tensor([0, 6, 3, 1, 9], dtype=torch.int32, device="cuda")
     ssu_replay(st_s, S["replay_dA"], S["replay_u"], S["replay_B"], S["replay_dt"], accepted,
