@@ -168,19 +168,23 @@ def test_io_and_bc_dtypes(io_dtype, bc_dtype):
         check_prefill(w, **valu_kernel(w))
 
 
-def test_ragged_context_lengths_and_padding():
+@pytest.mark.parametrize("io", ["bf16", "f16"])
+def test_ragged_context_lengths_and_padding(io):
     # ctx: zero, negative (clamped to 0), full, beyond seq_len (clamped), odd; one padding row
     w = inputs.prefill_workload(batch=6, seq_len=45, nheads=4, dim=64, dstate=64, ngroups=2,
                                 pool_rows=8, seed=4, ctx=[0, -3, 45, 100, 17, 33],
-                                indices=[5, 1, 7, 0, -1, 3], bc_std=0.125)
+                                indices=[5, 1, 7, 0, -1, 3], bc_std=0.125, io_dtype=io, bc_dtype=io)
     check_prefill(w)
     check_prefill(w, stash=True)
 
 
+@pytest.mark.parametrize("io", ["bf16", "f16"])
 @pytest.mark.parametrize("dim", [32, 100, 200])
-def test_row_blocks_and_ragged_dim(dim):
+def test_row_blocks_and_ragged_dim(dim, io):
+    # dim 32 and 200 on the matrix cores (a partial row block), 100 on the VALU kernel
     w = inputs.prefill_workload(batch=2, seq_len=19, nheads=3, dim=dim, dstate=128, ngroups=1,
-                                pool_rows=4, seed=dim, bc_std=128 ** -0.5, ctx=[19, 11])
+                                pool_rows=4, seed=dim, bc_std=128 ** -0.5, ctx=[19, 11],
+                                io_dtype=io, bc_dtype=io)
     check_prefill(w)
     check_prefill(w, stash=True)
 
@@ -216,11 +220,13 @@ def test_large_batch_without_length_sort():
     check_prefill(w)
 
 
+@pytest.mark.parametrize("io", ["bf16", "f16"])
 @pytest.mark.parametrize("opts", [dict(with_z=False), dict(with_D=False),
                                   dict(dt_softplus=False, with_bias=False), dict(indices="none")])
-def test_optional_inputs(opts):
+def test_optional_inputs(opts, io):
     w = inputs.prefill_workload(batch=2, seq_len=24, nheads=4, dim=64, dstate=128, ngroups=1,
-                                pool_rows=2, seed=9, bc_std=128 ** -0.5, ctx=[24, 9], **opts)
+                                pool_rows=2, seed=9, bc_std=128 ** -0.5, ctx=[24, 9],
+                                io_dtype=io, bc_dtype=io, **opts)
     if opts.get("dt_softplus") is False:
         w.tensors["dt"] = w["dt"].abs() * 0.1
     check_prefill(w)
