@@ -56,7 +56,7 @@ constexpr int kPmSeg = 16;  // chunks whose decay tables are formed together
 
 // LDS layout (bytes) of one workgroup
 struct PmLds {
-    int cs, bs, bt, xt, zs, ys, lc, rd, sf, tot, big, sb, total;
+    int cs, bs, xs, zs, ys, lc, rd, sf, tot, big, sb, total;
 };
 // C, B rows: a pitch of 16 bytes past whole 128-byte lines keeps the 16-byte
 // row stores aligned; rows 8-15 of each 16 swap the 8-byte halves of every
@@ -64,9 +64,8 @@ struct PmLds {
 // fall in 16 different 8-byte bank pairs of the 32 4-byte LDS banks.
 __host__ __device__ constexpr int pm_row_pitch(int NS) { return NS * 2 + 16; }
 __device__ __forceinline__ int pm_swz(int row) { return ((row >> 3) & 1) * 8; }
-__host__ __device__ constexpr int pm_t_pitch() { return kPmTT * 2 + 8; }          // B^T, x^T rows
 __host__ __device__ constexpr int pm_y_pitch() { return 64 * 4 + 16; }            // fp32 outputs
-__host__ __device__ constexpr int pm_z_pitch() { return 64 * 2 + 16; }            // z rows
+__host__ __device__ constexpr int pm_z_pitch() { return 64 * 2 + 16; }            // x, z rows
 __host__ __device__ inline PmLds pm_lds(int NS)
 {
     PmLds L;
@@ -74,8 +73,7 @@ __host__ __device__ inline PmLds pm_lds(int NS)
     auto take = [&o](int bytes) { const int r = o; o += (bytes + 15) & ~15; return r; };
     L.cs = take(kPmTT * pm_row_pitch(NS));   // C of the chunk [t][n]
     L.bs = take(kPmTT * pm_row_pitch(NS));   // B of the chunk [j][n]
-    L.bt = take(NS * pm_t_pitch());          // B^T [n][j]
-    L.xt = take(64 * pm_t_pitch());          // x^T [row][j]
+    L.xs = take(kPmTT * pm_z_pitch());       // x [j][row]
     L.zs = take(kPmTT * pm_z_pitch());       // z [t][row]
     L.ys = take(kPmTT * pm_y_pitch());       // outputs before the gate [t][row], fp32
     // decay tables of kPmSeg chunks, [chunk][token]
@@ -97,6 +95,25 @@ __device__ __forceinline__ u32x4 pm_op(const unsigned char *p)
     const u32x2 lo = *reinterpret_cast<const u32x2 *>(p);
     const u32x2 hi = *reinterpret_cast<const u32x2 *>(p + 32);
     return u32x4{lo[0], lo[1], hi[0], hi[1]};
+}
+
+typedef short pm_i16x4 __attribute__((ext_vector_type(4)));
+
+// Eight 16-bit values of one column of a row-major [token][column] LDS tile,
+// for tokens 4 qg + e and 16 + 4 qg + e (e < 4), as the MFMA operand order
+// used here: ds_read_b64_tr_b16 gives lane i of each 16-lane group element
+// i % 4 of the 8 bytes that lane 4 e + i / 4 addressed, for e = 0 .. 3, so
+// lane s of the group addresses token row 4 qg + s / 4, columns c0 + 4 (s % 4)
+// .. + 3, and lane i ends up with column c0 + i of four consecutive tokens.
+// p: the lane's address in token row 4 qg + s / 4; p + hi_off: the same
+// columns in token row 16 + 4 qg + s / 4
+__device__ __forceinline__ u32x4 pm_op_tr(const unsigned char *p, int hi_off)
+{
+    typedef __attribute__((address_space(3))) pm_i16x4 *lds_v4p;
+    const pm_i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4p)p);
+    const pm_i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4p)(p + hi_off));
+    const u32x2 l2 = __builtin_bit_cast(u32x2, lo), h2 = __builtin_bit_cast(u32x2, hi);
+    return u32x4{l2[0], l2[1], h2[0], h2[1]};
 }
 
 // D += A B on the matrix cores for 16-bit operands of type T (bf16_t or
@@ -228,7 +245,7 @@ __global__ __launch_bounds__(kPmNT) __attribute__((amdgpu_waves_per_eu(NS <= 128
     constexpr int NT = kPmNT;
     constexpr int KN = NS / 32;          // k-steps over dstate
     constexpr int NT16 = NS / 16;        // dstate tiles of the state
-    constexpr int PC = pm_row_pitch(NS), PT = pm_t_pitch(), PY = pm_y_pitch(), PZ = pm_z_pitch();
+    constexpr int PC = pm_row_pitch(NS), PY = pm_y_pitch(), PZ = pm_z_pitch();
     constexpr int NCB = NS / 8;                      // 16-byte column blocks of a B (C) row
     constexpr int NVP = (16 * NCB + NT - 1) / NT;    // token pairs x column blocks per thread
     static_assert(NS % 32 == 0, "dstate in whole 32-column steps");
@@ -237,7 +254,7 @@ __global__ __launch_bounds__(kPmNT) __attribute__((amdgpu_waves_per_eu(NS <= 128
 
     extern __shared__ __attribute__((aligned(16))) unsigned char lds[];
     const PmLds L = pm_lds(NS);
-    unsigned char *Cs = lds + L.cs, *Bs = lds + L.bs, *Bt = lds + L.bt, *Xt = lds + L.xt;
+    unsigned char *Cs = lds + L.cs, *Bs = lds + L.bs, *Xs = lds + L.xs;
     unsigned char *Zs = lds + L.zs;
     float *Ys = reinterpret_cast<float *>(lds + L.ys);
     float *const lcs_all = reinterpret_cast<float *>(lds + L.lc);
@@ -329,15 +346,12 @@ __global__ __launch_bounds__(kPmNT) __attribute__((amdgpu_waves_per_eu(NS <= 128
 
     // ---- chunk staging: global -> registers (prefetch) -> LDS ----
     // B and C: item v = (token pair p = v % 16, column block cb = v / 16), two
-    // 16-byte loads (tokens 2p, 2p+1); B^T takes the pair as one 32-bit word
-    // per column. x: threads < 128 take (token pair tid % 16, rows
-    // 8 (tid / 16) ..+7) and x^T the pair as one word per row. z (and the
-    // outputs): token tid / 8, rows 8 (tid % 8) ..+7.
-    u32x4 rB[NVP][2], rC[NVP][2], rX[2], rZ;
-    const int xtok = tid >> 3, xr8 = 8 * (tid & 7);  // z / output mapping
+    // 16-byte loads (tokens 2p, 2p+1). x, z (and the outputs): token tid / 8,
+    // rows 8 (tid % 8) ..+7. Every tile is stored row-major ([token][column]);
+    // the operands that need it transposed read it with ds_read_b64_tr_b16.
+    u32x4 rB[NVP][2], rC[NVP][2], rX, rZ;
+    const int xtok = tid >> 3, xr8 = 8 * (tid & 7);  // x / z / output mapping
     const bool xrv = rbase + xr8 < Dm;               // Dm is a multiple of 8
-    const int xp = tid & 15, xb8 = 8 * ((tid >> 4) & 7);  // x mapping (threads < 128)
-    const bool xbv = rbase + xb8 < Dm;
     auto load_chunk = [&](int t0, int nv) {
 #pragma unroll
         for (int k = 0; k < NVP; ++k) {
@@ -351,16 +365,11 @@ __global__ __launch_bounds__(kPmNT) __attribute__((amdgpu_waves_per_eu(NS <= 128
                 rC[k][q] = *reinterpret_cast<const u32x4 *>(crow + o);
             }
         }
-#pragma unroll
-        for (int q = 0; q < 2; ++q) {
-            const int tok = min(2 * xp + q, nv - 1);
-            rX[q] = *reinterpret_cast<const u32x4 *>(
-                xrow + (uint32_t)(((t0 + tok) * NSTR + min(rbase + xb8, Dm - 8)) * 2));
-        }
+        const uint32_t ox = (uint32_t)(((t0 + min(xtok, nv - 1)) * NSTR + min(rbase + xr8, Dm - 8)) * 2);
+        rX = *reinterpret_cast<const u32x4 *>(xrow + ox);
         // (without z the same words of x: a load on every path, never waited for
         // out of turn)
-        rZ = *reinterpret_cast<const u32x4 *>(
-            (zrow ? zrow : xrow) + (uint32_t)(((t0 + min(xtok, nv - 1)) * NSTR + min(rbase + xr8, Dm - 8)) * 2));
+        rZ = *reinterpret_cast<const u32x4 *>((zrow ? zrow : xrow) + ox);
     };
     // 16-bit element i of a 16-byte register group; the elements i of two
     // groups as one word (one v_perm_b32: bytes of the low or high halves)
@@ -368,10 +377,6 @@ __global__ __launch_bounds__(kPmNT) __attribute__((amdgpu_waves_per_eu(NS <= 128
     // the same element as fp32 bits, for the stash (bf16: the bits shifted up)
     auto c32 = [&](const u32x4 &w, int i) { return __float_as_uint(pm_to_f32<BCT>(h16(w, i))); };
     auto x32 = [&](const u32x4 &w, int i) { return __float_as_uint(pm_to_f32<IOT>(h16(w, i))); };
-    auto pair16 = [](const u32x4 &w0, const u32x4 &w1, int i) {
-        // selector bytes 0-3 pick from w0's word, 4-7 from w1's (perm takes (hi, lo))
-        return __builtin_amdgcn_perm(w1[i >> 1], w0[i >> 1], (i & 1) ? 0x07060302u : 0x05040100u);
-    };
     auto store_chunk = [&](int t0, int nv) {
 #pragma unroll
         for (int k = 0; k < NVP; ++k) {
@@ -388,20 +393,10 @@ __global__ __launch_bounds__(kPmNT) __attribute__((amdgpu_waves_per_eu(NS <= 128
                     *reinterpret_cast<u32x4 *>(Cs + row * PC + col * 2) =
                         sw ? u32x4{c[2], c[3], c[0], c[1]} : c;
                 }
-#pragma unroll
-                for (int i = 0; i < 8; ++i)
-                    *reinterpret_cast<uint32_t *>(Bt + (col + i) * PT + 4 * p) = pair16(rB[k][0], rB[k][1], i);
             }
         }
-        if (tid < 128) {
-            u32x4 w[2];
-#pragma unroll
-            for (int q = 0; q < 2; ++q)
-                w[q] = 2 * xp + q < nv && xbv ? rX[q] : u32x4{0u, 0u, 0u, 0u};
-#pragma unroll
-            for (int i = 0; i < 8; ++i)
-                *reinterpret_cast<uint32_t *>(Xt + (xb8 + i) * PT + 4 * xp) = pair16(w[0], w[1], i);
-        }
+        // x past the context or beyond dim as zeros (their loads were clamped)
+        *reinterpret_cast<u32x4 *>(Xs + xtok * PZ + xr8 * 2) = xtok < nv && xrv ? rX : u32x4{0u, 0u, 0u, 0u};
         *reinterpret_cast<u32x4 *>(Zs + xtok * PZ + xr8 * 2) = rZ;
     };
     // The stash stores of the staged chunk (B and x as fp32), issued after every
@@ -429,18 +424,12 @@ __global__ __launch_bounds__(kPmNT) __attribute__((amdgpu_waves_per_eu(NS <= 128
                 }
             }
         }
-        if (stash && tid < 128) {
+        if (stash && xtok < nv && xrv) {
+            float *su = sUrow + (uint32_t)((t0 + xtok) * NSTR + xr8);
 #pragma unroll
-            for (int q = 0; q < 2; ++q) {
-                if (2 * xp + q < nv && xbv) {
-                    float *su = sUrow + (uint32_t)((t0 + 2 * xp + q) * NSTR + xb8);
-#pragma unroll
-                    for (int i = 0; i < 8; i += 4)
-                        __builtin_nontemporal_store(u32x4{x32(rX[q], i), x32(rX[q], i + 1),
-                                                          x32(rX[q], i + 2), x32(rX[q], i + 3)},
-                                                    reinterpret_cast<u32x4 *>(su + i));
-                }
-            }
+            for (int i = 0; i < 8; i += 4)
+                __builtin_nontemporal_store(u32x4{x32(rX, i), x32(rX, i + 1), x32(rX, i + 2), x32(rX, i + 3)},
+                                            reinterpret_cast<u32x4 *>(su + i));
         }
     };
 
@@ -621,8 +610,10 @@ __global__ __launch_bounds__(kPmNT) __attribute__((amdgpu_waves_per_eu(NS <= 128
         // 2^(Lc[t]-Lc[j]) dt'_j as 2^(Lc[t]-Lc[j0]) (2^(Lc[j0]-Lc[j]) dt'_j): one exp2 per quad
         const float rd[8] = {rd0.x, rd0.y, rd0.z, rd0.w, rd1.x, rd1.y, rd1.z, rd1.w};
         const float lj[8] = {lj0.x, lj0.y, lj0.z, lj0.w, lj1.x, lj1.y, lj1.z, lj1.w};
-        // x^T operand in the same source order: lane (row rl, qg)
-        const u32x4 xop = pm_op(Xt + rl * PT + (4 * qg) * 2);
+        // x^T operand in the same source order, lane (row rl, qg), read
+        // transposed from the row-major x tile: this lane addresses token row
+        // 4 qg + ln / 4 at rows 16 wave + 4 (ln % 4) ..+3
+        const u32x4 xop = pm_op_tr(Xs + (4 * qg + (ln >> 2)) * PZ + 32 * wave + 8 * (ln & 3), 16 * PZ);
         // Q of token tile t: per quad, or (chunks with extreme decays) per entry
         auto q_tile = [&](auto per_entry, int t) {
             const int tq = 16 * t + ln;  // this lane's token as a Q row
@@ -705,6 +696,12 @@ __global__ __launch_bounds__(kPmNT) __attribute__((amdgpu_waves_per_eu(NS <= 128
             for (int e = 0; e < 8; ++e)
                 xw[e] = wj[e] * xf[e];
             const float ws = tot_all[cs];
+            // B^T operand reads straight from the row-major B tile: this lane
+            // addresses token row 4 qg + ln / 4 at columns 16 nt + 4 (ln % 4)
+            // (rows 8-15 of each 16 with their 8-byte halves swapped; the
+            // swap is the same for row + 16)
+            const int trow = 4 * qg + (ln >> 2);
+            const unsigned char *btr = Bs + trow * PC + ((8 * (ln & 3)) ^ pm_swz(trow));
             if constexpr (BCH) {
                 // X' scaled per row into two fp16 parts; the product, unscaled,
                 // is added to the decayed state
@@ -718,7 +715,7 @@ __global__ __launch_bounds__(kPmNT) __attribute__((amdgpu_waves_per_eu(NS <= 128
                 pm_split_f16(xw, xsc, xh);
 #pragma unroll
                 for (int nt = 0; nt < NT16; ++nt) {
-                    const u32x4 bt = pm_op(Bt + (16 * nt + ln) * PT + (4 * qg) * 2);
+                    const u32x4 bt = pm_op_tr(btr + 32 * nt, 16 * PC);
                     pm_f32x4 pr = pm_mfma<_Float16>(bt, xh[0], pm_f32x4{0.0f, 0.0f, 0.0f, 0.0f});
                     pr = pm_mfma<_Float16>(bt, xh[1], pr);
 #pragma unroll
@@ -730,7 +727,7 @@ __global__ __launch_bounds__(kPmNT) __attribute__((amdgpu_waves_per_eu(NS <= 128
                 pm_split<3>(xw, xp);
 #pragma unroll
                 for (int nt = 0; nt < NT16; ++nt) {
-                    const u32x4 bt = pm_op(Bt + (16 * nt + ln) * PT + (4 * qg) * 2);
+                    const u32x4 bt = pm_op_tr(btr + 32 * nt, 16 * PC);
 #pragma unroll
                     for (int v = 0; v < 4; ++v)
                         S[nt][v] *= ws;
