@@ -58,14 +58,18 @@ constexpr int kPmSeg = 16;  // chunks whose decay tables are formed together
 struct PmLds {
     int cs, bs, xs, zs, ys, lc, rd, sf, tot, big, sb, total;
 };
-// C, B rows: a pitch of 16 bytes past whole 128-byte lines keeps the 16-byte
-// row stores aligned; rows 8-15 of each 16 swap the 8-byte halves of every
-// 16-byte block (pm_swz), so that the 16 rows an operand read touches at once
-// fall in 16 different 8-byte bank pairs of the 32 4-byte LDS banks.
-__host__ __device__ constexpr int pm_row_pitch(int NS) { return NS * 2 + 16; }
-__device__ __forceinline__ int pm_swz(int row) { return ((row >> 3) & 1) * 8; }
+// C, B rows: a pitch of 32 bytes past whole 64-byte runs puts consecutive rows
+// 8 banks apart (of the 32 4-byte LDS banks), so the four rows a transposed
+// read takes per 16 lanes (32 bytes each) cover all 32 banks; row r permutes
+// the four 8-byte slots of every 32-byte block by XOR with 8 ((r / 4) % 4)
+// (pm_swz), so that the 16 rows a row-major operand read touches at once (8
+// bytes each, one column) fall in 16 different bank pairs as well. A 16-byte
+// row store stays one 16-byte store, its halves swapped for odd r / 4.
+__host__ __device__ constexpr int pm_row_pitch(int NS) { return NS * 2 + 32; }
+__device__ __forceinline__ int pm_swz(int row) { return ((row >> 2) & 3) * 8; }
 __host__ __device__ constexpr int pm_y_pitch() { return 64 * 4 + 16; }            // fp32 outputs
-__host__ __device__ constexpr int pm_z_pitch() { return 64 * 2 + 16; }            // x, z rows
+__host__ __device__ constexpr int pm_z_pitch() { return 64 * 2 + 16; }            // z rows
+__host__ __device__ constexpr int pm_x_pitch() { return 64 * 2 + 32; }            // x rows (8 banks apart)
 __host__ __device__ inline PmLds pm_lds(int NS)
 {
     PmLds L;
@@ -73,7 +77,7 @@ __host__ __device__ inline PmLds pm_lds(int NS)
     auto take = [&o](int bytes) { const int r = o; o += (bytes + 15) & ~15; return r; };
     L.cs = take(kPmTT * pm_row_pitch(NS));   // C of the chunk [t][n]
     L.bs = take(kPmTT * pm_row_pitch(NS));   // B of the chunk [j][n]
-    L.xs = take(kPmTT * pm_z_pitch());       // x [j][row]
+    L.xs = take(kPmTT * pm_x_pitch());       // x [j][row]
     L.zs = take(kPmTT * pm_z_pitch());       // z [t][row]
     L.ys = take(kPmTT * pm_y_pitch());       // outputs before the gate [t][row], fp32
     // decay tables of kPmSeg chunks, [chunk][token]
@@ -245,7 +249,7 @@ __global__ __launch_bounds__(kPmNT) __attribute__((amdgpu_waves_per_eu(NS <= 128
     constexpr int NT = kPmNT;
     constexpr int KN = NS / 32;          // k-steps over dstate
     constexpr int NT16 = NS / 16;        // dstate tiles of the state
-    constexpr int PC = pm_row_pitch(NS), PY = pm_y_pitch(), PZ = pm_z_pitch();
+    constexpr int PC = pm_row_pitch(NS), PY = pm_y_pitch(), PZ = pm_z_pitch(), PX = pm_x_pitch();
     constexpr int NCB = NS / 8;                      // 16-byte column blocks of a B (C) row
     constexpr int NVP = (16 * NCB + NT - 1) / NT;    // token pairs x column blocks per thread
     static_assert(NS % 32 == 0, "dstate in whole 32-column steps");
@@ -387,16 +391,16 @@ __global__ __launch_bounds__(kPmNT) __attribute__((amdgpu_waves_per_eu(NS <= 128
                 for (int q = 0; q < 2; ++q) {
                     const int row = 2 * p + q;
                     const u32x4 b = rB[k][q], c = rC[k][q];
-                    const bool sw = pm_swz(row) != 0;  // the block's 8-byte halves swapped
-                    *reinterpret_cast<u32x4 *>(Bs + row * PC + col * 2) =
-                        sw ? u32x4{b[2], b[3], b[0], b[1]} : b;
-                    *reinterpret_cast<u32x4 *>(Cs + row * PC + col * 2) =
-                        sw ? u32x4{c[2], c[3], c[0], c[1]} : c;
+                    const int sz = pm_swz(row);
+                    const bool sw = (sz & 8) != 0;  // the block's 8-byte halves swapped
+                    const int o = row * PC + ((col * 2) ^ (sz & 16));
+                    *reinterpret_cast<u32x4 *>(Bs + o) = sw ? u32x4{b[2], b[3], b[0], b[1]} : b;
+                    *reinterpret_cast<u32x4 *>(Cs + o) = sw ? u32x4{c[2], c[3], c[0], c[1]} : c;
                 }
             }
         }
         // x past the context or beyond dim as zeros (their loads were clamped)
-        *reinterpret_cast<u32x4 *>(Xs + xtok * PZ + xr8 * 2) = xtok < nv && xrv ? rX : u32x4{0u, 0u, 0u, 0u};
+        *reinterpret_cast<u32x4 *>(Xs + xtok * PX + xr8 * 2) = xtok < nv && xrv ? rX : u32x4{0u, 0u, 0u, 0u};
         *reinterpret_cast<u32x4 *>(Zs + xtok * PZ + xr8 * 2) = rZ;
     };
     // The stash stores of the staged chunk (B and x as fp32), issued after every
@@ -613,7 +617,7 @@ __global__ __launch_bounds__(kPmNT) __attribute__((amdgpu_waves_per_eu(NS <= 128
         // x^T operand in the same source order, lane (row rl, qg), read
         // transposed from the row-major x tile: this lane addresses token row
         // 4 qg + ln / 4 at rows 16 wave + 4 (ln % 4) ..+3
-        const u32x4 xop = pm_op_tr(Xs + (4 * qg + (ln >> 2)) * PZ + 32 * wave + 8 * (ln & 3), 16 * PZ);
+        const u32x4 xop = pm_op_tr(Xs + (4 * qg + (ln >> 2)) * PX + 32 * wave + 8 * (ln & 3), 16 * PX);
         // Q of token tile t: per quad, or (chunks with extreme decays) per entry
         auto q_tile = [&](auto per_entry, int t) {
             const int tq = 16 * t + ln;  // this lane's token as a Q row
@@ -698,8 +702,7 @@ __global__ __launch_bounds__(kPmNT) __attribute__((amdgpu_waves_per_eu(NS <= 128
             const float ws = tot_all[cs];
             // B^T operand reads straight from the row-major B tile: this lane
             // addresses token row 4 qg + ln / 4 at columns 16 nt + 4 (ln % 4)
-            // (rows 8-15 of each 16 with their 8-byte halves swapped; the
-            // swap is the same for row + 16)
+            // (the row's slot permutation is the same for row + 16)
             const int trow = 4 * qg + (ln >> 2);
             const unsigned char *btr = Bs + trow * PC + ((8 * (ln & 3)) ^ pm_swz(trow));
             if constexpr (BCH) {
