@@ -13,7 +13,8 @@
 //    D k channels and the D v channels of its G = HV/Hq value heads), so each
 //    conv-state channel is read, shifted and written by exactly one thread;
 //    it also takes the q/k L2 norms and writes q*scale/|q|, k/|k| and v to the
-//    workspace. The remaining workgroups, one per (b, chunk of 256 hidden
+//    workspace (at width 4 on a dense channel-major pool a thread takes two
+//    adjacent channels as 32-bit words). The remaining workgroups, one per (b, chunk of 256 hidden
 //    rows), compute partial sums of the b/a projection (hidden x 2HV) over
 //    their rows, reading the weight in whole rows (it is [hidden, 2HV]
 //    row-major: a per-head column slice would touch a cache line per row for
@@ -62,20 +63,27 @@ __host__ __device__ inline int64_t ws_p_off(int64_t B, int64_t hq, int64_t hv, i
 // 16- or 4-byte load per row) and row phase rp = t / NCH; the partial sums are
 // combined over the row phases through LDS and written per chunk.
 // ---------------------------------------------------------------------------
+// CWC bf16 weights of one row as raw words (loaded), then as floats
 template <int CWC>
-__device__ __forceinline__ void proj_row(const uint16_t *p, float (&w)[CWC])
+__device__ __forceinline__ void proj_load(const uint16_t *p, uint32_t (&v)[CWC / 2])
 {
     if constexpr (CWC == 8) {
-        const u32x4 v = *reinterpret_cast<const u32x4 *>(p);
+        const u32x4 q = *reinterpret_cast<const u32x4 *>(p);
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
-            w[2 * j] = __uint_as_float(v[j] << 16);
-            w[2 * j + 1] = __uint_as_float(v[j] & 0xFFFF0000u);
-        }
+        for (int j = 0; j < 4; ++j)
+            v[j] = q[j];
     } else {
-        const uint32_t v = *reinterpret_cast<const uint32_t *>(p);
-        w[0] = __uint_as_float(v << 16);
-        w[1] = __uint_as_float(v & 0xFFFF0000u);
+        v[0] = *reinterpret_cast<const uint32_t *>(p);
+    }
+}
+
+template <int CWC>
+__device__ __forceinline__ void proj_cvt(const uint32_t (&v)[CWC / 2], float (&w)[CWC])
+{
+#pragma unroll
+    for (int j = 0; j < CWC / 2; ++j) {
+        w[2 * j] = __uint_as_float(v[j] << 16);
+        w[2 * j + 1] = __uint_as_float(v[j] & 0xFFFF0000u);
     }
 }
 
@@ -96,27 +104,37 @@ __device__ void gdn_projection(int b, int ck, const uint16_t *__restrict__ hs,
     const int cn = min(kProjRows, sh.hidden - r0);
     float *hid = lds;                // this chunk's hidden values
     float *part = lds + kProjRows;   // [RPH][NC] partial sums
+    const uint16_t *wb = w_ba + (int64_t)r0 * NC + cc * CWC;
+    // the first U weight rows are loaded before the hidden values are staged
+    // (they do not depend on them), so both loads are in flight together
+    uint32_t wr[U][CWC / 2];
+    auto load_rows = [&](int ra) {
+#pragma unroll
+        for (int u = 0; u < U; ++u)
+            proj_load<CWC>(wb + (int64_t)min(ra + u * RPH, cn - 1) * NC, wr[u]);
+    };
+    const uint16_t hval = hs[(int64_t)b * sh.hidden + r0 + min(tid, cn - 1)];
+    load_rows(rp);  // rows clamped: in bounds for every thread
     if (tid < cn)
-        hid[tid] = bf16_to_f32(hs[(int64_t)b * sh.hidden + r0 + tid]);
+        hid[tid] = bf16_to_f32(hval);
     float acc[CWC];
 #pragma unroll
     for (int j = 0; j < CWC; ++j)
         acc[j] = 0.0f;
-    const uint16_t *wb = w_ba + (int64_t)r0 * NC + cc * CWC;
     __syncthreads();
     if (active) {
         for (int ra = rp; ra < cn; ra += U * RPH) {
-            float w[U][CWC];
-#pragma unroll
-            for (int u = 0; u < U; ++u)
-                proj_row<CWC>(wb + (int64_t)min(ra + u * RPH, cn - 1) * NC, w[u]);
+            if (ra != rp)
+                load_rows(ra);
 #pragma unroll
             for (int u = 0; u < U; ++u) {
                 const int r = ra + u * RPH;
                 const float x = r < cn ? hid[r] : 0.0f;
+                float w[CWC];
+                proj_cvt<CWC>(wr[u], w);
 #pragma unroll
                 for (int j = 0; j < CWC; ++j)
-                    acc[j] = fmaf(x, w[u][j], acc[j]);
+                    acc[j] = fmaf(x, w[j], acc[j]);
             }
         }
 #pragma unroll
@@ -233,7 +251,110 @@ __device__ void gdn_conv(int b, int h, const uint16_t *__restrict__ mixed_qkv,
     }
 }
 
-template <int D, int GM, int WM>
+// The conv role for width 4 on a dense channel-major pool ([slot][channel][3
+// taps], 16-bit words 4-byte aligned): thread t takes channel pairs (2 jp,
+// 2 jp + 1), jp = t + NT k. A pair's three taps each are six consecutive
+// 16-bit values (three 32-bit words), its weights eight (four words), its bias
+// and input two (one word each), so a thread moves its pair in six vector
+// accesses where the per-channel path takes 24 16-bit ones. Same arithmetic,
+// in the same order, as gdn_conv.
+template <int D, int GM>
+__device__ void gdn_conv_pairs(int b, int h, const uint16_t *__restrict__ mixed_qkv,
+                               const uint16_t *__restrict__ conv_w, const uint16_t *__restrict__ conv_b,
+                               uint16_t *__restrict__ conv_state, int s, float *__restrict__ ws,
+                               const GdnPrepShape &sh, float *lds)
+{
+    constexpr int NT = kGdnNT;
+    constexpr int G = GM;
+    constexpr int NPR = (2 + G) * D / 2;      // owned channel pairs (D is even)
+    constexpr int PPT = (NPR + NT - 1) / NT;  // pairs per thread
+    const int tid = threadIdx.x;
+    const int lane = tid & 63, wave = tid >> 6;
+    const int Hq = sh.hq, HV = sh.hv;
+    const int hv0 = h * G;
+    const int HD = Hq * D;
+    const int64_t qkv_dim = 2 * (int64_t)HD + (int64_t)HV * D;
+    // owned channel j (even) -> pool channel; a pair never straddles the q, k, v runs
+    auto chan = [&](int j) {
+        return j < D ? h * D + j : (j < 2 * D ? HD + h * D + (j - D) : 2 * HD + hv0 * D + (j - 2 * D));
+    };
+    uint32_t tw[PPT][3], ww[PPT][4], bw[PPT], xw[PPT];
+#pragma unroll
+    for (int k = 0; k < PPT; ++k) {
+        const int c = chan(2 * min(tid + NT * k, NPR - 1));
+        const uint32_t *cs = reinterpret_cast<const uint32_t *>(conv_state + (int64_t)s * sh.cs_slot + (int64_t)c * 3);
+        const uint32_t *cw = reinterpret_cast<const uint32_t *>(conv_w + (int64_t)c * 4);
+#pragma unroll
+        for (int i = 0; i < 3; ++i)
+            tw[k][i] = cs[i];
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+            ww[k][i] = cw[i];
+        bw[k] = *reinterpret_cast<const uint32_t *>(conv_b + c);
+        xw[k] = *reinterpret_cast<const uint32_t *>(mixed_qkv + b * qkv_dim + c);
+    }
+    auto lo = [](uint32_t w) { return __uint_as_float(w << 16); };
+    auto hi = [](uint32_t w) { return __uint_as_float(w & 0xFFFF0000u); };
+    float y[PPT][2];
+    float ssq = 0.0f, ssk = 0.0f;
+#pragma unroll
+    for (int k = 0; k < PPT; ++k) {
+        const int j = 2 * (tid + NT * k);
+        // taps: (c0 t0, c0 t1), (c0 t2, c1 t0), (c1 t1, c1 t2); weights
+        // (c0 w0, c0 w1), (c0 w2, c0 w3), (c1 w0, c1 w1), (c1 w2, c1 w3)
+        float a0 = lo(bw[k]);
+        a0 = fmaf(lo(tw[k][0]), lo(ww[k][0]), a0);
+        a0 = fmaf(hi(tw[k][0]), hi(ww[k][0]), a0);
+        a0 = fmaf(lo(tw[k][1]), lo(ww[k][1]), a0);
+        a0 = fmaf(lo(xw[k]), hi(ww[k][1]), a0);
+        float a1 = hi(bw[k]);
+        a1 = fmaf(hi(tw[k][1]), lo(ww[k][2]), a1);
+        a1 = fmaf(lo(tw[k][2]), hi(ww[k][2]), a1);
+        a1 = fmaf(hi(tw[k][2]), lo(ww[k][3]), a1);
+        a1 = fmaf(hi(xw[k]), hi(ww[k][3]), a1);
+        y[k][0] = silu_f32(a0);
+        y[k][1] = silu_f32(a1);
+        if (j < 2 * NPR) {
+            // the pool keeps the last 3 raw inputs, newest last: (c0 t1, c0 t2),
+            // (c0 x, c1 t1), (c1 t2, c1 x)
+            uint32_t *cs = reinterpret_cast<uint32_t *>(conv_state + (int64_t)s * sh.cs_slot + (int64_t)chan(j) * 3);
+            cs[0] = __builtin_amdgcn_perm(tw[k][1], tw[k][0], 0x05040302u);
+            cs[1] = __builtin_amdgcn_perm(tw[k][2], xw[k], 0x05040100u);
+            cs[2] = __builtin_amdgcn_perm(xw[k], tw[k][2], 0x07060302u);
+            const float y2 = y[k][0] * y[k][0] + y[k][1] * y[k][1];
+            ssq += j < D ? y2 : 0.0f;
+            ssk += (j >= D && j < 2 * D) ? y2 : 0.0f;
+        }
+    }
+    const float wq = wave_sum(ssq), wk = wave_sum(ssk);
+    if (lane == 0) {
+        lds[2 * wave] = wq;
+        lds[2 * wave + 1] = wk;
+    }
+    __syncthreads();
+    const float sq = (lds[0] + lds[2]) + (lds[4] + lds[6]);
+    const float sk = (lds[1] + lds[3]) + (lds[5] + lds[7]);
+    const float iq = (sh.use_l2 ? 1.0f / sqrtf(sq + 1e-6f) : 1.0f) * sh.scale;
+    const float ik = sh.use_l2 ? 1.0f / sqrtf(sk + 1e-6f) : 1.0f;
+    float *qk = ws + ((int64_t)b * Hq + h) * 2 * D;
+    float *vv = ws + ws_v_off(sh.batch, Hq, D) + ((int64_t)b * HV + hv0) * D;
+#pragma unroll
+    for (int k = 0; k < PPT; ++k) {
+        const int j = 2 * (tid + NT * k);
+        if (j < D) {
+            qk[j] = y[k][0] * iq;
+            qk[j + 1] = y[k][1] * iq;
+        } else if (j < 2 * D) {
+            qk[j] = y[k][0] * ik;
+            qk[j + 1] = y[k][1] * ik;
+        } else if (j < 2 * NPR) {
+            vv[j - 2 * D] = y[k][0];
+            vv[j - 2 * D + 1] = y[k][1];
+        }
+    }
+}
+
+template <int D, int GM, int WM, bool PAIRS>
 __global__ __launch_bounds__(kGdnNT) void gdn_prep_kernel(
     const uint16_t *__restrict__ hs, const uint16_t *__restrict__ w_ba,
     const uint16_t *__restrict__ mixed_qkv, const uint16_t *__restrict__ conv_w,
@@ -260,7 +381,10 @@ __global__ __launch_bounds__(kGdnNT) void gdn_prep_kernel(
     const int s = idx[b];
     if (s < 0)  // padding entry: no pool access; the stream writes its zero output
         return;
-    gdn_conv<D, GM, WM>(b, h, mixed_qkv, conv_w, conv_b, conv_state, s, ws, sh, lds);
+    if constexpr (PAIRS)
+        gdn_conv_pairs<D, GM>(b, h, mixed_qkv, conv_w, conv_b, conv_state, s, ws, sh, lds);
+    else
+        gdn_conv<D, GM, WM>(b, h, mixed_qkv, conv_w, conv_b, conv_state, s, ws, sh, lds);
 }
 
 // ---------------------------------------------------------------------------
@@ -424,13 +548,13 @@ __global__ __launch_bounds__(kGdnNT) void gdn_stream_kernel(
     }
 }
 
-template <int D, int GM, int WM>
+template <int D, int GM, int WM, bool PAIRS = false>
 hipError_t launch_prep(const GdnParams &p, const GdnPrepShape &sh, hipStream_t stream)
 {
     const int64_t blocks = (int64_t)p.batch * p.hq + (int64_t)p.batch * sh.nck;
     if (blocks > 0x7fffffff)
         return hipErrorInvalidConfiguration;
-    hipLaunchKernelGGL((gdn_prep_kernel<D, GM, WM>), dim3((unsigned)blocks), dim3(kGdnNT), 0,
+    hipLaunchKernelGGL((gdn_prep_kernel<D, GM, WM, PAIRS>), dim3((unsigned)blocks), dim3(kGdnNT), 0,
                        stream, static_cast<const uint16_t *>(p.hs),
                        static_cast<const uint16_t *>(p.w_ba), static_cast<const uint16_t *>(p.qkv),
                        static_cast<const uint16_t *>(p.conv_w),
@@ -445,6 +569,10 @@ hipError_t launch_prep_g(const GdnParams &p, const GdnPrepShape &sh, hipStream_t
 {
     if (p.width == 1)
         return launch_prep<D, GM, 1>(p, sh, stream);
+    auto al4 = [](const void *q) { return (reinterpret_cast<uintptr_t>(q) & 3) == 0; };
+    if (p.width == 4 && p.cs_tap == 1 && p.cs_chan == 3 && p.cs_slot % 2 == 0 && al4(p.conv_state) &&
+        al4(p.conv_w) && al4(p.conv_b) && al4(p.qkv))
+        return launch_prep<D, GM, 4, true>(p, sh, stream);
     return p.width <= 4 ? launch_prep<D, GM, 4>(p, sh, stream) : launch_prep<D, GM, 8>(p, sh, stream);
 }
 

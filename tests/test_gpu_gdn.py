@@ -101,6 +101,25 @@ def test_sd_layout_padding_and_options():
     check_gdn(w)
 
 
+def test_width4_dense_pool_off_word_alignment():
+    # a dense width-4 pool whose taps are not 4-byte aligned takes the per-channel
+    # conv path (aligned ones move channel pairs as 32-bit words)
+    w = inputs.gdn_workload(batch=3, hidden=64, num_q_heads=2, num_v_heads=4, head_dim=64,
+                            conv_width=4, pool_rows=4, seed=15, indices=[2, -1, 0])
+    cs = w["conv_state"]
+    flat = torch.empty(cs.numel() + 1, dtype=cs.dtype, device="cuda")
+    view = flat[1:].view(cs.shape)
+    view.copy_(cs.cuda())
+    out, csg, st = run_gdn(w, conv_state=view)
+    out_r, cs_r, st_r = oracle_gdn(w)
+    idx = w["state_indices"].numpy()
+    live = idx >= 0
+    assert_close(out.cpu()[torch.from_numpy(live)], out_r[live], TOL_LOW, "out (live entries)")
+    assert_close(st.cpu()[idx[live]], st_r[idx[live]], TOL_F32, "ssm_state")
+    assert_bitwise(csg.cpu().contiguous(), torch.from_numpy(cs_r).to(torch.bfloat16).contiguous(),
+                   "conv_state")
+
+
 def test_padded_ssm_row_stride():
     w = inputs.gdn_workload(batch=3, hidden=64, num_q_heads=1, num_v_heads=2, head_dim=64,
                             conv_width=4, pool_rows=4, seed=13)
