@@ -496,7 +496,7 @@ def main():
         src = source_hash("ssu_prefill_impl.h", "ssu_prefill_mm.h", "ssu_rowblock.h", "ssu_device.h",
                           "ssu_dpp.h")
         kkey = "prefill_config2"
-        if args.operands != "bf16" or args.stash:  # no counters are kept for these variants
+        if args.operands != "bf16" or args.stash:  # each variant has its own counter record
             kkey += f"_{args.operands}" + ("_stash" if args.stash else "")
         if args.operands != "f32":
             matrix = {"flops_per_step": prefill_method_flops(T, L),
