@@ -20,11 +20,11 @@
 //   S^T  = e^{Lc[last]} S^T + B^T . X'^T   (X'[r][j] = w_j x_j[r], w_j the
 //                              suffix weight; X' as three bf16 terms, so the
 //                              carried fp32 state keeps fp32 accuracy)
-// With fp16 operands every product runs on v_mfma_f32_16x16x32_f16: B . C^T
-// as it is; C . S^T, B^T . X'^T and Q . X^T with S and X' scaled per row, Q per
-// 16-token tile, by the power of two that puts the largest magnitude in
-// [2^14, 2^15), then cut into two fp16 parts, the scale undone on the fp32
-// result.
+// With fp16 operands B . C^T runs on v_mfma_f32_16x16x32_f16 as it is, and
+// C . S^T and B^T . X'^T with S and X' scaled per row, by the power of two that
+// puts the largest magnitude in [2^14, 2^15), then cut into two fp16 parts, the
+// scale undone on the fp32 result; Q . X^T (32 sources) runs on
+// v_mfma_f32_16x16x4_f32 with Q as formed and x exact in fp32.
 // The state never leaves registers: each lane holds S[r][16 nt + 4 qg + v],
 // the accumulator layout of the last product, and the inter-chunk product
 // takes it as its B operand directly by ordering the dstate index of the
@@ -178,16 +178,6 @@ __device__ __forceinline__ float pm_row_max(float m)
     return fmaxf(__uint_as_float(b[0]), __uint_as_float(b[1]));
 }
 
-// The largest of m over the 64 lanes of a wave
-__device__ __forceinline__ float pm_wave_max(float m)
-{
-    m = pm_row_max(m);                   // the four rows of 16
-    m = fmaxf(m, dpp_f32<0xB1>(m));      // quad_perm [1,0,3,2]
-    m = fmaxf(m, dpp_f32<0x4E>(m));      // quad_perm [2,3,0,1]
-    m = fmaxf(m, dpp_f32<0x141>(m));     // row_half_mirror
-    return fmaxf(m, dpp_f32<0x140>(m));  // row_mirror
-}
-
 // The power of two 2^k that puts a row's largest magnitude m in [2^14, 2^15)
 // (k clamped to the normal range; m = 0 gives 2^15), and its inverse
 __device__ __forceinline__ void pm_row_scale(float m, float &sc, float &inv)
@@ -254,7 +244,7 @@ __global__ __launch_bounds__(kPmNT) __attribute__((amdgpu_waves_per_eu(NS <= 128
     constexpr int NVP = (16 * NCB + NT - 1) / NT;    // token pairs x column blocks per thread
     static_assert(NS % 32 == 0, "dstate in whole 32-column steps");
     constexpr bool BCH = __is_same(BCT, _Float16);  // fp16 B/C: scaled fp16 parts of S and X'
-    constexpr bool IOH = __is_same(IOT, _Float16);  // fp16 x: Q . X^T on fp16, Q in scaled parts
+    constexpr bool IOH = __is_same(IOT, _Float16);  // fp16 x: Q . X^T on the fp32 matrix cores
 
     extern __shared__ __attribute__((aligned(16))) unsigned char lds[];
     const PmLds L = pm_lds(NS);
@@ -618,6 +608,9 @@ __global__ __launch_bounds__(kPmNT) __attribute__((amdgpu_waves_per_eu(NS <= 128
         // transposed from the row-major x tile: this lane addresses token row
         // 4 qg + ln / 4 at rows 16 wave + 4 (ln % 4) ..+3
         const u32x4 xop = pm_op_tr(Xs + (4 * qg + (ln >> 2)) * PX + 32 * wave + 8 * (ln & 3), 16 * PX);
+        float xf[8];  // the same x in fp32 (fp16 x: before the Q tiles, which use it)
+        if constexpr (IOH)
+            pm_to_f32x8<IOT>(xop, xf);
         // Q of token tile t: per quad, or (chunks with extreme decays) per entry
         auto q_tile = [&](auto per_entry, int t) {
             const int tq = 16 * t + ln;  // this lane's token as a Q row
@@ -641,21 +634,14 @@ __global__ __launch_bounds__(kPmNT) __attribute__((amdgpu_waves_per_eu(NS <= 128
                 qv[e] = q;
             }
             if constexpr (IOH) {
-                // fp16 x as it is; Q scaled per tile into two fp16 parts, the
-                // product unscaled into the output
-                float m = 0.0f;
+                // fp16 x: on the fp32 matrix cores, Q as formed and x exact in
+                // fp32, one 4-source step per element (lane group qg holds
+                // source 4qg + e, resp. 16 + 4qg + e - 4, in both operands);
+                // sources 16.. are past every token of tile 0
 #pragma unroll
                 for (int e = 0; e < 8; ++e)
-                    m = fmaxf(m, fabsf(qv[e]));
-                float qsc, qinv;
-                pm_row_scale(pm_wave_max(m), qsc, qinv);
-                u32x4 qh[2];
-                pm_split_f16(qv, qsc, qh);
-                pm_f32x4 pq = pm_mfma<_Float16>(qh[0], xop, pm_f32x4{0.0f, 0.0f, 0.0f, 0.0f});
-                pq = pm_mfma<_Float16>(qh[1], xop, pq);
-#pragma unroll
-                for (int v = 0; v < 4; ++v)
-                    ay[t][v] = fmaf(pq[v], qinv, ay[t][v]);
+                    if (t == 1 || e < 4)
+                        ay[t] = __builtin_amdgcn_mfma_f32_16x16x4f32(qv[e], xf[e], ay[t], 0, 0, 0);
             } else {
                 pm_bf16x8 qp[2];
                 pm_split<2>(qv, qp);
@@ -675,8 +661,8 @@ __global__ __launch_bounds__(kPmNT) __attribute__((amdgpu_waves_per_eu(NS <= 128
         }
         // D x_t in fp32: the x^T operand holds x of tokens 4qg + v (elements
         // 0-3) and 16 + 4qg + v (4-7) of row rl, the tokens of ay[0][v], ay[1][v]
-        float xf[8];
-        pm_to_f32x8<IOT>(xop, xf);
+        if constexpr (!IOH)
+            pm_to_f32x8<IOT>(xop, xf);
 #pragma unroll
         for (int v = 0; v < 4; ++v) {
             ay[0][v] = fmaf(dskip, xf[v], ay[0][v]);
